@@ -1,0 +1,165 @@
+"""Reference block manager (integers only; the GPU library must match it bit for bit).
+
+What the pages fix:
+
+* KV is split into fixed-size blocks; each request keeps a block table from
+  logical block index to physical block, and blocks are handed out on demand
+  as tokens accumulate (youngju.dev "KV cache and paged attention", section
+  "PagedAttention: OS 가상 메모리식 관리"; opsoai "vLLM PagedAttention은 KV
+  캐시를 어떻게 관리할까", section "PagedAttention은 논리 블록과 물리 블록을
+  분리한다"; iq-blog ch.4, sections "OS Paging에서 가져온 해법" and
+  "PagedAttention 알고리즘").
+* Free blocks live in a free list / free queue, and an allocation is given up
+  when not enough free blocks remain (openakashic KV-cache failure-modes note,
+  Key Points; iq-blog ch.4, "OS Paging에서 가져온 해법").
+* Sequences with a common prefix point at the same physical blocks with a
+  reference count; a shared block is copied at the moment one sharer writes
+  into it (copy-on-write) (youngju.dev page, section "prefix 공유와
+  copy-on-write"; iq-blog ch.4, "Prefix Caching").
+
+Readings where the pages are silent (each also listed in the design notes):
+
+* The free queue is FIFO; its initial order is the caller's permutation (or
+  0..N-1).  Allocation pops from the head.  When a sequence is freed, its
+  blocks are visited last-to-first and every block whose count drops to zero
+  is pushed to the tail.
+* An append that needs more blocks than are free fails with no state change;
+  the block a copy-on-write needs counts toward the requirement.
+* Copy-on-write triggers only when the append lands in a partly filled last
+  block whose count exceeds one; the appending sequence receives the copy.
+* Sequence ids are 0, 1, 2, ... in creation order and are never reused.
+"""
+from __future__ import annotations
+
+from collections import deque
+
+
+class NoBlocks(Exception):
+    """Raised when an append needs more free blocks than the pool holds."""
+
+
+class BadSeq(Exception):
+    """Raised for an unknown or already-freed sequence id."""
+
+
+class OracleAllocator:
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        order = list(range(self.num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(self.num_blocks)):
+            raise ValueError("free_order must be a permutation of range(num_blocks)")
+        self.free = deque(order)
+        self.ref = [0] * self.num_blocks
+        self.tables = {}  # seq id -> list of physical block ids
+        self.lens = {}  # seq id -> number of tokens
+        self.next_id = 0
+        self.cow_log = []  # (src, dst) in the order they happened
+        self.failures = 0
+
+    # -- sequence lifecycle ------------------------------------------------
+    def seq_create(self) -> int:
+        sid = self.next_id
+        self.next_id += 1
+        self.tables[sid] = []
+        self.lens[sid] = 0
+        return sid
+
+    def _check(self, sid):
+        if sid not in self.tables:
+            raise BadSeq(sid)
+
+    def alloc(self, sid: int, n: int):
+        """Append ``n`` tokens to ``sid``; return (slots, cow) where cow is (src, dst) or None.
+
+        Slot of logical token t is table[t // B] * B + t % B (the block table maps
+        the logical block to its physical block; the offset within the block is kept).
+        """
+        self._check(sid)
+        if n < 0:
+            raise ValueError("n must be >= 0")
+        bs = self.block_size
+        table = self.tables[sid]
+        length = self.lens[sid]
+        need = -(-(length + n) // bs) - len(table)
+        cow = n > 0 and length % bs != 0 and self.ref[table[-1]] > 1
+        if need + int(cow) > len(self.free):
+            self.failures += 1
+            raise NoBlocks(sid)
+        cow_pair = None
+        if cow:
+            old = table[-1]
+            new = self.free.popleft()
+            self.ref[new] = 1
+            self.ref[old] -= 1
+            table[-1] = new
+            cow_pair = (old, new)
+            self.cow_log.append(cow_pair)
+        for _ in range(need):
+            b = self.free.popleft()
+            self.ref[b] = 1
+            table.append(b)
+        slots = [table[(length + j) // bs] * bs + (length + j) % bs for j in range(n)]
+        self.lens[sid] = length + n
+        return slots, cow_pair
+
+    def fork(self, parent: int) -> int:
+        """New sequence sharing every block of ``parent`` (each count +1)."""
+        self._check(parent)
+        sid = self.seq_create()
+        self.tables[sid] = list(self.tables[parent])
+        self.lens[sid] = self.lens[parent]
+        for b in self.tables[sid]:
+            self.ref[b] += 1
+        return sid
+
+    def free_seq(self, sid: int) -> None:
+        """Drop ``sid``; blocks whose count reaches zero go to the free-queue tail."""
+        self._check(sid)
+        for b in reversed(self.tables[sid]):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.tables[sid]
+        del self.lens[sid]
+
+    # -- views ---------------------------------------------------------------
+    def block_tables(self, seqs, max_blocks: int):
+        """Rows of physical ids padded with -1, and the lengths."""
+        rows, lens = [], []
+        for s in seqs:
+            self._check(s)
+            t = self.tables[s]
+            if len(t) > max_blocks:
+                raise ValueError("table longer than max_blocks")
+            rows.append(t + [-1] * (max_blocks - len(t)))
+            lens.append(self.lens[s])
+        return rows, lens
+
+    def stats(self):
+        used = sum(1 for r in self.ref if r > 0)
+        shared = sum(1 for r in self.ref if r > 1)
+        return {
+            "num_blocks": self.num_blocks,
+            "free_blocks": len(self.free),
+            "used_blocks": used,
+            "shared_blocks": shared,
+            "num_seqs": len(self.tables),
+            "cow_copies": len(self.cow_log),
+            "alloc_failures": self.failures,
+        }
+
+    def check_invariants(self) -> None:
+        """Structural invariants that must hold after every operation."""
+        total_refs = sum(self.ref)
+        total_entries = sum(len(t) for t in self.tables.values())
+        assert total_refs == total_entries, (total_refs, total_entries)
+        free_set = set(self.free)
+        assert len(free_set) == len(self.free), "duplicate block in free queue"
+        zero = {b for b, r in enumerate(self.ref) if r == 0}
+        assert zero == free_set, "free queue != blocks with zero references"
+        assert all(r >= 0 for r in self.ref)
+        bs = self.block_size
+        for s, t in self.tables.items():
+            assert len(t) == -(-self.lens[s] // bs), (s, len(t), self.lens[s])
+        assert len(self.free) + sum(1 for r in self.ref if r > 0) == self.num_blocks

@@ -1,0 +1,258 @@
+"""Pins of the oracle block manager: the page's worked block-table example,
+the pages' closed forms, content round trips through forks and copy-on-write,
+structural invariants under random operation sequences, atomic failure."""
+import copy
+import json
+import os
+
+import numpy as np
+import pytest
+from hypothesis import settings, strategies as st
+from hypothesis.stateful import RuleBasedStateMachine, invariant, precondition, rule
+
+from oracle import formulas
+from oracle.allocator import BadSeq, NoBlocks, OracleAllocator
+from oracle.kvstore import OracleKVStore
+from workloads import cb_prefix_script
+from workloads.configs import PAGE_EXAMPLE_FREE_ORDER
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_page_block_table_example():
+    g = _golden("block_table_example.json")
+    bs = g["block_size"]
+    a = OracleAllocator(8, bs, PAGE_EXAMPLE_FREE_ORDER)
+    req = {}
+    for r in g["requests"]:
+        s = a.seq_create()
+        slots, cow = a.alloc(s, r["tokens"])
+        assert cow is None
+        req[r["name"]] = (s, slots)
+        assert a.tables[s] == r["table"]
+    # 16 + 16 + 8 tokens in A's three blocks; only the last one is partly used.
+    sa, slots_a = req["A"]
+    per_block = [sum(1 for x in slots_a if x // bs == b) for b in a.tables[sa]]
+    assert per_block == g["requests"][0]["tokens_per_block"]
+    assert slots_a[39] == 5 * 16 + 7 and req["B"][1][19] == 2 * 16 + 3
+    a.check_invariants()
+    # Tail waste: 8 + 12 empty slots of 80 allocated, under the Theorem 1 bound 16 / 20.
+    waste = sum(formulas.tail_waste_tokens(r["tokens"], bs) for r in g["requests"])
+    assert waste == 20 and waste / 80 < formulas.paged_waste_bound(bs, 20)
+
+
+def test_slot_mapping_content_round_trip_through_fork_and_cow():
+    """Write each token's logical index into its slot and read every sequence
+    back contiguously through its table: must give 0..T-1 for every sequence."""
+    bs, nb = 8, 64
+    a = OracleAllocator(nb, bs, list(np.random.default_rng(3).permutation(nb)))
+    store = OracleKVStore(2, nb, 1, bs, 4)
+
+    def append(s, n):
+        start = a.lens[s]
+        slots, cow = a.alloc(s, n)
+        if cow:
+            store.copy_block(*cow)
+        vals = np.arange(start, start + n, dtype=np.float16)[:, None, None] * np.ones((1, 1, 4), np.float16)
+        for layer in range(2):
+            store.write(layer, vals + layer, vals + 1000 + layer, slots)
+
+    s0 = a.seq_create()
+    append(s0, 13)
+    s1 = a.fork(s0)
+    s2 = a.fork(s1)
+    append(s1, 5)   # copy-on-write of the shared partial block
+    append(s2, 20)  # again (still shared with s0)
+    append(s0, 3)   # s0 now owns its last block alone: no copy
+    s3 = a.fork(s2)
+    append(s3, 9)   # shared with s2: copied
+    a.free_seq(s2)
+    append(s3, 4)   # s3 is now the only holder: no copy
+    assert len(a.cow_log) == 3
+    for s in a.tables:
+        t = a.lens[s]
+        for layer in range(2):
+            ks, vs = [], []
+            for j, b in enumerate(a.tables[s]):
+                kb, vb = store.block_values(layer, b)
+                ks.append(kb[0, :, 0])
+                vs.append(vb[0, :, 0])
+            k = np.concatenate(ks)[:t]
+            v = np.concatenate(vs)[:t]
+            np.testing.assert_array_equal(k, np.arange(t) + layer)
+            np.testing.assert_array_equal(v, np.arange(t) + 1000 + layer)
+    a.check_invariants()
+
+
+def test_allocation_failure_is_atomic():
+    a = OracleAllocator(4, 16, [2, 0, 3, 1])
+    s = a.seq_create()
+    a.alloc(s, 40)  # 3 blocks
+    t = a.fork(s)
+    before = copy.deepcopy((list(a.free), a.ref, a.tables, a.lens))
+    with pytest.raises(NoBlocks):
+        a.alloc(t, 40)  # needs copy-on-write block + 2 new blocks, only 1 free
+    assert (list(a.free), a.ref, a.tables, a.lens) == before
+    assert a.stats()["alloc_failures"] == 1
+    a.alloc(t, 8)  # the copy only: fits
+    assert a.free == type(a.free)() and a.cow_log == [(a.tables[s][2], a.tables[t][2])]
+    with pytest.raises(BadSeq):
+        a.alloc(99, 1)
+
+
+def test_free_returns_blocks_to_tail_in_reverse_order():
+    a = OracleAllocator(6, 4, None)
+    s = a.seq_create()
+    a.alloc(s, 10)  # blocks 0, 1, 2
+    a.free_seq(s)
+    assert list(a.free) == [3, 4, 5, 2, 1, 0]
+
+
+def test_kv_memory_arithmetic_matches_page():
+    g = _golden("kv_memory_arithmetic.json")
+    per_tok = formulas.kv_bytes(g["layers"], g["kv_heads"], g["head_dim"], g["dtype_bytes"], 1)
+    assert per_tok == g["bytes_per_token_per_request"]
+    assert per_tok * g["request_tokens"] == g["bytes_per_request"]
+    assert per_tok * g["request_tokens"] * g["requests"] == g["bytes_for_all_requests"]
+
+
+def test_closed_forms_match_page_numbers():
+    g = _golden("closed_forms.json")
+    c = g["internal_fragmentation"]
+    assert formulas.internal_fragmentation(c["tokens"], c["max_tokens"]) * 100 == c["printed_percent"]
+    c = g["reservation_waste"]
+    assert abs(formulas.reservation_waste(c["used"], c["reserved"]) * 100 - c["printed_percent"]) <= c["printed_rounding"]
+    c = g["paged_waste_bound"]
+    assert abs(formulas.paged_waste_bound(c["block_size"], c["min_tokens"]) * 100 - c["printed_percent_upper"]) <= c["printed_rounding"]
+    c = g["shared_copy_savings"]
+    assert round(formulas.shared_copy_savings(c["requests"]) * 100, 9) == c["printed_percent"]
+    c = g["prefix_savings"]
+    assert round(formulas.prefix_savings(c["requests"], c["prefix"], c["mean_suffix"]) * 100, 9) == c["printed_percent"]
+    c = g["kv_head_ratio"]
+    for case in c["cases"]:
+        r = formulas.kv_head_ratio(case["kv_heads"], c["reference_heads"]) * 100
+        assert abs(r - case["printed_percent"]) <= case["printed_rounding"]
+    c = g["fp8_bytes"]
+    assert (1 - c["fp8_bytes"] / c["fp16_bytes"]) * 100 == c["printed_percent_saving"]
+    c = g["block_table_overhead"]
+    assert abs(formulas.block_table_bytes(c["requests"], 128) / 1000 - c["printed_kb"]) <= c["printed_rounding_kb"]
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_theorem1_waste_bound(seed):
+    rng = np.random.default_rng(seed)
+    for bs in (8, 16, 32):
+        lens = rng.integers(64, 4096, size=50)
+        a = OracleAllocator(int(sum(-(-int(t) // bs) for t in lens)), bs)
+        for t in lens:
+            a.alloc(a.seq_create(), int(t))
+        allocated = sum(len(tb) for tb in a.tables.values()) * bs
+        waste = allocated - int(lens.sum())
+        for s, t in a.lens.items():
+            assert 0 <= formulas.tail_waste_tokens(t, bs) <= bs - 1
+        assert waste / allocated < formulas.paged_waste_bound(bs, int(lens.min()))
+
+
+def _stored_tokens(a):
+    """Distinct physical slots holding data: each block counted once, filled up to
+    the longest sharer's offset in it."""
+    fill = {}
+    for s, tb in a.tables.items():
+        for j, b in enumerate(tb):
+            n = min(a.block_size, a.lens[s] - j * a.block_size)
+            fill[b] = max(fill.get(b, 0), n)
+    return sum(fill.values())
+
+
+def test_prefix_sharing_savings_formula_exact_for_block_aligned_prefix():
+    r, p, s_bar, bs = 100, 208, 50, 16
+    a = OracleAllocator(2000, bs)
+    parent = a.seq_create()
+    a.alloc(parent, p)
+    kids = [a.fork(parent) for _ in range(r)]
+    a.free_seq(parent)
+    for k in kids:
+        a.alloc(k, s_bar)
+    stored = _stored_tokens(a)
+    logical = sum(a.lens.values())
+    assert stored == p + r * s_bar and logical == r * (p + s_bar)
+    assert abs((1 - stored / logical) - formulas.prefix_savings(r, p, s_bar)) < 1e-15
+    # The same workload with the page's unaligned p = 200 shares 12 full blocks;
+    # the partial 13th block is copied by every writer but the last one.
+    a = OracleAllocator(2000, bs)
+    parent = a.seq_create()
+    a.alloc(parent, 200)
+    kids = [a.fork(parent) for _ in range(r)]
+    a.free_seq(parent)
+    for k in kids:
+        a.alloc(k, s_bar)
+    assert len(a.cow_log) == r - 1
+    assert _stored_tokens(a) == 192 + r * (8 + s_bar)
+
+
+def test_cb_prefix_script_replays_cleanly():
+    ops, rows = cb_prefix_script(464_003)
+    a = OracleAllocator(16384, 16)
+    n_rows = 0
+    for op in ops:
+        if op[0] == "create":
+            a.seq_create()
+        elif op[0] == "alloc":
+            a.alloc(op[1], op[2])
+            n_rows += op[2]
+        elif op[0] == "fork":
+            a.fork(op[1])
+        elif op[0] == "free":
+            a.free_seq(op[1])
+    a.check_invariants()
+    assert n_rows == rows and len(a.tables) == 256
+    assert len(a.cow_log) == 99  # every fork but the last one to write copies the partial block
+    assert 128 + 1 <= min(a.lens.values()) and max(a.lens.values()) <= 2048 + 512
+
+
+class AllocatorMachine(RuleBasedStateMachine):
+    def __init__(self):
+        super().__init__()
+        self.a = OracleAllocator(24, 4, list(np.random.default_rng(0).permutation(24)))
+        self.live = []
+
+    @rule()
+    def create(self):
+        self.live.append(self.a.seq_create())
+
+    @precondition(lambda self: self.live)
+    @rule(i=st.integers(0, 1000), n=st.integers(0, 13))
+    def alloc(self, i, n):
+        s = self.live[i % len(self.live)]
+        before = copy.deepcopy((list(self.a.free), self.a.ref, self.a.tables, self.a.lens))
+        try:
+            slots, cow = self.a.alloc(s, n)
+        except NoBlocks:
+            assert (list(self.a.free), self.a.ref, self.a.tables, self.a.lens) == before
+            return
+        assert len(slots) == n and len(set(slots)) == n
+        for x in slots:
+            assert self.a.ref[x // 4] == 1  # an appended slot is never in a shared block
+
+    @precondition(lambda self: self.live)
+    @rule(i=st.integers(0, 1000))
+    def fork(self, i):
+        self.live.append(self.a.fork(self.live[i % len(self.live)]))
+
+    @precondition(lambda self: self.live)
+    @rule(i=st.integers(0, 1000))
+    def free(self, i):
+        self.a.free_seq(self.live.pop(i % len(self.live)))
+
+    @invariant()
+    def invariants(self):
+        self.a.check_invariants()
+
+
+TestAllocatorMachine = AllocatorMachine.TestCase
+TestAllocatorMachine.settings = settings(max_examples=60, stateful_step_count=40, deadline=None)

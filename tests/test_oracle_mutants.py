@@ -1,0 +1,95 @@
+"""Planted mistakes in the oracle (CPU only) must be caught by its pins.
+
+Each test patches one plausible slip into an oracle function (a dropped
+scale, a wrong index, a swapped operand, a wrong exponent bias, truncation
+instead of round-to-nearest-even) and checks that at least one pin fails.
+"""
+import numpy as np
+import pytest
+
+from oracle import allocator as alloc_mod
+from oracle import attention, fp8
+from tests import test_oracle_allocator as ta
+from tests import test_oracle_attention as tt
+from tests import test_oracle_fp8 as tf
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_dropped_softmax_scale_is_caught(monkeypatch):
+    orig = attention._attend
+    monkeypatch.setattr(attention, "_attend", lambda q, k, v, scale: orig(q, k, v, 1.0))
+    _fails(tt.test_decode_matches_sdpa_fp16, 8, 2, 16)
+
+
+def test_wrong_kv_head_is_caught(monkeypatch):
+    orig = attention.gather_context
+    monkeypatch.setattr(attention, "gather_context",
+                        lambda s, l, t, n, h: orig(s, l, t, n, (h + 1) % s.kv_heads))
+    _fails(tt.test_decode_matches_sdpa_fp16, 8, 2, 16)
+
+
+def test_reversed_block_order_is_caught(monkeypatch):
+    orig = attention.gather_context
+
+    def bad(s, l, table, n, h):
+        nb = -(-int(n) // s.block_size)
+        return orig(s, l, list(table[:nb])[::-1], n, h)
+
+    monkeypatch.setattr(attention, "gather_context", bad)
+    _fails(tt.test_decode_matches_sdpa_fp16, 32, 8, 8)
+
+
+def test_off_by_one_context_is_caught(monkeypatch):
+    orig = attention.gather_context
+    monkeypatch.setattr(attention, "gather_context", lambda s, l, t, n, h: orig(s, l, t, max(1, n - 1), h))
+    _fails(tt.test_decode_matches_sdpa_fp16, 4, 4, 32)
+
+
+def test_transposed_pv_is_caught(monkeypatch):
+    def bad(q, k, v, scale):
+        s = (k @ q) * scale
+        p = np.exp(s - s.max())
+        return (v.T @ p)[::-1] / p.sum()  # dims reversed
+    monkeypatch.setattr(attention, "_attend", bad)
+    _fails(tt.test_decode_matches_sdpa_fp16, 8, 2, 16)
+
+
+def test_wrong_fp8_bias_is_caught(monkeypatch):
+    orig = fp8.decode
+    monkeypatch.setattr(fp8, "decode", lambda c: orig(c) * 2.0)
+    _fails(tf.test_decode_matches_torch_for_all_codes)
+
+
+def test_truncating_fp8_encode_is_caught(monkeypatch):
+    monkeypatch.setattr(np, "rint", np.trunc)
+    _fails(tf.test_encode_matches_torch_on_all_fp16_values)
+
+
+def test_unsaturated_fp8_encode_is_caught(monkeypatch):
+    monkeypatch.setattr(fp8, "E4M3_MAX", 480.0)
+    _fails(tf.test_encode_ties_and_saturation)
+
+
+def test_wrong_slot_offset_is_caught(monkeypatch):
+    class Bad(alloc_mod.OracleAllocator):
+        def alloc(self, sid, n):
+            start = self.lens[sid]
+            slots, cow = super().alloc(sid, n)
+            bs = self.block_size
+            # offset taken from the wrong end of the block
+            return [s - (start + j) % bs + (bs - 1 - (start + j) % bs) for j, s in enumerate(slots)], cow
+    monkeypatch.setattr(ta, "OracleAllocator", Bad)
+    _fails(ta.test_page_block_table_example)
+
+
+def test_cow_without_copy_is_caught(monkeypatch):
+    class Bad(alloc_mod.OracleAllocator):
+        def alloc(self, sid, n):
+            slots, cow = super().alloc(sid, n)
+            return slots, None  # forgets to report (so nobody copies) the shared block
+    monkeypatch.setattr(ta, "OracleAllocator", Bad)
+    _fails(ta.test_slot_mapping_content_round_trip_through_fork_and_cow)
