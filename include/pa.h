@@ -1,0 +1,249 @@
+/*
+ * pa.h - C ABI of the paged KV-cache decode library (libpa.so, gfx950 / MI355X).
+ *
+ * What the library implements, and where each piece is defined:
+ *
+ *  - A KV cache split into fixed-size blocks of `block_size` tokens held in
+ *    one physical pool; a per-sequence block table maps logical blocks to
+ *    physical ones; blocks are handed out on demand from a free queue
+ *    (youngju.dev "KV cache and paged attention", section "PagedAttention:
+ *    OS 가상 메모리식 관리"; opsoai "vLLM PagedAttention은 KV 캐시를 어떻게
+ *    관리할까", section "PagedAttention은 논리 블록과 물리 블록을 분리한다").
+ *  - Allocation gives up when too few free blocks remain (openakashic
+ *    KV-cache failure-modes note, Key Points).
+ *  - Sequences sharing a prefix point at the same physical blocks with a
+ *    reference count, and a shared block is copied when one sharer writes
+ *    into it (youngju.dev page, section "prefix 공유와 copy-on-write";
+ *    iq-blog ch.4 "Why PagedAttention cuts GPU memory waste", section
+ *    "Prefix Caching").
+ *  - Decode attention softmax(q K^T / sqrt(d)) V for one new query token per
+ *    sequence (youngju.dev page, section "핵심 원리: KV 캐시란 무엇인가"),
+ *    computed by a kernel that follows the block table to gather
+ *    non-contiguous K/V blocks (iq-blog ch.4, section "PagedAttention
+ *    알고리즘"), with query heads grouped onto fewer KV heads (GQA / MQA;
+ *    youngju.dev page, section "GQA와 MQA").
+ *  - fp8 KV storage at one byte per element (youngju.dev page, section
+ *    "KV 양자화: FP8과 INT8"), as OCP E4M3FN with one fp32 scale per
+ *    (layer, KV head) for K and one for V.
+ *
+ * Conventions shared by every call:
+ *  - Every call returns an int status: PA_OK (0) or a negative PA_ERR_*.
+ *    Nothing throws across the ABI.  pa_last_error() returns a thread-local
+ *    message describing the most recent failure on the calling thread.
+ *  - "host" pointers are ordinary CPU memory; "device" pointers are GPU
+ *    memory on the device that was current when the pool was bound.
+ *    All device memory (the pool itself, q, out, tables, slot mappings,
+ *    workspaces) is owned by the caller; the library keeps raw pointers only
+ *    and frees nothing it did not allocate.  Host metadata (free queue,
+ *    reference counts, block tables) is owned by the library and released by
+ *    pa_pool_destroy.
+ *  - `stream` is a hipStream_t (0 = the null stream).  Device work is
+ *    enqueued asynchronously on that stream; host-only calls are synchronous.
+ *  - A pool is not thread-safe; serialise calls on one pool.
+ *  - Integer sizes are int32; byte sizes are uint64.
+ *
+ * Pool byte layout (device buffer given to pa_pool_bind, 256-byte aligned):
+ *    [layers][2 (K, V)][num_blocks][kv_heads][tile]  then a metadata tail
+ *    (fp32 scales and inverse scales, a device status word).
+ *  A tile holds one (block, KV head): block_size x head_dim elements in a
+ *  kernel-specific order (K in 16-byte chunks of consecutive dims, V with
+ *  4-token x 16-dim sub-tiles).  Use pa_gather_kv to read tokens back in
+ *  logical [token][kv_head][dim] order.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+#define PA_OK 0
+#define PA_ERR_INVALID (-1)   /* bad argument, shape or state                  */
+#define PA_ERR_NO_BLOCKS (-2) /* not enough free blocks; nothing was changed    */
+#define PA_ERR_BAD_SEQ (-3)   /* unknown or freed sequence id                   */
+#define PA_ERR_HIP (-4)       /* a HIP runtime call failed                      */
+#define PA_ERR_UNBOUND (-5)   /* device call on a pool with no device memory    */
+
+/* ---- KV element types ---------------------------------------------------- */
+#define PA_DTYPE_FP16 0     /* IEEE binary16                                   */
+#define PA_DTYPE_FP8_E4M3 1 /* OCP E4M3FN: value = decode(code) * scale        */
+
+/* ---- device status bits (pa_device_status) -------------------------------- */
+#define PA_DEV_BAD_SLOT 1u  /* a slot >= num_blocks*block_size was skipped      */
+#define PA_DEV_BAD_BLOCK 2u /* a table entry outside [0, num_blocks) was read as block 0 */
+#define PA_DEV_BAD_LEN 4u   /* a context length < 1 or > max_blocks*block_size  */
+
+typedef struct pa_pool pa_pool; /* opaque */
+
+typedef struct pa_pool_info {
+  int32_t layers, kv_heads, head_dim, block_size, dtype, num_blocks;
+  int32_t elem_bytes; /* 2 (fp16) or 1 (fp8)                                  */
+  int32_t bound;      /* 1 once pa_pool_bind succeeded                        */
+  uint64_t tile_bytes;  /* block_size * head_dim * elem_bytes                  */
+  uint64_t kv_bytes;    /* 2 * layers * kv_heads * head_dim * elem_bytes *
+                           num_blocks * block_size: the pages' KV-size formula
+                           (openakashic note, Key Points; youngju.dev page,
+                           section "KV 캐시는 왜 메모리를 먹는가") at full pool */
+  uint64_t total_bytes; /* kv_bytes + metadata tail: what pa_pool_bind needs   */
+} pa_pool_info;
+
+typedef struct pa_stats {
+  int64_t num_blocks, free_blocks, used_blocks, shared_blocks;
+  int64_t num_seqs, cow_copies, alloc_failures;
+} pa_stats;
+
+typedef struct pa_profile {
+  int32_t decode_launches, reduce_launches;
+  double decode_ms, reduce_ms; /* summed HIP-event durations on the launch stream */
+} pa_profile;
+
+/* ---- pool ------------------------------------------------------------------ */
+
+/* Create a pool descriptor: per layer, K and V pools of `num_blocks` blocks of
+ * `block_size` tokens x `kv_heads` x `head_dim`.  Supported: head_dim 128,
+ * block_size 8/16/32, dtype PA_DTYPE_*, num_blocks*block_size < 2^31.
+ * No device memory is touched; host-side block management works unbound. */
+int pa_pool_create(int32_t layers, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t dtype, int32_t num_blocks, pa_pool** out);
+
+/* Release the host metadata (the caller frees the device buffer). NULL is a no-op. */
+int pa_pool_destroy(pa_pool* pool);
+
+int pa_pool_info_get(const pa_pool* pool, pa_pool_info* out);
+
+/* Replace the initial free-queue order by a permutation of 0..num_blocks-1
+ * (host int32[n], n == num_blocks).  Only valid before the first allocation. */
+int pa_pool_set_free_order(pa_pool* pool, const int32_t* perm, int32_t n);
+
+/* Attach caller-owned device memory of info.total_bytes, 256-byte aligned.
+ * fp8 pools need host fp32 scales k_scales[layers*kv_heads] and v_scales[...]
+ * (layer-major); fp16 pools pass NULL.  The library writes the scales, their
+ * fp32 reciprocals and a zeroed status word into the tail (synchronously). */
+int pa_pool_bind(pa_pool* pool, void* dev_base, const float* k_scales, const float* v_scales);
+
+/* ---- block manager (host) ------------------------------------------------------ */
+
+/* New empty sequence; ids are 0, 1, 2, ... in creation order, never reused. */
+int pa_seq_create(pa_pool* pool, int32_t* seq_out);
+
+/* Append n_tokens >= 0 tokens to `seq`.  slots_out (host int32[n_tokens]):
+ * slot of the j-th new token = table[t / B] * B + t % B, t = old_len + j.
+ * If the append lands in a partly filled last block shared with another
+ * sequence, that block is copied first into a fresh block which replaces it
+ * in this sequence's table (copy-on-write, the writer receives the copy);
+ * cow_out (host int32[2], may be NULL) receives {src, dst} or {-1, -1}.  On a
+ * bound pool the copy (all layers, K and V) is enqueued on `stream` before
+ * returning, so later pa_write_kv calls on that stream see it.
+ * Atomic: on PA_ERR_NO_BLOCKS (the copy's block counts toward the need)
+ * nothing changes. */
+int pa_alloc(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* slots_out,
+             int32_t* cow_out, void* stream);
+
+/* New sequence sharing every block of `parent` (each reference count + 1). */
+int pa_fork(pa_pool* pool, int32_t parent, int32_t* child_out);
+
+/* Drop `seq`: its blocks are visited last to first, and each one whose
+ * reference count reaches zero is appended to the free-queue tail. */
+int pa_free(pa_pool* pool, int32_t seq);
+
+int pa_seq_len(const pa_pool* pool, int32_t seq, int32_t* len_out, int32_t* num_blocks_out);
+
+/* Export block tables: tables_out host int32[n][max_blocks] (rows padded with
+ * -1), lens_out host int32[n].  PA_ERR_INVALID if a table is longer than max_blocks. */
+int pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n, int32_t max_blocks,
+                    int32_t* tables_out, int32_t* lens_out);
+
+int pa_pool_stats(const pa_pool* pool, pa_stats* out);
+
+/* Allocator state for inspection: reference count of every block (host
+ * int32[num_blocks]); the free queue head to tail (host int32[num_blocks],
+ * *n_out = number of free blocks). */
+int pa_refcounts(const pa_pool* pool, int32_t* out);
+int pa_free_queue(const pa_pool* pool, int32_t* out, int32_t* n_out);
+
+/* ---- device operations ---------------------------------------------------------- */
+
+/* Reshape-and-cache scatter: token t's K and V (device fp16 [n][kv_heads][head_dim])
+ * go to slot slot_mapping[t] (device int32[n]) of `layer`; negative slots are
+ * skipped.  fp8 pools store encode(f32(x) * f32(1/scale)) with saturation to
+ * +-448 and round-to-nearest-even. */
+int pa_write_kv(pa_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                const int32_t* slot_mapping, int32_t n_tokens, void* stream);
+
+/* Inverse of pa_write_kv: read the stored K/V of each slot into device
+ * k_out/v_out [n][kv_heads][head_dim] (fp16 values, or raw uint8 codes for fp8).
+ * Negative slots leave their rows untouched. */
+int pa_gather_kv(const pa_pool* pool, int32_t layer, const int32_t* slot_mapping,
+                 int32_t n_tokens, void* k_out, void* v_out, void* stream);
+
+/* Copy whole blocks src[i] -> dst[i] (host int32[n]) across all layers, K and V. */
+int pa_copy_blocks(pa_pool* pool, const int32_t* src, const int32_t* dst, int32_t n, void* stream);
+
+/* Device bytes of the workspace pa_decode needs for this launch shape
+ * (0 when it runs in a single pass).  partition_tokens as in pa_decode. */
+int pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_blocks, int32_t partition_tokens, uint64_t* bytes_out);
+
+/* Paged decode attention for one layer.
+ *   q            device fp16 [num_seqs][num_q_heads][head_dim]
+ *   block_tables device int32 [num_seqs][max_blocks] (entries past a sequence's
+ *                last block are ignored)
+ *   context_lens device int32 [num_seqs], 1 <= T_i <= max_blocks*block_size,
+ *                the tokens each query attends to (the new one included)
+ *   scale        softmax temperature, normally 1/sqrt(head_dim)
+ *   out          device fp16 [num_seqs][num_q_heads][head_dim]
+ * Query head h reads KV head h / (num_q_heads / kv_heads); num_q_heads must
+ * be a multiple of kv_heads with a group of at most 32.
+ * partition_tokens: 0 lets the library choose; -1 forces one pass per
+ * (sequence, KV head); P > 0 (a multiple of 16 and of block_size) splits each
+ * context into chunks of P tokens whose partials are merged by log-sum-exp.
+ * workspace: device memory of pa_decode_workspace_bytes() bytes (may be NULL
+ * when that is 0).  Out-of-range table entries or lengths never cause an
+ * out-of-bounds access; they set PA_DEV_* bits instead. */
+int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+              const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+              int32_t num_seqs, float scale, int32_t partition_tokens, void* out,
+              void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* The two halves of a partitioned pa_decode, callable separately.
+ * pa_decode_partials writes, for chunk c of every (sequence, query head), into
+ * the workspace laid out as three consecutive fp32 arrays of C = ceil(max_blocks
+ * * block_size / P) chunks each:
+ *    m[num_seqs][num_q_heads][C]   max score of the chunk in base-2 units,
+ *                                  max_t (q.k_t * scale * log2 e)
+ *    l[num_seqs][num_q_heads][C]   sum_t 2^(s_t - m)
+ *    o[num_seqs][num_q_heads][C][head_dim]  sum_t 2^(s_t - m) v_t / l
+ * Chunks at or past ceil(T_i / P) are not written.
+ * pa_lse_reduce merges chunks 0 .. ceil(T_i/P)-1 into out:
+ *    out = sum_c w_c o_c / sum_c w_c,  w_c = l_c * 2^(m_c - max_c m_c). */
+int pa_decode_partials(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                       const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* context_lens, int32_t num_seqs, float scale,
+                       int32_t partition_tokens, void* workspace, uint64_t workspace_bytes,
+                       void* stream);
+int pa_lse_reduce(pa_pool* pool, const void* workspace, uint64_t workspace_bytes,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t max_blocks, int32_t partition_tokens, void* out, void* stream);
+
+/* Read (and optionally clear) the pool's device status word; synchronises `stream`. */
+int pa_device_status(pa_pool* pool, uint32_t* flags_out, int32_t clear, void* stream);
+
+/* Kernel timing: while enabled, every pa_decode records HIP events around its
+ * attention kernel and its reduce kernel on the launch stream (up to
+ * max_launches launches).  pa_profile_end synchronises those events, returns
+ * the summed durations and disables timing. */
+int pa_profile_begin(pa_pool* pool, int32_t max_launches);
+int pa_profile_end(pa_pool* pool, pa_profile* out);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

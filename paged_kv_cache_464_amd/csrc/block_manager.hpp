@@ -1,0 +1,85 @@
+// Host-side block manager of the paged KV cache.
+//
+// Blocks of B tokens come from one physical pool; each sequence owns a block
+// table (logical block -> physical block) that grows on demand (youngju.dev
+// "KV cache and paged attention", section "PagedAttention: OS 가상 메모리식
+// 관리"; iq-blog ch.4, section "OS Paging에서 가져온 해법").  Free blocks
+// wait in a FIFO queue; an append that needs more blocks than are free fails
+// and changes nothing (openakashic KV-cache failure-modes note, Key Points).
+// Forked sequences share physical blocks with reference counts; appending into
+// a shared, partly filled last block first copies it for the writer
+// (youngju.dev page, section "prefix 공유와 copy-on-write"; iq-blog ch.4,
+// section "Prefix Caching").
+//
+// Policy details the pages leave open, fixed here:
+//  * the free queue pops from its head; freed blocks are appended at its tail,
+//    visiting the freed sequence's table from last block to first;
+//  * the block a copy-on-write needs counts toward an append's requirement;
+//  * copy-on-write happens only for an append of >= 1 token into a partly
+//    filled last block whose reference count exceeds one;
+//  * sequence ids are 0, 1, 2, ... in creation order and never reused.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+namespace pa {
+
+enum class BmStatus { kOk, kInvalid, kNoBlocks, kBadSeq };
+
+class BlockManager {
+ public:
+  BlockManager(int32_t num_blocks, int32_t block_size);
+
+  int32_t num_blocks() const { return num_blocks_; }
+  int32_t block_size() const { return block_size_; }
+
+  // Permutation of 0..N-1 as the initial free-queue order; only before any allocation.
+  BmStatus set_free_order(const int32_t* perm, int32_t n);
+
+  int32_t seq_create();
+
+  // Append n tokens.  slots[n] receive the new tokens' slots; *cow_src/*cow_dst the
+  // copied block pair or -1.
+  BmStatus alloc(int32_t seq, int32_t n, int32_t* slots, int32_t* cow_src, int32_t* cow_dst);
+  BmStatus fork(int32_t parent, int32_t* child);
+  BmStatus free_seq(int32_t seq);
+
+  BmStatus seq_len(int32_t seq, int32_t* len, int32_t* nblocks) const;
+  // Row of `max_blocks` entries padded with -1.
+  BmStatus table_row(int32_t seq, int32_t max_blocks, int32_t* row, int32_t* len) const;
+
+  int64_t free_count() const { return free_count_; }
+  int64_t live_seqs() const { return live_seqs_; }
+  int64_t cow_copies() const { return cow_copies_; }
+  int64_t alloc_failures() const { return alloc_failures_; }
+  int64_t shared_blocks() const;
+  const std::vector<int32_t>& refcounts() const { return ref_; }
+  void free_queue(int32_t* out) const;  // head to tail, free_count() entries
+
+ private:
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t len = 0;
+    bool alive = false;
+  };
+  bool valid_seq(int32_t s) const {
+    return s >= 0 && s < static_cast<int32_t>(seqs_.size()) && seqs_[s].alive;
+  }
+  int32_t pop_free();
+  void push_free(int32_t b);
+
+  int32_t num_blocks_;
+  int32_t block_size_;
+  std::vector<int32_t> ring_;  // FIFO ring of capacity num_blocks_
+  int64_t head_ = 0;
+  int64_t free_count_ = 0;
+  std::vector<int32_t> ref_;
+  std::vector<Seq> seqs_;
+  int64_t live_seqs_ = 0;
+  int64_t cow_copies_ = 0;
+  int64_t alloc_failures_ = 0;
+  bool touched_ = false;  // any allocation happened
+};
+
+}  // namespace pa

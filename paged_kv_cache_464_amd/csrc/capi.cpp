@@ -1,0 +1,541 @@
+// C ABI of libpa: argument validation, the pool descriptor, dispatch to the
+// HIP kernels, device status and kernel timing.  Nothing throws across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "block_manager.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kDefaultPartition = 512;
+
+}  // namespace
+
+struct pa_pool {
+  int32_t layers, kv_heads, head_dim, block_size, dtype, num_blocks, elem_bytes;
+  uint64_t tile_bytes, kv_bytes, scales_offset, status_offset, total_bytes;
+  pa::BlockManager bm;
+  bool bound = false;
+  int device = -1;
+  int num_cus = 256;
+  pa::PoolGeom geom{};
+  // kernel timing
+  bool profiling = false;
+  int32_t max_records = 0;
+  std::vector<hipEvent_t> ev;  // 3 per record: before decode, after decode, after reduce
+  std::vector<int8_t> has_reduce;
+  int32_t n_records = 0;
+
+  pa_pool(int32_t L, int32_t H, int32_t D, int32_t B, int32_t dt, int32_t N)
+      : layers(L), kv_heads(H), head_dim(D), block_size(B), dtype(dt), num_blocks(N),
+        elem_bytes(dt == PA_DTYPE_FP16 ? 2 : 1), bm(N, B) {
+    tile_bytes = static_cast<uint64_t>(B) * D * elem_bytes;
+    kv_bytes = 2ull * L * N * H * tile_bytes;
+    scales_offset = align_up(kv_bytes, 256);
+    status_offset = align_up(scales_offset + 16ull * L * H, 256);
+    total_bytes = status_offset + 256;
+  }
+  ~pa_pool() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+
+namespace {
+
+// Launch shape of one decode: single pass (C = 1) or chunks of P tokens.
+struct Plan {
+  bool partial;
+  int partition_tokens;
+  int num_partitions;
+  uint64_t ws_bytes, off_l, off_o;
+};
+
+int make_plan(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
+              int32_t partition_tokens, Plan* out) {
+  if (max_blocks < 1 || static_cast<int64_t>(max_blocks) * p->block_size > 0x7FFFFFFF)
+    return fail(PA_ERR_INVALID, "max_blocks %d out of range", max_blocks);
+  if (num_seqs < 0) return fail(PA_ERR_INVALID, "num_seqs %d < 0", num_seqs);
+  if (num_q_heads < 1 || num_q_heads % p->kv_heads != 0)
+    return fail(PA_ERR_INVALID, "num_q_heads %d is not a multiple of kv_heads %d", num_q_heads,
+                p->kv_heads);
+  const int group = num_q_heads / p->kv_heads;
+  if (group > 32) return fail(PA_ERR_INVALID, "query heads per KV head %d > 32", group);
+  const int64_t t_cap = static_cast<int64_t>(max_blocks) * p->block_size;
+  int P;
+  if (partition_tokens == -1) {
+    P = 0;
+  } else if (partition_tokens == 0) {
+    const int64_t units = static_cast<int64_t>(num_seqs) * p->kv_heads;
+    P = (t_cap <= kDefaultPartition || units >= 4ll * p->num_cus) ? 0 : kDefaultPartition;
+  } else {
+    if (partition_tokens % 16 != 0 || partition_tokens % p->block_size != 0)
+      return fail(PA_ERR_INVALID, "partition_tokens %d must be a multiple of 16 and of block_size %d",
+                  partition_tokens, p->block_size);
+    P = partition_tokens;
+  }
+  Plan pl{};
+  if (P == 0) {
+    pl.partial = false;
+    pl.partition_tokens = static_cast<int>(align_up(static_cast<uint64_t>(t_cap), 16));
+    pl.num_partitions = 1;
+  } else {
+    pl.partial = true;
+    pl.partition_tokens = P;
+    pl.num_partitions = static_cast<int>((t_cap + P - 1) / P);
+    const uint64_t rows = static_cast<uint64_t>(num_seqs) * num_q_heads * pl.num_partitions;
+    pl.off_l = align_up(rows * 4, 256);
+    pl.off_o = pl.off_l + align_up(rows * 4, 256);
+    pl.ws_bytes = pl.off_o + align_up(rows * p->head_dim * 4, 256);
+  }
+  *out = pl;
+  return PA_OK;
+}
+
+int check_bound(const pa_pool* p) {
+  if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (!p->bound) return fail(PA_ERR_UNBOUND, "pool has no device memory (call pa_pool_bind)");
+  return PA_OK;
+}
+
+int check_layer(const pa_pool* p, int32_t layer) {
+  if (layer < 0 || layer >= p->layers)
+    return fail(PA_ERR_INVALID, "layer %d outside [0, %d)", layer, p->layers);
+  return PA_OK;
+}
+
+int bm_status(pa::BmStatus s, int32_t seq) {
+  switch (s) {
+    case pa::BmStatus::kOk: return PA_OK;
+    case pa::BmStatus::kNoBlocks: return fail(PA_ERR_NO_BLOCKS, "not enough free blocks for sequence %d", seq);
+    case pa::BmStatus::kBadSeq: return fail(PA_ERR_BAD_SEQ, "unknown or freed sequence %d", seq);
+    default: return fail(PA_ERR_INVALID, "invalid argument for sequence %d", seq);
+  }
+}
+
+pa::DecodeLaunch make_launch(int32_t layer, const void* q, int32_t num_q_heads,
+                             const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                             int32_t num_seqs, float scale, const Plan& pl, void* out,
+                             void* workspace) {
+  pa::DecodeLaunch d{};
+  d.layer = layer;
+  d.q = q;
+  d.tables = tables;
+  d.lens = lens;
+  d.out = out;
+  d.num_seqs = num_seqs;
+  d.num_q_heads = num_q_heads;
+  d.max_blocks = max_blocks;
+  d.partition_tokens = pl.partition_tokens;
+  d.num_partitions = pl.num_partitions;
+  d.scale = scale;
+  if (pl.partial) {
+    auto* ws = static_cast<uint8_t*>(workspace);
+    d.part_m = reinterpret_cast<float*>(ws);
+    d.part_l = reinterpret_cast<float*>(ws + pl.off_l);
+    d.part_o = reinterpret_cast<float*>(ws + pl.off_o);
+  }
+  return d;
+}
+
+int check_decode_args(pa_pool* pool, int32_t layer, const void* q, const int32_t* tables,
+                      const int32_t* lens, int32_t num_seqs, float scale) {
+  int rc = check_bound(pool);
+  if (rc) return rc;
+  if ((rc = check_layer(pool, layer))) return rc;
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "scale is not finite");
+  if (num_seqs > 0 && (!q || !tables || !lens)) return fail(PA_ERR_INVALID, "NULL device pointer");
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_pool_create(int32_t layers, int32_t kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t dtype, int32_t num_blocks, pa_pool** out) {
+  if (!out) return fail(PA_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (layers < 1 || kv_heads < 1) return fail(PA_ERR_INVALID, "layers and kv_heads must be >= 1");
+  if (head_dim != pa::kHeadDim) return fail(PA_ERR_INVALID, "head_dim %d unsupported (128 only)", head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_ERR_INVALID, "block_size %d unsupported (8, 16, 32)", block_size);
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (num_blocks < 1 || static_cast<int64_t>(num_blocks) * block_size > 0x7FFFFFFF)
+    return fail(PA_ERR_INVALID, "num_blocks %d out of range", num_blocks);
+  try {
+    *out = new pa_pool(layers, kv_heads, head_dim, block_size, dtype, num_blocks);
+  } catch (const std::bad_alloc&) {
+    return fail(PA_ERR_INVALID, "out of host memory");
+  }
+  return PA_OK;
+}
+
+int pa_pool_destroy(pa_pool* pool) {
+  delete pool;
+  return PA_OK;
+}
+
+int pa_pool_info_get(const pa_pool* p, pa_pool_info* out) {
+  if (!p || !out) return fail(PA_ERR_INVALID, "NULL argument");
+  out->layers = p->layers;
+  out->kv_heads = p->kv_heads;
+  out->head_dim = p->head_dim;
+  out->block_size = p->block_size;
+  out->dtype = p->dtype;
+  out->num_blocks = p->num_blocks;
+  out->elem_bytes = p->elem_bytes;
+  out->bound = p->bound ? 1 : 0;
+  out->tile_bytes = p->tile_bytes;
+  out->kv_bytes = p->kv_bytes;
+  out->total_bytes = p->total_bytes;
+  return PA_OK;
+}
+
+int pa_pool_set_free_order(pa_pool* p, const int32_t* perm, int32_t n) {
+  if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (p->bm.set_free_order(perm, n) != pa::BmStatus::kOk)
+    return fail(PA_ERR_INVALID, "free order must be a permutation of 0..%d set before any allocation",
+                p->num_blocks - 1);
+  return PA_OK;
+}
+
+int pa_pool_bind(pa_pool* p, void* dev_base, const float* k_scales, const float* v_scales) {
+  if (!p || !dev_base) return fail(PA_ERR_INVALID, "NULL argument");
+  if (reinterpret_cast<uintptr_t>(dev_base) % 256 != 0)
+    return fail(PA_ERR_INVALID, "device buffer must be 256-byte aligned");
+  const size_t lh = static_cast<size_t>(p->layers) * p->kv_heads;
+  std::vector<float> sc(4 * lh, 1.0f);
+  if (p->dtype == PA_DTYPE_FP8_E4M3) {
+    if (!k_scales || !v_scales) return fail(PA_ERR_INVALID, "fp8 pools need k_scales and v_scales");
+    for (size_t i = 0; i < lh; ++i) {
+      const float ks = k_scales[i], vs = v_scales[i];
+      if (!(std::isfinite(ks) && ks > 0.0f && std::isfinite(vs) && vs > 0.0f))
+        return fail(PA_ERR_INVALID, "scale %zu is not a positive finite number", i);
+      sc[i] = ks;
+      sc[lh + i] = vs;
+      sc[2 * lh + i] = 1.0f / ks;  // IEEE fp32 division, round to nearest even
+      sc[3 * lh + i] = 1.0f / vs;
+    }
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    p->num_cus = cus;
+  auto* base = static_cast<uint8_t*>(dev_base);
+  e = hipMemcpy(base + p->scales_offset, sc.data(), sc.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(scales)");
+  e = hipMemset(base + p->status_offset, 0, 256);
+  if (e != hipSuccess) return hip_fail(e, "hipMemset(status)");
+  pa::PoolGeom& g = p->geom;
+  g.base = base;
+  g.layers = p->layers;
+  g.kv_heads = p->kv_heads;
+  g.head_dim = p->head_dim;
+  g.block_size = p->block_size;
+  g.num_blocks = p->num_blocks;
+  g.elem_bytes = p->elem_bytes;
+  g.tile_bytes = p->tile_bytes;
+  g.block_stride = p->tile_bytes * p->kv_heads;
+  g.half_stride = g.block_stride * p->num_blocks;
+  g.scales = reinterpret_cast<float*>(base + p->scales_offset);
+  g.status = reinterpret_cast<uint32_t*>(base + p->status_offset);
+  p->device = dev;
+  p->bound = true;
+  return PA_OK;
+}
+
+int pa_seq_create(pa_pool* p, int32_t* seq_out) {
+  if (!p || !seq_out) return fail(PA_ERR_INVALID, "NULL argument");
+  *seq_out = p->bm.seq_create();
+  return PA_OK;
+}
+
+int pa_alloc(pa_pool* p, int32_t seq, int32_t n_tokens, int32_t* slots_out, int32_t* cow_out,
+             void* stream) {
+  if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
+  int32_t src = -1, dst = -1;
+  const int rc = bm_status(p->bm.alloc(seq, n_tokens, slots_out, &src, &dst), seq);
+  if (cow_out) {
+    cow_out[0] = src;
+    cow_out[1] = dst;
+  }
+  if (rc) return rc;
+  if (src >= 0 && p->bound) {
+    const hipError_t e = pa::launch_copy_blocks(p->geom, &src, &dst, 1, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "copy-on-write block copy");
+  }
+  return PA_OK;
+}
+
+int pa_fork(pa_pool* p, int32_t parent, int32_t* child_out) {
+  if (!p || !child_out) return fail(PA_ERR_INVALID, "NULL argument");
+  return bm_status(p->bm.fork(parent, child_out), parent);
+}
+
+int pa_free(pa_pool* p, int32_t seq) {
+  if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
+  return bm_status(p->bm.free_seq(seq), seq);
+}
+
+int pa_seq_len(const pa_pool* p, int32_t seq, int32_t* len_out, int32_t* num_blocks_out) {
+  if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
+  return bm_status(p->bm.seq_len(seq, len_out, num_blocks_out), seq);
+}
+
+int pa_block_tables(const pa_pool* p, const int32_t* seqs, int32_t n, int32_t max_blocks,
+                    int32_t* tables_out, int32_t* lens_out) {
+  if (!p || n < 0 || max_blocks < 0 || (n > 0 && (!seqs || !tables_out)))
+    return fail(PA_ERR_INVALID, "bad arguments to pa_block_tables");
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t len = 0;
+    const pa::BmStatus s = p->bm.table_row(seqs[i], max_blocks,
+                                           tables_out + static_cast<int64_t>(i) * max_blocks, &len);
+    if (s == pa::BmStatus::kInvalid)
+      return fail(PA_ERR_INVALID, "block table of sequence %d is longer than max_blocks %d", seqs[i], max_blocks);
+    if (s != pa::BmStatus::kOk) return bm_status(s, seqs[i]);
+    if (lens_out) lens_out[i] = len;
+  }
+  return PA_OK;
+}
+
+int pa_pool_stats(const pa_pool* p, pa_stats* out) {
+  if (!p || !out) return fail(PA_ERR_INVALID, "NULL argument");
+  out->num_blocks = p->num_blocks;
+  out->free_blocks = p->bm.free_count();
+  out->used_blocks = p->num_blocks - p->bm.free_count();
+  out->shared_blocks = p->bm.shared_blocks();
+  out->num_seqs = p->bm.live_seqs();
+  out->cow_copies = p->bm.cow_copies();
+  out->alloc_failures = p->bm.alloc_failures();
+  return PA_OK;
+}
+
+int pa_refcounts(const pa_pool* p, int32_t* out) {
+  if (!p || !out) return fail(PA_ERR_INVALID, "NULL argument");
+  std::memcpy(out, p->bm.refcounts().data(), sizeof(int32_t) * p->num_blocks);
+  return PA_OK;
+}
+
+int pa_free_queue(const pa_pool* p, int32_t* out, int32_t* n_out) {
+  if (!p || !out || !n_out) return fail(PA_ERR_INVALID, "NULL argument");
+  p->bm.free_queue(out);
+  *n_out = static_cast<int32_t>(p->bm.free_count());
+  return PA_OK;
+}
+
+int pa_write_kv(pa_pool* p, int32_t layer, const void* k_new, const void* v_new,
+                const int32_t* slot_mapping, int32_t n_tokens, void* stream) {
+  int rc = check_bound(p);
+  if (rc) return rc;
+  if ((rc = check_layer(p, layer))) return rc;
+  if (n_tokens < 0) return fail(PA_ERR_INVALID, "n_tokens %d < 0", n_tokens);
+  if (n_tokens > 0 && (!k_new || !v_new || !slot_mapping)) return fail(PA_ERR_INVALID, "NULL device pointer");
+  const hipError_t e = pa::launch_write_kv(p->geom, layer, k_new, v_new, slot_mapping, n_tokens,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : hip_fail(e, "write_kv launch");
+}
+
+int pa_gather_kv(const pa_pool* p, int32_t layer, const int32_t* slot_mapping, int32_t n_tokens,
+                 void* k_out, void* v_out, void* stream) {
+  int rc = check_bound(p);
+  if (rc) return rc;
+  if ((rc = check_layer(p, layer))) return rc;
+  if (n_tokens < 0) return fail(PA_ERR_INVALID, "n_tokens %d < 0", n_tokens);
+  if (n_tokens > 0 && (!k_out || !v_out || !slot_mapping)) return fail(PA_ERR_INVALID, "NULL device pointer");
+  const hipError_t e = pa::launch_gather_kv(p->geom, layer, slot_mapping, n_tokens, k_out, v_out,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : hip_fail(e, "gather_kv launch");
+}
+
+int pa_copy_blocks(pa_pool* p, const int32_t* src, const int32_t* dst, int32_t n, void* stream) {
+  int rc = check_bound(p);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!src || !dst))) return fail(PA_ERR_INVALID, "bad copy list");
+  for (int32_t i = 0; i < n; ++i) {
+    if (src[i] < 0 || src[i] >= p->num_blocks || dst[i] < 0 || dst[i] >= p->num_blocks)
+      return fail(PA_ERR_INVALID, "copy pair %d (%d -> %d) outside the pool", i, src[i], dst[i]);
+  }
+  const hipError_t e = pa::launch_copy_blocks(p->geom, src, dst, n, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : hip_fail(e, "copy_blocks launch");
+}
+
+int pa_decode_workspace_bytes(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_blocks, int32_t partition_tokens, uint64_t* bytes_out) {
+  if (!p || !bytes_out) return fail(PA_ERR_INVALID, "NULL argument");
+  Plan pl;
+  const int rc = make_plan(p, num_seqs, num_q_heads, max_blocks, partition_tokens, &pl);
+  if (rc) return rc;
+  *bytes_out = pl.partial ? pl.ws_bytes : 0;
+  return PA_OK;
+}
+
+static void record(pa_pool* p, int slot, hipStream_t s) {
+  (void)hipEventRecord(p->ev[slot], s);
+}
+
+static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
+                      const int32_t* tables, int32_t max_blocks, const int32_t* lens,
+                      int32_t num_seqs, float scale, int32_t partition_tokens, void* out,
+                      void* workspace, uint64_t workspace_bytes, void* stream, int mode) {
+  // mode 0: full decode, 1: partials only
+  int rc = check_decode_args(p, layer, q, tables, lens, num_seqs, scale);
+  if (rc) return rc;
+  Plan pl;
+  if ((rc = make_plan(p, num_seqs, num_q_heads, max_blocks, partition_tokens, &pl))) return rc;
+  if (mode == 1 && !pl.partial) return fail(PA_ERR_INVALID, "pa_decode_partials needs partition_tokens > 0");
+  if (mode == 0 && num_seqs > 0 && !out) return fail(PA_ERR_INVALID, "out is NULL");
+  if (pl.partial && (!workspace || workspace_bytes < pl.ws_bytes))
+    return fail(PA_ERR_INVALID, "workspace of %llu bytes needed", static_cast<unsigned long long>(pl.ws_bytes));
+  if (num_seqs == 0) return PA_OK;
+  const pa::DecodeLaunch d = make_launch(layer, q, num_q_heads, tables, max_blocks, lens, num_seqs,
+                                         scale, pl, out, workspace);
+  auto s = static_cast<hipStream_t>(stream);
+  const bool rec = p->profiling && p->n_records < p->max_records;
+  const int base = 3 * p->n_records;
+  if (rec) record(p, base, s);
+  hipError_t e = pa::launch_decode(p->geom, d, pl.partial, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (rec) record(p, base + 1, s);
+  if (pl.partial && mode == 0) {
+    e = pa::launch_lse_reduce(p->geom, d, s);
+    if (e != hipSuccess) return hip_fail(e, "lse_reduce launch");
+  }
+  if (rec) {
+    record(p, base + 2, s);
+    p->has_reduce[p->n_records] = (pl.partial && mode == 0) ? 1 : 0;
+    ++p->n_records;
+  }
+  return PA_OK;
+}
+
+int pa_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
+              const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+              int32_t num_seqs, float scale, int32_t partition_tokens, void* out, void* workspace,
+              uint64_t workspace_bytes, void* stream) {
+  return run_decode(p, layer, q, num_q_heads, block_tables, max_blocks, context_lens, num_seqs,
+                    scale, partition_tokens, out, workspace, workspace_bytes, stream, 0);
+}
+
+int pa_decode_partials(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
+                       const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                       int32_t num_seqs, float scale, int32_t partition_tokens, void* workspace,
+                       uint64_t workspace_bytes, void* stream) {
+  if (partition_tokens <= 0) return fail(PA_ERR_INVALID, "pa_decode_partials needs partition_tokens > 0");
+  return run_decode(p, layer, q, num_q_heads, block_tables, max_blocks, context_lens, num_seqs,
+                    scale, partition_tokens, nullptr, workspace, workspace_bytes, stream, 1);
+}
+
+int pa_lse_reduce(pa_pool* p, const void* workspace, uint64_t workspace_bytes,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t max_blocks, int32_t partition_tokens, void* out, void* stream) {
+  int rc = check_bound(p);
+  if (rc) return rc;
+  if (partition_tokens <= 0) return fail(PA_ERR_INVALID, "pa_lse_reduce needs partition_tokens > 0");
+  Plan pl;
+  if ((rc = make_plan(p, num_seqs, num_q_heads, max_blocks, partition_tokens, &pl))) return rc;
+  if (num_seqs == 0) return PA_OK;
+  if (!workspace || workspace_bytes < pl.ws_bytes || !out || !context_lens)
+    return fail(PA_ERR_INVALID, "workspace of %llu bytes, out and context_lens needed",
+                static_cast<unsigned long long>(pl.ws_bytes));
+  const pa::DecodeLaunch d = make_launch(0, nullptr, num_q_heads, nullptr, max_blocks, context_lens,
+                                         num_seqs, 1.0f, pl, out, const_cast<void*>(workspace));
+  const hipError_t e = pa::launch_lse_reduce(p->geom, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : hip_fail(e, "lse_reduce launch");
+}
+
+int pa_device_status(pa_pool* p, uint32_t* flags_out, int32_t clear, void* stream) {
+  int rc = check_bound(p);
+  if (rc) return rc;
+  if (!flags_out) return fail(PA_ERR_INVALID, "flags_out is NULL");
+  auto s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, p->geom.status, sizeof(v), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading device status");
+  *flags_out = v;
+  if (clear) {
+    const uint32_t zero = 0;
+    e = hipMemcpyAsync(p->geom.status, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "clearing device status");
+  }
+  return PA_OK;
+}
+
+int pa_profile_begin(pa_pool* p, int32_t max_launches) {
+  int rc = check_bound(p);
+  if (rc) return rc;
+  if (max_launches < 1) return fail(PA_ERR_INVALID, "max_launches must be >= 1");
+  const size_t need = 3ull * max_launches;
+  while (p->ev.size() < need) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+    p->ev.push_back(e);
+  }
+  p->has_reduce.assign(max_launches, 0);
+  p->max_records = max_launches;
+  p->n_records = 0;
+  p->profiling = true;
+  return PA_OK;
+}
+
+int pa_profile_end(pa_pool* p, pa_profile* out) {
+  int rc = check_bound(p);
+  if (rc) return rc;
+  if (!out) return fail(PA_ERR_INVALID, "out is NULL");
+  pa_profile r{};
+  for (int32_t i = 0; i < p->n_records; ++i) {
+    hipError_t e = hipEventSynchronize(p->ev[3 * i + 2]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, p->ev[3 * i], p->ev[3 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    r.decode_ms += ms;
+    ++r.decode_launches;
+    if (p->has_reduce[i]) {
+      e = hipEventElapsedTime(&ms, p->ev[3 * i + 1], p->ev[3 * i + 2]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      r.reduce_ms += ms;
+      ++r.reduce_launches;
+    }
+  }
+  p->profiling = false;
+  p->n_records = 0;
+  *out = r;
+  return PA_OK;
+}
+
+}  // extern "C"

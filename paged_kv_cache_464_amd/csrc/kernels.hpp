@@ -1,0 +1,42 @@
+// Launchers of the HIP kernels (gfx950).  All take a PoolGeom of a bound pool
+// and enqueue on `stream`; they return the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "layout.hpp"
+
+namespace pa {
+
+constexpr uint32_t kDevBadSlot = 1u;
+constexpr uint32_t kDevBadBlock = 2u;
+constexpr uint32_t kDevBadLen = 4u;
+
+hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k_new, const void* v_new,
+                           const int32_t* slots, int n_tokens, hipStream_t stream);
+hipError_t launch_gather_kv(const PoolGeom& g, int layer, const int32_t* slots, int n_tokens,
+                            void* k_out, void* v_out, hipStream_t stream);
+hipError_t launch_copy_blocks(const PoolGeom& g, const int32_t* src, const int32_t* dst, int n,
+                              hipStream_t stream);
+
+struct DecodeLaunch {
+  int layer;
+  const void* q;
+  const int32_t* tables;
+  const int32_t* lens;
+  void* out;       // fp16 [S][Hq][D] (single pass / reduce)
+  float* part_m;   // [S][Hq][C]
+  float* part_l;   // [S][Hq][C]
+  float* part_o;   // [S][Hq][C][D]
+  int num_seqs, num_q_heads, max_blocks;
+  int partition_tokens;  // tokens per chunk (single pass: covers max_blocks*block_size)
+  int num_partitions;    // C
+  float scale;
+};
+
+hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, bool partial, hipStream_t stream);
+hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream);
+
+}  // namespace pa

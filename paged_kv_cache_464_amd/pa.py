@@ -1,0 +1,401 @@
+"""Python binding of libpa with the C ABI's names (argument marshalling only).
+
+Every function here converts Python/torch arguments to the plain pointers and
+sizes of include/pa.h, checks that device tensors have the shapes, dtypes and
+devices the kernels assume (so a wrong shape is an exception on the host, not
+an out-of-bounds access on the GPU), calls the C function and raises on a
+non-zero status.  All computation happens in libpa.so.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (PA_DTYPE_FP16, PA_DTYPE_FP8_E4M3, PA_ERR_BAD_SEQ, PA_ERR_NO_BLOCKS,  # noqa: F401
+                   PA_DEV_BAD_BLOCK, PA_DEV_BAD_LEN, PA_DEV_BAD_SLOT)
+
+
+class PAError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libpa error {code}: {msg}")
+        self.code = code
+
+
+class NoBlocksError(PAError):
+    pass
+
+
+class BadSeqError(PAError):
+    pass
+
+
+def _check(rc):
+    if rc != 0:
+        msg = _lib.load().pa_last_error().decode()
+        cls = {PA_ERR_NO_BLOCKS: NoBlocksError, PA_ERR_BAD_SEQ: BadSeqError}.get(rc, PAError)
+        raise cls(rc, msg)
+
+
+def _L():
+    return _lib.load()
+
+
+def _i32_host(a):
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _stream(stream):
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+def _dev(t, dtype, shape=None, name="tensor"):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return C.c_void_p(t.data_ptr())
+
+
+# ---- pool ------------------------------------------------------------------
+
+def pa_pool_create(layers, kv_heads, head_dim, block_size, dtype, num_blocks) -> int:
+    h = C.c_void_p()
+    _check(_L().pa_pool_create(layers, kv_heads, head_dim, block_size, dtype, num_blocks, C.byref(h)))
+    return h.value
+
+
+def pa_pool_destroy(h):
+    _check(_L().pa_pool_destroy(C.c_void_p(h)))
+
+
+def pa_pool_info_get(h) -> dict:
+    info = _lib.pa_pool_info()
+    _check(_L().pa_pool_info_get(C.c_void_p(h), C.byref(info)))
+    return {f: getattr(info, f) for f, _ in info._fields_}
+
+
+def pa_pool_set_free_order(h, perm):
+    arr, ptr = _i32_host(perm)
+    _check(_L().pa_pool_set_free_order(C.c_void_p(h), ptr, len(arr)))
+
+
+def pa_pool_bind(h, dev_ptr: int, k_scales=None, v_scales=None):
+    def fp(a):
+        if a is None:
+            return None, None
+        arr = np.ascontiguousarray(np.asarray(a, dtype=np.float32).reshape(-1))
+        return arr, arr.ctypes.data_as(C.POINTER(C.c_float))
+    ka, kp = fp(k_scales)
+    va, vp = fp(v_scales)
+    _check(_L().pa_pool_bind(C.c_void_p(h), C.c_void_p(dev_ptr), kp, vp))
+
+
+# ---- block manager ---------------------------------------------------------
+
+def pa_seq_create(h) -> int:
+    s = C.c_int32()
+    _check(_L().pa_seq_create(C.c_void_p(h), C.byref(s)))
+    return s.value
+
+
+def pa_alloc(h, seq, n_tokens, stream=0):
+    """Returns (slots int32[n_tokens], (src, dst) or None)."""
+    slots = np.empty(max(int(n_tokens), 0), dtype=np.int32)
+    cow = np.full(2, -1, dtype=np.int32)
+    st = C.c_void_p(0) if stream == 0 else _stream(stream)
+    _check(_L().pa_alloc(C.c_void_p(h), int(seq), int(n_tokens),
+                         slots.ctypes.data_as(C.POINTER(C.c_int32)),
+                         cow.ctypes.data_as(C.POINTER(C.c_int32)), st))
+    return slots, (None if cow[0] < 0 else (int(cow[0]), int(cow[1])))
+
+
+def pa_fork(h, parent) -> int:
+    c = C.c_int32()
+    _check(_L().pa_fork(C.c_void_p(h), int(parent), C.byref(c)))
+    return c.value
+
+
+def pa_free(h, seq):
+    _check(_L().pa_free(C.c_void_p(h), int(seq)))
+
+
+def pa_seq_len(h, seq):
+    ln, nb = C.c_int32(), C.c_int32()
+    _check(_L().pa_seq_len(C.c_void_p(h), int(seq), C.byref(ln), C.byref(nb)))
+    return ln.value, nb.value
+
+
+def pa_block_tables(h, seqs, max_blocks):
+    s, sp = _i32_host(seqs)
+    tables = np.empty((len(s), int(max_blocks)), dtype=np.int32)
+    lens = np.empty(len(s), dtype=np.int32)
+    _check(_L().pa_block_tables(C.c_void_p(h), sp, len(s), int(max_blocks),
+                                tables.ctypes.data_as(C.POINTER(C.c_int32)),
+                                lens.ctypes.data_as(C.POINTER(C.c_int32))))
+    return tables, lens
+
+
+def pa_pool_stats(h) -> dict:
+    st = _lib.pa_stats()
+    _check(_L().pa_pool_stats(C.c_void_p(h), C.byref(st)))
+    return {f: getattr(st, f) for f, _ in st._fields_}
+
+
+def pa_refcounts(h):
+    n = pa_pool_info_get(h)["num_blocks"]
+    out = np.empty(n, dtype=np.int32)
+    _check(_L().pa_refcounts(C.c_void_p(h), out.ctypes.data_as(C.POINTER(C.c_int32))))
+    return out
+
+
+def pa_free_queue(h):
+    n = pa_pool_info_get(h)["num_blocks"]
+    out = np.empty(n, dtype=np.int32)
+    cnt = C.c_int32()
+    _check(_L().pa_free_queue(C.c_void_p(h), out.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(cnt)))
+    return out[:cnt.value].copy()
+
+
+# ---- device operations ------------------------------------------------------
+
+def pa_write_kv(h, layer, k_new, v_new, slot_mapping, stream=None):
+    info = pa_pool_info_get(h)
+    n = slot_mapping.numel()
+    shape = (n, info["kv_heads"], info["head_dim"])
+    kp = _dev(k_new, torch.float16, shape, "k_new")
+    vp = _dev(v_new, torch.float16, shape, "v_new")
+    sp = _dev(slot_mapping, torch.int32, (n,), "slot_mapping")
+    _check(_L().pa_write_kv(C.c_void_p(h), int(layer), kp, vp, sp, n, _stream(stream)))
+
+
+def pa_gather_kv(h, layer, slot_mapping, k_out, v_out, stream=None):
+    info = pa_pool_info_get(h)
+    n = slot_mapping.numel()
+    dt = torch.float16 if info["dtype"] == PA_DTYPE_FP16 else torch.uint8
+    shape = (n, info["kv_heads"], info["head_dim"])
+    sp = _dev(slot_mapping, torch.int32, (n,), "slot_mapping")
+    kp = _dev(k_out, dt, shape, "k_out")
+    vp = _dev(v_out, dt, shape, "v_out")
+    _check(_L().pa_gather_kv(C.c_void_p(h), int(layer), sp, n, kp, vp, _stream(stream)))
+
+
+def pa_copy_blocks(h, src, dst, stream=None):
+    s, sp = _i32_host(src)
+    d, dp = _i32_host(dst)
+    if len(s) != len(d):
+        raise ValueError("src and dst differ in length")
+    _check(_L().pa_copy_blocks(C.c_void_p(h), sp, dp, len(s), _stream(stream)))
+
+
+def pa_decode_workspace_bytes(h, num_seqs, num_q_heads, max_blocks, partition_tokens=0) -> int:
+    out = C.c_uint64()
+    _check(_L().pa_decode_workspace_bytes(C.c_void_p(h), int(num_seqs), int(num_q_heads),
+                                          int(max_blocks), int(partition_tokens), C.byref(out)))
+    return out.value
+
+
+def _decode_args(h, q, block_tables, context_lens):
+    info = pa_pool_info_get(h)
+    if q.dim() != 3 or q.shape[2] != info["head_dim"]:
+        raise ValueError(f"q must be [num_seqs][num_q_heads][{info['head_dim']}]")
+    s, hq = int(q.shape[0]), int(q.shape[1])
+    if block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    mb = int(block_tables.shape[1])
+    qp = _dev(q, torch.float16, None, "q")
+    tp = _dev(block_tables, torch.int32, None, "block_tables")
+    lp = _dev(context_lens, torch.int32, (s,), "context_lens")
+    return info, s, hq, mb, qp, tp, lp
+
+
+def _workspace(h, s, hq, mb, partition_tokens, workspace, device):
+    need = pa_decode_workspace_bytes(h, s, hq, mb, partition_tokens)
+    if need == 0:
+        return C.c_void_p(0), 0, workspace
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    return C.c_void_p(workspace.data_ptr()), need, workspace
+
+
+def pa_decode(h, layer, q, block_tables, context_lens, out=None, scale=None, partition_tokens=0,
+              workspace=None, stream=None):
+    info, s, hq, mb, qp, tp, lp = _decode_args(h, q, block_tables, context_lens)
+    if out is None:
+        out = torch.empty_like(q)
+    op = _dev(out, torch.float16, tuple(q.shape), "out")
+    wp, wb, workspace = _workspace(h, s, hq, mb, partition_tokens, workspace, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(info["head_dim"])
+    _check(_L().pa_decode(C.c_void_p(h), int(layer), qp, hq, tp, mb, lp, s, float(scale),
+                          int(partition_tokens), op, wp, wb, _stream(stream)))
+    return out
+
+
+def pa_decode_partials(h, layer, q, block_tables, context_lens, partition_tokens, scale=None,
+                       workspace=None, stream=None):
+    """Returns (m, l, o) views into the workspace: [S][Hq][C], [S][Hq][C], [S][Hq][C][d]."""
+    info, s, hq, mb, qp, tp, lp = _decode_args(h, q, block_tables, context_lens)
+    wp, wb, workspace = _workspace(h, s, hq, mb, partition_tokens, workspace, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(info["head_dim"])
+    _check(_L().pa_decode_partials(C.c_void_p(h), int(layer), qp, hq, tp, mb, lp, s, float(scale),
+                                   int(partition_tokens), wp, wb, _stream(stream)))
+    return workspace_views(workspace, s, hq, mb * info["block_size"], partition_tokens, info["head_dim"])
+
+
+def workspace_views(workspace, num_seqs, num_q_heads, max_tokens, partition_tokens, head_dim):
+    """(m, l, o) float32 views of a partitioned-decode workspace (layout of include/pa.h)."""
+    c = -(-int(max_tokens) // int(partition_tokens))
+    rows = num_seqs * num_q_heads * c
+
+    def up(x):
+        return (x + 255) // 256 * 256
+    off_l = up(rows * 4)
+    off_o = off_l + up(rows * 4)
+    f = workspace.view(torch.uint8)
+    m = f[:rows * 4].view(torch.float32).view(num_seqs, num_q_heads, c)
+    l = f[off_l:off_l + rows * 4].view(torch.float32).view(num_seqs, num_q_heads, c)
+    o = f[off_o:off_o + rows * head_dim * 4].view(torch.float32).view(num_seqs, num_q_heads, c, head_dim)
+    return m, l, o
+
+
+def pa_lse_reduce(h, workspace, context_lens, num_q_heads, max_blocks, partition_tokens, out,
+                  stream=None):
+    s = int(context_lens.numel())
+    lp = _dev(context_lens, torch.int32, (s,), "context_lens")
+    info = pa_pool_info_get(h)
+    op = _dev(out, torch.float16, (s, num_q_heads, info["head_dim"]), "out")
+    need = pa_decode_workspace_bytes(h, s, num_q_heads, max_blocks, partition_tokens)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check(_L().pa_lse_reduce(C.c_void_p(h), C.c_void_p(workspace.data_ptr()), need, lp, s,
+                              int(num_q_heads), int(max_blocks), int(partition_tokens), op,
+                              _stream(stream)))
+    return out
+
+
+def pa_device_status(h, clear=False, stream=None) -> int:
+    v = C.c_uint32()
+    _check(_L().pa_device_status(C.c_void_p(h), C.byref(v), 1 if clear else 0, _stream(stream)))
+    return v.value
+
+
+def pa_profile_begin(h, max_launches):
+    _check(_L().pa_profile_begin(C.c_void_p(h), int(max_launches)))
+
+
+def pa_profile_end(h) -> dict:
+    p = _lib.pa_profile()
+    _check(_L().pa_profile_end(C.c_void_p(h), C.byref(p)))
+    return {f: getattr(p, f) for f, _ in p._fields_}
+
+
+# ---- convenience owner of a bound pool ------------------------------------------
+
+class PagedKVPool:
+    """A pool descriptor plus the torch-allocated device buffer it is bound to."""
+
+    def __init__(self, layers, kv_heads, head_dim, block_size, num_blocks, dtype="fp16",
+                 device="cuda", free_order=None, k_scales=None, v_scales=None, bind=True):
+        code = {"fp16": PA_DTYPE_FP16, "fp8": PA_DTYPE_FP8_E4M3}[dtype]
+        self.handle = pa_pool_create(layers, kv_heads, head_dim, block_size, code, num_blocks)
+        self.dtype = dtype
+        self.buffer = None
+        try:
+            if free_order is not None:
+                pa_pool_set_free_order(self.handle, free_order)
+            self.info = pa_pool_info_get(self.handle)
+            if bind:
+                total = self.info["total_bytes"]
+                self.buffer = torch.empty(total + 256, dtype=torch.uint8, device=device)
+                base = self.buffer.data_ptr()
+                aligned = (base + 255) // 256 * 256
+                self.base_ptr = aligned
+                pa_pool_bind(self.handle, aligned, k_scales, v_scales)
+                self.info = pa_pool_info_get(self.handle)
+        except Exception:
+            pa_pool_destroy(self.handle)
+            self.handle = None
+            raise
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                pa_pool_destroy(self.handle)
+            except Exception:
+                pass
+            self.handle = None
+
+    @property
+    def block_size(self):
+        return self.info["block_size"]
+
+    def pool_bytes(self):
+        """The pool's data region (K and V of every layer) as a uint8 tensor view."""
+        off = self.base_ptr - self.buffer.data_ptr()
+        return self.buffer[off:off + self.info["kv_bytes"]]
+
+    def seq_create(self):
+        return pa_seq_create(self.handle)
+
+    def alloc(self, seq, n, stream=None):
+        return pa_alloc(self.handle, seq, n, stream if self.buffer is not None else 0)
+
+    def fork(self, parent):
+        return pa_fork(self.handle, parent)
+
+    def free(self, seq):
+        pa_free(self.handle, seq)
+
+    def seq_len(self, seq):
+        return pa_seq_len(self.handle, seq)
+
+    def block_tables(self, seqs, max_blocks):
+        return pa_block_tables(self.handle, seqs, max_blocks)
+
+    def stats(self):
+        return pa_pool_stats(self.handle)
+
+    def refcounts(self):
+        return pa_refcounts(self.handle)
+
+    def free_queue(self):
+        return pa_free_queue(self.handle)
+
+    def write_kv(self, layer, k_new, v_new, slot_mapping, stream=None):
+        pa_write_kv(self.handle, layer, k_new, v_new, slot_mapping, stream)
+
+    def gather_kv(self, layer, slot_mapping, stream=None):
+        dt = torch.float16 if self.dtype == "fp16" else torch.uint8
+        n = slot_mapping.numel()
+        shape = (n, self.info["kv_heads"], self.info["head_dim"])
+        k = torch.zeros(shape, dtype=dt, device=slot_mapping.device)
+        v = torch.zeros(shape, dtype=dt, device=slot_mapping.device)
+        pa_gather_kv(self.handle, layer, slot_mapping, k, v, stream)
+        return k, v
+
+    def copy_blocks(self, src, dst, stream=None):
+        pa_copy_blocks(self.handle, src, dst, stream)
+
+    def decode(self, layer, q, block_tables, context_lens, **kw):
+        return pa_decode(self.handle, layer, q, block_tables, context_lens, **kw)
+
+    def device_status(self, clear=False):
+        return pa_device_status(self.handle, clear)

@@ -9,3 +9,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_sessionstart(session):
+    # The HIP library is built in-tree; build it once if this checkout has none.
+    lib = os.path.join(ROOT, "paged_kv_cache_464_amd", "libpa.so")
+    if not os.path.exists(lib):
+        from paged_kv_cache_464_amd import build as _build
+        _build.build()
