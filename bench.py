@@ -19,6 +19,7 @@ oracle timed on this host on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -123,32 +124,49 @@ class GqaStep:
         self.k_new = normal_fp16((self.L, self.S, self.hkv, 128), w.seed, 2, self.dev)
         self.v_new = normal_fp16((self.L, self.S, self.hkv, 128), w.seed, 3, self.dev)
         self.out = torch.empty((self.L, self.S, self.hq, 128), dtype=torch.float16, device=self.dev)
-        max_blocks_cap = -(-(self.prefill + total_steps) // self.bs)
-        ws = pa.pa_decode_workspace_bytes(self.pool.handle, self.S, self.hq, max_blocks_cap,
+        # Block tables are uploaded at a fixed width with room for every appended token.
+        self.mb_cap = -(-(self.prefill + total_steps) // self.bs)
+        ws = pa.pa_decode_workspace_bytes(self.pool.handle, self.S, self.hq, self.mb_cap,
                                           self.partition)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.dev)
+        # Step metadata (slot mapping, lengths, block tables) is packed into one
+        # int32 buffer so that each step makes a single upload: two pinned host
+        # copies used alternately (each guarded by the event of the upload that
+        # last read it) and one device copy.
+        n_meta = self.S * (2 + self.mb_cap)
+        self.pinned = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self.uploaded = [torch.cuda.Event(), torch.cuda.Event()]
+        self.meta_d = torch.empty(n_meta, dtype=torch.int32, device=self.dev)
+        self.slots_d = self.meta_d[:self.S]
+        self.lens_d = self.meta_d[self.S:2 * self.S]
+        self.tables_d = self.meta_d[2 * self.S:].view(self.S, self.mb_cap)
+        self.n_step = 0
+        self.stream = torch.cuda.current_stream().cuda_stream  # every launch goes here
         self.kv_bytes_log = []
         self.first_step_slots = None
         torch.cuda.synchronize()
 
     def step(self):
-        torch, pa = self.torch, self.pa
-        slots = np.empty(self.S, dtype=np.int32)
+        pa = self.pa
+        k = self.n_step % 2
+        self.n_step += 1
+        self.uploaded[k].synchronize()  # the upload that last read this pinned set is done
+        meta = self.pinned[k].numpy()
+        slots = meta[:self.S]
         for i, s in enumerate(self.seqs):
             slots[i] = self.pool.alloc(s, 1)[0][0]
         if self.first_step_slots is None:
             self.first_step_slots = slots.copy()
-        length = self.pool.seq_len(self.seqs[0])[0]
-        max_blocks = -(-length // self.bs)
-        tables, lens = self.pool.block_tables(self.seqs, max_blocks)
-        slots_d = torch.from_numpy(slots).pin_memory().to(self.dev, non_blocking=True)
-        tables_d = torch.from_numpy(tables).pin_memory().to(self.dev, non_blocking=True)
-        lens_d = torch.from_numpy(lens).pin_memory().to(self.dev, non_blocking=True)
-        h = self.pool.handle
+        tables, lens = self.pool.block_tables(self.seqs, self.mb_cap)
+        meta[self.S:2 * self.S] = lens
+        meta[2 * self.S:] = tables.reshape(-1)
+        self.meta_d.copy_(self.pinned[k], non_blocking=True)
+        self.uploaded[k].record()
+        h, st = self.pool.handle, self.stream
         for layer in range(self.L):
-            pa.pa_write_kv(h, layer, self.k_new[layer], self.v_new[layer], slots_d)
-            pa.pa_decode(h, layer, self.q[layer], tables_d, lens_d, out=self.out[layer],
-                         partition_tokens=self.partition, workspace=self.workspace)
+            pa.pa_write_kv(h, layer, self.k_new[layer], self.v_new[layer], self.slots_d, stream=st)
+            pa.pa_decode(h, layer, self.q[layer], self.tables_d, self.lens_d, out=self.out[layer],
+                         partition_tokens=self.partition, workspace=self.workspace, stream=st)
         self.kv_bytes_log.append(int(lens.astype(np.int64).sum()) * 2 * self.hkv * 128 * 2)
         return lens
 
@@ -227,24 +245,28 @@ def main(argv=None):
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = bench.cpu_baseline(args.cpu_budget)
-
     bench.kv_bytes_log.clear()
     pa.pa_profile_begin(bench.pool.handle, args.steps * bench.L)
+    lens_seen = []
+    gc.collect()
+    gc.disable()  # no collector pauses inside the timed steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    lens_seen = []
     for _ in range(args.steps):
         lens_seen.append(int(bench.step()[0]))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     prof = pa.pa_profile_end(bench.pool.handle)
     status = bench.pool.device_status()
     if status:
         print(f"device status flags {status:#x}", file=sys.stderr)
         return 1
+    # The CPU oracle runs after the timed steps so that its BLAS threads cannot
+    # compete with the host side of the step.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = bench.cpu_baseline(args.cpu_budget)
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = bench.S * args.steps / elapsed

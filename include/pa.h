@@ -198,9 +198,12 @@ int pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num
  *   out          device fp16 [num_seqs][num_q_heads][head_dim]
  * Query head h reads KV head h / (num_q_heads / kv_heads); num_q_heads must
  * be a multiple of kv_heads with a group of at most 32.
- * partition_tokens: 0 lets the library choose; -1 forces one pass per
- * (sequence, KV head); P > 0 (a multiple of 16 and of block_size) splits each
- * context into chunks of P tokens whose partials are merged by log-sum-exp.
+ * partition_tokens: 0 lets the library choose (one pass per (sequence, KV
+ * head) when num_seqs * kv_heads >= the device's CU count or
+ * max_blocks * block_size <= 1024; otherwise ceil(CUs / (num_seqs * kv_heads))
+ * chunks per context); -1 forces one pass per (sequence, KV head); P > 0 (a
+ * multiple of 16 and of block_size) splits each context into chunks of P
+ * tokens whose partials are merged by log-sum-exp.
  * workspace: device memory of pa_decode_workspace_bytes() bytes (may be NULL
  * when that is 0).  Out-of-range table entries or lengths never cause an
  * out-of-bounds access; they set PA_DEV_* bits instead. */
@@ -232,10 +235,12 @@ int pa_lse_reduce(pa_pool* pool, const void* workspace, uint64_t workspace_bytes
 /* Read (and optionally clear) the pool's device status word; synchronises `stream`. */
 int pa_device_status(pa_pool* pool, uint32_t* flags_out, int32_t clear, void* stream);
 
-/* Kernel timing: while enabled, every pa_decode records HIP events around its
- * attention kernel and its reduce kernel on the launch stream (up to
- * max_launches launches).  pa_profile_end synchronises those events, returns
- * the summed durations and disables timing. */
+/* Kernel timing: while enabled, every pa_decode / pa_decode_partials launch
+ * (up to max_launches of them) is dispatched with HIP start/stop events that
+ * the dispatch itself stamps at the kernel's start and end on the launch
+ * stream (hipExtLaunchKernel), for the attention kernel and for the reduce
+ * kernel; no extra packets are enqueued.  pa_profile_end synchronises those
+ * events, returns the summed durations and disables timing. */
 int pa_profile_begin(pa_pool* pool, int32_t max_launches);
 int pa_profile_end(pa_pool* pool, pa_profile* out);
 

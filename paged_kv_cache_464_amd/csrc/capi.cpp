@@ -34,7 +34,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
-constexpr int kDefaultPartition = 512;
+constexpr int kMinSplitTokens = 1024;  // shorter contexts always run in one pass
 
 }  // namespace
 
@@ -49,7 +49,7 @@ struct pa_pool {
   // kernel timing
   bool profiling = false;
   int32_t max_records = 0;
-  std::vector<hipEvent_t> ev;  // 3 per record: before decode, after decode, after reduce
+  std::vector<hipEvent_t> ev;  // 4 per record: decode start/end, reduce start/end (if any)
   std::vector<int8_t> has_reduce;
   int32_t n_records = 0;
 
@@ -88,12 +88,23 @@ int make_plan(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t m
   const int group = num_q_heads / p->kv_heads;
   if (group > 32) return fail(PA_ERR_INVALID, "query heads per KV head %d > 32", group);
   const int64_t t_cap = static_cast<int64_t>(max_blocks) * p->block_size;
+  const int64_t units = static_cast<int64_t>(num_seqs) * p->kv_heads;
   int P;
   if (partition_tokens == -1) {
     P = 0;
   } else if (partition_tokens == 0) {
-    const int64_t units = static_cast<int64_t>(num_seqs) * p->kv_heads;
-    P = (t_cap <= kDefaultPartition || units >= 4ll * p->num_cus) ? 0 : kDefaultPartition;
+    // One workgroup per (sequence, KV head) streams its whole context at full
+    // rate once every CU has one; with fewer units, split each context into
+    // just enough chunks to give every CU a workgroup (measured on MI355X:
+    // more, shorter chunks only add partial writes and start-up latency).
+    P = 0;
+    if (t_cap > kMinSplitTokens && units < p->num_cus) {
+      const int64_t parts = (p->num_cus + units - 1) / units;
+      const int64_t quantum = p->block_size > 16 ? p->block_size : 16;
+      const int64_t len = (t_cap + parts - 1) / parts;
+      const int64_t chunk = (len + quantum - 1) / quantum * quantum;
+      if (chunk < t_cap) P = static_cast<int>(chunk);
+    }
   } else {
     if (partition_tokens % 16 != 0 || partition_tokens % p->block_size != 0)
       return fail(PA_ERR_INVALID, "partition_tokens %d must be a multiple of 16 and of block_size %d",
@@ -401,10 +412,6 @@ int pa_decode_workspace_bytes(const pa_pool* p, int32_t num_seqs, int32_t num_q_
   return PA_OK;
 }
 
-static void record(pa_pool* p, int slot, hipStream_t s) {
-  (void)hipEventRecord(p->ev[slot], s);
-}
-
 static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
                       const int32_t* tables, int32_t max_blocks, const int32_t* lens,
                       int32_t num_seqs, float scale, int32_t partition_tokens, void* out,
@@ -423,18 +430,16 @@ static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_he
                                          scale, pl, out, workspace);
   auto s = static_cast<hipStream_t>(stream);
   const bool rec = p->profiling && p->n_records < p->max_records;
-  const int base = 3 * p->n_records;
-  if (rec) record(p, base, s);
-  hipError_t e = pa::launch_decode(p->geom, d, pl.partial, s);
+  hipEvent_t* ev = rec ? &p->ev[4 * static_cast<size_t>(p->n_records)] : nullptr;
+  const bool reduced = pl.partial && mode == 0;
+  hipError_t e = pa::launch_decode(p->geom, d, pl.partial, s, rec ? ev[0] : nullptr, rec ? ev[1] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (rec) record(p, base + 1, s);
-  if (pl.partial && mode == 0) {
-    e = pa::launch_lse_reduce(p->geom, d, s);
+  if (reduced) {
+    e = pa::launch_lse_reduce(p->geom, d, s, rec ? ev[2] : nullptr, rec ? ev[3] : nullptr);
     if (e != hipSuccess) return hip_fail(e, "lse_reduce launch");
   }
   if (rec) {
-    record(p, base + 2, s);
-    p->has_reduce[p->n_records] = (pl.partial && mode == 0) ? 1 : 0;
+    p->has_reduce[p->n_records] = reduced ? 1 : 0;
     ++p->n_records;
   }
   return PA_OK;
@@ -498,10 +503,11 @@ int pa_profile_begin(pa_pool* p, int32_t max_launches) {
   int rc = check_bound(p);
   if (rc) return rc;
   if (max_launches < 1) return fail(PA_ERR_INVALID, "max_launches must be >= 1");
-  const size_t need = 3ull * max_launches;
+  const size_t need = 4ull * max_launches;
   while (p->ev.size() < need) {
     hipEvent_t e;
-    const hipError_t err = hipEventCreate(&e);
+    // Agent-scope release: recording needs no system-wide cache write-back.
+    const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
     if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
     p->ev.push_back(e);
   }
@@ -518,15 +524,16 @@ int pa_profile_end(pa_pool* p, pa_profile* out) {
   if (!out) return fail(PA_ERR_INVALID, "out is NULL");
   pa_profile r{};
   for (int32_t i = 0; i < p->n_records; ++i) {
-    hipError_t e = hipEventSynchronize(p->ev[3 * i + 2]);
+    const hipEvent_t* ev = &p->ev[4 * static_cast<size_t>(i)];
+    hipError_t e = hipEventSynchronize(ev[p->has_reduce[i] ? 3 : 1]);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     float ms = 0.0f;
-    e = hipEventElapsedTime(&ms, p->ev[3 * i], p->ev[3 * i + 1]);
+    e = hipEventElapsedTime(&ms, ev[0], ev[1]);
     if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
     r.decode_ms += ms;
     ++r.decode_launches;
     if (p->has_reduce[i]) {
-      e = hipEventElapsedTime(&ms, p->ev[3 * i + 1], p->ev[3 * i + 2]);
+      e = hipEventElapsedTime(&ms, ev[2], ev[3]);
       if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
       r.reduce_ms += ms;
       ++r.reduce_launches;

@@ -36,7 +36,10 @@ struct DecodeLaunch {
   float scale;
 };
 
-hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, bool partial, hipStream_t stream);
-hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream);
+// t0/t1: optional events stamped at the kernel's start and end (null: untimed).
+hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, bool partial, hipStream_t stream,
+                         hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
+                             hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 }  // namespace pa

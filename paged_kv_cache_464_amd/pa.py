@@ -79,7 +79,21 @@ def pa_pool_create(layers, kv_heads, head_dim, block_size, dtype, num_blocks) ->
     return h.value
 
 
+# Per-handle caches of values that cannot change once a pool is bound (its
+# geometry, and the workspace size of a launch shape), so that the per-launch
+# wrappers below make one library call instead of three.
+_BOUND_INFO = {}
+_WS_BYTES = {}
+
+
+def _forget(h):
+    _BOUND_INFO.pop(h, None)
+    for key in [k for k in _WS_BYTES if k[0] == h]:
+        del _WS_BYTES[key]
+
+
 def pa_pool_destroy(h):
+    _forget(h)
     _check(_L().pa_pool_destroy(C.c_void_p(h)))
 
 
@@ -87,6 +101,15 @@ def pa_pool_info_get(h) -> dict:
     info = _lib.pa_pool_info()
     _check(_L().pa_pool_info_get(C.c_void_p(h), C.byref(info)))
     return {f: getattr(info, f) for f, _ in info._fields_}
+
+
+def _info(h) -> dict:
+    info = _BOUND_INFO.get(h)
+    if info is None:
+        info = pa_pool_info_get(h)
+        if info["bound"]:
+            _BOUND_INFO[h] = info
+    return info
 
 
 def pa_pool_set_free_order(h, perm):
@@ -102,6 +125,7 @@ def pa_pool_bind(h, dev_ptr: int, k_scales=None, v_scales=None):
         return arr, arr.ctypes.data_as(C.POINTER(C.c_float))
     ka, kp = fp(k_scales)
     va, vp = fp(v_scales)
+    _forget(h)
     _check(_L().pa_pool_bind(C.c_void_p(h), C.c_void_p(dev_ptr), kp, vp))
 
 
@@ -174,7 +198,7 @@ def pa_free_queue(h):
 # ---- device operations ------------------------------------------------------
 
 def pa_write_kv(h, layer, k_new, v_new, slot_mapping, stream=None):
-    info = pa_pool_info_get(h)
+    info = _info(h)
     n = slot_mapping.numel()
     shape = (n, info["kv_heads"], info["head_dim"])
     kp = _dev(k_new, torch.float16, shape, "k_new")
@@ -184,7 +208,7 @@ def pa_write_kv(h, layer, k_new, v_new, slot_mapping, stream=None):
 
 
 def pa_gather_kv(h, layer, slot_mapping, k_out, v_out, stream=None):
-    info = pa_pool_info_get(h)
+    info = _info(h)
     n = slot_mapping.numel()
     dt = torch.float16 if info["dtype"] == PA_DTYPE_FP16 else torch.uint8
     shape = (n, info["kv_heads"], info["head_dim"])
@@ -210,7 +234,7 @@ def pa_decode_workspace_bytes(h, num_seqs, num_q_heads, max_blocks, partition_to
 
 
 def _decode_args(h, q, block_tables, context_lens):
-    info = pa_pool_info_get(h)
+    info = _info(h)
     if q.dim() != 3 or q.shape[2] != info["head_dim"]:
         raise ValueError(f"q must be [num_seqs][num_q_heads][{info['head_dim']}]")
     s, hq = int(q.shape[0]), int(q.shape[1])
@@ -224,7 +248,12 @@ def _decode_args(h, q, block_tables, context_lens):
 
 
 def _workspace(h, s, hq, mb, partition_tokens, workspace, device):
-    need = pa_decode_workspace_bytes(h, s, hq, mb, partition_tokens)
+    key = (h, s, hq, mb, int(partition_tokens))
+    need = _WS_BYTES.get(key)
+    if need is None:
+        need = pa_decode_workspace_bytes(h, s, hq, mb, partition_tokens)
+        if _info(h)["bound"]:
+            _WS_BYTES[key] = need
     if need == 0:
         return C.c_void_p(0), 0, workspace
     if workspace is None:
