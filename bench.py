@@ -2,19 +2,27 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Default workload: 32 layers, 32 query / 8 KV heads, head_dim 128, fp16 K/V,
-16-token blocks, 32 sequences with 4095 prefilled tokens, block placement a
-seeded permutation of the pool.  One step = for every sequence append one
-token (block manager), upload slot mapping / block tables / lengths, then for
-each of the 32 layers scatter the new tokens' K/V into the cache and run paged
-decode attention over the whole context (the first timed step attends to 4096
-tokens).  The timed region holds exactly K steps; inputs are resident in HBM.
+Default workload ``gqa_32x4096``: 32 layers, 32 query / 8 KV heads, head_dim
+128, fp16 K/V, 16-token blocks, 32 sequences prefilled to 4095 tokens, block
+placement a seeded permutation of the pool.  One step = append one token to
+every sequence (host block manager), upload the slot mapping, lengths and
+block tables (one packed copy), then for each of the 32 layers scatter the new
+tokens' K/V into the cache (``pa_write_kv``) and run paged decode attention
+over the whole context (``pa_decode``).  The timed region holds exactly K
+steps; inputs are resident in HBM.
+
+The other workloads (``tiny``, ``cb_prefix``, ``long_ctx``,
+``fp8_{gqa,mqa}_bs{8,16,32}``) time one pool layer R times per step ("1 layer
+timed xR").  When one layer's KV would fit in the 256 MB last-level cache, the
+pool holds several copies of it and launch r reads copy r mod copies, so that
+the bandwidth figure is HBM's and not the cache's.
 
 Prints one JSON line.  ``roofline`` is for the decode attention kernel: its
-algorithmic KV bytes (each sequence's K and V, every KV head once) divided by
-its average duration from HIP events recorded around every launch on the
-launch stream during the timed steps.  ``cpu_baseline`` is the fp64 CPU
-oracle timed on this host on a bounded sample of the same workload.
+algorithmic KV bytes per launch (each sequence's K and V, every KV head once,
+plus the fp8 scales) divided by its average duration, from HIP events that
+the dispatches themselves stamp on the launch stream for every decode launch
+of the timed steps.  ``cpu_baseline`` is the fp64 CPU oracle timed on this
+host on a bounded sample of the same workload, after the timed steps.
 """
 from __future__ import annotations
 
@@ -22,7 +30,6 @@ import argparse
 import gc
 import hashlib
 import json
-import math
 import os
 import re
 import sys
@@ -36,9 +43,13 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: KV GB/s read + % HBM peak; tokens/s at 32×4096 GQA"
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_gqa_32x4096.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_464_amd", "csrc", f)
                   for f in ("decode_kernels.hip", "layout.hpp", "kernels.hpp")]
+LLC_BYTES = 256 << 20  # MI355X Infinity Cache
+CPU_SAMPLE_TOKENS = 1 << 18  # bound on the context tokens the CPU oracle is given
+BENCH_WORKLOADS = ["gqa_32x4096", "tiny", "cb_prefix", "long_ctx",
+                   "fp8_gqa_bs8", "fp8_gqa_bs16", "fp8_gqa_bs32",
+                   "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32"]
 
 
 def kernel_source_hash() -> str:
@@ -49,12 +60,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel sources; else None."""
-    if not os.path.exists(TRAFFIC_PROFILE):
+def traffic_profile_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.txt")
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    of this workload, if it was taken on the current kernel sources; else None."""
+    path = traffic_profile_path(workload)
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_PROFILE).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256:\s*(\w+)", text)
     m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m_hash and m_val) or m_hash.group(1) != kernel_source_hash():
@@ -81,53 +97,78 @@ def cpu_model() -> str:
     return "unknown"
 
 
-# ---------------------------------------------------------------------------
-# GQA decode step: 32 layers x 32 sequences x 4096 tokens
-# ---------------------------------------------------------------------------
+class DecodeBench:
+    """One workload's pool, resident inputs and timed step."""
 
-class GqaStep:
-    def __init__(self, args):
+    def __init__(self, name, args):
         import torch
 
         from paged_kv_cache_464_amd import pa
-        from workloads import free_order, normal_fp16, workload
+        from workloads import amax_scales, cb_prefix_script, free_order, normal_fp16, workload
 
         self.torch, self.pa = torch, pa
-        w = workload("gqa_32x4096")
-        self.w = w
+        self.name = name
+        w = self.w = workload(name)
         self.dev = "cuda"
-        self.L, self.S, self.hq, self.hkv, self.bs = w.layers, w.num_seqs, w.q_heads, w.kv_heads, w.block_size
-        self.prefill = w.context[0] - 1
+        self.S, self.hq, self.hkv, self.bs = w.num_seqs, w.q_heads, w.kv_heads, w.block_size
+        self.fp8 = w.dtype == "fp8"
+        self.elem = 1 if self.fp8 else 2
         total_steps = args.warmup + args.steps
-        # Exactly the 4096-token working set plus room for the appended tokens.
-        extra_blocks = self.S * (-(-(self.prefill + total_steps) // self.bs) - w.context[0] // self.bs)
-        self.num_blocks = w.num_blocks + max(extra_blocks, 0)
+        # Launches per step, and the distinct pool layers they rotate over.
+        self.R = w.layers if w.layers > 1 else w.repeats
+        layer_bytes = 2 * w.num_blocks * self.hkv * self.bs * 128 * self.elem
+        if w.layers > 1:
+            self.copies = w.layers
+        elif layer_bytes < (64 << 20):
+            self.copies = 1  # launch-latency bound: no bandwidth claim
+        else:
+            self.copies = max(1, -(-(4 * LLC_BYTES) // layer_bytes))
+        self.partition = w.partition_tokens if args.partition is None else args.partition
+        # Room for the appended tokens: one more block per sequence per 16 steps.
+        self.num_blocks = w.num_blocks + self.S * (-(-total_steps // self.bs) + 1)
         self.order = free_order(w.seed, self.num_blocks)
-        self.pool = pa.PagedKVPool(self.L, self.hkv, 128, self.bs, self.num_blocks, "fp16",
-                                   free_order=self.order)
-        self.partition = args.partition
-        self.seqs = [self.pool.seq_create() for _ in range(self.S)]
-        slots = [self.pool.alloc(s, self.prefill)[0] for s in self.seqs]
-        slot_all = torch.from_numpy(np.concatenate(slots)).to(self.dev)
-        self.prefill_slots = slots
-        n_tok = self.S * self.prefill
-        self.sample_kv = None
-        for layer in range(self.L):
-            k = normal_fp16((n_tok, self.hkv, 128), w.seed, 10_000 + 2 * layer, self.dev)
-            v = normal_fp16((n_tok, self.hkv, 128), w.seed, 10_001 + 2 * layer, self.dev)
-            self.pool.write_kv(layer, k, v, slot_all)
-            if layer == 0 and not args.no_cpu_baseline:
-                self.sample_kv = (k.cpu().numpy(), v.cpu().numpy())
-            del k, v
-        # Per-layer step inputs, resident for the whole run.
-        self.q = normal_fp16((self.L, self.S, self.hq, 128), w.seed, 1, self.dev)
-        self.k_new = normal_fp16((self.L, self.S, self.hkv, 128), w.seed, 2, self.dev)
-        self.v_new = normal_fp16((self.L, self.S, self.hkv, 128), w.seed, 3, self.dev)
-        self.out = torch.empty((self.L, self.S, self.hq, 128), dtype=torch.float16, device=self.dev)
-        # Block tables are uploaded at a fixed width with room for every appended token.
-        self.mb_cap = -(-(self.prefill + total_steps) // self.bs)
-        ws = pa.pa_decode_workspace_bytes(self.pool.handle, self.S, self.hq, self.mb_cap,
-                                          self.partition)
+
+        # Setup rows: every token whose K/V is generated before the timed steps.
+        if name == "cb_prefix":
+            self.script, self.n_rows = cb_prefix_script(w.seed)
+        else:
+            self.prefill = [t - 1 for t in w.context]  # the first step makes them T_i
+            self.n_rows = int(sum(self.prefill))
+        k0, v0 = self._rows_data(0)
+        ks = vs = self.scales = None
+        if self.fp8:
+            self.scales = (amax_scales(k0), amax_scales(v0))
+            ks = np.tile(self.scales[0], (self.copies, 1))
+            vs = np.tile(self.scales[1], (self.copies, 1))
+        self.pool = pa.PagedKVPool(self.copies, self.hkv, 128, self.bs, self.num_blocks, w.dtype,
+                                   free_order=self.order, k_scales=ks, v_scales=vs)
+        self.seq_rows = {}  # sequence -> row ids of its logical tokens
+        self._setup_sequences(k0, v0)
+        self.setup_lens = np.array([self.pool.seq_len(s)[0] for s in self.seqs], dtype=np.int64)
+        # Host copy of copy 0's rows of the sequences the CPU oracle samples:
+        # evenly spaced sequences, at most CPU_SAMPLE_TOKENS context tokens.
+        stride = max(1, len(self.seqs) // max(1, args.cpu_sample_seqs))
+        self.sample_seqs, tok = [], 0
+        for s in self.seqs[::stride][:args.cpu_sample_seqs]:
+            n = len(self.seq_rows[s])
+            if self.sample_seqs and tok + n > CPU_SAMPLE_TOKENS:
+                break
+            self.sample_seqs.append(s)
+            tok += n
+        self.sample = None
+        if not args.no_cpu_baseline:
+            idx = torch.from_numpy(np.concatenate([self.seq_rows[s] for s in self.sample_seqs])).to(self.dev)
+            self.sample = (k0[idx].cpu().numpy(), v0[idx].cpu().numpy())
+        del k0, v0
+        torch.cuda.empty_cache()
+
+        # Per-launch step inputs, resident for the whole run.
+        self.q = normal_fp16((self.R, self.S, self.hq, 128), w.seed, 1, self.dev)
+        self.k_new = normal_fp16((self.R, self.S, self.hkv, 128), w.seed, 2, self.dev)
+        self.v_new = normal_fp16((self.R, self.S, self.hkv, 128), w.seed, 3, self.dev)
+        self.out = torch.empty((self.R, self.S, self.hq, 128), dtype=torch.float16, device=self.dev)
+        self.mb_cap = int(-(-(self.setup_lens.max() + total_steps) // self.bs))
+        ws = pa.pa_decode_workspace_bytes(self.pool.handle, self.S, self.hq, self.mb_cap, self.partition)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.dev)
         # Step metadata (slot mapping, lengths, block tables) is packed into one
         # int32 buffer so that each step makes a single upload: two pinned host
@@ -142,9 +183,69 @@ class GqaStep:
         self.tables_d = self.meta_d[2 * self.S:].view(self.S, self.mb_cap)
         self.n_step = 0
         self.stream = torch.cuda.current_stream().cuda_stream  # every launch goes here
-        self.kv_bytes_log = []
-        self.first_step_slots = None
+        self.kv_bytes_log, self.unique_bytes_log, self.lens_log = [], [], []
         torch.cuda.synchronize()
+
+    # ---- setup ------------------------------------------------------------------
+
+    def _rows_data(self, copy):
+        """Generated K/V rows [n_rows][Hkv][128] fp16 of one pool copy: the 32
+        model layers of gqa_32x4096 each have their own data; the copies of a
+        one-layer workload all hold copy 0's."""
+        from workloads import normal_fp16
+        tag = 10_000 + 2 * (copy if self.w.layers > 1 else 0)
+        k = normal_fp16((self.n_rows, self.hkv, 128), self.w.seed, tag, self.dev)
+        v = normal_fp16((self.n_rows, self.hkv, 128), self.w.seed, tag + 1, self.dev)
+        return k, v
+
+    def _write_rows(self, k0, v0, rows, slots):
+        """Scatter setup rows into every pool copy."""
+        torch = self.torch
+        r = torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(self.dev)
+        s = torch.from_numpy(np.asarray(slots, dtype=np.int32)).to(self.dev)
+        for c in range(self.copies):
+            k, v = (k0, v0) if (c == 0 or self.w.layers == 1) else self._rows_data(c)
+            self.pool.write_kv(c, k[r].contiguous(), v[r].contiguous(), s)
+            del k, v
+
+    def _setup_sequences(self, k0, v0):
+        pool = self.pool
+        if self.name != "cb_prefix":
+            self.seqs, slots = [], []
+            base = 0
+            for n in self.prefill:
+                s = pool.seq_create()
+                slots.append(pool.alloc(s, n)[0])
+                self.seqs.append(s)
+                self.seq_rows[s] = np.arange(base, base + n, dtype=np.int64)
+                base += n
+            self._write_rows(k0, v0, np.arange(self.n_rows), np.concatenate(slots))
+            return
+        # Continuous-batching mix with one shared, copy-on-write prefix.
+        pending_rows, pending_slots = [], []
+        row = 0
+        for op in self.script:
+            if op[0] == "create":
+                self.seq_rows[pool.seq_create()] = np.zeros(0, dtype=np.int64)
+            elif op[0] == "alloc":
+                s, n = op[1], op[2]
+                sl, _ = pool.alloc(s, n)  # a copy-on-write copy is enqueued on the stream
+                new = np.arange(row, row + n, dtype=np.int64)
+                self.seq_rows[s] = np.concatenate([self.seq_rows[s], new])
+                pending_rows.append(new)
+                pending_slots.append(sl)
+                row += n
+            elif op[0] == "fork":
+                self.seq_rows[pool.fork(op[1])] = self.seq_rows[op[1]].copy()
+            elif op[0] == "free":
+                pool.free(op[1])
+                del self.seq_rows[op[1]]
+            elif op[0] == "flush" and pending_rows:
+                self._write_rows(k0, v0, np.concatenate(pending_rows), np.concatenate(pending_slots))
+                pending_rows, pending_slots = [], []
+        self.seqs = sorted(self.seq_rows)
+
+    # ---- the timed step ---------------------------------------------------------
 
     def step(self):
         pa = self.pa
@@ -155,56 +256,81 @@ class GqaStep:
         slots = meta[:self.S]
         for i, s in enumerate(self.seqs):
             slots[i] = self.pool.alloc(s, 1)[0][0]
-        if self.first_step_slots is None:
-            self.first_step_slots = slots.copy()
         tables, lens = self.pool.block_tables(self.seqs, self.mb_cap)
         meta[self.S:2 * self.S] = lens
         meta[2 * self.S:] = tables.reshape(-1)
         self.meta_d.copy_(self.pinned[k], non_blocking=True)
         self.uploaded[k].record()
         h, st = self.pool.handle, self.stream
-        for layer in range(self.L):
-            pa.pa_write_kv(h, layer, self.k_new[layer], self.v_new[layer], self.slots_d, stream=st)
-            pa.pa_decode(h, layer, self.q[layer], self.tables_d, self.lens_d, out=self.out[layer],
+        for r in range(self.R):
+            layer = r % self.copies
+            pa.pa_write_kv(h, layer, self.k_new[r], self.v_new[r], self.slots_d, stream=st)
+            pa.pa_decode(h, layer, self.q[r], self.tables_d, self.lens_d, out=self.out[r],
                          partition_tokens=self.partition, workspace=self.workspace, stream=st)
-        self.kv_bytes_log.append(int(lens.astype(np.int64).sum()) * 2 * self.hkv * 128 * 2)
-        return lens
+        per_tok = 2 * self.hkv * 128 * self.elem
+        scales = 2 * self.hkv * 4 if self.fp8 else 0
+        self.kv_bytes_log.append(int(lens.astype(np.int64).sum()) * per_tok + scales)
+        if self.name == "cb_prefix":
+            self.unique_bytes_log.append(self._unique_tokens(tables, lens) * per_tok + scales)
+        self.lens_log.append(lens)
+
+    def _unique_tokens(self, tables, lens):
+        """Tokens held in distinct physical blocks (a shared block counted once)."""
+        filled = {}
+        for row, t in zip(tables, lens):
+            for j in range(-(-int(t) // self.bs)):
+                f = min(self.bs, int(t) - j * self.bs)
+                b = int(row[j])
+                if f > filled.get(b, 0):
+                    filled[b] = f
+        return sum(filled.values())
+
+    # ---- CPU oracle baseline ----------------------------------------------------
 
     def cpu_baseline(self, budget_s):
-        """fp64 oracle on layer 0 of this workload at the first step's context
-        (4096 tokens), whole sequences, repeated over sequences until about
-        ``budget_s`` seconds of attention math; scaled to all 32 layers."""
+        """fp64 oracle decode (as it stands) over the setup contexts of the sampled
+        sequences of pool copy 0, one sequence at a time until about ``budget_s``
+        seconds of attention math, scaled by context tokens to one step (all
+        sequences, all launches)."""
         from oracle import attention
         from oracle.kvstore import OracleKVStore
 
-        k_all, v_all = self.sample_kv
-        st = OracleKVStore(1, self.num_blocks, self.hkv, self.bs, 128)
-        for i in range(self.S):
-            a, b = i * self.prefill, (i + 1) * self.prefill
-            st.write(0, k_all[a:b], v_all[a:b], self.prefill_slots[i])
-        st.write(0, self.k_new[0].cpu().numpy(), self.v_new[0].cpu().numpy(), self.first_step_slots)
-        ctx = self.prefill + 1
-        nb = -(-ctx // self.bs)
-        tables, _ = self.pool.block_tables(self.seqs, self.pool.seq_len(self.seqs[0])[1])
-        tables = tables[:, :nb]
-        q0 = self.q[0].cpu().numpy()
-        done, t_total = 0, 0.0
-        while t_total < budget_s and done < self.S:
+        k_all, v_all = self.sample
+        sc = self.scales
+        st = OracleKVStore(1, self.num_blocks, self.hkv, self.bs, 128, self.w.dtype,
+                           None if sc is None else sc[0][None, :],
+                           None if sc is None else sc[1][None, :])
+        sample = self.sample_seqs
+        pos = {s: i for i, s in enumerate(self.seqs)}
+        lens = [int(self.setup_lens[pos[s]]) for s in sample]
+        # Tables as they were at the end of setup (the steps only appended blocks).
+        tables, _ = self.pool.block_tables(sample, self.mb_cap)
+        off = 0
+        for i, n in enumerate(lens):
+            t = np.arange(n)
+            slots = tables[i][t // self.bs].astype(np.int64) * self.bs + t % self.bs
+            st.write(0, k_all[off:off + n], v_all[off:off + n], slots)
+            off += n
+        q0 = self.q[0].cpu().numpy()[[pos[s] for s in sample]]
+        done, t_total, tok = 0, 0.0, 0
+        while t_total < budget_s and done < len(sample):
             t0 = time.perf_counter()
-            attention.decode(st, 0, q0[done:done + 1], tables[done:done + 1], [ctx])
+            attention.decode(st, 0, q0[done:done + 1], tables[done:done + 1], [lens[done]])
             t_total += time.perf_counter() - t0
+            tok += lens[done]
             done += 1
-        per_seq_layer = t_total / done
-        step_s = per_seq_layer * self.S * self.L
+        step_s = t_total * (float(self.setup_lens.sum()) / tok) * self.R
+        per_tok = 2 * self.hkv * 128 * self.elem
         return {
             "value": self.S / step_s,
             "unit": "tokens/s",
             "cores": blas_threads(),
             "kind": "oracle",
-            "sample": (f"layer 0, {done} of {self.S} sequences x {ctx} tokens x {self.hq} query heads "
-                       f"({t_total:.1f} s of attention math, numpy fp64); scaled x{self.S}/{done} "
-                       f"sequences x {self.L} layers to one decode step"),
-            "kv_gbps": (ctx * 2 * self.hkv * 128 * 2) / per_seq_layer / 1e9,
+            "sample": (f"pool copy 0, {done} of {self.S} sequences ({tok} context tokens x "
+                       f"{self.hq} query heads, {t_total:.1f} s of fp64 numpy attention at the "
+                       f"setup contexts), scaled by context tokens to all {self.S} sequences "
+                       f"and x{self.R} launches per step"),
+            "kv_gbps": tok * per_tok / t_total / 1e9,
             "host_cpus": len(os.sched_getaffinity(0)),
             "cpu_count": os.cpu_count(),
             "cpu_model": cpu_model(),
@@ -216,11 +342,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa_32x4096", choices=["gqa_32x4096"])
-    ap.add_argument("--partition", type=int, default=0,
-                    help="partition_tokens for pa_decode (0: library default)")
+    ap.add_argument("--workload", default="gqa_32x4096", choices=BENCH_WORKLOADS)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="partition_tokens for pa_decode (default: the workload's; 0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=32)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB once (HBM counter calibration)")
     args = ap.parse_args(argv)
@@ -241,19 +368,20 @@ def main(argv=None):
         return 1
     torch.cuda.set_device(0)
 
-    bench = GqaStep(args)
+    bench = DecodeBench(args.workload, args)
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
     bench.kv_bytes_log.clear()
-    pa.pa_profile_begin(bench.pool.handle, args.steps * bench.L)
-    lens_seen = []
+    bench.unique_bytes_log.clear()
+    bench.lens_log.clear()
+    pa.pa_profile_begin(bench.pool.handle, args.steps * bench.R)
     gc.collect()
     gc.disable()  # no collector pauses inside the timed steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        lens_seen.append(int(bench.step()[0]))
+        bench.step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gc.enable()
@@ -264,18 +392,15 @@ def main(argv=None):
         return 1
     # The CPU oracle runs after the timed steps so that its BLAS threads cannot
     # compete with the host side of the step.
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = bench.cpu_baseline(args.cpu_budget)
+    cpu = None if args.no_cpu_baseline else bench.cpu_baseline(args.cpu_budget)
 
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = bench.S * args.steps / elapsed
-    kv_bytes = float(sum(bench.kv_bytes_log)) * bench.L  # over all timed decode launches
+    w = bench.w
+    n_launch = max(prof["decode_launches"], 1)
+    kv_bytes = float(sum(bench.kv_bytes_log)) * bench.R  # over all timed decode launches
     decode_s = prof["decode_ms"] / 1e3
     reduce_s = prof["reduce_ms"] / 1e3
     achieved = kv_bytes / decode_s / 1e9
     kv_gbps = kv_bytes / (decode_s + reduce_s) / 1e9
-    traffic = stored_traffic()
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -283,30 +408,35 @@ def main(argv=None):
         torch.cuda.synchronize()
         b.copy_(a)
         torch.cuda.synchronize()
+    first, last = bench.lens_log[0], bench.lens_log[-1]
     result = {
         "metric": METRIC,
-        "value": tokens_per_s,
+        "value": bench.S * args.steps / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": elapsed * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16",
+        "dtype": "fp8_e4m3 KV, fp16 q/out, fp32 accumulate" if bench.fp8 else "fp16",
         "data": "synthetic",
         "config": {
-            "workload": "gqa_32x4096",
-            "layers": bench.L, "num_seqs": bench.S, "q_heads": bench.hq, "kv_heads": bench.hkv,
-            "head_dim": 128, "block_size": bench.bs, "kv_dtype": "fp16", "accumulate": "fp32",
-            "context_first_timed_step": lens_seen[0], "context_last_timed_step": lens_seen[-1],
-            "num_blocks": bench.num_blocks, "partition_tokens": args.partition,
-            "step": "alloc 1 token/seq + 32 x (write_kv + paged decode); attention only",
+            "workload": bench.name,
+            "layers": w.layers, "launches_per_step": bench.R, "pool_copies": bench.copies,
+            "num_seqs": bench.S, "q_heads": bench.hq, "kv_heads": bench.hkv, "head_dim": 128,
+            "block_size": bench.bs, "kv_dtype": "fp8_e4m3" if bench.fp8 else "fp16",
+            "accumulate": "fp32",
+            "context_tokens_first_timed_step": int(first.sum()),
+            "context_min_max_first_timed_step": [int(first.min()), int(first.max())],
+            "context_tokens_last_timed_step": int(last.sum()),
+            "num_blocks": bench.num_blocks, "partition_tokens": bench.partition,
+            "step": f"alloc 1 token/seq + {bench.R} x (write_kv + paged decode); attention only",
         },
         "kv_gbps": kv_gbps,
         "hbm_frac": kv_gbps / HBM_PEAK_GBPS,
-        "decode_kernel_us": prof["decode_ms"] * 1e3 / max(prof["decode_launches"], 1),
+        "decode_kernel_us": prof["decode_ms"] * 1e3 / n_launch,
         "reduce_kernel_us": prof["reduce_ms"] * 1e3 / max(prof["reduce_launches"], 1),
         "roofline": {
             "bound": "hbm",
@@ -314,13 +444,19 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic,
-            "kernel": "paged decode attention (per launch: 32 seqs x T x 8 KV heads x 128 x 2 B x K,V)",
-            "algorithmic_bytes_per_launch": kv_bytes / max(prof["decode_launches"], 1),
+            "traffic": stored_traffic(bench.name),
+            "kernel": (f"paged decode attention (per launch: {bench.S} seqs x T_i tokens x "
+                       f"{bench.hkv} KV heads x 128 x {bench.elem} B x K,V"
+                       + (" + fp8 scales)" if bench.fp8 else ")")),
+            "algorithmic_bytes_per_launch": kv_bytes / n_launch,
             "kernel_source": kernel_source_hash(),
         },
         "cpu_baseline": cpu,
     }
+    if bench.unique_bytes_log:
+        ub = float(sum(bench.unique_bytes_log)) * bench.R
+        result["unique_kv_gbps"] = ub / (decode_s + reduce_s) / 1e9
+        result["unique_bytes_per_launch"] = ub / n_launch
     print(json.dumps(result), flush=True)
     return 0
 

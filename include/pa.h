@@ -199,9 +199,10 @@ int pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num
  * Query head h reads KV head h / (num_q_heads / kv_heads); num_q_heads must
  * be a multiple of kv_heads with a group of at most 32.
  * partition_tokens: 0 lets the library choose (one pass per (sequence, KV
- * head) when num_seqs * kv_heads >= the device's CU count or
- * max_blocks * block_size <= 1024; otherwise ceil(CUs / (num_seqs * kv_heads))
- * chunks per context); -1 forces one pass per (sequence, KV head); P > 0 (a
+ * head) when num_seqs * kv_heads >= U or max_blocks * block_size <= 1024;
+ * otherwise ceil(U / (num_seqs * kv_heads)) chunks per context, where U is the
+ * device's CU count, doubled when a KV head serves more than 16 query
+ * heads); -1 forces one pass per (sequence, KV head); P > 0 (a
  * multiple of 16 and of block_size) splits each context into chunks of P
  * tokens whose partials are merged by log-sum-exp.
  * workspace: device memory of pa_decode_workspace_bytes() bytes (may be NULL

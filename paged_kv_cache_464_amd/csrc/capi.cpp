@@ -72,10 +72,15 @@ namespace {
 // Launch shape of one decode: single pass (C = 1) or chunks of P tokens.
 struct Plan {
   bool partial;
+  int mode;  // pa::DecodeLaunch::mode
   int partition_tokens;
   int num_partitions;
+  int chunks_per_wave;
+  int waves_per_unit;
   uint64_t ws_bytes, off_l, off_o;
 };
+
+constexpr int kModeSingle = 0, kModeSplit4 = 1, kModeSplit1 = 2;
 
 int make_plan(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
               int32_t partition_tokens, Plan* out) {
@@ -97,12 +102,14 @@ int make_plan(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t m
     // rate once every CU has one; with fewer units, split each context into
     // just enough chunks to give every CU a workgroup (measured on MI355X:
     // more, shorter chunks only add partial writes and start-up latency).
+    // Wide head groups (more than 16 query heads per KV head) do twice the
+    // math per byte and want two workgroups per CU.
     P = 0;
-    if (t_cap > kMinSplitTokens && units < p->num_cus) {
-      const int64_t parts = (p->num_cus + units - 1) / units;
-      const int64_t quantum = p->block_size > 16 ? p->block_size : 16;
+    const int64_t target = static_cast<int64_t>(p->num_cus) * (group > 16 ? 2 : 1);
+    if (t_cap > kMinSplitTokens && units < target) {
+      const int64_t parts = (target + units - 1) / units;
       const int64_t len = (t_cap + parts - 1) / parts;
-      const int64_t chunk = (len + quantum - 1) / quantum * quantum;
+      const int64_t chunk = align_up(static_cast<uint64_t>(len), 64);  // four waves x 16 tokens
       if (chunk < t_cap) P = static_cast<int>(chunk);
     }
   } else {
@@ -114,12 +121,33 @@ int make_plan(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t m
   Plan pl{};
   if (P == 0) {
     pl.partial = false;
+    pl.mode = kModeSingle;
     pl.partition_tokens = static_cast<int>(align_up(static_cast<uint64_t>(t_cap), 16));
     pl.num_partitions = 1;
+    pl.chunks_per_wave = 1;
+    pl.waves_per_unit = 1;
   } else {
     pl.partial = true;
     pl.partition_tokens = P;
-    pl.num_partitions = static_cast<int>((t_cap + P - 1) / P);
+    const int64_t C = (t_cap + P - 1) / P;
+    pl.num_partitions = static_cast<int>(C);
+    // Schedule: about eight waves per CU.  With at least one chunk per wave
+    // available, each wave streams a run of k whole chunks on its own (no
+    // merges); otherwise the four waves of a workgroup share every chunk of a
+    // run and merge at each chunk end (needs P to be a multiple of 64).
+    const int64_t target_waves = static_cast<int64_t>(p->num_cus) * 8;
+    const int64_t chunks = units * C;
+    int64_t k;
+    if (chunks >= target_waves || P % 64 != 0) {
+      pl.mode = kModeSplit1;
+      k = chunks / target_waves;
+    } else {
+      pl.mode = kModeSplit4;
+      k = 4 * chunks / target_waves;
+    }
+    k = k < 1 ? 1 : (k > C ? C : k);
+    pl.chunks_per_wave = static_cast<int>(k);
+    pl.waves_per_unit = static_cast<int>((C + k - 1) / k);
     const uint64_t rows = static_cast<uint64_t>(num_seqs) * num_q_heads * pl.num_partitions;
     pl.off_l = align_up(rows * 4, 256);
     pl.off_o = pl.off_l + align_up(rows * 4, 256);
@@ -163,8 +191,11 @@ pa::DecodeLaunch make_launch(int32_t layer, const void* q, int32_t num_q_heads,
   d.num_seqs = num_seqs;
   d.num_q_heads = num_q_heads;
   d.max_blocks = max_blocks;
+  d.mode = pl.mode;
   d.partition_tokens = pl.partition_tokens;
   d.num_partitions = pl.num_partitions;
+  d.chunks_per_wave = pl.chunks_per_wave;
+  d.waves_per_unit = pl.waves_per_unit;
   d.scale = scale;
   if (pl.partial) {
     auto* ws = static_cast<uint8_t*>(workspace);
@@ -432,7 +463,7 @@ static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_he
   const bool rec = p->profiling && p->n_records < p->max_records;
   hipEvent_t* ev = rec ? &p->ev[4 * static_cast<size_t>(p->n_records)] : nullptr;
   const bool reduced = pl.partial && mode == 0;
-  hipError_t e = pa::launch_decode(p->geom, d, pl.partial, s, rec ? ev[0] : nullptr, rec ? ev[1] : nullptr);
+  hipError_t e = pa::launch_decode(p->geom, d, s, rec ? ev[0] : nullptr, rec ? ev[1] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (reduced) {
     e = pa::launch_lse_reduce(p->geom, d, s, rec ? ev[2] : nullptr, rec ? ev[3] : nullptr);

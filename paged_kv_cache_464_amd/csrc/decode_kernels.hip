@@ -8,26 +8,35 @@
 // "PagedAttention 알고리즘").  Query head h reads KV head h / G (youngju.dev
 // page, section "GQA와 MQA").
 //
-// Mapping to CDNA4:
-//  * one workgroup of four waves per (sequence, KV head, context chunk); its
-//    waves take interleaved 16-token steps of the chunk;
-//  * K/V are read with nontemporal 16-byte loads: each byte is used once per
-//    launch, and on MI355X such loads sustain about 11% more bandwidth over
-//    randomly placed 4 KiB tiles than ordinary ones;
-//  * each step loads the K and V tiles of 16 tokens with 16-byte lane loads
-//    (one contiguous 1 KiB run per load instruction), directly in the
-//    register layout of the MFMA operands -- no LDS round trip;
+// Mapping to CDNA4.  A wave works on 16-token steps of one (sequence, KV
+// head):
+//  * each step loads the K and V tiles of 16 tokens with nontemporal 16-byte
+//    lane loads (one contiguous 1 KiB run per load instruction) directly in
+//    the register layout of the MFMA operands -- no LDS round trip; each byte
+//    is used once per launch, and on MI355X nontemporal loads sustain about
+//    11% more bandwidth over randomly placed 4 KiB tiles than ordinary ones;
 //  * S^T[token][head] = K * Q^T with v_mfma_f32_16x16x32_f16 (rows = 16 tokens,
 //    columns = the G query heads of the KV head, padded to 16), so the K tile
 //    is read once for all G heads of the group;
 //  * online softmax in fp32 (base-2 exponent), with the per-head maximum
-//    exchanged across the four 16-lane groups by two xor shuffles;
+//    exchanged across the four 16-lane rows by two VALU row swaps;
 //  * O^T[dim][head] += V^T * P^T with v_mfma_f32_16x16x16_f16, P in fp16;
-//  * the waves merge their (max, sum, O) through LDS at the end, and the
-//    workgroup writes either the final fp16 output or one chunk's partials.
-// fp8 (E4M3FN) tiles are widened to fp16 in registers (exactly: every E4M3
-// value times 2^-8 is an fp16 value); the 2^8 and the per-(layer, KV head)
-// scales are folded into the score and output multipliers.
+//  * block ids are wave-uniform and read with scalar loads one pipeline block
+//    ahead; K/V loads run a two-step register pipeline with no data-dependent
+//    branch around any vector load.
+// decode_kernel runs this per-wave engine in one of three schedules:
+//  * single pass: one workgroup of four waves per (sequence, KV head); the
+//    waves take interleaved steps and merge (max, sum, O) through LDS;
+//  * split, four waves per chunk: a workgroup streams a run of P-token chunks
+//    of one (sequence, KV head), the waves interleaving within each chunk and
+//    merging at its end into that chunk's partials (max, sum, normalised O);
+//  * split, one wave per run: each wave streams its own run of chunks and
+//    writes each chunk's partials without any merge;
+// lse_reduce_kernel merges the partials.
+// fp8 (E4M3FN) tiles are widened to fp16 in registers with the hardware
+// packed converter (exact: every E4M3 value is an fp16 value); the
+// per-(layer, KV head) scales are folded into the score and output
+// multipliers.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -40,26 +49,49 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Read-only view of a block-table row: loads with wave-uniform indices become
+// scalar loads (the table is not written while a kernel runs).
+typedef const int32_t __attribute__((address_space(4))) ConstI32;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kD = kHeadDim;
 constexpr int kSmoStride = kD + 4;  // padded LDS row of the merge buffer
-constexpr int kDecodeWaves = 4;     // waves per decode workgroup
+constexpr int kWaves = 4;           // waves per decode workgroup
 
-// Two E4M3FN bytes (bits 8..15 and 24..31 of x) -> two fp16 equal to value * 2^-8:
-// sign to bit 15, exponent+mantissa bits shifted into place.  Exact for every
-// finite code, normal and subnormal.
-__device__ inline uint32_t e4m3x2_to_f16x2_scaled(uint32_t x) {
-  return (x & 0x80008000u) | ((x >> 1) & 0x3F803F80u);
+// Steps of K/V loads each wave keeps in flight beyond the one it computes on.
+// One step is 16 tokens of one KV head (8 KiB fp16, 4 KiB fp8).  Measured on
+// MI355X over depths 1-6: 2 is best or within noise of the best for fp16 and
+// fp8, GQA and MQA; deeper pipelines only cost registers and occupancy.
+constexpr int kDepth = 2;
+
+// Four E4M3FN codes (bytes 0..3 of w) -> four fp16 in byte order, with the
+// gfx950 packed converter at scale 1: every E4M3FN value is an fp16 value, so
+// the conversion is exact (checked for all byte pairs on MI355X).
+__device__ inline f16x4 e4m3x4_to_f16x4(uint32_t w) {
+  const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return f16x4{lo[0], lo[1], hi[0], hi[1]};
 }
-// Bytes b0..b3 of w -> 4 fp16 (x 2^-8) in two dwords.
-__device__ inline u32x2 e4m3x4_to_f16x4(uint32_t w) {
-  const uint32_t lo = ((w & 0x000000FFu) << 8) | ((w & 0x0000FF00u) << 16);  // [0, b0, 0, b1]
-  const uint32_t hi = ((w & 0x00FF0000u) >> 8) | (w & 0xFF000000u);          // [0, b2, 0, b3]
-  return u32x2{e4m3x2_to_f16x2_scaled(lo), e4m3x2_to_f16x2_scaled(hi)};
+
+// Maximum / sum of x over the four 16-lane rows of the wave (lanes n, n+16,
+// n+32, n+48 end up with the same value), with two VALU row swaps:
+// permlane16_swap pairs rows 0-1 and 2-3, permlane32_swap the two halves.
+__device__ inline float max_across_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum_across_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int ELEM>
@@ -69,161 +101,146 @@ struct StepRegs {
   u32x4 v[kLoads];
 };
 
-template <int ELEM, int BS, int NT, bool PARTIAL, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(PoolGeom g, DecodeLaunch p) {
-  constexpr int X = 16 / ELEM;             // elements per 16-byte chunk
-  constexpr int NLD = StepRegs<ELEM>::kLoads;
-  constexpr int R = X / 4;                 // V dim sub-tiles per 16-byte load
-  constexpr int NCOL = NT * 16;
+// The per-wave engine: operands, softmax state and the load / compute of one
+// 16-token step of one (sequence, KV head).  Lane (gq, n): gq = lane / 16 is
+// its row group, n = lane % 16 its head column.
+template <int ELEM, int BS, int NT>
+struct WaveDecoder {
+  static constexpr int kElem = ELEM;
+  static constexpr int kNT = NT;
+  static constexpr int X = 16 / ELEM;  // elements per 16-byte chunk
+  static constexpr int NLD = StepRegs<ELEM>::kLoads;
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int gq = lane >> 4;  // 16-lane group
-  const int n = lane & 15;
-
-  int wg = blockIdx.x;
-  const int part = wg % p.num_partitions;
-  wg /= p.num_partitions;
-  const int kvh = wg % g.kv_heads;
-  const int seq = wg / g.kv_heads;
-  const int group = p.num_q_heads / g.kv_heads;
-
-  const int32_t* trow = p.tables + static_cast<int64_t>(seq) * p.max_blocks;
-  const int start = part * p.partition_tokens;
-  // Block ids of this wave's steps, one per lane (lane L: wave-step c0 + L),
-  // refilled every 64 steps.  Entries are clamped to the table width only, so
-  // the first load is issued together with the context length instead of
-  // after it; ids of steps past the end are never used.
-  int tl_lo = 0, tl_hi = 0;
-  auto load_ids = [&](int c0) {
-    const int64_t b = (start + 16ll * (w + NW * (c0 + lane))) / BS;
-    const int64_t last = p.max_blocks - 1;
-    tl_lo = trow[b < last ? b : last];
-    if constexpr (BS == 8) tl_hi = trow[b + 1 < last ? b + 1 : last];
-  };
-  load_ids(0);
-
-  int T = p.lens[seq];
-  const int t_cap = p.max_blocks * BS;
-  if (T < 1 || T > t_cap) {
-    if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
-    T = T < 0 ? 0 : (T > t_cap ? t_cap : T);
-  }
-  if (T == 0) {
-    if constexpr (!PARTIAL) {
-      // Nothing to attend to: defined output of zeros.
-      for (int i = threadIdx.x; i < group * kD; i += NW * 64) {
-        reinterpret_cast<_Float16*>(p.out)[(static_cast<int64_t>(seq) * p.num_q_heads +
-                                            kvh * group) * kD + i] = 0;
-      }
-    }
-    return;
-  }
-  if (start >= T) return;
-  const int end = (start + p.partition_tokens < T) ? start + p.partition_tokens : T;
-  const int nsteps = (end - start + 15) >> 4;
-  const int my_steps = (w < nsteps) ? (nsteps - w + NW - 1) / NW : 0;
-
-  // ---- scales ----------------------------------------------------------------
-  float qk_mul = p.scale * kLog2e;
-  float out_mul = 1.0f;
-  if constexpr (ELEM == 1) {
-    const int lhs = g.layers * g.kv_heads;
-    const int lh = p.layer * g.kv_heads + kvh;
-    qk_mul *= g.scales[lh] * 256.0f;
-    out_mul = g.scales[lhs + lh] * 256.0f;
-  }
-
-  // ---- Q^T operands: lane (gq, n) holds head column n, 8 dims per MFMA -------
-  f16x8 qop[NT][4];
-  const _Float16* qs = static_cast<const _Float16*>(p.q) +
-                       static_cast<int64_t>(seq) * p.num_q_heads * kD;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int col = nt * 16 + n;
-    const bool valid = col < group;
-    const _Float16* qh = qs + static_cast<int64_t>(kvh * group + (valid ? col : 0)) * kD;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int dim0 = (ELEM == 2) ? (u * 4 + gq) * 8 : ((u >> 1) * 4 + gq) * 16 + (u & 1) * 8;
-      f16x8 v = *reinterpret_cast<const f16x8*>(qh + dim0);
-      qop[nt][u] = valid ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-
-  // ---- per-lane byte offsets inside the tiles --------------------------------
+  int gq, n, T, max_blocks, num_blocks;
+  uint64_t block_stride;
+  const ConstI32* trow;
+  const uint8_t* kbase;
+  const uint8_t* vbase;
   uint32_t koff[NLD], voff[NLD];
-#pragma unroll
-  for (int j = 0; j < NLD; ++j) {
-    const int c = j * 4 + gq;  // K chunk of this lane for load j
-    if constexpr (BS == 8) {
-      koff[j] = ((c * 8 + (n & 7)) * X) * ELEM;
-      voff[j] = (((j * 2 + (gq & 1)) * 16 + n) * X) * ELEM;
-    } else {
-      koff[j] = ((c * 16 + n) * X) * ELEM;
-      voff[j] = (((j * (BS / 4) + gq) * 16 + n) * X) * ELEM;
-    }
-  }
-
-  const uint8_t* kbase = g.k_layer(p.layer) + static_cast<uint64_t>(kvh) * g.tile_bytes;
-  const uint8_t* vbase = g.v_layer(p.layer) + static_cast<uint64_t>(kvh) * g.tile_bytes;
-
+  float qk_mul, out_mul;
+  f16x8 qop[NT][4];
   f32x4 oacc[NT][8];
   float m_run[NT], l_part[NT];
+  uint32_t bad;
+
+  // Geometry and the block-table row; needs no context length.
+  __device__ void bind(const PoolGeom& g, const DecodeLaunch& p, int seq, int kvh, int lane) {
+    gq = lane >> 4;
+    n = lane & 15;
+    T = 0;
+    max_blocks = p.max_blocks;
+    num_blocks = g.num_blocks;
+    block_stride = g.block_stride;
+    trow = (const ConstI32*)(p.tables + static_cast<int64_t>(seq) * p.max_blocks);
+    kbase = g.k_layer(p.layer) + static_cast<uint64_t>(kvh) * g.tile_bytes;
+    vbase = g.v_layer(p.layer) + static_cast<uint64_t>(kvh) * g.tile_bytes;
+    bad = 0;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -__builtin_inff();
-    l_part[nt] = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) oacc[nt][r] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < NLD; ++j) {
+      const int c = j * 4 + gq;  // K chunk of this lane for load j
+      if constexpr (BS == 8) {
+        koff[j] = ((c * 8 + (n & 7)) * X) * ELEM;
+        voff[j] = (((j * 2 + (gq & 1)) * 16 + n) * X) * ELEM;
+      } else {
+        koff[j] = ((c * 16 + n) * X) * ELEM;
+        voff[j] = (((j * (BS / 4) + gq) * 16 + n) * X) * ELEM;
+      }
+    }
   }
 
-  uint32_t bad = 0;
+  // Q^T operands (lane (gq, n) holds head column n, 8 dims per MFMA) and the
+  // score / output multipliers.
+  __device__ void load_q(const PoolGeom& g, const DecodeLaunch& p, int seq, int kvh, int group) {
+    qk_mul = p.scale * kLog2e;
+    out_mul = 1.0f;
+    if constexpr (ELEM == 1) {
+      const int lhs = g.layers * g.kv_heads;
+      const int lh = p.layer * g.kv_heads + kvh;
+      qk_mul *= g.scales[lh];
+      out_mul = g.scales[lhs + lh];
+    }
+    const _Float16* qs = static_cast<const _Float16*>(p.q) + static_cast<int64_t>(seq) * p.num_q_heads * kD;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = nt * 16 + n;
+      const bool valid = col < group;
+      const _Float16* qh = qs + static_cast<int64_t>(kvh * group + (valid ? col : 0)) * kD;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int dim0 = (ELEM == 2) ? (u * 4 + gq) * 8 : ((u >> 1) * 4 + gq) * 16 + (u & 1) * 8;
+        const f16x8 v = *reinterpret_cast<const f16x8*>(qh + dim0);
+        qop[nt][u] = valid ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  }
 
-  auto phys_ok = [&](int b) -> int {
-    if (static_cast<uint32_t>(b) >= static_cast<uint32_t>(g.num_blocks)) {
+  __device__ void reset() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      m_run[nt] = -__builtin_inff();
+      l_part[nt] = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) oacc[nt][r] = f32x4{0, 0, 0, 0};
+    }
+  }
+
+  // Block ids of the step starting at token tb (scalar loads; the table index
+  // is clamped to the table width, so any tb is safe to ask for).
+  __device__ void fetch_ids(int64_t tb, int& lo, int& hi) const {
+    const int64_t b = tb / BS;
+    const int64_t last = max_blocks - 1;
+    lo = trow[b < last ? b : last];
+    hi = 0;
+    if constexpr (BS == 8) hi = trow[b + 1 < last ? b + 1 : last];
+  }
+
+  __device__ int phys_ok(int b) {
+    if (static_cast<uint32_t>(b) >= static_cast<uint32_t>(num_blocks)) {
       bad |= kDevBadBlock;
       return 0;
     }
     return b;
-  };
+  }
 
-  // K/V are streamed once per launch: nontemporal loads keep them from
-  // displacing anything in the caches.
-  auto ld16 = [](const uint8_t* a) {
+  static __device__ u32x4 ld16(const uint8_t* a) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
-  };
-  auto issue = [&](StepRegs<ELEM>& r, int i_in_chunk, int tb) {
+  }
+
+  // Loads of the step starting at token tb, whose blocks are id_lo (and
+  // id_hi, the block of its second 8 tokens when blocks hold 8).
+  __device__ void issue(StepRegs<ELEM>& r, int tb, int id_lo, int id_hi) {
     if constexpr (BS == 8) {
-      const int b0 = phys_ok(__builtin_amdgcn_readlane(tl_lo, i_in_chunk));
+      const int b0 = phys_ok(id_lo);
       // The second block of the step exists only if its first token does.
-      const int b1 = (tb + 8 < T) ? phys_ok(__builtin_amdgcn_readlane(tl_hi, i_in_chunk)) : b0;
-      const uint8_t* kp = kbase + static_cast<uint64_t>(n < 8 ? b0 : b1) * g.block_stride;
-      const uint8_t* vp = vbase + static_cast<uint64_t>(gq < 2 ? b0 : b1) * g.block_stride;
+      const int b1 = (tb + 8 < T) ? phys_ok(id_hi) : b0;
+      const uint8_t* kp = kbase + static_cast<uint64_t>(n < 8 ? b0 : b1) * block_stride;
+      const uint8_t* vp = vbase + static_cast<uint64_t>(gq < 2 ? b0 : b1) * block_stride;
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         r.k[j] = ld16(kp + koff[j]);
         r.v[j] = ld16(vp + voff[j]);
       }
     } else {
-      const int b = phys_ok(__builtin_amdgcn_readlane(tl_lo, i_in_chunk));
+      (void)id_hi;
+      const int b = phys_ok(id_lo);
       uint64_t koff_sub = 0, voff_sub = 0;
       if constexpr (BS == 32) {
         const int sub = (tb >> 4) & 1;
         koff_sub = static_cast<uint64_t>(sub) * 16 * kD * ELEM;
         voff_sub = static_cast<uint64_t>(sub) * 4 * 16 * X * ELEM;
       }
-      const uint8_t* kp = kbase + static_cast<uint64_t>(b) * g.block_stride + koff_sub;
-      const uint8_t* vp = vbase + static_cast<uint64_t>(b) * g.block_stride + voff_sub;
+      const uint8_t* kp = kbase + static_cast<uint64_t>(b) * block_stride + koff_sub;
+      const uint8_t* vp = vbase + static_cast<uint64_t>(b) * block_stride + voff_sub;
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         r.k[j] = ld16(kp + koff[j]);
         r.v[j] = ld16(vp + voff[j]);
       }
     }
-  };
+  }
 
-  auto compute = [&](StepRegs<ELEM>& r, int tb) {
+  // Attention over the 16 tokens tb .. tb+15 held in r (those >= T masked).
+  __device__ void compute(StepRegs<ELEM>& r, int tb) {
     // S^T = K Q^T
     f32x4 s[NT];
 #pragma unroll
@@ -235,9 +252,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(PoolGeom g, DecodeLaunc
         kop = __builtin_bit_cast(f16x8, r.k[u]);
       } else {
         const u32x4 raw = r.k[u >> 1];
-        const u32x2 a = e4m3x4_to_f16x4((u & 1) ? raw[2] : raw[0]);
-        const u32x2 b = e4m3x4_to_f16x4((u & 1) ? raw[3] : raw[1]);
-        kop = __builtin_bit_cast(f16x8, u32x4{a[0], a[1], b[0], b[1]});
+        const f16x4 a = e4m3x4_to_f16x4((u & 1) ? raw[2] : raw[0]);
+        const f16x4 b = e4m3x4_to_f16x4((u & 1) ? raw[3] : raw[1]);
+        kop = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -246,7 +263,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(PoolGeom g, DecodeLaunc
     // Scores of tokens tb + 4*gq + e for head column n; mask the tail.
     const bool tail = tb + 16 > T;
     const int valid_here = T - (tb + 4 * gq);  // tokens of this lane's 4 that exist
-    float mx[NT], mnew[NT];
+    float mnew[NT];
     bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -256,10 +273,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(PoolGeom g, DecodeLaunc
         if (tail && e >= valid_here) x = -__builtin_inff();
         s[nt][e] = x;
       }
-      float m = fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3]));
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      mx[nt] = m;
+      const float m = max_across_rows(fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3])));
       mnew[nt] = fmaxf(m_run[nt], m);
       grow |= mnew[nt] > m_run[nt];
     }
@@ -307,46 +321,90 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(PoolGeom g, DecodeLaunc
         vop = __builtin_bit_cast(f16x4, (rr & 1) ? u32x2{raw[2], raw[3]} : u32x2{raw[0], raw[1]});
       } else {
         const u32x4 raw = r.v[rr >> 2];
-        vop = __builtin_bit_cast(f16x4, e4m3x4_to_f16x4(raw[rr & 3]));
+        vop = e4m3x4_to_f16x4(raw[rr & 3]);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         oacc[nt][rr] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, pop[nt], oacc[nt][rr], 0, 0, 0);
     }
-  };
+  }
+};
 
-  // ---- main loop: chunks of up to 64 wave-steps, two-deep register pipeline ----
-  constexpr int kStepTok = 16 * NW;  // tokens between a wave's consecutive steps
-  for (int c0 = 0; c0 < my_steps; c0 += 64) {
-    const int cn = (my_steps - c0) < 64 ? (my_steps - c0) : 64;
-    if (c0 > 0) load_ids(c0);
-    StepRegs<ELEM> ra, rb;
-    issue(ra, 0, start + 16 * (w + NW * c0));
-    for (int i = 0; i < cn; i += 2) {
-      const int tb_a = start + 16 * (w + NW * (c0 + i));
-      if (i + 1 < cn) issue(rb, i + 1, tb_a + kStepTok);
-      compute(ra, tb_a);
-      if (i + 1 >= cn) break;
-      if (i + 2 < cn) issue(ra, i + 2, tb_a + 2 * kStepTok);
-      compute(rb, tb_a + kStepTok);
+// Ids of the first 2*kDepth - 1 steps of a stream, requested before the
+// context length is known so the two loads overlap.
+struct FirstIds {
+  int lo[2 * kDepth - 1], hi[2 * kDepth - 1];
+};
+
+// Runs the scheduled steps j = 0 .. n-1 (n >= 1) of a wave through a
+// kDepth-deep register pipeline.  tok_of(j) is the first token of step j when
+// the step holds real tokens, and otherwise the first token of a real step
+// whose tiles it re-reads; real(j) tells which.  Real steps are computed;
+// after(j) is called for every scheduled step.  The steady state has no
+// data-dependent branch around any vector load, so the compiler's wait counts
+// see the same outstanding loads on every path and each step waits only for
+// its own tiles; to keep it so, steps are padded to a multiple of kDepth with
+// look-ahead loads that re-read a real step's tiles (cache hits).  The ids of
+// a block of look-ahead steps are fetched one block ahead.
+template <class Dec, class TokOf, class Real, class After>
+__device__ inline void stream_steps(Dec& dec, int n, TokOf tok_of, Real real, FirstIds& f, After after) {
+  constexpr int D = kDepth;
+  const int n_pad = (n + D - 1) / D * D;
+  auto tok_at = [&](int j) { return tok_of(j < n ? j : n - 1); };
+  if (!real(2 * D - 2 < n ? 2 * D - 2 : n - 1) || n < 2 * D - 1) {
+#pragma unroll
+    for (int j = 0; j < 2 * D - 1; ++j) dec.fetch_ids(tok_at(j), f.lo[j], f.hi[j]);
+  }
+  StepRegs<Dec::kElem> rr[D];
+  int cur_lo[D], cur_hi[D], nxt_lo[D], nxt_hi[D];
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) dec.issue(rr[d], tok_at(d), f.lo[d], f.hi[d]);
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    cur_lo[d] = f.lo[d + D - 1];
+    cur_hi[d] = f.hi[d + D - 1];
+  }
+  for (int j = 0; j < n_pad; j += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) dec.fetch_ids(tok_at(j + d + 2 * D - 1), nxt_lo[d], nxt_hi[d]);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      dec.issue(rr[(d + D - 1) % D], tok_at(j + d + D - 1), cur_lo[d], cur_hi[d]);
+      if (j + d < n) {
+        if (real(j + d)) dec.compute(rr[d], tok_of(j + d));
+        after(j + d);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      cur_lo[d] = nxt_lo[d];
+      cur_hi[d] = nxt_hi[d];
     }
   }
-  if (bad && lane == 0) atomicOr(g.status, bad);
+}
 
-  // ---- merge the four waves ---------------------------------------------------
-  __shared__ float sm_m[NW][NCOL];
-  __shared__ float sm_l[NW][NCOL];
-  __shared__ float sm_o[NW - 1][NCOL][kSmoStride];
-  float l_head[NT];
+// LDS of the four-wave merge.
+template <int NT>
+struct MergeLds {
+  float m[kWaves][NT * 16];
+  float l[kWaves][NT * 16];
+  float o[kWaves - 1][NT * 16][kSmoStride];
+};
+
+// Merges the (max, sum, O) of the workgroup's four waves for every head
+// column and lets wave 0 emit(nt, col, acc[8] = sum_w O_w * 2^(m_w - M), M, L)
+// with L = sum_w l_w * 2^(m_w - M).  All four waves must call it; two
+// barriers.
+template <class Dec, class Emit>
+__device__ inline void merge_waves(Dec& dec, MergeLds<Dec::kNT>& sm, int w, int group, Emit emit) {
+  constexpr int NT = Dec::kNT;
+  const int gq = dec.gq, n = dec.n;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float l = l_part[nt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    l_head[nt] = l;
+    const float l = sum_across_rows(dec.l_part[nt]);
     if (gq == 0) {
-      sm_m[w][nt * 16 + n] = m_run[nt];
-      sm_l[w][nt * 16 + n] = l;
+      sm.m[w][nt * 16 + n] = dec.m_run[nt];
+      sm.l[w][nt * 16 + n] = l;
     }
   }
   __syncthreads();
@@ -354,24 +412,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(PoolGeom g, DecodeLaunc
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int col = nt * 16 + n;
-    float M = sm_m[0][col];
+    float M = sm.m[0][col];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][col]);
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][col]);
     float L = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float mw = sm_m[ww][col];
-      L += (mw == -__builtin_inff()) ? 0.0f : sm_l[ww][col] * exp2f(mw - M);
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = sm.m[ww][col];
+      L += (mw == -__builtin_inff()) ? 0.0f : sm.l[ww][col] * exp2f(mw - M);
     }
     big_m[nt] = M;
     big_l[nt] = L;
-    f[nt] = (m_run[nt] == -__builtin_inff()) ? 0.0f : exp2f(m_run[nt] - M);
-    (void)l_head[nt];
+    f[nt] = (dec.m_run[nt] == -__builtin_inff()) ? 0.0f : exp2f(dec.m_run[nt] - M);
     if (w > 0 && col < group) {
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        *reinterpret_cast<f32x4*>(&sm_o[w - 1][col][rr * 16 + 4 * gq]) = oacc[nt][rr] * f[nt];
-      }
+      for (int rr = 0; rr < 8; ++rr)
+        *reinterpret_cast<f32x4*>(&sm.o[w - 1][col][rr * 16 + 4 * gq]) = dec.oacc[nt][rr] * f[nt];
     }
   }
   __syncthreads();
@@ -380,101 +436,313 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(PoolGeom g, DecodeLaunc
   for (int nt = 0; nt < NT; ++nt) {
     const int col = nt * 16 + n;
     if (col >= group) continue;
-    const int head = kvh * group + col;
-    const float inv_l = out_mul / big_l[nt];
-    const int64_t row = static_cast<int64_t>(seq) * p.num_q_heads + head;
+    f32x4 acc[8];
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
       const int dim = rr * 16 + 4 * gq;
-      f32x4 acc = oacc[nt][rr] * f[nt];
+      acc[rr] = dec.oacc[nt][rr] * f[nt];
 #pragma unroll
-      for (int ww = 0; ww < NW - 1; ++ww) acc += *reinterpret_cast<const f32x4*>(&sm_o[ww][col][dim]);
-      acc *= inv_l;
-      if constexpr (PARTIAL) {
-        float* po = p.part_o + (row * p.num_partitions + part) * kD + dim;
-        *reinterpret_cast<f32x4*>(po) = acc;
-      } else {
-        _Float16* po = static_cast<_Float16*>(p.out) + row * kD + dim;
-        *reinterpret_cast<f16x4*>(po) =
-            f16x4{(_Float16)acc[0], (_Float16)acc[1], (_Float16)acc[2], (_Float16)acc[3]};
-      }
+      for (int ww = 0; ww < kWaves - 1; ++ww) acc[rr] += *reinterpret_cast<const f32x4*>(&sm.o[ww][col][dim]);
     }
-    if constexpr (PARTIAL) {
-      if (gq == 0) {
-        p.part_m[row * p.num_partitions + part] = big_m[nt];
-        p.part_l[row * p.num_partitions + part] = big_l[nt];
-      }
+    emit(nt, col, acc, big_m[nt], big_l[nt]);
+  }
+}
+
+enum DecodeMode : int {
+  kSingle = 0,   // one workgroup per (sequence, KV head), fp16 output
+  kSplit4 = 1,   // a workgroup's four waves share each chunk of a chunk run
+  kSplit1 = 2,   // each wave streams its own chunk run
+};
+
+// Context length of a sequence, clamped to the table width; bad lengths set
+// PA_DEV_BAD_LEN (by one lane of the grid's first wave of the unit).
+template <int BS>
+__device__ inline int context_len(const PoolGeom& g, const DecodeLaunch& p, int seq, bool report) {
+  int T = p.lens[seq];
+  const int t_cap = p.max_blocks * BS;
+  if (T < 1 || T > t_cap) {
+    if (report) atomicOr(g.status, kDevBadLen);
+    T = T < 0 ? 0 : (T > t_cap ? t_cap : T);
+  }
+  return T;
+}
+
+// Paged decode for one layer.
+//  kSingle: workgroup = (sequence, KV head); wave w takes steps w, w+4, ...
+//    of the whole context; the waves merge and write the fp16 output.
+//  kSplit4: workgroup = (unit, r): chunks [r*k, min((r+1)*k, C)) of the unit,
+//    chunk by chunk; within a chunk wave w takes steps w, w+4, ...; at each
+//    chunk end the waves merge and write that chunk's partials.
+//  kSplit1: wave (unit, r): the same chunk run, streamed by one wave, which
+//    writes each chunk's partials itself.
+// Partials of chunk c of query head h: m = max_t s_t (base 2),
+// l = sum_t 2^(s_t - m), o = sum_t 2^(s_t - m) v_t / l (times the fp8 V scale).
+// Chunks at or past ceil(T / P) are not written.
+template <int ELEM, int BS, int NT, int MODE>
+__global__ __launch_bounds__(kWaves * 64) void decode_kernel(PoolGeom g, DecodeLaunch p) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int group = p.num_q_heads / g.kv_heads;
+  const int64_t num_units = static_cast<int64_t>(p.num_seqs) * g.kv_heads;
+  int64_t unit;
+  int r = 0;
+  if constexpr (MODE == kSingle) {
+    unit = blockIdx.x;
+  } else if constexpr (MODE == kSplit4) {
+    unit = blockIdx.x / p.waves_per_unit;
+    r = static_cast<int>(blockIdx.x % p.waves_per_unit);
+  } else {
+    const int64_t v = static_cast<int64_t>(blockIdx.x) * kWaves + w;
+    unit = v / p.waves_per_unit;
+    r = static_cast<int>(v % p.waves_per_unit);
+    if (unit >= num_units) return;  // whole waves only: no barrier in this mode
+  }
+  const int kvh = static_cast<int>(unit % g.kv_heads);
+  const int seq = static_cast<int>(unit / g.kv_heads);
+  const int P = p.partition_tokens;
+  const int c_begin = r * p.chunks_per_wave;
+  const int c_end = (c_begin + p.chunks_per_wave < p.num_partitions) ? c_begin + p.chunks_per_wave
+                                                                      : p.num_partitions;
+  const int qs = P >> 6;   // kSplit4: steps of each wave per chunk
+  const int spc = P >> 4;  // kSplit1: steps per chunk
+  // First token of scheduled step j, before any clamping to the context.
+  auto raw_tok = [&](int j) -> int64_t {
+    if constexpr (MODE == kSingle) return 16ll * (w + kWaves * j);
+    else if constexpr (MODE == kSplit4) return static_cast<int64_t>(c_begin + j / qs) * P + 16 * (w + kWaves * (j % qs));
+    else return static_cast<int64_t>(c_begin) * P + 16ll * j;
+  };
+
+  WaveDecoder<ELEM, BS, NT> dec;
+  dec.bind(g, p, seq, kvh, lane);
+  FirstIds first;
+#pragma unroll
+  for (int j = 0; j < 2 * kDepth - 1; ++j) dec.fetch_ids(raw_tok(j), first.lo[j], first.hi[j]);
+  const bool reporter = (MODE == kSplit1) ? (lane == 0 && r == 0) : (threadIdx.x == 0 && r == 0);
+  const int T = context_len<BS>(g, p, seq, reporter);
+  dec.T = T;
+
+  if constexpr (MODE == kSingle) {
+    if (T == 0) {
+      // Nothing to attend to: defined output of zeros.
+      for (int i = threadIdx.x; i < group * kD; i += kWaves * 64)
+        static_cast<_Float16*>(p.out)[(static_cast<int64_t>(seq) * p.num_q_heads + kvh * group) * kD + i] = 0;
+      return;
     }
+  }
+  // Chunks of the run that hold tokens, and the scheduled steps of each wave.
+  const int c_last = (MODE == kSingle) ? 0 : ((T + P - 1) / P < c_end ? (T + P - 1) / P : c_end);
+  int n;
+  if constexpr (MODE == kSingle) {
+    n = (T + 16 * kWaves - 1) / (16 * kWaves);  // same count for every wave
+  } else if constexpr (MODE == kSplit4) {
+    if (c_begin >= c_last) return;  // whole workgroup
+    const int rest = static_cast<int>(T - static_cast<int64_t>(c_last - 1) * P);  // tokens of the run's last chunk
+    n = (c_last - 1 - c_begin) * qs + ((rest < P ? rest : P) + 16 * kWaves - 1) / (16 * kWaves);
+  } else {
+    if (c_begin >= c_last) return;
+    const int64_t tok1 = (static_cast<int64_t>(c_last) * P < T) ? static_cast<int64_t>(c_last) * P : T;
+    n = static_cast<int>((tok1 - static_cast<int64_t>(c_begin) * P + 15) >> 4);
+  }
+  // Steps at or past the context re-read the context's last step.
+  const int last_tok = ((T - 1) >> 4) << 4;
+  auto real = [&](int j) { return raw_tok(j) < T; };
+  auto tok_of = [&](int j) -> int { return real(j) ? static_cast<int>(raw_tok(j)) : last_tok; };
+
+  dec.load_q(g, p, seq, kvh, group);
+  dec.reset();
+  const int gq = dec.gq;
+  const int64_t row0 = static_cast<int64_t>(seq) * p.num_q_heads + kvh * group;
+
+  if constexpr (MODE == kSingle) {
+    __shared__ MergeLds<NT> sm;
+    stream_steps(dec, n, tok_of, real, first, [](int) {});
+    if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
+    merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float, float L) {
+      (void)nt;
+      const float inv_l = dec.out_mul / L;
+      _Float16* po = static_cast<_Float16*>(p.out) + (row0 + col) * kD + 4 * gq;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const f32x4 a = acc[rr] * inv_l;
+        *reinterpret_cast<f16x4*>(po + rr * 16) = f16x4{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
+      }
+    });
+  } else if constexpr (MODE == kSplit4) {
+    __shared__ MergeLds<NT> sm;
+    auto after = [&](int j) {
+      if ((j + 1) % qs != 0 && j + 1 != n) return;
+      const int64_t c = c_begin + j / qs;
+      merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float M, float L) {
+        (void)nt;
+        const int64_t idx = (row0 + col) * p.num_partitions + c;
+        const float inv_l = dec.out_mul / L;
+        float* po = p.part_o + idx * kD + 4 * gq;
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<f32x4*>(po + rr * 16) = acc[rr] * inv_l;
+        if (gq == 0) {
+          p.part_m[idx] = M;
+          p.part_l[idx] = L;
+        }
+      });
+      dec.reset();
+    };
+    stream_steps(dec, n, tok_of, real, first, after);
+    if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
+  } else {
+    const int nn = dec.n;
+    auto after = [&](int j) {
+      if ((j + 1) % spc != 0 && j + 1 != n) return;
+      const int64_t c = c_begin + j / spc;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float l = sum_across_rows(dec.l_part[nt]);
+        const int col = nt * 16 + nn;
+        if (col < group) {
+          const int64_t idx = (row0 + col) * p.num_partitions + c;
+          const float inv_l = dec.out_mul / l;
+          float* po = p.part_o + idx * kD + 4 * gq;
+#pragma unroll
+          for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<f32x4*>(po + rr * 16) = dec.oacc[nt][rr] * inv_l;
+          if (gq == 0) {
+            p.part_m[idx] = dec.m_run[nt];
+            p.part_l[idx] = l;
+          }
+        }
+      }
+      dec.reset();
+    };
+    stream_steps(dec, n, tok_of, real, first, after);
+    if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
   }
 }
 
 // Log-sum-exp merge of the chunk partials of one (sequence, query head):
 // out = sum_c w_c o_c / sum_c w_c with w_c = l_c * 2^(m_c - max_c m_c).
+// One 256-thread workgroup per row: the four waves take every fourth chunk
+// (eight chunks' loads in flight per wave), each lane two of the 128 dims;
+// the waves' sums meet in LDS.
+constexpr int kReduceThreads = 256;
+constexpr int kReduceUnroll = 8;
+
 template <int BS>
-__global__ __launch_bounds__(128) void lse_reduce_kernel(PoolGeom g, DecodeLaunch p) {
+__global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(PoolGeom g, DecodeLaunch p) {
   const int row = blockIdx.x;  // seq * Hq + head
   const int seq = row / p.num_q_heads;
-  const int dim = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
   int T = p.lens[seq];
   const int t_cap = p.max_blocks * BS;
   T = T < 0 ? 0 : (T > t_cap ? t_cap : T);
   const int cv = (T + p.partition_tokens - 1) / p.partition_tokens;
-  const float* m = p.part_m + static_cast<int64_t>(row) * p.num_partitions;
-  const float* l = p.part_l + static_cast<int64_t>(row) * p.num_partitions;
-  const float* o = p.part_o + static_cast<int64_t>(row) * p.num_partitions * kD + dim;
+  const int64_t base = static_cast<int64_t>(row) * p.num_partitions;
+  const float* m = p.part_m + base;
+  const float* l = p.part_l + base;
+  const float* o = p.part_o + base * kD + 2 * lane;
+
+  __shared__ float sm_red[4];
+  __shared__ float sm_acc[4][kD];
+  __shared__ float sm_den[4];
+  // 1. M = max_c m_c
   float M = -__builtin_inff();
-  for (int c = 0; c < cv; ++c) M = fmaxf(M, m[c]);
-  float num = 0.0f, den = 0.0f;
-  for (int c = 0; c < cv; ++c) {
-    const float wgt = l[c] * exp2f(m[c] - M);
-    den += wgt;
-    num += wgt * o[static_cast<int64_t>(c) * kD];
+  for (int c = threadIdx.x; c < cv; c += kReduceThreads) M = fmaxf(M, m[c]);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) sm_red[w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
+  // 2. this wave's chunks c = w, w + 4, ...
+  float a0 = 0.0f, a1 = 0.0f, den = 0.0f;
+  for (int c0 = w; c0 < cv; c0 += 4 * kReduceUnroll) {
+    float2 ov[kReduceUnroll];
+    float wt[kReduceUnroll];
+#pragma unroll
+    for (int u = 0; u < kReduceUnroll; ++u) {
+      const int c = c0 + 4 * u;
+      const bool ok = c < cv;
+      ov[u] = ok ? *reinterpret_cast<const float2*>(o + static_cast<int64_t>(c) * kD) : float2{0.0f, 0.0f};
+      wt[u] = ok ? l[c] * exp2f(m[c] - M) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kReduceUnroll; ++u) {
+      den += wt[u];
+      a0 += wt[u] * ov[u].x;
+      a1 += wt[u] * ov[u].y;
+    }
   }
-  _Float16* out = static_cast<_Float16*>(p.out) + static_cast<int64_t>(row) * kD + dim;
-  *out = (_Float16)(cv > 0 ? num / den : 0.0f);
+  sm_acc[w][2 * lane] = a0;
+  sm_acc[w][2 * lane + 1] = a1;
+  if (lane == 0) sm_den[w] = den;
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    const int d = threadIdx.x;
+    const float num = (sm_acc[0][d] + sm_acc[1][d]) + (sm_acc[2][d] + sm_acc[3][d]);
+    const float dd = (sm_den[0] + sm_den[1]) + (sm_den[2] + sm_den[3]);
+    _Float16* out = static_cast<_Float16*>(p.out) + static_cast<int64_t>(row) * kD + d;
+    *out = (_Float16)(cv > 0 ? num / dd : 0.0f);
+  }
   (void)g;
 }
 
 // Kernels are launched with hipExtLaunchKernelGGL: its start/stop events (null
 // when not timing) are stamped by the dispatch itself, so timing a launch adds
 // no barrier packets to the stream.
-template <int ELEM, int BS>
-hipError_t launch_decode_bs(const PoolGeom& g, const DecodeLaunch& d, bool partial, int nt,
-                            dim3 grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  constexpr int NW = kDecodeWaves;
-  const dim3 block(NW * 64);
-  if (nt == 1) {
-    if (partial) hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, 1, true, NW>), grid, block, 0, s, t0, t1, 0, g, d);
-    else hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, 1, false, NW>), grid, block, 0, s, t0, t1, 0, g, d);
-  } else {
-    if (partial) hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, 2, true, NW>), grid, block, 0, s, t0, t1, 0, g, d);
-    else hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, 2, false, NW>), grid, block, 0, s, t0, t1, 0, g, d);
+template <int ELEM, int BS, int NT>
+hipError_t launch_decode_nt(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
+                            hipEvent_t t1) {
+  const dim3 block(kWaves * 64);
+  const int64_t units = static_cast<int64_t>(d.num_seqs) * g.kv_heads;
+  switch (d.mode) {
+    case kSingle:
+      hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, NT, kSingle>), dim3(static_cast<unsigned>(units)),
+                            block, 0, s, t0, t1, 0, g, d);
+      break;
+    case kSplit4:
+      hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, NT, kSplit4>),
+                            dim3(static_cast<unsigned>(units * d.waves_per_unit)), block, 0, s, t0, t1, 0, g, d);
+      break;
+    case kSplit1:
+      hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, NT, kSplit1>),
+                            dim3(static_cast<unsigned>((units * d.waves_per_unit + kWaves - 1) / kWaves)), block,
+                            0, s, t0, t1, 0, g, d);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int ELEM, int BS>
+hipError_t launch_decode_bs(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s,
+                            hipEvent_t t0, hipEvent_t t1) {
+  return nt == 1 ? launch_decode_nt<ELEM, BS, 1>(g, d, s, t0, t1) : launch_decode_nt<ELEM, BS, 2>(g, d, s, t0, t1);
+}
+
 template <int ELEM>
-hipError_t launch_decode_elem(const PoolGeom& g, const DecodeLaunch& d, bool partial, int nt,
-                              dim3 grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+hipError_t launch_decode_elem(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s,
+                              hipEvent_t t0, hipEvent_t t1) {
   switch (g.block_size) {
-    case 8: return launch_decode_bs<ELEM, 8>(g, d, partial, nt, grid, s, t0, t1);
-    case 16: return launch_decode_bs<ELEM, 16>(g, d, partial, nt, grid, s, t0, t1);
-    case 32: return launch_decode_bs<ELEM, 32>(g, d, partial, nt, grid, s, t0, t1);
+    case 8: return launch_decode_bs<ELEM, 8>(g, d, nt, s, t0, t1);
+    case 16: return launch_decode_bs<ELEM, 16>(g, d, nt, s, t0, t1);
+    case 32: return launch_decode_bs<ELEM, 32>(g, d, nt, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, bool partial, hipStream_t s,
-                         hipEvent_t t0, hipEvent_t t1) {
+hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
+                         hipEvent_t t1) {
   const int group = d.num_q_heads / g.kv_heads;
   const int nt = group > 16 ? 2 : 1;
-  const int64_t wgs = static_cast<int64_t>(d.num_partitions) * g.kv_heads * d.num_seqs;
-  if (wgs <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(wgs));
-  if (g.elem_bytes == 2) return launch_decode_elem<2>(g, d, partial, nt, grid, s, t0, t1);
-  return launch_decode_elem<1>(g, d, partial, nt, grid, s, t0, t1);
+  if (static_cast<int64_t>(d.num_seqs) * g.kv_heads <= 0) return hipSuccess;
+  if (d.mode != kSingle) {
+    // The split schedules need whole steps per chunk (and per wave quarter).
+    const int quantum = d.mode == kSplit4 ? 64 : 16;
+    if (d.waves_per_unit < 1 || d.chunks_per_wave < 1 || d.partition_tokens < quantum ||
+        d.partition_tokens % quantum != 0)
+      return hipErrorInvalidValue;
+  }
+  if (g.elem_bytes == 2) return launch_decode_elem<2>(g, d, nt, s, t0, t1);
+  return launch_decode_elem<1>(g, d, nt, s, t0, t1);
 }
 
 hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s,
@@ -483,9 +751,9 @@ hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream
   if (rows <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(rows));
   switch (g.block_size) {
-    case 8: hipExtLaunchKernelGGL(lse_reduce_kernel<8>, grid, dim3(kD), 0, s, t0, t1, 0, g, d); break;
-    case 16: hipExtLaunchKernelGGL(lse_reduce_kernel<16>, grid, dim3(kD), 0, s, t0, t1, 0, g, d); break;
-    case 32: hipExtLaunchKernelGGL(lse_reduce_kernel<32>, grid, dim3(kD), 0, s, t0, t1, 0, g, d); break;
+    case 8: hipExtLaunchKernelGGL(lse_reduce_kernel<8>, grid, dim3(kReduceThreads), 0, s, t0, t1, 0, g, d); break;
+    case 16: hipExtLaunchKernelGGL(lse_reduce_kernel<16>, grid, dim3(kReduceThreads), 0, s, t0, t1, 0, g, d); break;
+    case 32: hipExtLaunchKernelGGL(lse_reduce_kernel<32>, grid, dim3(kReduceThreads), 0, s, t0, t1, 0, g, d); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -31,13 +31,16 @@ struct DecodeLaunch {
   float* part_l;   // [S][Hq][C]
   float* part_o;   // [S][Hq][C][D]
   int num_seqs, num_q_heads, max_blocks;
-  int partition_tokens;  // tokens per chunk (single pass: covers max_blocks*block_size)
-  int num_partitions;    // C
+  int mode;              // 0: single pass, 1: split, four waves per chunk, 2: split, one wave per run
+  int partition_tokens;  // P: tokens per chunk (split modes)
+  int num_partitions;    // C = ceil(max_blocks * block_size / P) (1 in a single pass)
+  int chunks_per_wave;   // k: chunks in one run (split modes)
+  int waves_per_unit;    // runs per (sequence, KV head) = ceil(C / k) (split modes)
   float scale;
 };
 
 // t0/t1: optional events stamped at the kernel's start and end (null: untimed).
-hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, bool partial, hipStream_t stream,
+hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
                          hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
                              hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
