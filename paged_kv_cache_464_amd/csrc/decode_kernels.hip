@@ -69,6 +69,13 @@ constexpr int kWaves = 4;           // waves per decode workgroup
 // fp8, GQA and MQA; deeper pipelines only cost registers and occupancy.
 constexpr int kDepth = 2;
 
+// How far (base 2) a score may exceed the softmax reference before the
+// accumulators are rescaled, where rescaling is lazy (two or more column
+// tiles): probabilities then stay below 2^8, exact as fp16 operands.  Lazy
+// rescaling saves the wide rescale on most steps of MQA-sized groups; with
+// one column tile the eager form schedules better (measured on MI355X).
+constexpr float kRescaleSlack = 8.0f;
+
 // Four E4M3FN codes (bytes 0..3 of w) -> four fp16 in byte order, with the
 // gfx950 packed converter at scale 1: every E4M3FN value is an fp16 value, so
 // the conversion is exact (checked for all byte pairs on MI355X).
@@ -120,8 +127,20 @@ struct WaveDecoder {
   float qk_mul, out_mul;
   f16x8 qop[NT][4];
   f32x4 oacc[NT][8];
-  float m_run[NT], l_part[NT];
+  // Online-softmax state per head column: accumulators relative to the
+  // reference m_run (base 2).  With kLazy the reference may trail the true
+  // running maximum m_true by less than kRescaleSlack and fresh marks a state
+  // with nothing accumulated; otherwise m_run is the running maximum itself.
+  static constexpr bool kLazy = NT > 1;
+  float m_run[NT], m_true[NT], l_part[NT];
+  bool fresh;
   uint32_t bad;
+
+  // Largest score seen since the last reset.
+  __device__ float top(int nt) const {
+    if constexpr (kLazy) return m_true[nt];
+    return m_run[nt];
+  }
 
   // Geometry and the block-table row; needs no context length.
   __device__ void bind(const PoolGeom& g, const DecodeLaunch& p, int seq, int kvh, int lane) {
@@ -175,9 +194,11 @@ struct WaveDecoder {
   }
 
   __device__ void reset() {
+    fresh = true;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       m_run[nt] = -__builtin_inff();
+      m_true[nt] = -__builtin_inff();
       l_part[nt] = 0.0f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) oacc[nt][r] = f32x4{0, 0, 0, 0};
@@ -240,6 +261,27 @@ struct WaveDecoder {
   }
 
   // Attention over the 16 tokens tb .. tb+15 held in r (those >= T masked).
+  // Scales one column's four raw scores to base-2 logits, masks those past
+  // the context, and returns the column's maximum over the step's 16 tokens.
+  __device__ float scale_mask(f32x4& sc, bool tail, int valid_here) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x = sc[e] * qk_mul;
+      if (tail && e >= valid_here) x = -__builtin_inff();
+      sc[e] = x;
+    }
+    return max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+  }
+
+  // Moves column tile nt's reference to m_new, rescaling what it holds.
+  __device__ void rescale(int nt, float m_new) {
+    const float alpha = exp2f(m_run[nt] - m_new);
+    l_part[nt] *= alpha;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) oacc[nt][rr] *= alpha;
+    m_run[nt] = m_new;
+  }
+
   __device__ void compute(StepRegs<ELEM>& r, int tb) {
     // S^T = K Q^T
     f32x4 s[NT];
@@ -263,28 +305,44 @@ struct WaveDecoder {
     // Scores of tokens tb + 4*gq + e for head column n; mask the tail.
     const bool tail = tb + 16 > T;
     const int valid_here = T - (tb + 4 * gq);  // tokens of this lane's 4 that exist
-    float mnew[NT];
-    bool grow = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = s[nt][e] * qk_mul;
-        if (tail && e >= valid_here) x = -__builtin_inff();
-        s[nt][e] = x;
-      }
-      const float m = max_across_rows(fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3])));
-      mnew[nt] = fmaxf(m_run[nt], m);
-      grow |= mnew[nt] > m_run[nt];
-    }
-    if (__any(grow)) {
+    if constexpr (kLazy) {
+      // The reference moves only when a score exceeds it by kRescaleSlack or
+      // more, so exponentials stay below 2^kRescaleSlack (exact in fp16 and
+      // fp32) and the accumulators are rescaled rarely; the first step after a
+      // reset takes its own maximum, with nothing to rescale.
+      bool need = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float alpha = exp2f(m_run[nt] - mnew[nt]);
-        l_part[nt] *= alpha;
+        const float m = scale_mask(s[nt], tail, valid_here);
+        m_true[nt] = fmaxf(m_true[nt], m);
+        need |= m - m_run[nt] >= kRescaleSlack;
+      }
+      if (fresh) {
+        fresh = false;
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) oacc[nt][rr] *= alpha;
-        m_run[nt] = mnew[nt];
+        for (int nt = 0; nt < NT; ++nt) m_run[nt] = m_true[nt];
+      } else if (__any(need)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) rescale(nt, m_true[nt]);
+      }
+    } else {
+      float mnew[NT];
+      bool grow = false;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = s[nt][e] * qk_mul;
+          if (tail && e >= valid_here) x = -__builtin_inff();
+          s[nt][e] = x;
+        }
+        const float m = max_across_rows(fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3])));
+        mnew[nt] = fmaxf(m_run[nt], m);
+        grow |= mnew[nt] > m_run[nt];
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) rescale(nt, mnew[nt]);
       }
     }
     f16x4 pop[NT];
@@ -389,12 +447,14 @@ struct MergeLds {
   float m[kWaves][NT * 16];
   float l[kWaves][NT * 16];
   float o[kWaves - 1][NT * 16][kSmoStride];
+  float mt[kWaves][NT * 16];  // largest scores (lazy rescaling only)
 };
 
-// Merges the (max, sum, O) of the workgroup's four waves for every head
-// column and lets wave 0 emit(nt, col, acc[8] = sum_w O_w * 2^(m_w - M), M, L)
-// with L = sum_w l_w * 2^(m_w - M).  All four waves must call it; two
-// barriers.
+// Merges the (reference, sum, O) of the workgroup's four waves for every head
+// column and lets wave 0 emit(nt, col, acc[8] = sum_w O_w * 2^(m_w - M), M, L,
+// Mt) with M the largest reference, L = sum_w l_w * 2^(m_w - M) and Mt the
+// largest score (Mt = M where the reference is the running maximum).  All
+// four waves must call it; two barriers.
 template <class Dec, class Emit>
 __device__ inline void merge_waves(Dec& dec, MergeLds<Dec::kNT>& sm, int w, int group, Emit emit) {
   constexpr int NT = Dec::kNT;
@@ -404,17 +464,25 @@ __device__ inline void merge_waves(Dec& dec, MergeLds<Dec::kNT>& sm, int w, int 
     const float l = sum_across_rows(dec.l_part[nt]);
     if (gq == 0) {
       sm.m[w][nt * 16 + n] = dec.m_run[nt];
+      if constexpr (Dec::kLazy) sm.mt[w][nt * 16 + n] = dec.m_true[nt];
       sm.l[w][nt * 16 + n] = l;
     }
   }
   __syncthreads();
-  float big_m[NT], big_l[NT], f[NT];
+  float big_m[NT], big_mt[NT], big_l[NT], f[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int col = nt * 16 + n;
     float M = sm.m[0][col];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm.m[ww][col]);
+    big_mt[nt] = M;
+    if constexpr (Dec::kLazy) {
+      float Mt = sm.mt[0][col];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) Mt = fmaxf(Mt, sm.mt[ww][col]);
+      big_mt[nt] = Mt;
+    }
     float L = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
@@ -444,7 +512,7 @@ __device__ inline void merge_waves(Dec& dec, MergeLds<Dec::kNT>& sm, int w, int 
 #pragma unroll
       for (int ww = 0; ww < kWaves - 1; ++ww) acc[rr] += *reinterpret_cast<const f32x4*>(&sm.o[ww][col][dim]);
     }
-    emit(nt, col, acc, big_m[nt], big_l[nt]);
+    emit(nt, col, acc, big_m[nt], big_l[nt], big_mt[nt]);
   }
 }
 
@@ -512,7 +580,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(PoolGeom g, DecodeL
     else return static_cast<int64_t>(c_begin) * P + 16ll * j;
   };
 
-  WaveDecoder<ELEM, BS, NT> dec;
+  using Dec = WaveDecoder<ELEM, BS, NT>;
+  Dec dec;
   dec.bind(g, p, seq, kvh, lane);
   FirstIds first;
 #pragma unroll
@@ -557,7 +626,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(PoolGeom g, DecodeL
     __shared__ MergeLds<NT> sm;
     stream_steps(dec, n, tok_of, real, first, [](int) {});
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
-    merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float, float L) {
+    merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float, float L, float) {
       (void)nt;
       const float inv_l = dec.out_mul / L;
       _Float16* po = static_cast<_Float16*>(p.out) + (row0 + col) * kD + 4 * gq;
@@ -572,7 +641,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(PoolGeom g, DecodeL
     auto after = [&](int j) {
       if ((j + 1) % qs != 0 && j + 1 != n) return;
       const int64_t c = c_begin + j / qs;
-      merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float M, float L) {
+      merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float M, float L, float Mt) {
         (void)nt;
         const int64_t idx = (row0 + col) * p.num_partitions + c;
         const float inv_l = dec.out_mul / L;
@@ -580,8 +649,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(PoolGeom g, DecodeL
 #pragma unroll
         for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<f32x4*>(po + rr * 16) = acc[rr] * inv_l;
         if (gq == 0) {
-          p.part_m[idx] = M;
-          p.part_l[idx] = L;
+          p.part_m[idx] = Mt;
+          p.part_l[idx] = (!Dec::kLazy || M == Mt) ? L : L * exp2f(M - Mt);
         }
       });
       dec.reset();
@@ -604,8 +673,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(PoolGeom g, DecodeL
 #pragma unroll
           for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<f32x4*>(po + rr * 16) = dec.oacc[nt][rr] * inv_l;
           if (gq == 0) {
-            p.part_m[idx] = dec.m_run[nt];
-            p.part_l[idx] = l;
+            const float mt = dec.top(nt);
+            p.part_m[idx] = mt;
+            p.part_l[idx] = (!Dec::kLazy || dec.m_run[nt] == mt) ? l : l * exp2f(dec.m_run[nt] - mt);
           }
         }
       }
