@@ -236,13 +236,14 @@ int pa_lse_reduce(pa_pool* pool, const void* workspace, uint64_t workspace_bytes
 /* Read (and optionally clear) the pool's device status word; synchronises `stream`. */
 int pa_device_status(pa_pool* pool, uint32_t* flags_out, int32_t clear, void* stream);
 
-/* Kernel timing: while enabled, every pa_decode / pa_decode_partials launch
- * (up to max_launches of them) is dispatched with HIP start/stop events that
+/* Kernel timing: while enabled, the pa_decode / pa_decode_partials launches
+ * numbered 0, every, 2*every, ... since pa_profile_begin (up to max_launches of
+ * them; every >= 1, 1 = all) are dispatched with HIP start/stop events that
  * the dispatch itself stamps at the kernel's start and end on the launch
  * stream (hipExtLaunchKernel), for the attention kernel and for the reduce
  * kernel; no extra packets are enqueued.  pa_profile_end synchronises those
  * events, returns the summed durations and disables timing. */
-int pa_profile_begin(pa_pool* pool, int32_t max_launches);
+int pa_profile_begin(pa_pool* pool, int32_t max_launches, int32_t every);
 int pa_profile_end(pa_pool* pool, pa_profile* out);
 
 /* Message of the last failure on this thread ("" if none). */

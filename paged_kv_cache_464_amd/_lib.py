@@ -73,7 +73,7 @@ SIGNATURES = {
                                      _P, C.c_uint64, _P]),
     "pa_lse_reduce": (C.c_int, [_P, _P, C.c_uint64, _P, _I32, _I32, _I32, _I32, _P, _P]),
     "pa_device_status": (C.c_int, [_P, C.POINTER(C.c_uint32), _I32, _P]),
-    "pa_profile_begin": (C.c_int, [_P, _I32]),
+    "pa_profile_begin": (C.c_int, [_P, _I32, _I32]),
     "pa_profile_end": (C.c_int, [_P, C.POINTER(pa_profile)]),
     "pa_last_error": (C.c_char_p, []),
 }

@@ -49,6 +49,8 @@ struct pa_pool {
   // kernel timing
   bool profiling = false;
   int32_t max_records = 0;
+  int32_t every = 1;      // time one launch in `every`
+  int64_t launches = 0;   // launches seen since pa_profile_begin
   std::vector<hipEvent_t> ev;  // 4 per record: decode start/end, reduce start/end (if any)
   std::vector<int8_t> has_reduce;
   int32_t n_records = 0;
@@ -460,7 +462,7 @@ static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_he
   const pa::DecodeLaunch d = make_launch(layer, q, num_q_heads, tables, max_blocks, lens, num_seqs,
                                          scale, pl, out, workspace);
   auto s = static_cast<hipStream_t>(stream);
-  const bool rec = p->profiling && p->n_records < p->max_records;
+  const bool rec = p->profiling && p->launches++ % p->every == 0 && p->n_records < p->max_records;
   hipEvent_t* ev = rec ? &p->ev[4 * static_cast<size_t>(p->n_records)] : nullptr;
   const bool reduced = pl.partial && mode == 0;
   hipError_t e = pa::launch_decode(p->geom, d, s, rec ? ev[0] : nullptr, rec ? ev[1] : nullptr);
@@ -530,10 +532,11 @@ int pa_device_status(pa_pool* p, uint32_t* flags_out, int32_t clear, void* strea
   return PA_OK;
 }
 
-int pa_profile_begin(pa_pool* p, int32_t max_launches) {
+int pa_profile_begin(pa_pool* p, int32_t max_launches, int32_t every) {
   int rc = check_bound(p);
   if (rc) return rc;
   if (max_launches < 1) return fail(PA_ERR_INVALID, "max_launches must be >= 1");
+  if (every < 1) return fail(PA_ERR_INVALID, "every must be >= 1");
   const size_t need = 4ull * max_launches;
   while (p->ev.size() < need) {
     hipEvent_t e;
@@ -545,6 +548,8 @@ int pa_profile_begin(pa_pool* p, int32_t max_launches) {
   p->has_reduce.assign(max_launches, 0);
   p->max_records = max_launches;
   p->n_records = 0;
+  p->every = every;
+  p->launches = 0;
   p->profiling = true;
   return PA_OK;
 }

@@ -326,8 +326,8 @@ def pa_device_status(h, clear=False, stream=None) -> int:
     return v.value
 
 
-def pa_profile_begin(h, max_launches):
-    _check(_L().pa_profile_begin(C.c_void_p(h), int(max_launches)))
+def pa_profile_begin(h, max_launches, every=1):
+    _check(_L().pa_profile_begin(C.c_void_p(h), int(max_launches), int(every)))
 
 
 def pa_profile_end(h) -> dict:

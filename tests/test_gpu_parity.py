@@ -226,3 +226,23 @@ def test_copy_blocks_all_layers():
     for ly in range(layers):
         kk, vv = pool.gather_kv(ly, dst_slots)
         assert torch.equal(kk, k[ly]) and torch.equal(vv, k[ly])
+
+
+def test_kernel_timing_samples_every_nth_launch():
+    """pa_profile_begin(max, every) stamps launches 0, every, 2*every, ... only,
+    for the decode kernel and, in split mode, the reduce kernel."""
+    say("profile sampling")
+    lens = [300, 1000]
+    c = build_case(lens, 8, 2, 16, 100, 31)
+    ref = oracle_decode(c, range(len(lens)))
+    for every, launches, expect in ((3, 7, 3), (1, 4, 4), (2, 9, 3)):
+        pa.pa_profile_begin(c.pool.handle, expect if every == 2 else 64, every)
+        for _ in range(launches):
+            out = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=128)
+        prof = pa.pa_profile_end(c.pool.handle)
+        assert prof["decode_launches"] == expect, (every, prof)
+        assert prof["reduce_launches"] == expect, (every, prof)
+        assert prof["decode_ms"] > 0 and prof["reduce_ms"] > 0
+        assert_close(out, ref, "fp16", f"every={every}")
+    with pytest.raises(RuntimeError):
+        pa.pa_profile_begin(c.pool.handle, 4, 0)
