@@ -5,10 +5,11 @@
 Default workload ``gqa_32x4096``: 32 layers, 32 query / 8 KV heads, head_dim
 128, fp16 K/V, 16-token blocks, 32 sequences prefilled to 4095 tokens, block
 placement a seeded permutation of the pool.  One step = append one token to
-every sequence (host block manager), upload the slot mapping, lengths and
-block tables (one packed copy), then for each of the 32 layers scatter the new
-tokens' K/V into the cache (``pa_write_kv``) and run paged decode attention
-over the whole context (``pa_decode``).  The timed region holds exactly K
+every sequence (host block manager), upload the slot mapping, lengths, a
+longest-first sequence order and block tables (one packed copy), then for
+each of the 32 layers scatter the new tokens' K/V into the cache
+(``pa_write_kv``) and run paged decode attention over the whole context
+(``pa_decode``).  The timed region holds exactly K
 steps; inputs are resident in HBM.
 
 The other workloads (``tiny``, ``cb_prefix``, ``long_ctx``,
@@ -171,17 +172,18 @@ class DecodeBench:
         self.mb_cap = int(-(-(self.setup_lens.max() + total_steps) // self.bs))
         ws = pa.pa_decode_workspace_bytes(self.pool.handle, self.S, self.hq, self.mb_cap, self.partition)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.dev)
-        # Step metadata (slot mapping, lengths, block tables) is packed into one
-        # int32 buffer so that each step makes a single upload: two pinned host
-        # copies used alternately (each guarded by the event of the upload that
-        # last read it) and one device copy.
-        n_meta = self.S * (2 + self.mb_cap)
+        # Step metadata (slot mapping, lengths, longest-first sequence order,
+        # block tables) is packed into one int32 buffer so that each step makes
+        # a single upload: two pinned host copies used alternately (each guarded
+        # by the event of the upload that last read it) and one device copy.
+        n_meta = self.S * (3 + self.mb_cap)
         self.pinned = [torch.empty(n_meta, dtype=torch.int32, pin_memory=True) for _ in range(2)]
         self.uploaded = [torch.cuda.Event(), torch.cuda.Event()]
         self.meta_d = torch.empty(n_meta, dtype=torch.int32, device=self.dev)
         self.slots_d = self.meta_d[:self.S]
         self.lens_d = self.meta_d[self.S:2 * self.S]
-        self.tables_d = self.meta_d[2 * self.S:].view(self.S, self.mb_cap)
+        self.order_d = self.meta_d[2 * self.S:3 * self.S]
+        self.tables_d = self.meta_d[3 * self.S:].view(self.S, self.mb_cap)
         self.n_step = 0
         self.stream = torch.cuda.current_stream().cuda_stream  # every launch goes here
         self.kv_bytes_log, self.unique_bytes_log, self.lens_log = [], [], []
@@ -259,7 +261,8 @@ class DecodeBench:
             slots[i] = self.pool.alloc(s, 1)[0][0]
         tables, lens = self.pool.block_tables(self.seqs, self.mb_cap)
         meta[self.S:2 * self.S] = lens
-        meta[2 * self.S:] = tables.reshape(-1)
+        meta[2 * self.S:3 * self.S] = pa.pa_order_longest_first(lens)
+        meta[3 * self.S:] = tables.reshape(-1)
         self.meta_d.copy_(self.pinned[k], non_blocking=True)
         self.uploaded[k].record()
         h, st = self.pool.handle, self.stream
@@ -267,7 +270,8 @@ class DecodeBench:
             layer = r % self.copies
             pa.pa_write_kv(h, layer, self.k_new[r], self.v_new[r], self.slots_d, stream=st)
             pa.pa_decode(h, layer, self.q[r], self.tables_d, self.lens_d, out=self.out[r],
-                         partition_tokens=self.partition, workspace=self.workspace, stream=st)
+                         partition_tokens=self.partition, workspace=self.workspace, stream=st,
+                         seq_order=self.order_d)
         per_tok = 2 * self.hkv * 128 * self.elem
         scales = 2 * self.hkv * 4 if self.fp8 else 0
         self.kv_bytes_log.append(int(lens.astype(np.int64).sum()) * per_tok + scales)

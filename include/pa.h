@@ -76,6 +76,7 @@ extern "C" {
 #define PA_DEV_BAD_SLOT 1u  /* a slot >= num_blocks*block_size was skipped      */
 #define PA_DEV_BAD_BLOCK 2u /* a table entry outside [0, num_blocks) was read as block 0 */
 #define PA_DEV_BAD_LEN 4u   /* a context length < 1 or > max_blocks*block_size  */
+#define PA_DEV_BAD_ORDER 8u /* a seq_order entry outside [0, num_seqs) was skipped */
 
 typedef struct pa_pool pa_pool; /* opaque */
 
@@ -205,13 +206,23 @@ int pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num
  * heads); -1 forces one pass per (sequence, KV head); P > 0 (a
  * multiple of 16 and of block_size) splits each context into chunks of P
  * tokens whose partials are merged by log-sum-exp.
+ * seq_order: NULL, or device int32 [num_seqs], a permutation of 0..num_seqs-1
+ * giving the order in which workgroups take the sequences.  Results do not
+ * depend on it; with uneven lengths, longest first (pa_order_longest_first)
+ * keeps long sequences from starting last and idling the other CUs.  An entry
+ * outside [0, num_seqs) sets PA_DEV_BAD_ORDER and is skipped; a repeated entry
+ * leaves some sequence's output unwritten.
  * workspace: device memory of pa_decode_workspace_bytes() bytes (may be NULL
  * when that is 0).  Out-of-range table entries or lengths never cause an
  * out-of-bounds access; they set PA_DEV_* bits instead. */
 int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
-              int32_t num_seqs, float scale, int32_t partition_tokens, void* out,
-              void* workspace, uint64_t workspace_bytes, void* stream);
+              int32_t num_seqs, const int32_t* seq_order, float scale, int32_t partition_tokens,
+              void* out, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Host helper: order_out[0..n) = indices of lens[0..n) by decreasing length,
+ * equal lengths in increasing index (a stable sort), for pa_decode's seq_order. */
+int pa_order_longest_first(const int32_t* lens, int32_t n, int32_t* order_out);
 
 /* The two halves of a partitioned pa_decode, callable separately.
  * pa_decode_partials writes, for chunk c of every (sequence, query head), into
@@ -226,9 +237,9 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
  *    out = sum_c w_c o_c / sum_c w_c,  w_c = l_c * 2^(m_c - max_c m_c). */
 int pa_decode_partials(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
                        const int32_t* block_tables, int32_t max_blocks,
-                       const int32_t* context_lens, int32_t num_seqs, float scale,
-                       int32_t partition_tokens, void* workspace, uint64_t workspace_bytes,
-                       void* stream);
+                       const int32_t* context_lens, int32_t num_seqs, const int32_t* seq_order,
+                       float scale, int32_t partition_tokens, void* workspace,
+                       uint64_t workspace_bytes, void* stream);
 int pa_lse_reduce(pa_pool* pool, const void* workspace, uint64_t workspace_bytes,
                   const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                   int32_t max_blocks, int32_t partition_tokens, void* out, void* stream);

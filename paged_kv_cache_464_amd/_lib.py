@@ -23,6 +23,7 @@ PA_DTYPE_FP8_E4M3 = 1
 PA_DEV_BAD_SLOT = 1
 PA_DEV_BAD_BLOCK = 2
 PA_DEV_BAD_LEN = 4
+PA_DEV_BAD_ORDER = 8
 
 
 class pa_pool_info(C.Structure):
@@ -67,9 +68,10 @@ SIGNATURES = {
     "pa_gather_kv": (C.c_int, [_P, _I32, _P, _I32, _P, _P, _P]),
     "pa_copy_blocks": (C.c_int, [_P, _PI32, _PI32, _I32, _P]),
     "pa_decode_workspace_bytes": (C.c_int, [_P, _I32, _I32, _I32, _I32, C.POINTER(C.c_uint64)]),
-    "pa_decode": (C.c_int, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, C.c_float, _I32, _P, _P,
+    "pa_decode": (C.c_int, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _P, C.c_float, _I32, _P, _P,
                             C.c_uint64, _P]),
-    "pa_decode_partials": (C.c_int, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, C.c_float, _I32,
+    "pa_order_longest_first": (C.c_int, [_PI32, _I32, _PI32]),
+    "pa_decode_partials": (C.c_int, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _P, C.c_float, _I32,
                                      _P, C.c_uint64, _P]),
     "pa_lse_reduce": (C.c_int, [_P, _P, C.c_uint64, _P, _I32, _I32, _I32, _I32, _P, _P]),
     "pa_device_status": (C.c_int, [_P, C.POINTER(C.c_uint32), _I32, _P]),

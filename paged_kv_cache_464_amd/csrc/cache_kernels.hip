@@ -163,12 +163,9 @@ hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k_new, cons
   const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves));
   const auto* k = static_cast<const _Float16*>(k_new);
   const auto* v = static_cast<const _Float16*>(v_new);
-  if (g.elem_bytes == 2) {
-    hipLaunchKernelGGL(write_kv_kernel<2>, grid, dim3(256), 0, stream, g, layer, k, v, slots, n_tokens);
-  } else {
-    hipLaunchKernelGGL(write_kv_kernel<1>, grid, dim3(256), 0, stream, g, layer, k, v, slots, n_tokens);
-  }
-  return hipGetLastError();
+  if (g.elem_bytes == 2)
+    return launch_kernel(write_kv_kernel<2>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
+  return launch_kernel(write_kv_kernel<1>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
 }
 
 hipError_t launch_gather_kv(const PoolGeom& g, int layer, const int32_t* slots, int n_tokens,
@@ -178,12 +175,9 @@ hipError_t launch_gather_kv(const PoolGeom& g, int layer, const int32_t* slots, 
   const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves));
   auto* ko = static_cast<uint8_t*>(k_out);
   auto* vo = static_cast<uint8_t*>(v_out);
-  if (g.elem_bytes == 2) {
-    hipLaunchKernelGGL(gather_kv_kernel<2>, grid, dim3(256), 0, stream, g, layer, slots, n_tokens, ko, vo);
-  } else {
-    hipLaunchKernelGGL(gather_kv_kernel<1>, grid, dim3(256), 0, stream, g, layer, slots, n_tokens, ko, vo);
-  }
-  return hipGetLastError();
+  if (g.elem_bytes == 2)
+    return launch_kernel(gather_kv_kernel<2>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
+  return launch_kernel(gather_kv_kernel<1>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
 }
 
 hipError_t launch_copy_blocks(const PoolGeom& g, const int32_t* src, const int32_t* dst, int n,
@@ -195,8 +189,8 @@ hipError_t launch_copy_blocks(const PoolGeom& g, const int32_t* src, const int32
       p.src[i] = i < m ? src[base + i] : -1;
       p.dst[i] = i < m ? dst[base + i] : -1;
     }
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3(m * 2 * g.layers), dim3(256), 0, stream, g, p);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_kernel(copy_blocks_kernel, dim3(m * 2 * g.layers), dim3(256), stream, nullptr,
+                                       nullptr, g, p);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -2,6 +2,7 @@
 // HIP kernels, device status and kernel timing.  Nothing throws across the ABI.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -182,13 +183,14 @@ int bm_status(pa::BmStatus s, int32_t seq) {
 
 pa::DecodeLaunch make_launch(int32_t layer, const void* q, int32_t num_q_heads,
                              const int32_t* tables, int32_t max_blocks, const int32_t* lens,
-                             int32_t num_seqs, float scale, const Plan& pl, void* out,
-                             void* workspace) {
+                             int32_t num_seqs, const int32_t* order, float scale, const Plan& pl,
+                             void* out, void* workspace) {
   pa::DecodeLaunch d{};
   d.layer = layer;
   d.q = q;
   d.tables = tables;
   d.lens = lens;
+  d.order = order;
   d.out = out;
   d.num_seqs = num_seqs;
   d.num_q_heads = num_q_heads;
@@ -447,8 +449,9 @@ int pa_decode_workspace_bytes(const pa_pool* p, int32_t num_seqs, int32_t num_q_
 
 static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
                       const int32_t* tables, int32_t max_blocks, const int32_t* lens,
-                      int32_t num_seqs, float scale, int32_t partition_tokens, void* out,
-                      void* workspace, uint64_t workspace_bytes, void* stream, int mode) {
+                      int32_t num_seqs, const int32_t* order, float scale,
+                      int32_t partition_tokens, void* out, void* workspace,
+                      uint64_t workspace_bytes, void* stream, int mode) {
   // mode 0: full decode, 1: partials only
   int rc = check_decode_args(p, layer, q, tables, lens, num_seqs, scale);
   if (rc) return rc;
@@ -460,7 +463,7 @@ static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_he
     return fail(PA_ERR_INVALID, "workspace of %llu bytes needed", static_cast<unsigned long long>(pl.ws_bytes));
   if (num_seqs == 0) return PA_OK;
   const pa::DecodeLaunch d = make_launch(layer, q, num_q_heads, tables, max_blocks, lens, num_seqs,
-                                         scale, pl, out, workspace);
+                                         order, scale, pl, out, workspace);
   auto s = static_cast<hipStream_t>(stream);
   const bool rec = p->profiling && p->launches++ % p->every == 0 && p->n_records < p->max_records;
   hipEvent_t* ev = rec ? &p->ev[4 * static_cast<size_t>(p->n_records)] : nullptr;
@@ -480,19 +483,28 @@ static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_he
 
 int pa_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
-              int32_t num_seqs, float scale, int32_t partition_tokens, void* out, void* workspace,
-              uint64_t workspace_bytes, void* stream) {
+              int32_t num_seqs, const int32_t* seq_order, float scale, int32_t partition_tokens,
+              void* out, void* workspace, uint64_t workspace_bytes, void* stream) {
   return run_decode(p, layer, q, num_q_heads, block_tables, max_blocks, context_lens, num_seqs,
-                    scale, partition_tokens, out, workspace, workspace_bytes, stream, 0);
+                    seq_order, scale, partition_tokens, out, workspace, workspace_bytes, stream, 0);
+}
+
+int pa_order_longest_first(const int32_t* lens, int32_t n, int32_t* order_out) {
+  if (n < 0) return fail(PA_ERR_INVALID, "n %d < 0", n);
+  if (n > 0 && (!lens || !order_out)) return fail(PA_ERR_INVALID, "NULL argument");
+  for (int32_t i = 0; i < n; ++i) order_out[i] = i;
+  std::stable_sort(order_out, order_out + n, [lens](int32_t a, int32_t b) { return lens[a] > lens[b]; });
+  return PA_OK;
 }
 
 int pa_decode_partials(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
                        const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
-                       int32_t num_seqs, float scale, int32_t partition_tokens, void* workspace,
-                       uint64_t workspace_bytes, void* stream) {
+                       int32_t num_seqs, const int32_t* seq_order, float scale,
+                       int32_t partition_tokens, void* workspace, uint64_t workspace_bytes,
+                       void* stream) {
   if (partition_tokens <= 0) return fail(PA_ERR_INVALID, "pa_decode_partials needs partition_tokens > 0");
   return run_decode(p, layer, q, num_q_heads, block_tables, max_blocks, context_lens, num_seqs,
-                    scale, partition_tokens, nullptr, workspace, workspace_bytes, stream, 1);
+                    seq_order, scale, partition_tokens, nullptr, workspace, workspace_bytes, stream, 1);
 }
 
 int pa_lse_reduce(pa_pool* p, const void* workspace, uint64_t workspace_bytes,
@@ -508,7 +520,7 @@ int pa_lse_reduce(pa_pool* p, const void* workspace, uint64_t workspace_bytes,
     return fail(PA_ERR_INVALID, "workspace of %llu bytes, out and context_lens needed",
                 static_cast<unsigned long long>(pl.ws_bytes));
   const pa::DecodeLaunch d = make_launch(0, nullptr, num_q_heads, nullptr, max_blocks, context_lens,
-                                         num_seqs, 1.0f, pl, out, const_cast<void*>(workspace));
+                                         num_seqs, nullptr, 1.0f, pl, out, const_cast<void*>(workspace));
   const hipError_t e = pa::launch_lse_reduce(p->geom, d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : hip_fail(e, "lse_reduce launch");
 }

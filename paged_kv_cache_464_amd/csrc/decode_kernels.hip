@@ -76,6 +76,12 @@ constexpr int kDepth = 2;
 // one column tile the eager form schedules better (measured on MI355X).
 constexpr float kRescaleSlack = 8.0f;
 
+// 2^x with the bare v_exp_f32: results below 2^-126 flush to zero instead of
+// going through exp2f's denormal rescaling (four more VALU instructions per
+// call).  Used for probabilities and rescale factors, which are at most 2^8
+// and where a value below 2^-126 is zero after the fp16 conversion anyway.
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Four E4M3FN codes (bytes 0..3 of w) -> four fp16 in byte order, with the
 // gfx950 packed converter at scale 1: every E4M3FN value is an fp16 value, so
 // the conversion is exact (checked for all byte pairs on MI355X).
@@ -275,7 +281,7 @@ struct WaveDecoder {
 
   // Moves column tile nt's reference to m_new, rescaling what it holds.
   __device__ void rescale(int nt, float m_new) {
-    const float alpha = exp2f(m_run[nt] - m_new);
+    const float alpha = fast_exp2(m_run[nt] - m_new);
     l_part[nt] *= alpha;
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) oacc[nt][rr] *= alpha;
@@ -350,7 +356,7 @@ struct WaveDecoder {
     for (int nt = 0; nt < NT; ++nt) {
       float pe[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pe[e] = exp2f(s[nt][e] - m_run[nt]);
+      for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(s[nt][e] - m_run[nt]);
       l_part[nt] += (pe[0] + pe[1]) + (pe[2] + pe[3]);
       pop[nt] = f16x4{(_Float16)pe[0], (_Float16)pe[1], (_Float16)pe[2], (_Float16)pe[3]};
     }
@@ -546,8 +552,13 @@ __device__ inline int context_len(const PoolGeom& g, const DecodeLaunch& p, int 
 // Partials of chunk c of query head h: m = max_t s_t (base 2),
 // l = sum_t 2^(s_t - m), o = sum_t 2^(s_t - m) v_t / l (times the fp8 V scale).
 // Chunks at or past ceil(T / P) are not written.
+// At least two waves per SIMD: left to itself, the compiler gives the
+// two-tile (G > 16) variants 340 VGPR+AGPR registers and one wave per SIMD,
+// though they fit in 256 without spills; with two, MQA decode ran 10-13%
+// faster on MI355X (one-tile variants measured the same either way).
 template <int ELEM, int BS, int NT, int MODE>
-__global__ __launch_bounds__(kWaves * 64) void decode_kernel(PoolGeom g, DecodeLaunch p) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(PoolGeom g, DecodeLaunch p) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int group = p.num_q_heads / g.kv_heads;
@@ -566,7 +577,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(PoolGeom g, DecodeL
     if (unit >= num_units) return;  // whole waves only: no barrier in this mode
   }
   const int kvh = static_cast<int>(unit % g.kv_heads);
-  const int seq = static_cast<int>(unit / g.kv_heads);
+  int seq = static_cast<int>(unit / g.kv_heads);
+  if (p.order) {
+    // Units are taken in the caller's sequence order (longest first evens out
+    // the CUs' loads); the entry is wave-uniform, so this is a scalar load.
+    seq = ((const ConstI32*)p.order)[seq];
+    if (static_cast<uint32_t>(seq) >= static_cast<uint32_t>(p.num_seqs)) {
+      if (lane == 0 && (MODE == kSplit1 || w == 0)) atomicOr(g.status, kDevBadOrder);
+      return;  // whole workgroup (whole wave in kSplit1)
+    }
+  }
   const int P = p.partition_tokens;
   const int c_begin = r * p.chunks_per_wave;
   const int c_end = (c_begin + p.chunks_per_wave < p.num_partitions) ? c_begin + p.chunks_per_wave
@@ -752,9 +772,9 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(PoolGeom g, 
   (void)g;
 }
 
-// Kernels are launched with hipExtLaunchKernelGGL: its start/stop events (null
-// when not timing) are stamped by the dispatch itself, so timing a launch adds
-// no barrier packets to the stream.
+// Kernels are launched with hipExtLaunchKernel (launch_kernel): its start/stop
+// events (null when not timing) are stamped by the dispatch itself, so timing a
+// launch adds no barrier packets to the stream.
 template <int ELEM, int BS, int NT>
 hipError_t launch_decode_nt(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
                             hipEvent_t t1) {
@@ -762,22 +782,18 @@ hipError_t launch_decode_nt(const PoolGeom& g, const DecodeLaunch& d, hipStream_
   const int64_t units = static_cast<int64_t>(d.num_seqs) * g.kv_heads;
   switch (d.mode) {
     case kSingle:
-      hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, NT, kSingle>), dim3(static_cast<unsigned>(units)),
-                            block, 0, s, t0, t1, 0, g, d);
-      break;
+      return launch_kernel(decode_kernel<ELEM, BS, NT, kSingle>, dim3(static_cast<unsigned>(units)), block, s,
+                           t0, t1, g, d);
     case kSplit4:
-      hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, NT, kSplit4>),
-                            dim3(static_cast<unsigned>(units * d.waves_per_unit)), block, 0, s, t0, t1, 0, g, d);
-      break;
+      return launch_kernel(decode_kernel<ELEM, BS, NT, kSplit4>,
+                           dim3(static_cast<unsigned>(units * d.waves_per_unit)), block, s, t0, t1, g, d);
     case kSplit1:
-      hipExtLaunchKernelGGL((decode_kernel<ELEM, BS, NT, kSplit1>),
-                            dim3(static_cast<unsigned>((units * d.waves_per_unit + kWaves - 1) / kWaves)), block,
-                            0, s, t0, t1, 0, g, d);
-      break;
+      return launch_kernel(decode_kernel<ELEM, BS, NT, kSplit1>,
+                           dim3(static_cast<unsigned>((units * d.waves_per_unit + kWaves - 1) / kWaves)), block,
+                           s, t0, t1, g, d);
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int ELEM, int BS>
@@ -821,12 +837,11 @@ hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream
   if (rows <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(rows));
   switch (g.block_size) {
-    case 8: hipExtLaunchKernelGGL(lse_reduce_kernel<8>, grid, dim3(kReduceThreads), 0, s, t0, t1, 0, g, d); break;
-    case 16: hipExtLaunchKernelGGL(lse_reduce_kernel<16>, grid, dim3(kReduceThreads), 0, s, t0, t1, 0, g, d); break;
-    case 32: hipExtLaunchKernelGGL(lse_reduce_kernel<32>, grid, dim3(kReduceThreads), 0, s, t0, t1, 0, g, d); break;
+    case 8: return launch_kernel(lse_reduce_kernel<8>, grid, dim3(kReduceThreads), s, t0, t1, g, d);
+    case 16: return launch_kernel(lse_reduce_kernel<16>, grid, dim3(kReduceThreads), s, t0, t1, g, d);
+    case 32: return launch_kernel(lse_reduce_kernel<32>, grid, dim3(kReduceThreads), s, t0, t1, g, d);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace pa

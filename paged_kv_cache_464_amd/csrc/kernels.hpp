@@ -2,17 +2,37 @@
 // and enqueue on `stream`; they return the hipError_t of the launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <tuple>
+#include <utility>
 
 #include "layout.hpp"
 
 namespace pa {
 
+// Enqueues kernel(args...) on `stream` and returns the status of this launch
+// itself (hipGetLastError would also report an error some earlier, unrelated
+// call left on the thread).  t0/t1: optional events the dispatch stamps at the
+// kernel's start and end.
+template <class... P, class... A>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream,
+                                hipEvent_t t0, hipEvent_t t1, A&&... args) {
+  std::tuple<P...> vals(std::forward<A>(args)...);
+  void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1];
+  std::apply([&ptrs](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream, t0, t1, 0);
+}
+
 constexpr uint32_t kDevBadSlot = 1u;
 constexpr uint32_t kDevBadBlock = 2u;
 constexpr uint32_t kDevBadLen = 4u;
+constexpr uint32_t kDevBadOrder = 8u;
 
 hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k_new, const void* v_new,
                            const int32_t* slots, int n_tokens, hipStream_t stream);
@@ -26,6 +46,7 @@ struct DecodeLaunch {
   const void* q;
   const int32_t* tables;
   const int32_t* lens;
+  const int32_t* order;  // optional [S]: workgroup order of the sequences (null: 0..S-1)
   void* out;       // fp16 [S][Hq][D] (single pass / reduce)
   float* part_m;   // [S][Hq][C]
   float* part_l;   // [S][Hq][C]

@@ -16,7 +16,7 @@ import torch
 
 from . import _lib
 from ._lib import (PA_DTYPE_FP16, PA_DTYPE_FP8_E4M3, PA_ERR_BAD_SEQ, PA_ERR_NO_BLOCKS,  # noqa: F401
-                   PA_DEV_BAD_BLOCK, PA_DEV_BAD_LEN, PA_DEV_BAD_SLOT)
+                   PA_DEV_BAD_BLOCK, PA_DEV_BAD_LEN, PA_DEV_BAD_ORDER, PA_DEV_BAD_SLOT)
 
 
 class PAError(RuntimeError):
@@ -263,28 +263,44 @@ def _workspace(h, s, hq, mb, partition_tokens, workspace, device):
     return C.c_void_p(workspace.data_ptr()), need, workspace
 
 
+def pa_order_longest_first(lens):
+    """Indices of lens by decreasing length, ties in increasing index (host int32)."""
+    a, ap = _i32_host(lens)
+    order = np.empty(len(a), dtype=np.int32)
+    _check(_L().pa_order_longest_first(ap, len(a), order.ctypes.data_as(C.POINTER(C.c_int32))))
+    return order
+
+
+def _order_arg(seq_order, s):
+    if seq_order is None:
+        return C.c_void_p(0)
+    return _dev(seq_order, torch.int32, (s,), "seq_order")
+
+
 def pa_decode(h, layer, q, block_tables, context_lens, out=None, scale=None, partition_tokens=0,
-              workspace=None, stream=None):
+              workspace=None, stream=None, seq_order=None):
     info, s, hq, mb, qp, tp, lp = _decode_args(h, q, block_tables, context_lens)
+    orp = _order_arg(seq_order, s)
     if out is None:
         out = torch.empty_like(q)
     op = _dev(out, torch.float16, tuple(q.shape), "out")
     wp, wb, workspace = _workspace(h, s, hq, mb, partition_tokens, workspace, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(info["head_dim"])
-    _check(_L().pa_decode(C.c_void_p(h), int(layer), qp, hq, tp, mb, lp, s, float(scale),
+    _check(_L().pa_decode(C.c_void_p(h), int(layer), qp, hq, tp, mb, lp, s, orp, float(scale),
                           int(partition_tokens), op, wp, wb, _stream(stream)))
     return out
 
 
 def pa_decode_partials(h, layer, q, block_tables, context_lens, partition_tokens, scale=None,
-                       workspace=None, stream=None):
+                       workspace=None, stream=None, seq_order=None):
     """Returns (m, l, o) views into the workspace: [S][Hq][C], [S][Hq][C], [S][Hq][C][d]."""
     info, s, hq, mb, qp, tp, lp = _decode_args(h, q, block_tables, context_lens)
+    orp = _order_arg(seq_order, s)
     wp, wb, workspace = _workspace(h, s, hq, mb, partition_tokens, workspace, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(info["head_dim"])
-    _check(_L().pa_decode_partials(C.c_void_p(h), int(layer), qp, hq, tp, mb, lp, s, float(scale),
+    _check(_L().pa_decode_partials(C.c_void_p(h), int(layer), qp, hq, tp, mb, lp, s, orp, float(scale),
                                    int(partition_tokens), wp, wb, _stream(stream)))
     return workspace_views(workspace, s, hq, mb * info["block_size"], partition_tokens, info["head_dim"])
 

@@ -30,3 +30,11 @@ def test_library_exports_every_declared_symbol():
 def test_binding_declares_every_symbol():
     assert sorted(_lib.SIGNATURES) == _declared()
     _lib.load()  # argtypes/restype set without error
+
+
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"^#define (PA_[A-Z0-9_]+) \(?(-?\d+)u?\)?", text, flags=re.M))
+    assert len(defs) >= 12
+    for name, val in defs.items():
+        assert getattr(_lib, name) == int(val), name

@@ -192,3 +192,13 @@ class DifferentialMachine(RuleBasedStateMachine):
 
 TestDifferential = DifferentialMachine.TestCase
 TestDifferential.settings = settings(max_examples=80, stateful_step_count=50, deadline=None)
+
+
+def test_order_longest_first_is_a_stable_descending_sort():
+    """pa_order_longest_first against numpy's stable argsort of -lens, with ties."""
+    rng = np.random.default_rng(464)
+    for n in (0, 1, 7, 256, 1000):
+        lens = rng.integers(1, 40, n).astype(np.int32)
+        got = pa.pa_order_longest_first(lens)
+        np.testing.assert_array_equal(got, np.argsort(-lens.astype(np.int64), kind="stable"))
+    np.testing.assert_array_equal(pa.pa_order_longest_first([5, 9, 5, 9, 1]), [1, 3, 0, 2, 4])

@@ -246,3 +246,46 @@ def test_kernel_timing_samples_every_nth_launch():
         assert_close(out, ref, "fp16", f"every={every}")
     with pytest.raises(RuntimeError):
         pa.pa_profile_begin(c.pool.handle, 4, 0)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+def test_seq_order_changes_nothing_but_the_schedule(dtype):
+    """seq_order only reorders the workgroups: outputs and partials are bitwise
+    those of the natural order, in every schedule."""
+    say("seq_order", dtype)
+    lens = [700, 1, 33, 1000, 129, 64, 5, 512]
+    c = build_case(lens, 32, 8, 16, 200, 909, dtype)
+    s = len(lens)
+    ref = oracle_decode(c, range(s))
+    orders = [pa.pa_order_longest_first(lens), np.arange(s)[::-1].copy(),
+              np.random.default_rng(9).permutation(s)]
+    for mode in (-1, 0, 64, 512):
+        base = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode)
+        assert_close(base, ref, dtype, f"natural P={mode}")
+        for o in orders:
+            od = torch.from_numpy(np.ascontiguousarray(o, dtype=np.int32)).cuda()
+            out = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode, seq_order=od)
+            assert torch.equal(out, base), (mode, list(o))
+    m0, l0, o0 = [t.clone() for t in pa.pa_decode_partials(c.pool.handle, 0, c.q, c.tables, c.lens_dev, 64)]
+    od = torch.from_numpy(orders[0]).cuda()
+    m1, l1, o1 = pa.pa_decode_partials(c.pool.handle, 0, c.q, c.tables, c.lens_dev, 64, seq_order=od)
+    C = m0.shape[2]
+    for i, t in enumerate(lens):  # written chunks only
+        nc = -(-t // 64)
+        assert nc <= C
+        assert torch.equal(m0[i, :, :nc], m1[i, :, :nc]) and torch.equal(l0[i, :, :nc], l1[i, :, :nc])
+        assert torch.equal(o0[i, :, :nc], o1[i, :, :nc])
+    assert c.pool.device_status() == 0
+
+
+def test_seq_order_out_of_range_entry_is_flagged_and_skipped():
+    say("seq_order bad entry")
+    lens = [100, 300, 50]
+    c = build_case(lens, 8, 2, 16, 40, 910)
+    ref = oracle_decode(c, range(3))
+    for mode in (-1, 64):
+        out = torch.zeros_like(c.q)
+        od = torch.tensor([2, 3, 0], dtype=torch.int32, device="cuda")  # 3 is out of range; 1 missing
+        c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode, seq_order=od, out=out)
+        assert c.pool.device_status(clear=True) == pa.PA_DEV_BAD_ORDER
+        assert_close(out[[0, 2]], ref[[0, 2]], "fp16", f"P={mode}")
