@@ -7,10 +7,11 @@ Default workload ``gqa_32x4096``: 32 layers, 32 query / 8 KV heads, head_dim
 placement a seeded permutation of the pool.  One step = append one token to
 every sequence (host block manager), upload the slot mapping, lengths, a
 longest-first sequence order and block tables (one packed copy), then for
-each of the 32 layers scatter the new tokens' K/V into the cache
-(``pa_write_kv``) and run paged decode attention over the whole context
-(``pa_decode``).  The timed region holds exactly K
-steps; inputs are resident in HBM.
+each of the 32 layers scatter the new tokens' K/V into the cache and run
+paged decode attention over the whole context, in one launch per layer
+(``pa_write_kv_decode``; ``--separate-write`` uses ``pa_write_kv`` then
+``pa_decode``).  The timed region holds exactly K steps; inputs are resident
+in HBM.
 
 The other workloads (``tiny``, ``cb_prefix``, ``long_ctx``,
 ``fp8_{gqa,mqa}_bs{8,16,32}``) time one pool layer R times per step ("1 layer
@@ -126,6 +127,7 @@ class DecodeBench:
         else:
             self.copies = max(1, -(-(4 * LLC_BYTES) // layer_bytes))
         self.partition = w.partition_tokens if args.partition is None else args.partition
+        self.separate_write = bool(args.separate_write)
         # Room for the appended tokens: one more block per sequence per 16 steps.
         self.num_blocks = w.num_blocks + self.S * (-(-total_steps // self.bs) + 1)
         self.order = free_order(w.seed, self.num_blocks)
@@ -268,10 +270,16 @@ class DecodeBench:
         h, st = self.pool.handle, self.stream
         for r in range(self.R):
             layer = r % self.copies
-            pa.pa_write_kv(h, layer, self.k_new[r], self.v_new[r], self.slots_d, stream=st)
-            pa.pa_decode(h, layer, self.q[r], self.tables_d, self.lens_d, out=self.out[r],
-                         partition_tokens=self.partition, workspace=self.workspace, stream=st,
-                         seq_order=self.order_d)
+            if self.separate_write:
+                pa.pa_write_kv(h, layer, self.k_new[r], self.v_new[r], self.slots_d, stream=st)
+                pa.pa_decode(h, layer, self.q[r], self.tables_d, self.lens_d, out=self.out[r],
+                             partition_tokens=self.partition, workspace=self.workspace, stream=st,
+                             seq_order=self.order_d)
+            else:
+                pa.pa_write_kv_decode(h, layer, self.k_new[r], self.v_new[r], self.slots_d, self.q[r],
+                                      self.tables_d, self.lens_d, out=self.out[r],
+                                      partition_tokens=self.partition, workspace=self.workspace,
+                                      stream=st, seq_order=self.order_d)
         per_tok = 2 * self.hkv * 128 * self.elem
         scales = 2 * self.hkv * 4 if self.fp8 else 0
         self.kv_bytes_log.append(int(lens.astype(np.int64).sum()) * per_tok + scales)
@@ -353,6 +361,9 @@ def main(argv=None):
     ap.add_argument("--time-every", type=int, default=4,
                     help="stamp HIP events on one decode launch in this many (1 = all); "
                          "each stamped launch costs a few microseconds of queue time")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="scatter the new tokens with pa_write_kv and attend with pa_decode "
+                         "(two launches per layer) instead of the fused pa_write_kv_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)
@@ -442,7 +453,9 @@ def main(argv=None):
             "context_min_max_first_timed_step": [int(first.min()), int(first.max())],
             "context_tokens_last_timed_step": int(last.sum()),
             "num_blocks": bench.num_blocks, "partition_tokens": bench.partition,
-            "step": f"alloc 1 token/seq + {bench.R} x (write_kv + paged decode); attention only",
+            "step": (f"alloc 1 token/seq + {bench.R} x "
+                     + ("(write_kv, then paged decode)" if bench.separate_write
+                        else "fused (write_kv + paged decode) launch") + "; attention only"),
         },
         "kv_gbps": kv_gbps,
         "hbm_frac": kv_gbps / HBM_PEAK_GBPS,

@@ -168,8 +168,8 @@ int pa_free_queue(const pa_pool* pool, int32_t* out, int32_t* n_out);
 
 /* ---- device operations ---------------------------------------------------------- */
 
-/* Reshape-and-cache scatter: token t's K and V (device fp16 [n][kv_heads][head_dim])
- * go to slot slot_mapping[t] (device int32[n]) of `layer`; negative slots are
+/* Reshape-and-cache scatter: token t's K and V (device fp16 [n][kv_heads][head_dim],
+ * 4-byte aligned) go to slot slot_mapping[t] (device int32[n]) of `layer`; negative slots are
  * skipped.  fp8 pools store encode(f32(x) * f32(1/scale)) with saturation to
  * +-448 and round-to-nearest-even. */
 int pa_write_kv(pa_pool* pool, int32_t layer, const void* k_new, const void* v_new,
@@ -190,13 +190,13 @@ int pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num
                               int32_t max_blocks, int32_t partition_tokens, uint64_t* bytes_out);
 
 /* Paged decode attention for one layer.
- *   q            device fp16 [num_seqs][num_q_heads][head_dim]
+ *   q            device fp16 [num_seqs][num_q_heads][head_dim], 16-byte aligned
  *   block_tables device int32 [num_seqs][max_blocks] (entries past a sequence's
  *                last block are ignored)
  *   context_lens device int32 [num_seqs], 1 <= T_i <= max_blocks*block_size,
  *                the tokens each query attends to (the new one included)
  *   scale        softmax temperature, normally 1/sqrt(head_dim)
- *   out          device fp16 [num_seqs][num_q_heads][head_dim]
+ *   out          device fp16 [num_seqs][num_q_heads][head_dim], 8-byte aligned
  * Query head h reads KV head h / (num_q_heads / kv_heads); num_q_heads must
  * be a multiple of kv_heads with a group of at most 32.
  * partition_tokens: 0 lets the library choose (one pass per (sequence, KV
@@ -212,13 +212,31 @@ int pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num
  * keeps long sequences from starting last and idling the other CUs.  An entry
  * outside [0, num_seqs) sets PA_DEV_BAD_ORDER and is skipped; a repeated entry
  * leaves some sequence's output unwritten.
- * workspace: device memory of pa_decode_workspace_bytes() bytes (may be NULL
- * when that is 0).  Out-of-range table entries or lengths never cause an
+ * workspace: device memory of pa_decode_workspace_bytes() bytes, 16-byte
+ * aligned (may be NULL when that is 0).  Out-of-range table entries or lengths never cause an
  * out-of-bounds access; they set PA_DEV_* bits instead. */
 int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
               int32_t num_seqs, const int32_t* seq_order, float scale, int32_t partition_tokens,
               void* out, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* One decode step fused: the scatter of pa_write_kv and the attention of
+ * pa_decode in one launch.  k_new, v_new: device fp16 [num_seqs][kv_heads]
+ * [head_dim], 16-byte aligned, the new token of every sequence; slot_mapping: device int32
+ * [num_seqs].  Each sequence's new token must be its last one, T_i - 1, at
+ * the slot its block table gives that token (what pa_alloc returned for it);
+ * then the result equals pa_write_kv(layer, k_new, v_new, slot_mapping,
+ * num_seqs) followed by pa_decode(...) with the same arguments, pool contents
+ * included.  A negative slot skips the store (the pool's copy of token
+ * T_i - 1 is used); any other slot sets PA_DEV_BAD_SLOT and is skipped too.
+ * The wave that attends over token T_i - 1 takes it from k_new / v_new (as the
+ * pool will hold it: fp16, or its E4M3FN code) and then stores it. */
+int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                       const int32_t* slot_mapping, const void* q, int32_t num_q_heads,
+                       const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* context_lens, int32_t num_seqs, const int32_t* seq_order,
+                       float scale, int32_t partition_tokens, void* out, void* workspace,
+                       uint64_t workspace_bytes, void* stream);
 
 /* Host helper: order_out[0..n) = indices of lens[0..n) by decreasing length,
  * equal lengths in increasing index (a stable sort), for pa_decode's seq_order. */

@@ -12,31 +12,12 @@
 #include <cstdint>
 
 #include "kernels.hpp"
+#include "token_store.hpp"
 
 namespace pa {
 namespace {
 
 constexpr int kWaves = 4;  // waves per 256-thread workgroup
-
-// OCP E4M3FN encode of an fp32 value: NaN -> 0x7F, |y| >= 448 -> +-448
-// (saturation), otherwise round to nearest, ties to even mantissa code.
-// Integer arithmetic on the fp32 bit pattern, so the result is exact.
-__device__ inline uint32_t e4m3_encode(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return 0x7Fu;                // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;        // >= 448.0f: saturate
-  if (a < 0x3C800000u) {                            // < 2^-6: spacing 2^-9
-    const float q = rintf(__uint_as_float(a) * 512.0f);  // exact scale, then RNE
-    return sign | static_cast<uint32_t>(q);         // q in [0, 8]; 8 is 2^-6 (code 8)
-  }
-  const uint32_t e = (a >> 23) - 127u + 7u;         // biased e4m3 exponent, 1..15
-  uint32_t keep = ((a >> 20) & 0x7u) | (e << 3);    // code before rounding
-  const uint32_t rem = a & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;  // carry into exponent is correct
-  return sign | keep;
-}
 
 template <int ELEM>
 __global__ __launch_bounds__(256) void write_kv_kernel(PoolGeom g, int layer,
@@ -44,7 +25,6 @@ __global__ __launch_bounds__(256) void write_kv_kernel(PoolGeom g, int layer,
                                                        const _Float16* __restrict__ v_new,
                                                        const int32_t* __restrict__ slots,
                                                        int n_tokens) {
-  constexpr int X = 16 / ELEM;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wave >= static_cast<int64_t>(n_tokens) * g.kv_heads) return;
@@ -56,37 +36,8 @@ __global__ __launch_bounds__(256) void write_kv_kernel(PoolGeom g, int layer,
     if (lane == 0) atomicOr(g.status, kDevBadSlot);
     return;
   }
-  const int blk = slot / g.block_size, t = slot % g.block_size;
-  uint8_t* kt = g.k_layer(layer) + static_cast<uint64_t>(blk) * g.block_stride +
-                static_cast<uint64_t>(h) * g.tile_bytes;
-  uint8_t* vt = g.v_layer(layer) + static_cast<uint64_t>(blk) * g.block_stride +
-                static_cast<uint64_t>(h) * g.tile_bytes;
   const int64_t src = (static_cast<int64_t>(tok) * g.kv_heads + h) * kHeadDim;
-  const int d0 = 2 * lane;  // this lane's two dims
-  const uint32_t kk = *reinterpret_cast<const uint32_t*>(k_new + src + d0);
-  const uint32_t vv = *reinterpret_cast<const uint32_t*>(v_new + src + d0);
-  const int bs = g.block_size;
-  if constexpr (ELEM == 2) {
-    // d0, d0+1 are adjacent inside one K chunk.
-    *reinterpret_cast<uint32_t*>(kt + 2 * k_index(t, d0, bs, X, kHeadDim)) = kk;
-    *reinterpret_cast<uint16_t*>(vt + 2 * v_index(t, d0, bs, X)) = static_cast<uint16_t>(vv);
-    *reinterpret_cast<uint16_t*>(vt + 2 * v_index(t, d0 + 1, bs, X)) =
-        static_cast<uint16_t>(vv >> 16);
-  } else {
-    const int lh = layer * g.kv_heads + h;
-    const int lhs = g.layers * g.kv_heads;
-    const float k_inv = g.scales[2 * lhs + lh];
-    const float v_inv = g.scales[3 * lhs + lh];
-    auto h2f = [](uint32_t bits) {
-      return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
-    };
-    const uint32_t k0 = e4m3_encode(h2f(kk) * k_inv), k1 = e4m3_encode(h2f(kk >> 16) * k_inv);
-    const uint32_t v0 = e4m3_encode(h2f(vv) * v_inv), v1 = e4m3_encode(h2f(vv >> 16) * v_inv);
-    *reinterpret_cast<uint16_t*>(kt + k_index(t, d0, bs, X, kHeadDim)) =
-        static_cast<uint16_t>(k0 | (k1 << 8));
-    vt[v_index(t, d0, bs, X)] = static_cast<uint8_t>(v0);
-    vt[v_index(t, d0 + 1, bs, X)] = static_cast<uint8_t>(v1);
-  }
+  store_token<ELEM>(g, layer, h, slot, k_new + src, v_new + src, lane);
 }
 
 template <int ELEM>

@@ -210,6 +210,8 @@ pa::DecodeLaunch make_launch(int32_t layer, const void* q, int32_t num_q_heads,
   return d;
 }
 
+bool misaligned(const void* ptr, uintptr_t bytes) { return reinterpret_cast<uintptr_t>(ptr) % bytes != 0; }
+
 int check_decode_args(pa_pool* pool, int32_t layer, const void* q, const int32_t* tables,
                       const int32_t* lens, int32_t num_seqs, float scale) {
   int rc = check_bound(pool);
@@ -217,6 +219,7 @@ int check_decode_args(pa_pool* pool, int32_t layer, const void* q, const int32_t
   if ((rc = check_layer(pool, layer))) return rc;
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "scale is not finite");
   if (num_seqs > 0 && (!q || !tables || !lens)) return fail(PA_ERR_INVALID, "NULL device pointer");
+  if (misaligned(q, 16)) return fail(PA_ERR_INVALID, "q must be 16-byte aligned");
   return PA_OK;
 }
 
@@ -408,6 +411,7 @@ int pa_write_kv(pa_pool* p, int32_t layer, const void* k_new, const void* v_new,
   if ((rc = check_layer(p, layer))) return rc;
   if (n_tokens < 0) return fail(PA_ERR_INVALID, "n_tokens %d < 0", n_tokens);
   if (n_tokens > 0 && (!k_new || !v_new || !slot_mapping)) return fail(PA_ERR_INVALID, "NULL device pointer");
+  if (misaligned(k_new, 4) || misaligned(v_new, 4)) return fail(PA_ERR_INVALID, "k_new and v_new must be 4-byte aligned");
   const hipError_t e = pa::launch_write_kv(p->geom, layer, k_new, v_new, slot_mapping, n_tokens,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : hip_fail(e, "write_kv launch");
@@ -447,11 +451,18 @@ int pa_decode_workspace_bytes(const pa_pool* p, int32_t num_seqs, int32_t num_q_
   return PA_OK;
 }
 
+struct NewTokens {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* slots = nullptr;
+};
+
 static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
                       const int32_t* tables, int32_t max_blocks, const int32_t* lens,
                       int32_t num_seqs, const int32_t* order, float scale,
                       int32_t partition_tokens, void* out, void* workspace,
-                      uint64_t workspace_bytes, void* stream, int mode) {
+                      uint64_t workspace_bytes, void* stream, int mode,
+                      const NewTokens& nt = NewTokens{}) {
   // mode 0: full decode, 1: partials only
   int rc = check_decode_args(p, layer, q, tables, lens, num_seqs, scale);
   if (rc) return rc;
@@ -459,11 +470,16 @@ static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_he
   if ((rc = make_plan(p, num_seqs, num_q_heads, max_blocks, partition_tokens, &pl))) return rc;
   if (mode == 1 && !pl.partial) return fail(PA_ERR_INVALID, "pa_decode_partials needs partition_tokens > 0");
   if (mode == 0 && num_seqs > 0 && !out) return fail(PA_ERR_INVALID, "out is NULL");
+  if (mode == 0 && misaligned(out, 8)) return fail(PA_ERR_INVALID, "out must be 8-byte aligned");
+  if (pl.partial && misaligned(workspace, 16)) return fail(PA_ERR_INVALID, "workspace must be 16-byte aligned");
   if (pl.partial && (!workspace || workspace_bytes < pl.ws_bytes))
     return fail(PA_ERR_INVALID, "workspace of %llu bytes needed", static_cast<unsigned long long>(pl.ws_bytes));
   if (num_seqs == 0) return PA_OK;
-  const pa::DecodeLaunch d = make_launch(layer, q, num_q_heads, tables, max_blocks, lens, num_seqs,
-                                         order, scale, pl, out, workspace);
+  pa::DecodeLaunch d = make_launch(layer, q, num_q_heads, tables, max_blocks, lens, num_seqs,
+                                   order, scale, pl, out, workspace);
+  d.k_new = nt.k;
+  d.v_new = nt.v;
+  d.new_slots = nt.slots;
   auto s = static_cast<hipStream_t>(stream);
   const bool rec = p->profiling && p->launches++ % p->every == 0 && p->n_records < p->max_records;
   hipEvent_t* ev = rec ? &p->ev[4 * static_cast<size_t>(p->n_records)] : nullptr;
@@ -487,6 +503,24 @@ int pa_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
               void* out, void* workspace, uint64_t workspace_bytes, void* stream) {
   return run_decode(p, layer, q, num_q_heads, block_tables, max_blocks, context_lens, num_seqs,
                     seq_order, scale, partition_tokens, out, workspace, workspace_bytes, stream, 0);
+}
+
+int pa_write_kv_decode(pa_pool* p, int32_t layer, const void* k_new, const void* v_new,
+                       const int32_t* slot_mapping, const void* q, int32_t num_q_heads,
+                       const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                       int32_t num_seqs, const int32_t* seq_order, float scale,
+                       int32_t partition_tokens, void* out, void* workspace,
+                       uint64_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+    return fail(PA_ERR_INVALID, "k_new, v_new and slot_mapping are required");
+  if (misaligned(k_new, 16) || misaligned(v_new, 16))
+    return fail(PA_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
+  NewTokens nt;
+  nt.k = k_new;
+  nt.v = v_new;
+  nt.slots = slot_mapping;
+  return run_decode(p, layer, q, num_q_heads, block_tables, max_blocks, context_lens, num_seqs,
+                    seq_order, scale, partition_tokens, out, workspace, workspace_bytes, stream, 0, nt);
 }
 
 int pa_order_longest_first(const int32_t* lens, int32_t n, int32_t* order_out) {

@@ -43,6 +43,7 @@
 #include <cstdint>
 
 #include "kernels.hpp"
+#include "token_store.hpp"
 
 namespace pa {
 namespace {
@@ -116,8 +117,9 @@ struct StepRegs {
 
 // The per-wave engine: operands, softmax state and the load / compute of one
 // 16-token step of one (sequence, KV head).  Lane (gq, n): gq = lane / 16 is
-// its row group, n = lane % 16 its head column.
-template <int ELEM, int BS, int NT>
+// its row group, n = lane % 16 its head column.  FUSE: the launch also
+// stores each unit's new token (the fused scatter).
+template <int ELEM, int BS, int NT, bool FUSE>
 struct WaveDecoder {
   static constexpr int kElem = ELEM;
   static constexpr int kNT = NT;
@@ -131,6 +133,15 @@ struct WaveDecoder {
   const uint8_t* vbase;
   uint32_t koff[NLD], voff[NLD];
   float qk_mul, out_mul;
+  // Fused scatter: this unit's new token (K and V of token T - 1, fp16), or
+  // null; owns_new marks the wave whose step holds that token.
+  const _Float16* knew;
+  const _Float16* vnew;
+  float new_kinv, new_vinv;  // fp8: inverse scales of this (layer, KV head)
+  bool owns_new;
+  int new_tr;
+  u32x4 newk[NLD];
+  uint32_t newv[NLD][X / 4];
   f16x8 qop[NT][4];
   f32x4 oacc[NT][8];
   // Online-softmax state per head column: accumulators relative to the
@@ -160,6 +171,9 @@ struct WaveDecoder {
     kbase = g.k_layer(p.layer) + static_cast<uint64_t>(kvh) * g.tile_bytes;
     vbase = g.v_layer(p.layer) + static_cast<uint64_t>(kvh) * g.tile_bytes;
     bad = 0;
+    knew = vnew = nullptr;
+    new_kinv = new_vinv = 1.0f;
+    owns_new = false;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int c = j * 4 + gq;  // K chunk of this lane for load j
@@ -195,6 +209,74 @@ struct WaveDecoder {
         const int dim0 = (ELEM == 2) ? (u * 4 + gq) * 8 : ((u >> 1) * 4 + gq) * 16 + (u & 1) * 8;
         const f16x8 v = *reinterpret_cast<const f16x8*>(qh + dim0);
         qop[nt][u] = valid ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  }
+
+  // Fused scatter, before the stream: lanes that will hold token T - 1 in
+  // its step load their part of the new token, in the pool's form (fp16
+  // bits, or E4M3FN codes).  K: lanes n == tr hold its chunks j*4+gq (X dims
+  // each).  V: lanes gq == tr/4 hold element q*4 + tr%4 of the 16-byte chunk
+  // of dims (j*X/4 + q)*16 + n, q < X/4.  tr = (T - 1) mod 16.
+  static constexpr int kRR = X / 4;
+  __device__ void load_new() {
+    new_tr = (T - 1) & 15;
+    if (n == new_tr) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int c = j * 4 + gq;
+        if constexpr (ELEM == 2) {
+          newk[j] = *reinterpret_cast<const u32x4*>(knew + c * X);
+        } else {
+          const u32x4 h0 = *reinterpret_cast<const u32x4*>(knew + c * X);
+          const u32x4 h1 = *reinterpret_cast<const u32x4*>(knew + c * X + 8);
+          u32x4 w = {0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t hw = (e < 8 ? h0 : h1)[(e & 7) >> 1] >> (16 * (e & 1));
+            w[e >> 2] |= e4m3_encode(half_bits_to_float(hw) * new_kinv) << (8 * (e & 3));
+          }
+          newk[j] = w;
+        }
+      }
+    }
+    if (gq == (new_tr >> 2)) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+#pragma unroll
+        for (int q = 0; q < kRR; ++q) {
+          const uint32_t bits = __builtin_bit_cast(uint16_t, vnew[(j * kRR + q) * 16 + n]);
+          newv[j][q] = (ELEM == 2) ? bits : e4m3_encode(half_bits_to_float(bits) * new_vinv);
+        }
+      }
+    }
+  }
+
+  // In the step holding token T - 1 (loads landed), puts the new token in
+  // place of the pool's copy, so that the step never reads the slot that this
+  // very launch stores into.
+  __device__ void substitute_new(StepRegs<ELEM>& r) {
+    owns_new = true;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) r.k[j][d] = (n == new_tr) ? newk[j][d] : r.k[j][d];
+    }
+    const bool vlane = gq == (new_tr >> 2);
+    const int tt = new_tr & 3;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+#pragma unroll
+      for (int q = 0; q < kRR; ++q) {
+        const int e = q * 4 + tt;  // element of the 16-byte chunk
+        constexpr int kBits = 8 * ELEM;
+        constexpr uint32_t kMask = (1u << kBits) - 1u;
+        const int dw = (e * kBits) >> 5, sh = (e * kBits) & 31;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t put = (r.v[j][d] & ~(kMask << sh)) | (newv[j][q] << sh);
+          r.v[j][d] = (vlane && d == dw) ? put : r.v[j][d];
+        }
       }
     }
   }
@@ -289,6 +371,9 @@ struct WaveDecoder {
   }
 
   __device__ void compute(StepRegs<ELEM>& r, int tb) {
+    if constexpr (FUSE) {
+      if (knew && tb + 16 >= T) substitute_new(r);
+    }
     // S^T = K Q^T
     f32x4 s[NT];
 #pragma unroll
@@ -556,7 +641,7 @@ __device__ inline int context_len(const PoolGeom& g, const DecodeLaunch& p, int 
 // two-tile (G > 16) variants 340 VGPR+AGPR registers and one wave per SIMD,
 // though they fit in 256 without spills; with two, MQA decode ran 10-13%
 // faster on MI355X (one-tile variants measured the same either way).
-template <int ELEM, int BS, int NT, int MODE>
+template <int ELEM, int BS, int NT, int MODE, bool FUSE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(PoolGeom g, DecodeLaunch p) {
   const int lane = threadIdx.x & 63;
@@ -600,7 +685,7 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
     else return static_cast<int64_t>(c_begin) * P + 16ll * j;
   };
 
-  using Dec = WaveDecoder<ELEM, BS, NT>;
+  using Dec = WaveDecoder<ELEM, BS, NT, FUSE>;
   Dec dec;
   dec.bind(g, p, seq, kvh, lane);
   FirstIds first;
@@ -609,6 +694,37 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
   const bool reporter = (MODE == kSplit1) ? (lane == 0 && r == 0) : (threadIdx.x == 0 && r == 0);
   const int T = context_len<BS>(g, p, seq, reporter);
   dec.T = T;
+  int new_slot = -1;
+  if (FUSE && T > 0) {
+    // Fused scatter: the new token must be the context's last one, at the
+    // slot the table gives token T - 1; otherwise it is flagged and skipped.
+    const int slot = ((const ConstI32*)p.new_slots)[seq];
+    if (slot >= 0) {
+      const int blk = dec.trow[(T - 1) / BS];
+      if (static_cast<uint32_t>(blk) < static_cast<uint32_t>(g.num_blocks) &&
+          slot == blk * BS + (T - 1) % BS) {
+        new_slot = slot;
+        const int64_t off = (static_cast<int64_t>(seq) * g.kv_heads + kvh) * kD;
+        dec.knew = static_cast<const _Float16*>(p.k_new) + off;
+        dec.vnew = static_cast<const _Float16*>(p.v_new) + off;
+        if constexpr (ELEM == 1) {
+          const int lhs = g.layers * g.kv_heads;
+          const int lh = p.layer * g.kv_heads + kvh;
+          dec.new_kinv = g.scales[2 * lhs + lh];
+          dec.new_vinv = g.scales[3 * lhs + lh];
+        }
+        dec.load_new();
+      } else if (reporter) {
+        atomicOr(g.status, kDevBadSlot);
+      }
+    }
+  }
+  // The wave that used the new token stores it (after all of its own loads).
+  auto store_new = [&]() {
+    if constexpr (FUSE) {
+      if (dec.owns_new) store_token<ELEM>(g, p.layer, kvh, new_slot, dec.knew, dec.vnew, lane);
+    }
+  };
 
   if constexpr (MODE == kSingle) {
     if (T == 0) {
@@ -646,6 +762,7 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
     __shared__ MergeLds<NT> sm;
     stream_steps(dec, n, tok_of, real, first, [](int) {});
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
+    store_new();
     merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float, float L, float) {
       (void)nt;
       const float inv_l = dec.out_mul / L;
@@ -677,6 +794,7 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
     };
     stream_steps(dec, n, tok_of, real, first, after);
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
+    store_new();
   } else {
     const int nn = dec.n;
     auto after = [&](int j) {
@@ -703,6 +821,7 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
     };
     stream_steps(dec, n, tok_of, real, first, after);
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
+    store_new();
   }
 }
 
@@ -775,20 +894,20 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(PoolGeom g, 
 // Kernels are launched with hipExtLaunchKernel (launch_kernel): its start/stop
 // events (null when not timing) are stamped by the dispatch itself, so timing a
 // launch adds no barrier packets to the stream.
-template <int ELEM, int BS, int NT>
+template <int ELEM, int BS, int NT, bool FUSE>
 hipError_t launch_decode_nt(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
                             hipEvent_t t1) {
   const dim3 block(kWaves * 64);
   const int64_t units = static_cast<int64_t>(d.num_seqs) * g.kv_heads;
   switch (d.mode) {
     case kSingle:
-      return launch_kernel(decode_kernel<ELEM, BS, NT, kSingle>, dim3(static_cast<unsigned>(units)), block, s,
+      return launch_kernel(decode_kernel<ELEM, BS, NT, kSingle, FUSE>, dim3(static_cast<unsigned>(units)), block, s,
                            t0, t1, g, d);
     case kSplit4:
-      return launch_kernel(decode_kernel<ELEM, BS, NT, kSplit4>,
+      return launch_kernel(decode_kernel<ELEM, BS, NT, kSplit4, FUSE>,
                            dim3(static_cast<unsigned>(units * d.waves_per_unit)), block, s, t0, t1, g, d);
     case kSplit1:
-      return launch_kernel(decode_kernel<ELEM, BS, NT, kSplit1>,
+      return launch_kernel(decode_kernel<ELEM, BS, NT, kSplit1, FUSE>,
                            dim3(static_cast<unsigned>((units * d.waves_per_unit + kWaves - 1) / kWaves)), block,
                            s, t0, t1, g, d);
     default:
@@ -799,7 +918,11 @@ hipError_t launch_decode_nt(const PoolGeom& g, const DecodeLaunch& d, hipStream_
 template <int ELEM, int BS>
 hipError_t launch_decode_bs(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s,
                             hipEvent_t t0, hipEvent_t t1) {
-  return nt == 1 ? launch_decode_nt<ELEM, BS, 1>(g, d, s, t0, t1) : launch_decode_nt<ELEM, BS, 2>(g, d, s, t0, t1);
+  if (d.new_slots)
+    return nt == 1 ? launch_decode_nt<ELEM, BS, 1, true>(g, d, s, t0, t1)
+                   : launch_decode_nt<ELEM, BS, 2, true>(g, d, s, t0, t1);
+  return nt == 1 ? launch_decode_nt<ELEM, BS, 1, false>(g, d, s, t0, t1)
+                 : launch_decode_nt<ELEM, BS, 2, false>(g, d, s, t0, t1);
 }
 
 template <int ELEM>

@@ -47,6 +47,11 @@ struct DecodeLaunch {
   const int32_t* tables;
   const int32_t* lens;
   const int32_t* order;  // optional [S]: workgroup order of the sequences (null: 0..S-1)
+  // Optional fused scatter of each sequence's new token (null: none):
+  // fp16 [S][Hkv][D] K and V of token T_i - 1, stored at new_slots[i].
+  const void* k_new;
+  const void* v_new;
+  const int32_t* new_slots;
   void* out;       // fp16 [S][Hq][D] (single pass / reduce)
   float* part_m;   // [S][Hq][C]
   float* part_l;   // [S][Hq][C]

@@ -292,6 +292,27 @@ def pa_decode(h, layer, q, block_tables, context_lens, out=None, scale=None, par
     return out
 
 
+def pa_write_kv_decode(h, layer, k_new, v_new, slot_mapping, q, block_tables, context_lens,
+                       out=None, scale=None, partition_tokens=0, workspace=None, stream=None,
+                       seq_order=None):
+    """pa_write_kv of each sequence's new (last) token fused into pa_decode."""
+    info, s, hq, mb, qp, tp, lp = _decode_args(h, q, block_tables, context_lens)
+    shape = (s, info["kv_heads"], info["head_dim"])
+    kp = _dev(k_new, torch.float16, shape, "k_new")
+    vp = _dev(v_new, torch.float16, shape, "v_new")
+    sp = _dev(slot_mapping, torch.int32, (s,), "slot_mapping")
+    orp = _order_arg(seq_order, s)
+    if out is None:
+        out = torch.empty_like(q)
+    op = _dev(out, torch.float16, tuple(q.shape), "out")
+    wp, wb, workspace = _workspace(h, s, hq, mb, partition_tokens, workspace, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(info["head_dim"])
+    _check(_L().pa_write_kv_decode(C.c_void_p(h), int(layer), kp, vp, sp, qp, hq, tp, mb, lp, s, orp,
+                                   float(scale), int(partition_tokens), op, wp, wb, _stream(stream)))
+    return out
+
+
 def pa_decode_partials(h, layer, q, block_tables, context_lens, partition_tokens, scale=None,
                        workspace=None, stream=None, seq_order=None):
     """Returns (m, l, o) views into the workspace: [S][Hq][C], [S][Hq][C], [S][Hq][C][d]."""
@@ -441,6 +462,10 @@ class PagedKVPool:
 
     def decode(self, layer, q, block_tables, context_lens, **kw):
         return pa_decode(self.handle, layer, q, block_tables, context_lens, **kw)
+
+    def write_kv_decode(self, layer, k_new, v_new, slot_mapping, q, block_tables, context_lens, **kw):
+        return pa_write_kv_decode(self.handle, layer, k_new, v_new, slot_mapping, q, block_tables,
+                                  context_lens, **kw)
 
     def device_status(self, clear=False):
         return pa_device_status(self.handle, clear)

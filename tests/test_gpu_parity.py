@@ -289,3 +289,71 @@ def test_seq_order_out_of_range_entry_is_flagged_and_skipped():
         c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode, seq_order=od, out=out)
         assert c.pool.device_status(clear=True) == pa.PA_DEV_BAD_ORDER
         assert_close(out[[0, 2]], ref[[0, 2]], "fp16", f"P={mode}")
+
+
+def _poison_last(c, last_slots):
+    """Overwrite every sequence's last token with NaN (fp8: the NaN code)."""
+    nan = torch.full((len(last_slots), c.hkv, 128), float("nan"), dtype=torch.float16, device="cuda")
+    c.pool.write_kv(0, nan, nan, last_slots)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (32, 1)])
+def test_write_kv_decode_equals_write_then_decode(dtype, bs, hq, hkv):
+    """The fused step gives bit for bit the output and the pool of pa_write_kv
+    followed by pa_decode, in every schedule, with the new token's slot holding
+    NaN before the launch."""
+    seed = 3000 + bs + hq + hkv + (7 if dtype == "fp8" else 0)
+    lens = [1, 16, 17, 700, 33, 1000, 64, 5]
+    nb = int(sum(-(-t // bs) for t in lens)) + 4
+    say("write_kv_decode", dtype, bs, hq, hkv)
+    c = build_case(lens, hq, hkv, bs, nb, seed, dtype)
+    last = [int(c.offsets[i + 1] - 1) for i in range(len(lens))]
+    last_slots = torch.tensor([int(c.slots[i][-1]) for i in range(len(lens))], dtype=torch.int32, device="cuda")
+    k_new, v_new = c.k[last].contiguous(), c.v[last].contiguous()
+    k_all, v_all = c.pool.gather_kv(0, c.slot_all)
+    order = torch.from_numpy(pa.pa_order_longest_first(lens)).cuda()
+    for mode in (-1, 0, 64, 512):
+        if mode > 0 and mode % bs:
+            continue
+        ref = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode)
+        for so in (None, order):
+            _poison_last(c, last_slots)
+            out = c.pool.write_kv_decode(0, k_new, v_new, last_slots, c.q, c.tables, c.lens_dev,
+                                         partition_tokens=mode, seq_order=so)
+            assert torch.equal(out, ref), (mode, so is not None)
+            k2, v2 = c.pool.gather_kv(0, c.slot_all)
+            assert torch.equal(k2, k_all) and torch.equal(v2, v_all), mode
+    assert c.pool.device_status() == 0
+
+
+def test_write_kv_decode_slot_rules():
+    """A negative slot skips the store (the pool's copy is used); a slot that is
+    not the table's slot of token T-1 is flagged and skipped."""
+    say("write_kv_decode slots")
+    lens = [40, 100, 7]
+    c = build_case(lens, 8, 2, 16, 20, 77)
+    last = [int(c.offsets[i + 1] - 1) for i in range(3)]
+    slots = [int(c.slots[i][-1]) for i in range(3)]
+    k_new, v_new = c.k[last].contiguous(), c.v[last].contiguous()
+    ref = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=-1)
+    # negative slot: nothing stored and the pool's copy is read (poisoned here)
+    s0 = torch.tensor([slots[0]], dtype=torch.int32, device="cuda")
+    _poison_last(c, s0)
+    neg = torch.tensor([-1, slots[1], slots[2]], dtype=torch.int32, device="cuda")
+    out = c.pool.write_kv_decode(0, k_new, v_new, neg, c.q, c.tables, c.lens_dev, partition_tokens=-1)
+    assert torch.isnan(out[0].float()).any()
+    assert torch.equal(out[1:], ref[1:])
+    k0, _ = c.pool.gather_kv(0, s0)
+    assert torch.isnan(k0.float()).all()
+    assert c.pool.device_status() == 0
+    c.pool.write_kv(0, k_new[:1].contiguous(), v_new[:1].contiguous(), s0)
+    # wrong slot (the first token's): flagged; nothing stored there
+    k_before, _ = c.pool.gather_kv(0, c.slot_all)
+    bad = torch.tensor([int(c.slots[0][0]), slots[1], slots[2]], dtype=torch.int32, device="cuda")
+    out = c.pool.write_kv_decode(0, k_new, v_new, bad, c.q, c.tables, c.lens_dev, partition_tokens=-1)
+    assert c.pool.device_status(clear=True) == pa.PA_DEV_BAD_SLOT
+    k_after, _ = c.pool.gather_kv(0, c.slot_all)
+    assert torch.equal(k_before, k_after)
+    assert torch.equal(out, ref)
