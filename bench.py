@@ -47,7 +47,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: KV GB/s read + % HBM peak; tokens/s at 32×4096 GQA"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_464_amd", "csrc", f)
-                  for f in ("decode_kernels.hip", "layout.hpp", "kernels.hpp")]
+                  for f in ("decode_kernels.hip", "layout.hpp", "kernels.hpp", "token_store.hpp")]
 LLC_BYTES = 256 << 20  # MI355X Infinity Cache
 CPU_SAMPLE_TOKENS = 1 << 18  # bound on the context tokens the CPU oracle is given
 BENCH_WORKLOADS = ["gqa_32x4096", "tiny", "cb_prefix", "long_ctx",
