@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.hpp"
 #include "token_store.hpp"
@@ -122,6 +123,7 @@ struct StepRegs {
 template <int ELEM, int BS, int NT, bool FUSE>
 struct WaveDecoder {
   static constexpr int kElem = ELEM;
+  static constexpr bool kFuse = FUSE;
   static constexpr int kNT = NT;
   static constexpr int X = 16 / ELEM;  // elements per 16-byte chunk
   static constexpr int NLD = StepRegs<ELEM>::kLoads;
@@ -138,10 +140,11 @@ struct WaveDecoder {
   const _Float16* knew;
   const _Float16* vnew;
   float new_kinv, new_vinv;  // fp8: inverse scales of this (layer, KV head)
+  int new_slot, new_blk;     // slot given for the new token; table entry of token T - 1
   bool owns_new;
   int new_tr;
-  u32x4 newk[NLD];
-  uint32_t newv[NLD][X / 4];
+  u32x4 newk[NLD][3 - ELEM];  // the new token's K chunks (fp16, 16 dims per chunk for fp8)
+  _Float16 newv[NLD][X / 4];  // its V elements (fp16)
   f16x8 qop[NT][4];
   f32x4 oacc[NT][8];
   // Online-softmax state per head column: accumulators relative to the
@@ -173,6 +176,8 @@ struct WaveDecoder {
     bad = 0;
     knew = vnew = nullptr;
     new_kinv = new_vinv = 1.0f;
+    new_slot = -1;
+    new_blk = 0;
     owns_new = false;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
@@ -213,11 +218,14 @@ struct WaveDecoder {
     }
   }
 
-  // Fused scatter, before the stream: lanes that will hold token T - 1 in
-  // its step load their part of the new token, in the pool's form (fp16
-  // bits, or E4M3FN codes).  K: lanes n == tr hold its chunks j*4+gq (X dims
-  // each).  V: lanes gq == tr/4 hold element q*4 + tr%4 of the 16-byte chunk
-  // of dims (j*X/4 + q)*16 + n, q < X/4.  tr = (T - 1) mod 16.
+  // Fused scatter (owner wave only).  Before the stream, the lanes that will
+  // hold token T - 1 in its step load their part of the new token (fp16):
+  // K: lanes n == tr, chunks j*4+gq (X dims each); V: lanes gq == tr/4,
+  // dims (j*X/4 + q)*16 + n, q < X/4; tr = (T - 1) mod 16.  Nothing waits
+  // for these loads until that step, where the loaded K chunks and V
+  // elements of the token are replaced by the new token in the pool's form
+  // (fp16 bits or E4M3FN codes), so the step never reads the slot that this
+  // very launch stores into.
   static constexpr int kRR = X / 4;
   __device__ void load_new() {
     new_tr = (T - 1) & 15;
@@ -225,59 +233,110 @@ struct WaveDecoder {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int c = j * 4 + gq;
-        if constexpr (ELEM == 2) {
-          newk[j] = *reinterpret_cast<const u32x4*>(knew + c * X);
-        } else {
-          const u32x4 h0 = *reinterpret_cast<const u32x4*>(knew + c * X);
-          const u32x4 h1 = *reinterpret_cast<const u32x4*>(knew + c * X + 8);
-          u32x4 w = {0, 0, 0, 0};
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const uint32_t hw = (e < 8 ? h0 : h1)[(e & 7) >> 1] >> (16 * (e & 1));
-            w[e >> 2] |= e4m3_encode(half_bits_to_float(hw) * new_kinv) << (8 * (e & 3));
-          }
-          newk[j] = w;
-        }
+        newk[j][0] = *reinterpret_cast<const u32x4*>(knew + c * X);
+        if constexpr (ELEM == 1) newk[j][1] = *reinterpret_cast<const u32x4*>(knew + c * X + 8);
       }
     }
     if (gq == (new_tr >> 2)) {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
 #pragma unroll
-        for (int q = 0; q < kRR; ++q) {
-          const uint32_t bits = __builtin_bit_cast(uint16_t, vnew[(j * kRR + q) * 16 + n]);
-          newv[j][q] = (ELEM == 2) ? bits : e4m3_encode(half_bits_to_float(bits) * new_vinv);
-        }
+        for (int q = 0; q < kRR; ++q) newv[j][q] = vnew[(j * kRR + q) * 16 + n];
       }
     }
   }
 
-  // In the step holding token T - 1 (loads landed), puts the new token in
-  // place of the pool's copy, so that the step never reads the slot that this
-  // very launch stores into.
-  __device__ void substitute_new(StepRegs<ELEM>& r) {
-    owns_new = true;
+  // Whether the given slot is token T - 1's (a negative one is not).
+  __device__ bool new_slot_ok() const {
+    return new_slot >= 0 && static_cast<uint32_t>(new_blk) < static_cast<uint32_t>(num_blocks) &&
+           new_slot == new_blk * BS + (T - 1) % BS;
+  }
+
+  // K chunks of the new token, in the pool's form, for lanes n == tr.
+  __device__ void inject_k(StepRegs<ELEM>& r) {
+    if (n != new_tr) return;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
+      if constexpr (ELEM == 2) {
+        r.k[j] = newk[j][0];
+      } else {
+        u32x4 w = {0, 0, 0, 0};
 #pragma unroll
-      for (int d = 0; d < 4; ++d) r.k[j][d] = (n == new_tr) ? newk[j][d] : r.k[j][d];
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t hw = newk[j][e >> 3][(e & 7) >> 1] >> (16 * (e & 1));
+          w[e >> 2] |= e4m3_encode(half_bits_to_float(hw) * new_kinv) << (8 * (e & 3));
+        }
+        r.k[j] = w;
+      }
     }
-    const bool vlane = gq == (new_tr >> 2);
+  }
+
+  // V elements of the new token, in the pool's form, for lanes gq == tr/4.
+  __device__ void inject_v(StepRegs<ELEM>& r) {
+    if (gq != (new_tr >> 2)) return;
     const int tt = new_tr & 3;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
 #pragma unroll
       for (int q = 0; q < kRR; ++q) {
+        const uint32_t bits = __builtin_bit_cast(uint16_t, newv[j][q]);
+        const uint32_t val = (ELEM == 2) ? bits : e4m3_encode(half_bits_to_float(bits) * new_vinv);
         const int e = q * 4 + tt;  // element of the 16-byte chunk
         constexpr int kBits = 8 * ELEM;
         constexpr uint32_t kMask = (1u << kBits) - 1u;
         const int dw = (e * kBits) >> 5, sh = (e * kBits) & 31;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const uint32_t put = (r.v[j][d] & ~(kMask << sh)) | (newv[j][q] << sh);
-          r.v[j][d] = (vlane && d == dw) ? put : r.v[j][d];
+          if (d == dw) r.v[j][d] = (r.v[j][d] & ~(kMask << sh)) | (val << sh);
         }
       }
+    }
+  }
+
+  // The new token's tiles, as loaded and injected, go back to where they were
+  // loaded from: the lanes holding its K chunks store them (16 bytes each),
+  // the lanes holding its V elements store their whole 16-byte chunks (the
+  // three other tokens of a chunk are rewritten unchanged: the block of
+  // token T - 1 belongs to this sequence alone).
+  __device__ uint64_t new_sub_offset(bool v) const {
+    if constexpr (BS == 32) {
+      const int sub = ((T - 1) >> 4) & 1;
+      return static_cast<uint64_t>(sub) * (v ? 4 * 16 * X * ELEM : 16 * kD * ELEM);
+    }
+    return 0;
+  }
+  __device__ void store_new_k(const StepRegs<ELEM>& r) const {
+    if (n != new_tr) return;
+    uint8_t* kp = const_cast<uint8_t*>(kbase) + static_cast<uint64_t>(new_blk) * block_stride + new_sub_offset(false);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) *reinterpret_cast<u32x4*>(kp + koff[j]) = r.k[j];
+  }
+  __device__ void store_new_v(const StepRegs<ELEM>& r) const {
+    if (gq != (new_tr >> 2)) return;
+    uint8_t* vp = const_cast<uint8_t*>(vbase) + static_cast<uint64_t>(new_blk) * block_stride + new_sub_offset(true);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) *reinterpret_cast<u32x4*>(vp + voff[j]) = r.v[j];
+  }
+
+  // S^T = K Q^T for the 16 tokens of a K tile held as loaded (fp16 bits or
+  // E4M3FN codes), unscaled.
+  __device__ void raw_scores(const u32x4 (&kr)[NLD], f32x4 (&s)[NT]) const {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) s[nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f16x8 kop;
+      if constexpr (ELEM == 2) {
+        kop = __builtin_bit_cast(f16x8, kr[u]);
+      } else {
+        const u32x4 raw = kr[u >> 1];
+        const f16x4 a = e4m3x4_to_f16x4((u & 1) ? raw[2] : raw[0]);
+        const f16x4 b = e4m3x4_to_f16x4((u & 1) ? raw[3] : raw[1]);
+        kop = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[nt][u], s[nt], 0, 0, 0);
     }
   }
 
@@ -370,29 +429,23 @@ struct WaveDecoder {
     m_run[nt] = m_new;
   }
 
+  // INJ: the step may hold the fused new token (only the last scheduled
+  // steps of a stream are compiled with it, so the steady-state loop carries
+  // none of its code).
+  template <bool INJ = false>
   __device__ void compute(StepRegs<ELEM>& r, int tb) {
-    if constexpr (FUSE) {
-      if (knew && tb + 16 >= T) substitute_new(r);
+    bool new_here = false;  // step holds the fused new token, to be used
+    if constexpr (FUSE && INJ) {
+      if (knew && tb + 16 >= T && new_slot_ok()) {
+        new_here = true;
+        owns_new = true;
+        inject_k(r);
+        store_new_k(r);
+      }
     }
     // S^T = K Q^T
     f32x4 s[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) s[nt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      f16x8 kop;
-      if constexpr (ELEM == 2) {
-        kop = __builtin_bit_cast(f16x8, r.k[u]);
-      } else {
-        const u32x4 raw = r.k[u >> 1];
-        const f16x4 a = e4m3x4_to_f16x4((u & 1) ? raw[2] : raw[0]);
-        const f16x4 b = e4m3x4_to_f16x4((u & 1) ? raw[3] : raw[1]);
-        kop = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[nt][u], s[nt], 0, 0, 0);
-    }
+    raw_scores(r.k, s);
     // Scores of tokens tb + 4*gq + e for head column n; mask the tail.
     const bool tail = tb + 16 > T;
     const int valid_here = T - (tb + 4 * gq);  // tokens of this lane's 4 that exist
@@ -444,6 +497,12 @@ struct WaveDecoder {
       for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(s[nt][e] - m_run[nt]);
       l_part[nt] += (pe[0] + pe[1]) + (pe[2] + pe[3]);
       pop[nt] = f16x4{(_Float16)pe[0], (_Float16)pe[1], (_Float16)pe[2], (_Float16)pe[3]};
+    }
+    if constexpr (FUSE && INJ) {
+      if (new_here) {
+        inject_v(r);
+        store_new_v(r);
+      }
     }
     // Unused slots of the last block may hold anything (NaN included): zero them,
     // since 0 * NaN would poison the product.
@@ -513,14 +572,16 @@ __device__ inline void stream_steps(Dec& dec, int n, TokOf tok_of, Real real, Fi
     cur_lo[d] = f.lo[d + D - 1];
     cur_hi[d] = f.hi[d + D - 1];
   }
-  for (int j = 0; j < n_pad; j += D) {
+  // One block of D scheduled steps; LAST: the final block, whose steps may
+  // hold the fused new token.
+  auto block = [&](int j, auto last) {
 #pragma unroll
     for (int d = 0; d < D; ++d) dec.fetch_ids(tok_at(j + d + 2 * D - 1), nxt_lo[d], nxt_hi[d]);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       dec.issue(rr[(d + D - 1) % D], tok_at(j + d + D - 1), cur_lo[d], cur_hi[d]);
       if (j + d < n) {
-        if (real(j + d)) dec.compute(rr[d], tok_of(j + d));
+        if (real(j + d)) dec.template compute<decltype(last)::value>(rr[d], tok_of(j + d));
         after(j + d);
       }
     }
@@ -529,6 +590,12 @@ __device__ inline void stream_steps(Dec& dec, int n, TokOf tok_of, Real real, Fi
       cur_lo[d] = nxt_lo[d];
       cur_hi[d] = nxt_hi[d];
     }
+  };
+  if constexpr (Dec::kFuse) {
+    for (int j = 0; j < n_pad - D; j += D) block(j, std::false_type{});
+    block(n_pad - D, std::true_type{});
+  } else {
+    for (int j = 0; j < n_pad; j += D) block(j, std::false_type{});
   }
 }
 
@@ -694,35 +761,45 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
   const bool reporter = (MODE == kSplit1) ? (lane == 0 && r == 0) : (threadIdx.x == 0 && r == 0);
   const int T = context_len<BS>(g, p, seq, reporter);
   dec.T = T;
-  int new_slot = -1;
-  if (FUSE && T > 0) {
-    // Fused scatter: the new token must be the context's last one, at the
-    // slot the table gives token T - 1; otherwise it is flagged and skipped.
-    const int slot = ((const ConstI32*)p.new_slots)[seq];
-    if (slot >= 0) {
-      const int blk = dec.trow[(T - 1) / BS];
-      if (static_cast<uint32_t>(blk) < static_cast<uint32_t>(g.num_blocks) &&
-          slot == blk * BS + (T - 1) % BS) {
-        new_slot = slot;
-        const int64_t off = (static_cast<int64_t>(seq) * g.kv_heads + kvh) * kD;
-        dec.knew = static_cast<const _Float16*>(p.k_new) + off;
-        dec.vnew = static_cast<const _Float16*>(p.v_new) + off;
-        if constexpr (ELEM == 1) {
-          const int lhs = g.layers * g.kv_heads;
-          const int lh = p.layer * g.kv_heads + kvh;
-          dec.new_kinv = g.scales[2 * lhs + lh];
-          dec.new_vinv = g.scales[3 * lhs + lh];
-        }
-        dec.load_new();
-      } else if (reporter) {
-        atomicOr(g.status, kDevBadSlot);
+  // The one wave of the unit whose step holds token T - 1.
+  bool owner = false;
+  if constexpr (FUSE) {
+    if (T > 0) {
+      const int t_last = T - 1;
+      if constexpr (MODE == kSingle) {
+        owner = ((t_last >> 4) % kWaves) == w;
+      } else {
+        const int c_t = t_last / P;
+        const bool in_run = c_t >= c_begin && c_t < c_end;
+        if constexpr (MODE == kSplit4) owner = in_run && (((t_last - c_t * P) >> 4) % kWaves) == w;
+        else owner = in_run;
       }
     }
   }
-  // The wave that used the new token stores it (after all of its own loads).
+  if constexpr (FUSE) {
+    if (owner) {
+      // Fused scatter: the new token must be the context's last one, at the
+      // slot the table gives token T - 1.  The slot, the table entry and the
+      // scales are only requested here; the step holding token T - 1 checks
+      // them, long after they have arrived.
+      dec.new_slot = ((const ConstI32*)p.new_slots)[seq];
+      dec.new_blk = dec.trow[(T - 1) / BS];
+      const int64_t off = (static_cast<int64_t>(seq) * g.kv_heads + kvh) * kD;
+      dec.knew = static_cast<const _Float16*>(p.k_new) + off;
+      dec.vnew = static_cast<const _Float16*>(p.v_new) + off;
+      if constexpr (ELEM == 1) {
+        const int lhs = g.layers * g.kv_heads;
+        const int lh = p.layer * g.kv_heads + kvh;
+        dec.new_kinv = g.scales[2 * lhs + lh];
+        dec.new_vinv = g.scales[3 * lhs + lh];
+      }
+    }
+  }
+  // The owner flags a slot that is not token T - 1's (a negative slot means:
+  // no store); the store itself happened in the token's step.
   auto store_new = [&]() {
     if constexpr (FUSE) {
-      if (dec.owns_new) store_token<ELEM>(g, p.layer, kvh, new_slot, dec.knew, dec.vnew, lane);
+      if (owner && !dec.owns_new && dec.new_slot >= 0 && lane == 0) atomicOr(g.status, kDevBadSlot);
     }
   };
 
@@ -755,6 +832,9 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
 
   dec.load_q(g, p, seq, kvh, group);
   dec.reset();
+  if constexpr (FUSE) {
+    if (dec.knew) dec.load_new();
+  }
   const int gq = dec.gq;
   const int64_t row0 = static_cast<int64_t>(seq) * p.num_q_heads + kvh * group;
 
@@ -762,7 +842,6 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
     __shared__ MergeLds<NT> sm;
     stream_steps(dec, n, tok_of, real, first, [](int) {});
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
-    store_new();
     merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float, float L, float) {
       (void)nt;
       const float inv_l = dec.out_mul / L;
@@ -773,6 +852,7 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
         *reinterpret_cast<f16x4*>(po + rr * 16) = f16x4{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
       }
     });
+    store_new();  // after the merge: its barriers would wait for these stores
   } else if constexpr (MODE == kSplit4) {
     __shared__ MergeLds<NT> sm;
     auto after = [&](int j) {
