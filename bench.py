@@ -324,22 +324,28 @@ class DecodeBench:
             slots = tables[i][t // self.bs].astype(np.int64) * self.bs + t % self.bs
             st.write(0, k_all[off:off + n], v_all[off:off + n], slots)
             off += n
-        q0 = self.q[0].cpu().numpy()[[pos[s] for s in sample]]
+        rows = [pos[s] for s in sample]
+        qs = {}
         done, t_total, tok = 0, 0.0, 0
-        while t_total < budget_s and done < len(sample):
+        # Sequence i of launch r's queries, launch by launch, until the budget.
+        while t_total < budget_s and done < len(sample) * self.R:
+            i, r = done % len(sample), done // len(sample)
+            if r not in qs:
+                qs[r] = self.q[r].cpu().numpy()[rows]
             t0 = time.perf_counter()
-            attention.decode(st, 0, q0[done:done + 1], tables[done:done + 1], [lens[done]])
+            attention.decode(st, 0, qs[r][i:i + 1], tables[i:i + 1], [lens[i]])
             t_total += time.perf_counter() - t0
-            tok += lens[done]
+            tok += lens[i]
             done += 1
-        step_s = t_total * (float(self.setup_lens.sum()) / tok) * self.R
+        step_s = t_total * (float(self.setup_lens.sum()) * self.R / tok)
         per_tok = 2 * self.hkv * 128 * self.elem
         return {
             "value": self.S / step_s,
             "unit": "tokens/s",
             "cores": blas_threads(),
             "kind": "oracle",
-            "sample": (f"pool copy 0, {done} of {self.S} sequences ({tok} context tokens x "
+            "sample": (f"pool copy 0, {done} single-sequence decodes ({len(sample)} of {self.S} "
+                       f"sequences, the queries of {len(qs)} launches; {tok} context tokens x "
                        f"{self.hq} query heads, {t_total:.1f} s of fp64 numpy attention at the "
                        f"setup contexts), scaled by context tokens to all {self.S} sequences "
                        f"and x{self.R} launches per step"),
