@@ -151,6 +151,12 @@ int make_plan(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t m
     k = k < 1 ? 1 : (k > C ? C : k);
     pl.chunks_per_wave = static_cast<int>(k);
     pl.waves_per_unit = static_cast<int>((C + k - 1) / k);
+    // A remainder of at most k/4 chunks joins the unit's last run instead of
+    // forming a run of its own: that run would add a second, nearly empty
+    // round of workgroups when the runs exactly fill the device (for example
+    // 257 chunks of 512 tokens in runs of 8).
+    const int64_t rem = C % k;
+    if (C > k && rem != 0 && rem * 4 <= k) pl.waves_per_unit = static_cast<int>(C / k);
     const uint64_t rows = static_cast<uint64_t>(num_seqs) * num_q_heads * pl.num_partitions;
     pl.off_l = align_up(rows * 4, 256);
     pl.off_o = pl.off_l + align_up(rows * 4, 256);

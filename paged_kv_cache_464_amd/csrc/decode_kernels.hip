@@ -741,8 +741,10 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
   }
   const int P = p.partition_tokens;
   const int c_begin = r * p.chunks_per_wave;
-  const int c_end = (c_begin + p.chunks_per_wave < p.num_partitions) ? c_begin + p.chunks_per_wave
-                                                                      : p.num_partitions;
+  // The unit's last run also takes any remainder chunks (see the plan).
+  const int c_end = (r == p.waves_per_unit - 1 || c_begin + p.chunks_per_wave > p.num_partitions)
+                        ? p.num_partitions
+                        : c_begin + p.chunks_per_wave;
   const int qs = P >> 6;   // kSplit4: steps of each wave per chunk
   const int spc = P >> 4;  // kSplit1: steps per chunk
   // First token of scheduled step j, before any clamping to the context.

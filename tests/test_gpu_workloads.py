@@ -117,6 +117,11 @@ def test_long_context_sampled():
     ref = oracle_decode(c, sample)
     out = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=w.partition_tokens)
     assert_close(out[sample], ref, "fp16", "long_ctx P=512")
+    # The benchmark's wider table (room for appended tokens): 257 chunks, whose
+    # remainder joins each unit's last run.
+    wide, _ = c.pool.block_tables(c.seqs, 8194)
+    out_w = c.pool.decode(0, c.q, torch.from_numpy(wide).cuda(), c.lens_dev, partition_tokens=w.partition_tokens)
+    assert_close(out_w[sample], ref, "fp16", "long_ctx P=512, 257-chunk table")
     m, l, o = pa.pa_decode_partials(c.pool.handle, 0, c.q, c.tables, c.lens_dev, w.partition_tokens)
     st = oracle_for(c, [7])
     parts = attention.split_partials(st, 0, c.q.cpu().numpy()[[7]], c.tables_np[[7]], [w.context[7]],
