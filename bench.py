@@ -22,10 +22,12 @@ the bandwidth figure is HBM's and not the cache's.
 Prints one JSON line.  ``roofline`` is for the decode attention kernel: its
 algorithmic KV bytes per launch (each sequence's K and V, every KV head once,
 plus the fp8 scales) divided by its average duration, from HIP events that
-the dispatches themselves stamp on the launch stream for one decode launch in
-``--time-every`` (default 4) of the timed steps: a stamped launch costs a few
-microseconds of queue time, which would otherwise weigh on ``value``.  ``cpu_baseline`` is the fp64 CPU oracle timed on this
-host on a bounded sample of the same workload, after the timed steps.
+the dispatches themselves stamp on the launch stream for every decode launch
+of the last ``--stamp-steps`` (default 1) timed steps.  Event-stamped launches
+slow the stream down (on MI355X one stamped launch per step cost about
+0.09 ms of a 2.7 ms step, one in four 0.19 ms, all 0.32 ms), so only the
+final step carries them.  ``cpu_baseline`` is the fp64 CPU oracle timed on
+this host on a bounded sample of the same workload, after the timed steps.
 """
 from __future__ import annotations
 
@@ -364,9 +366,10 @@ def main(argv=None):
     ap.add_argument("--workload", default="gqa_32x4096", choices=BENCH_WORKLOADS)
     ap.add_argument("--partition", type=int, default=None,
                     help="partition_tokens for pa_decode (default: the workload's; 0 = library choice)")
-    ap.add_argument("--time-every", type=int, default=4,
-                    help="stamp HIP events on one decode launch in this many (1 = all); "
-                         "each stamped launch costs a few microseconds of queue time")
+    ap.add_argument("--stamp-steps", type=int, default=1,
+                    help="stamp HIP events on the decode launches of this many final timed steps")
+    ap.add_argument("--time-every", type=int, default=1,
+                    help="within those steps, stamp one decode launch in this many (1 = all)")
     ap.add_argument("--separate-write", action="store_true",
                     help="scatter the new tokens with pa_write_kv and attend with pa_decode "
                          "(two launches per layer) instead of the fused pa_write_kv_decode")
@@ -400,12 +403,14 @@ def main(argv=None):
     bench.kv_bytes_log.clear()
     bench.unique_bytes_log.clear()
     bench.lens_log.clear()
-    pa.pa_profile_begin(bench.pool.handle, args.steps * bench.R, args.time_every)
+    stamp = min(max(args.stamp_steps, 1), args.steps)
     gc.collect()
     gc.disable()  # no collector pauses inside the timed steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if i == args.steps - stamp:  # host-side switch, no synchronisation
+            pa.pa_profile_begin(bench.pool.handle, stamp * bench.R, args.time_every)
         bench.step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -423,7 +428,7 @@ def main(argv=None):
     n_launch = max(prof["decode_launches"], 1)
     # Every launch of a step reads the same bytes; steps differ by one token
     # per sequence.  Durations are averaged over the stamped launches.
-    bytes_per_launch = float(sum(bench.kv_bytes_log)) / len(bench.kv_bytes_log)
+    bytes_per_launch = float(sum(bench.kv_bytes_log[-stamp:])) / stamp  # the stamped steps
     decode_s = prof["decode_ms"] / 1e3 / n_launch
     reduce_s = prof["reduce_ms"] / 1e3 / max(prof["reduce_launches"], 1)
     achieved = bytes_per_launch / decode_s / 1e9
@@ -479,12 +484,13 @@ def main(argv=None):
                        + (" + fp8 scales)" if bench.fp8 else ")")),
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "timed_launches": prof["decode_launches"],
+            "timed_steps": f"last {stamp} of {args.steps}",
             "kernel_source": kernel_source_hash(),
         },
         "cpu_baseline": cpu,
     }
     if bench.unique_bytes_log:
-        ub = float(sum(bench.unique_bytes_log)) / len(bench.unique_bytes_log)
+        ub = float(sum(bench.unique_bytes_log[-stamp:])) / stamp
         result["unique_kv_gbps"] = ub / (decode_s + reduce_s) / 1e9
         result["unique_bytes_per_launch"] = ub
     print(json.dumps(result), flush=True)
