@@ -143,8 +143,10 @@ struct WaveDecoder {
   int new_slot, new_blk;     // slot given for the new token; table entry of token T - 1
   bool owns_new;
   int new_tr;
-  u32x4 newk[NLD][3 - ELEM];  // the new token's K chunks (fp16, 16 dims per chunk for fp8)
-  _Float16 newv[NLD][X / 4];  // its V elements (fp16)
+  u32x4 newk[NLD][1];         // fp16: the new token's K chunks
+  _Float16 newv[NLD][X / 4];  // fp16: its V elements
+  uint32_t new_kh, new_vh;    // fp8: its K and V dims 2*lane, 2*lane+1 (fp16)
+  uint8_t* lds_new;           // fp8: this wave's 256-byte LDS scratch for its codes
   f16x8 qop[NT][4];
   f32x4 oacc[NT][8];
   // Online-softmax state per head column: accumulators relative to the
@@ -219,9 +221,10 @@ struct WaveDecoder {
   }
 
   // Fused scatter (owner wave only).  Before the stream, the lanes that will
-  // hold token T - 1 in its step load their part of the new token (fp16):
-  // K: lanes n == tr, chunks j*4+gq (X dims each); V: lanes gq == tr/4,
-  // dims (j*X/4 + q)*16 + n, q < X/4; tr = (T - 1) mod 16.  Nothing waits
+  // hold token T - 1 in its step load their part of the new token: K: lanes
+  // n == tr, chunks j*4+gq (X dims each); V: lanes gq == tr/4, dims
+  // (j*X/4 + q)*16 + n, q < X/4; tr = (T - 1) mod 16 (fp8 pools: every lane
+  // loads two dims, and the wave encodes them together).  Nothing waits
   // for these loads until that step, where the loaded K chunks and V
   // elements of the token are replaced by the new token in the pool's form
   // (fp16 bits or E4M3FN codes), so the step never reads the slot that this
@@ -229,12 +232,17 @@ struct WaveDecoder {
   static constexpr int kRR = X / 4;
   __device__ void load_new() {
     new_tr = (T - 1) & 15;
+    if constexpr (ELEM == 1) {
+      // fp8: two dims per lane, encoded by all lanes together in the token's step.
+      new_kh = *reinterpret_cast<const uint32_t*>(knew + 2 * lane_id());
+      new_vh = *reinterpret_cast<const uint32_t*>(vnew + 2 * lane_id());
+      return;
+    }
     if (n == new_tr) {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int c = j * 4 + gq;
         newk[j][0] = *reinterpret_cast<const u32x4*>(knew + c * X);
-        if constexpr (ELEM == 1) newk[j][1] = *reinterpret_cast<const u32x4*>(knew + c * X + 8);
       }
     }
     if (gq == (new_tr >> 2)) {
@@ -252,21 +260,32 @@ struct WaveDecoder {
            new_slot == new_blk * BS + (T - 1) % BS;
   }
 
+  __device__ int lane_id() const { return gq * 16 + n; }
+
+  // fp8: the wave encodes the new token (two dims of K and of V per lane,
+  // lane-parallel) into its LDS scratch: K codes at bytes 0..127, V codes at
+  // 128..255, both in dim order; inject_k / inject_v read them back in the
+  // tile layout.  DS operations of one wave run in order.
+  __device__ void encode_new_to_lds() {
+    const int d0 = 2 * lane_id();
+    const uint32_t k0 = e4m3_encode(half_bits_to_float(new_kh) * new_kinv);
+    const uint32_t k1 = e4m3_encode(half_bits_to_float(new_kh >> 16) * new_kinv);
+    const uint32_t v0 = e4m3_encode(half_bits_to_float(new_vh) * new_vinv);
+    const uint32_t v1 = e4m3_encode(half_bits_to_float(new_vh >> 16) * new_vinv);
+    *reinterpret_cast<uint16_t*>(lds_new + d0) = static_cast<uint16_t>(k0 | (k1 << 8));
+    *reinterpret_cast<uint16_t*>(lds_new + kD + d0) = static_cast<uint16_t>(v0 | (v1 << 8));
+  }
+
   // K chunks of the new token, in the pool's form, for lanes n == tr.
   __device__ void inject_k(StepRegs<ELEM>& r) {
+    if constexpr (ELEM == 1) encode_new_to_lds();
     if (n != new_tr) return;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       if constexpr (ELEM == 2) {
         r.k[j] = newk[j][0];
       } else {
-        u32x4 w = {0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t hw = newk[j][e >> 3][(e & 7) >> 1] >> (16 * (e & 1));
-          w[e >> 2] |= e4m3_encode(half_bits_to_float(hw) * new_kinv) << (8 * (e & 3));
-        }
-        r.k[j] = w;
+        r.k[j] = *reinterpret_cast<const u32x4*>(lds_new + (j * 4 + gq) * X);
       }
     }
   }
@@ -279,8 +298,9 @@ struct WaveDecoder {
     for (int j = 0; j < NLD; ++j) {
 #pragma unroll
       for (int q = 0; q < kRR; ++q) {
-        const uint32_t bits = __builtin_bit_cast(uint16_t, newv[j][q]);
-        const uint32_t val = (ELEM == 2) ? bits : e4m3_encode(half_bits_to_float(bits) * new_vinv);
+        uint32_t val;
+        if constexpr (ELEM == 2) val = __builtin_bit_cast(uint16_t, newv[j][q]);
+        else val = lds_new[kD + (j * kRR + q) * 16 + n];
         const int e = q * 4 + tt;  // element of the 16-byte chunk
         constexpr int kBits = 8 * ELEM;
         constexpr uint32_t kMask = (1u << kBits) - 1u;
@@ -756,6 +776,10 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
 
   using Dec = WaveDecoder<ELEM, BS, NT, FUSE>;
   Dec dec;
+  if constexpr (FUSE && ELEM == 1) {
+    __shared__ __attribute__((aligned(16))) uint8_t new_codes[kWaves][2 * kD];
+    dec.lds_new = new_codes[w];
+  }
   dec.bind(g, p, seq, kvh, lane);
   FirstIds first;
 #pragma unroll
@@ -973,6 +997,56 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(PoolGeom g, 
   (void)g;
 }
 
+// The same merge for at most 64 chunks, one wave per row and four rows per
+// workgroup, without barriers: lane c takes chunk c's (m, l) and the weight
+// w_c = l_c * 2^(m_c - max m); the weights reach every lane by readlane while
+// each lane accumulates two of the 128 dims over all chunks.  All loads of a
+// row are issued before any is used, so a row costs about one memory round
+// trip (the 256-thread kernel above needs two, with barriers).
+constexpr int kReduceSmallChunks = 64;
+
+template <int BS>
+__global__ __launch_bounds__(kReduceThreads) void lse_reduce_small_kernel(PoolGeom g, DecodeLaunch p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // seq * Hq + head
+  if (row >= static_cast<int64_t>(p.num_seqs) * p.num_q_heads) return;
+  const int seq = static_cast<int>(row / p.num_q_heads);
+  int T = p.lens[seq];
+  const int t_cap = p.max_blocks * BS;
+  T = T < 0 ? 0 : (T > t_cap ? t_cap : T);
+  const int cv = (T + p.partition_tokens - 1) / p.partition_tokens;  // <= num_partitions <= 64
+  const int64_t base = row * p.num_partitions;
+  const float2* o = reinterpret_cast<const float2*>(p.part_o + base * kD) + lane;
+  const bool mine = lane < cv;
+  const float mc = mine ? p.part_m[base + lane] : -__builtin_inff();
+  const float lc = mine ? p.part_l[base + lane] : 0.0f;
+  float2 ov[kReduceSmallChunks / 4];
+  float a0 = 0.0f, a1 = 0.0f, den = 0.0f;
+  float M = mc;
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float wc = mine ? lc * exp2f(mc - M) : 0.0f;
+  for (int c0 = 0; c0 < cv; c0 += kReduceSmallChunks / 4) {
+#pragma unroll
+    for (int u = 0; u < kReduceSmallChunks / 4; ++u) {
+      const int c = c0 + u;
+      ov[u] = c < cv ? o[static_cast<int64_t>(c) * (kD / 2)] : float2{0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int u = 0; u < kReduceSmallChunks / 4; ++u) {
+      const int c = c0 + u;
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wc), c & 63));
+      const float wu = c < cv ? w : 0.0f;
+      den += wu;
+      a0 += wu * ov[u].x;
+      a1 += wu * ov[u].y;
+    }
+  }
+  _Float16* out = static_cast<_Float16*>(p.out) + row * kD + 2 * lane;
+  out[0] = (_Float16)(cv > 0 ? a0 / den : 0.0f);
+  out[1] = (_Float16)(cv > 0 ? a1 / den : 0.0f);
+  (void)g;
+}
+
 // Kernels are launched with hipExtLaunchKernel (launch_kernel): its start/stop
 // events (null when not timing) are stamped by the dispatch itself, so timing a
 // launch adds no barrier packets to the stream.
@@ -1040,6 +1114,15 @@ hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream
                              hipEvent_t t0, hipEvent_t t1) {
   const int64_t rows = static_cast<int64_t>(d.num_seqs) * d.num_q_heads;
   if (rows <= 0) return hipSuccess;
+  if (d.num_partitions <= kReduceSmallChunks) {
+    const dim3 grid4(static_cast<unsigned>((rows + 3) / 4));
+    switch (g.block_size) {
+      case 8: return launch_kernel(lse_reduce_small_kernel<8>, grid4, dim3(kReduceThreads), s, t0, t1, g, d);
+      case 16: return launch_kernel(lse_reduce_small_kernel<16>, grid4, dim3(kReduceThreads), s, t0, t1, g, d);
+      case 32: return launch_kernel(lse_reduce_small_kernel<32>, grid4, dim3(kReduceThreads), s, t0, t1, g, d);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const dim3 grid(static_cast<unsigned>(rows));
   switch (g.block_size) {
     case 8: return launch_kernel(lse_reduce_kernel<8>, grid, dim3(kReduceThreads), s, t0, t1, g, d);
