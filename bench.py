@@ -358,6 +358,26 @@ class DecodeBench:
         }
 
 
+def stream_read_gbps(torch, pa, gib=2, reps=5):
+    """Rate of the library's streaming-read reference kernel over a fresh
+    ``gib`` GiB buffer (beyond the 256 MB last-level cache): the practical
+    read ceiling on this machine.  Median of ``reps`` event-timed launches."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    pa.pa_stream_read(buf, sink)
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pa.pa_stream_read(buf, sink)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    del buf
+    torch.cuda.empty_cache()
+    return (gib << 30) / float(np.median(times)) / 1e9
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -420,6 +440,7 @@ def main(argv=None):
     if status:
         print(f"device status flags {status:#x}", file=sys.stderr)
         return 1
+    stream_gbps = stream_read_gbps(torch, pa)
     # The CPU oracle runs after the timed steps so that its BLAS threads cannot
     # compete with the host side of the step.
     cpu = None if args.no_cpu_baseline else bench.cpu_baseline(args.cpu_budget)
@@ -470,6 +491,8 @@ def main(argv=None):
         },
         "kv_gbps": kv_gbps,
         "hbm_frac": kv_gbps / HBM_PEAK_GBPS,
+        "stream_read_gbps": stream_gbps,
+        "frac_of_stream_read": achieved / stream_gbps,
         "decode_kernel_us": decode_s * 1e6,
         "reduce_kernel_us": reduce_s * 1e6,
         "roofline": {

@@ -181,6 +181,13 @@ int pa_write_kv(pa_pool* pool, int32_t layer, const void* k_new, const void* v_n
 int pa_gather_kv(const pa_pool* pool, int32_t layer, const int32_t* slot_mapping,
                  int32_t n_tokens, void* k_out, void* v_out, void* stream);
 
+/* Measurement reference, not part of the method: a kernel that only reads
+ * `bytes` (a multiple of 16) of device memory at `buf` (16-byte aligned) with
+ * 16-byte nontemporal loads, the best plain streaming read found on MI355X;
+ * `sink` is a device uint32 it may write.  Its rate is the practical read
+ * ceiling the decode kernel is compared with. */
+int pa_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
+
 /* Copy whole blocks src[i] -> dst[i] (host int32[n]) across all layers, K and V. */
 int pa_copy_blocks(pa_pool* pool, const int32_t* src, const int32_t* dst, int32_t n, void* stream);
 

@@ -71,6 +71,7 @@ SIGNATURES = {
     "pa_decode": (C.c_int, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _P, C.c_float, _I32, _P, _P,
                             C.c_uint64, _P]),
     "pa_order_longest_first": (C.c_int, [_PI32, _I32, _PI32]),
+    "pa_stream_read": (C.c_int, [_P, C.c_uint64, _P, _P]),
     "pa_write_kv_decode": (C.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P,
                                      C.c_float, _I32, _P, _P, C.c_uint64, _P]),
     "pa_decode_partials": (C.c_int, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _P, C.c_float, _I32,

@@ -529,6 +529,15 @@ int pa_write_kv_decode(pa_pool* p, int32_t layer, const void* k_new, const void*
                     seq_order, scale, partition_tokens, out, workspace, workspace_bytes, stream, 0, nt);
 }
 
+int pa_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return PA_OK;
+  if (!buf || !sink) return fail(PA_ERR_INVALID, "NULL device pointer");
+  if (bytes % 16 != 0 || misaligned(buf, 16))
+    return fail(PA_ERR_INVALID, "bytes must be a multiple of 16 and buf 16-byte aligned");
+  const hipError_t e = pa::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : hip_fail(e, "stream_read launch");
+}
+
 int pa_order_longest_first(const int32_t* lens, int32_t n, int32_t* order_out) {
   if (n < 0) return fail(PA_ERR_INVALID, "n %d < 0", n);
   if (n > 0 && (!lens || !order_out)) return fail(PA_ERR_INVALID, "NULL argument");

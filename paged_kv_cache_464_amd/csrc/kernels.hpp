@@ -38,6 +38,7 @@ hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k_new, cons
                            const int32_t* slots, int n_tokens, hipStream_t stream);
 hipError_t launch_gather_kv(const PoolGeom& g, int layer, const int32_t* slots, int n_tokens,
                             void* k_out, void* v_out, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_copy_blocks(const PoolGeom& g, const int32_t* src, const int32_t* dst, int n,
                               hipStream_t stream);
 

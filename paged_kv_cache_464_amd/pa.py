@@ -263,6 +263,13 @@ def _workspace(h, s, hq, mb, partition_tokens, workspace, device):
     return C.c_void_p(workspace.data_ptr()), need, workspace
 
 
+def pa_stream_read(buf, sink, stream=None):
+    """Streaming-read reference kernel over a device tensor (its whole storage)."""
+    n = buf.numel() * buf.element_size()
+    n -= n % 16
+    _check(_L().pa_stream_read(C.c_void_p(buf.data_ptr()), n, C.c_void_p(sink.data_ptr()), _stream(stream)))
+
+
 def pa_order_longest_first(lens):
     """Indices of lens by decreasing length, ties in increasing index (host int32)."""
     a, ap = _i32_host(lens)

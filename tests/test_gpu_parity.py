@@ -357,3 +357,14 @@ def test_write_kv_decode_slot_rules():
     k_after, _ = c.pool.gather_kv(0, c.slot_all)
     assert torch.equal(k_before, k_after)
     assert torch.equal(out, ref)
+
+
+def test_stream_read_reference_runs_and_checks_arguments():
+    say("stream read")
+    buf = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    pa.pa_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink[0]) == 0  # the fold of all-ones words is 0, never the sentinel
+    with pytest.raises(RuntimeError):
+        pa.pa_stream_read(buf[1:17], sink)  # misaligned start
