@@ -95,6 +95,10 @@ typedef struct pa_pool_info {
 typedef struct pa_stats {
   int64_t num_blocks, free_blocks, used_blocks, shared_blocks;
   int64_t num_seqs, cow_copies, alloc_failures;
+  /* prefix cache (pa_seq_create_cached): full prompt blocks served from and
+   * missed by the cache, entries dropped because their block was reused, and
+   * entries held now */
+  int64_t cache_hits, cache_misses, cache_evictions, cached_blocks;
 } pa_stats;
 
 typedef struct pa_profile {
@@ -130,6 +134,23 @@ int pa_pool_bind(pa_pool* pool, void* dev_base, const float* k_scales, const flo
 
 /* New empty sequence; ids are 0, 1, 2, ... in creation order, never reused. */
 int pa_seq_create(pa_pool* pool, int32_t* seq_out);
+
+/* Automatic prefix caching (iq-blog ch.4, section "Prefix Caching";
+ * youngju.dev page, section "prefix 캐시의 수명과 무효화"; openakashic note,
+ * Key Points).  New sequence holding the prompt tokens[n] (host int32 token
+ * ids): its leading full blocks are taken from the prefix cache as far as the
+ * prompt matches a cached prefix block by block (reference count + 1; a block
+ * that sat in the free queue leaves it), the rest is allocated like
+ * pa_alloc, and the prompt's newly allocated full blocks are entered in the
+ * cache.  *cached_out = tokens whose K/V the pool already holds (a multiple
+ * of block_size); slots_out (host int32[n]) receives the slots of tokens
+ * cached_out .. n-1, which the caller writes with pa_write_kv.  Freed cached
+ * blocks keep their entry at the free-queue tail and lose it when the queue
+ * hands them out again (least recently freed first).  Keys are 64-bit hashes
+ * chained over the prompt's blocks; a hit also compares the block's tokens.
+ * PA_ERR_NO_BLOCKS if the rest does not fit: nothing changes, no id is used. */
+int pa_seq_create_cached(pa_pool* pool, const int32_t* tokens, int32_t n, int32_t* seq_out,
+                         int32_t* cached_out, int32_t* slots_out);
 
 /* Append n_tokens >= 0 tokens to `seq`.  slots_out (host int32[n_tokens]):
  * slot of the j-th new token = table[t / B] * B + t % B, t = old_len + j.

@@ -28,6 +28,25 @@ Readings where the pages are silent (each also listed in the design notes):
 * Copy-on-write triggers only when the append lands in a partly filled last
   block whose count exceeds one; the appending sequence receives the copy.
 * Sequence ids are 0, 1, 2, ... in creation order and are never reused.
+
+Automatic prefix caching (iq-blog ch.4, section "Prefix Caching": identical
+prefixes are found by a hash of the prefix and their blocks shared with a
+reference count; youngju.dev page, section "prefix 캐시의 수명과 무효화": hits
+reuse blocks, old prefixes are evicted least recently used first; openakashic
+note, Key Points: a cached block taken from the free queue for a new
+allocation loses its prefix entry).  Readings:
+
+* Only full blocks of a prompt given at creation are cached; the key of a
+  block is the whole token prefix up to its end (here the tuple itself, so the
+  oracle is exact; the library hashes it).
+* Lookup walks the prompt's full blocks in order and stops at the first miss;
+  a hit takes the block (count + 1), out of the free queue if it sat there.
+* The rest of the prompt is allocated like an append; its full blocks are then
+  registered (replacing an entry with the same key).
+* Freed cached blocks keep their entry at the free-queue tail, so the least
+  recently freed is reused (and evicted) first.
+* A creation that needs more free blocks than remain (hits taken out of the
+  queue do not count as free) fails and changes nothing; no id is used.
 """
 from __future__ import annotations
 
@@ -56,6 +75,11 @@ class OracleAllocator:
         self.next_id = 0
         self.cow_log = []  # (src, dst) in the order they happened
         self.failures = 0
+        self.cache = {}  # prefix token tuple -> block
+        self.block_key = [None] * self.num_blocks  # block -> its prefix key, if cached
+        self.cache_hits = 0
+        self.cache_misses = 0
+        self.evictions = 0
 
     # -- sequence lifecycle ------------------------------------------------
     def seq_create(self) -> int:
@@ -89,19 +113,77 @@ class OracleAllocator:
         cow_pair = None
         if cow:
             old = table[-1]
-            new = self.free.popleft()
+            new = self._take_free()
             self.ref[new] = 1
             self.ref[old] -= 1
             table[-1] = new
             cow_pair = (old, new)
             self.cow_log.append(cow_pair)
         for _ in range(need):
-            b = self.free.popleft()
+            b = self._take_free()
             self.ref[b] = 1
             table.append(b)
         slots = [table[(length + j) // bs] * bs + (length + j) % bs for j in range(n)]
         self.lens[sid] = length + n
         return slots, cow_pair
+
+    def _take_free(self) -> int:
+        """Pop the free-queue head; a cached block loses its prefix entry."""
+        b = self.free.popleft()
+        key = self.block_key[b]
+        if key is not None:
+            if self.cache.get(key) == b:
+                del self.cache[key]
+            self.block_key[b] = None
+            self.evictions += 1
+        return b
+
+    def seq_create_cached(self, tokens):
+        """New sequence holding the prompt ``tokens``; returns (sid, cached, slots).
+
+        ``cached`` tokens (whole leading blocks) already have their K/V in the
+        pool; ``slots`` are the slots of the remaining tokens, to be written.
+        """
+        tokens = [int(t) for t in tokens]
+        bs = self.block_size
+        n = len(tokens)
+        full = n // bs
+        hits = []
+        for i in range(full):
+            b = self.cache.get(tuple(tokens[:(i + 1) * bs]))
+            if b is None:
+                break
+            hits.append(b)
+        h = len(hits)
+        need = -(-(n - h * bs) // bs)
+        revived = sum(1 for b in hits if self.ref[b] == 0)
+        if need > len(self.free) - revived:
+            self.failures += 1
+            raise NoBlocks(tokens[:8])
+        sid = self.seq_create()
+        table = self.tables[sid]
+        for b in hits:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+            table.append(b)
+        self.cache_hits += h
+        self.cache_misses += full - h
+        for _ in range(need):
+            b = self._take_free()
+            self.ref[b] = 1
+            table.append(b)
+        for i in range(h, full):
+            key = tuple(tokens[:(i + 1) * bs])
+            old = self.cache.get(key)
+            if old is not None:
+                self.block_key[old] = None
+            b = table[i]
+            self.cache[key] = b
+            self.block_key[b] = key
+        self.lens[sid] = n
+        slots = [table[t // bs] * bs + t % bs for t in range(h * bs, n)]
+        return sid, h * bs, slots
 
     def fork(self, parent: int) -> int:
         """New sequence sharing every block of ``parent`` (each count +1)."""
@@ -147,6 +229,10 @@ class OracleAllocator:
             "num_seqs": len(self.tables),
             "cow_copies": len(self.cow_log),
             "alloc_failures": self.failures,
+            "cache_hits": self.cache_hits,
+            "cache_misses": self.cache_misses,
+            "cache_evictions": self.evictions,
+            "cached_blocks": len(self.cache),
         }
 
     def check_invariants(self) -> None:
@@ -163,3 +249,6 @@ class OracleAllocator:
         for s, t in self.tables.items():
             assert len(t) == -(-self.lens[s] // bs), (s, len(t), self.lens[s])
         assert len(self.free) + sum(1 for r in self.ref if r > 0) == self.num_blocks
+        for key, b in self.cache.items():
+            assert self.block_key[b] == key, (key, b)
+        assert sum(1 for k in self.block_key if k is not None) == len(self.cache)

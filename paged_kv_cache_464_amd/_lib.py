@@ -36,7 +36,8 @@ class pa_pool_info(C.Structure):
 class pa_stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("num_blocks", "free_blocks", "used_blocks",
                                           "shared_blocks", "num_seqs", "cow_copies",
-                                          "alloc_failures")]
+                                          "alloc_failures", "cache_hits", "cache_misses",
+                                          "cache_evictions", "cached_blocks")]
 
 
 class pa_profile(C.Structure):
@@ -56,6 +57,7 @@ SIGNATURES = {
     "pa_pool_set_free_order": (C.c_int, [_P, _PI32, _I32]),
     "pa_pool_bind": (C.c_int, [_P, _P, C.POINTER(C.c_float), C.POINTER(C.c_float)]),
     "pa_seq_create": (C.c_int, [_P, _PI32]),
+    "pa_seq_create_cached": (C.c_int, [_P, _PI32, _I32, _PI32, _PI32, _PI32]),
     "pa_alloc": (C.c_int, [_P, _I32, _I32, _PI32, _PI32, _P]),
     "pa_fork": (C.c_int, [_P, _I32, _PI32]),
     "pa_free": (C.c_int, [_P, _I32]),

@@ -1,14 +1,21 @@
 #include "block_manager.hpp"
 
+#include <algorithm>
+
 namespace pa {
 
 BlockManager::BlockManager(int32_t num_blocks, int32_t block_size)
     : num_blocks_(num_blocks),
       block_size_(block_size),
-      ring_(static_cast<size_t>(num_blocks)),
+      next_(static_cast<size_t>(num_blocks), -1),
+      prev_(static_cast<size_t>(num_blocks), -1),
+      in_free_(static_cast<size_t>(num_blocks), 0),
+      key_(static_cast<size_t>(num_blocks), 0),
+      parent_key_(static_cast<size_t>(num_blocks), 0),
+      has_key_(static_cast<size_t>(num_blocks), 0),
+      key_tokens_(static_cast<size_t>(num_blocks) * block_size, 0),
       ref_(static_cast<size_t>(num_blocks), 0) {
-  for (int32_t b = 0; b < num_blocks; ++b) ring_[b] = b;
-  free_count_ = num_blocks;
+  for (int32_t b = 0; b < num_blocks; ++b) push_free(b);
 }
 
 BmStatus BlockManager::set_free_order(const int32_t* perm, int32_t n) {
@@ -18,22 +25,125 @@ BmStatus BlockManager::set_free_order(const int32_t* perm, int32_t n) {
     if (perm[i] < 0 || perm[i] >= num_blocks_ || seen[perm[i]]) return BmStatus::kInvalid;
     seen[perm[i]] = 1;
   }
-  for (int32_t i = 0; i < n; ++i) ring_[i] = perm[i];
-  head_ = 0;
-  free_count_ = num_blocks_;
+  head_ = tail_ = -1;
+  free_count_ = 0;
+  std::fill(in_free_.begin(), in_free_.end(), 0);
+  for (int32_t i = 0; i < n; ++i) push_free(perm[i]);
   return BmStatus::kOk;
 }
 
-int32_t BlockManager::pop_free() {
-  int32_t b = ring_[head_];
-  head_ = (head_ + 1) % num_blocks_;
+void BlockManager::unlink_free(int32_t b) {
+  const int32_t p = prev_[b], q = next_[b];
+  if (p >= 0) next_[p] = q; else head_ = q;
+  if (q >= 0) prev_[q] = p; else tail_ = p;
+  prev_[b] = next_[b] = -1;
+  in_free_[b] = 0;
   --free_count_;
+}
+
+int32_t BlockManager::pop_free() {
+  const int32_t b = head_;
+  unlink_free(b);
+  if (has_key_[b]) {  // the cached prefix block is reused: its entry goes
+    auto it = cache_.find(key_[b]);
+    if (it != cache_.end() && it->second == b) cache_.erase(it);
+    has_key_[b] = 0;
+    ++cache_evictions_;
+  }
   return b;
 }
 
 void BlockManager::push_free(int32_t b) {
-  ring_[(head_ + free_count_) % num_blocks_] = b;
+  prev_[b] = tail_;
+  next_[b] = -1;
+  if (tail_ >= 0) next_[tail_] = b; else head_ = b;
+  tail_ = b;
+  in_free_[b] = 1;
   ++free_count_;
+}
+
+// 64-bit key of a full block given its parent's key: FNV-1a over the token
+// ids, then the splitmix64 finalizer to spread the bits.
+uint64_t BlockManager::block_key(uint64_t parent, const int32_t* tokens) const {
+  uint64_t h = parent ^ 0xCBF29CE484222325ull;
+  for (int32_t i = 0; i < block_size_; ++i) {
+    h ^= static_cast<uint32_t>(tokens[i]);
+    h *= 0x100000001B3ull;
+  }
+  h ^= h >> 30;
+  h *= 0xBF58476D1CE4E5B9ull;
+  h ^= h >> 27;
+  h *= 0x94D049BB133111EBull;
+  h ^= h >> 31;
+  return h;
+}
+
+void BlockManager::register_block(int32_t b, uint64_t key, uint64_t parent, const int32_t* tokens) {
+  auto it = cache_.find(key);
+  if (it != cache_.end()) has_key_[it->second] = 0;  // replaced entry
+  cache_[key] = b;
+  key_[b] = key;
+  parent_key_[b] = parent;
+  has_key_[b] = 1;
+  std::copy(tokens, tokens + block_size_, key_tokens_.begin() + static_cast<int64_t>(b) * block_size_);
+}
+
+BmStatus BlockManager::seq_create_cached(const int32_t* tokens, int32_t n, int32_t* seq,
+                                         int32_t* cached, int32_t* slots) {
+  if (n < 0 || (n > 0 && (tokens == nullptr || slots == nullptr)) || seq == nullptr || cached == nullptr)
+    return BmStatus::kInvalid;
+  const int64_t bs = block_size_;
+  const int64_t full = n / bs;
+  // Look up the prompt's full blocks until the first miss.
+  std::vector<int32_t> hits;
+  std::vector<uint64_t> keys;
+  uint64_t parent = 0;
+  for (int64_t i = 0; i < full; ++i) {
+    const int32_t* tk = tokens + i * bs;
+    const uint64_t k = block_key(parent, tk);
+    keys.push_back(k);
+    auto it = cache_.find(k);
+    if (it == cache_.end()) break;
+    const int32_t b = it->second;
+    if (!has_key_[b] || key_[b] != k || parent_key_[b] != parent ||
+        !std::equal(tk, tk + bs, key_tokens_.begin() + static_cast<int64_t>(b) * bs))
+      break;
+    hits.push_back(b);
+    parent = k;
+  }
+  const int64_t h = static_cast<int64_t>(hits.size());
+  const int64_t need = (n - h * bs + bs - 1) / bs;
+  int64_t revived = 0;
+  for (int32_t b : hits) revived += ref_[b] == 0;
+  if (need > free_count_ - revived) {
+    ++alloc_failures_;
+    return BmStatus::kNoBlocks;
+  }
+  touched_ = true;
+  const int32_t s_id = seq_create();
+  Seq& s = seqs_[s_id];
+  for (int32_t b : hits) {
+    if (ref_[b] == 0) unlink_free(b);
+    ++ref_[b];
+    s.table.push_back(b);
+  }
+  cache_hits_ += h;
+  cache_misses_ += full - h;
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t b = pop_free();
+    ref_[b] = 1;
+    s.table.push_back(b);
+  }
+  for (int64_t i = h; i < full; ++i) {
+    if (i >= static_cast<int64_t>(keys.size())) keys.push_back(block_key(keys[i - 1], tokens + i * bs));
+    register_block(s.table[i], keys[i], i == 0 ? 0 : keys[i - 1], tokens + i * bs);
+  }
+  s.len = n;
+  for (int64_t t = h * bs; t < n; ++t)
+    slots[t - h * bs] = static_cast<int32_t>(static_cast<int64_t>(s.table[t / bs]) * bs + t % bs);
+  *seq = s_id;
+  *cached = static_cast<int32_t>(h * bs);
+  return BmStatus::kOk;
 }
 
 int32_t BlockManager::seq_create() {
@@ -135,7 +245,8 @@ int64_t BlockManager::shared_blocks() const {
 }
 
 void BlockManager::free_queue(int32_t* out) const {
-  for (int64_t i = 0; i < free_count_; ++i) out[i] = ring_[(head_ + i) % num_blocks_];
+  int64_t i = 0;
+  for (int32_t b = head_; b >= 0; b = next_[b]) out[i++] = b;
 }
 
 }  // namespace pa

@@ -18,9 +18,26 @@
 //  * copy-on-write happens only for an append of >= 1 token into a partly
 //    filled last block whose reference count exceeds one;
 //  * sequence ids are 0, 1, 2, ... in creation order and never reused.
+//
+// Automatic prefix caching (iq-blog ch.4, section "Prefix Caching": identical
+// prefixes found by a hash and shared by reference count; youngju.dev page,
+// section "prefix 캐시의 수명과 무효화": hits reuse blocks, least recently used
+// prefixes are evicted first; openakashic note, Key Points: a cached block
+// taken from the free queue for a new allocation loses its entry):
+//  * only full blocks of a prompt given at creation are cached, keyed by a
+//    64-bit hash chained over the prompt's blocks (the key of block i covers
+//    tokens 0 .. (i+1)B-1); a hit also checks the block's own tokens and its
+//    parent key;
+//  * lookup stops at the first miss; hits leave the free queue if they sat
+//    there; the rest of the prompt is allocated like an append and its full
+//    blocks are registered (replacing an entry with the same key);
+//  * freed cached blocks keep their entry at the free-queue tail, so the least
+//    recently freed is evicted first; the free queue is a doubly linked list
+//    so that a hit can take a block out of its middle.
 #pragma once
 
 #include <cstdint>
+#include <unordered_map>
 #include <vector>
 
 namespace pa {
@@ -42,6 +59,10 @@ class BlockManager {
   // Append n tokens.  slots[n] receive the new tokens' slots; *cow_src/*cow_dst the
   // copied block pair or -1.
   BmStatus alloc(int32_t seq, int32_t n, int32_t* slots, int32_t* cow_src, int32_t* cow_dst);
+  // New sequence holding the prompt tokens[n]: *cached leading tokens come from
+  // the prefix cache; slots[0 .. n - *cached) receive the rest's slots.
+  BmStatus seq_create_cached(const int32_t* tokens, int32_t n, int32_t* seq, int32_t* cached,
+                             int32_t* slots);
   BmStatus fork(int32_t parent, int32_t* child);
   BmStatus free_seq(int32_t seq);
 
@@ -54,6 +75,10 @@ class BlockManager {
   int64_t cow_copies() const { return cow_copies_; }
   int64_t alloc_failures() const { return alloc_failures_; }
   int64_t shared_blocks() const;
+  int64_t cache_hits() const { return cache_hits_; }
+  int64_t cache_misses() const { return cache_misses_; }
+  int64_t cache_evictions() const { return cache_evictions_; }
+  int64_t cached_blocks() const { return static_cast<int64_t>(cache_.size()); }
   const std::vector<int32_t>& refcounts() const { return ref_; }
   void free_queue(int32_t* out) const;  // head to tail, free_count() entries
 
@@ -66,14 +91,25 @@ class BlockManager {
   bool valid_seq(int32_t s) const {
     return s >= 0 && s < static_cast<int32_t>(seqs_.size()) && seqs_[s].alive;
   }
-  int32_t pop_free();
+  int32_t pop_free();  // head of the free queue; drops its cache entry, if any
   void push_free(int32_t b);
+  void unlink_free(int32_t b);
+  uint64_t block_key(uint64_t parent, const int32_t* tokens) const;
+  void register_block(int32_t b, uint64_t key, uint64_t parent, const int32_t* tokens);
 
   int32_t num_blocks_;
   int32_t block_size_;
-  std::vector<int32_t> ring_;  // FIFO ring of capacity num_blocks_
-  int64_t head_ = 0;
+  // Free queue: doubly linked list over block ids (-1 ends).
+  std::vector<int32_t> next_, prev_;
+  std::vector<char> in_free_;
+  int32_t head_ = -1, tail_ = -1;
   int64_t free_count_ = 0;
+  // Prefix cache.
+  std::unordered_map<uint64_t, int32_t> cache_;
+  std::vector<uint64_t> key_, parent_key_;
+  std::vector<char> has_key_;
+  std::vector<int32_t> key_tokens_;  // B tokens per cached block
+  int64_t cache_hits_ = 0, cache_misses_ = 0, cache_evictions_ = 0;
   std::vector<int32_t> ref_;
   std::vector<Seq> seqs_;
   int64_t live_seqs_ = 0;

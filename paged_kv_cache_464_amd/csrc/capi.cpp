@@ -337,6 +337,18 @@ int pa_seq_create(pa_pool* p, int32_t* seq_out) {
   return PA_OK;
 }
 
+int pa_seq_create_cached(pa_pool* p, const int32_t* tokens, int32_t n, int32_t* seq_out,
+                         int32_t* cached_out, int32_t* slots_out) {
+  if (!p || !seq_out || !cached_out) return fail(PA_ERR_INVALID, "NULL argument");
+  if (n < 0) return fail(PA_ERR_INVALID, "n %d < 0", n);
+  if (n > 0 && (!tokens || !slots_out)) return fail(PA_ERR_INVALID, "NULL argument");
+  switch (p->bm.seq_create_cached(tokens, n, seq_out, cached_out, slots_out)) {
+    case pa::BmStatus::kOk: return PA_OK;
+    case pa::BmStatus::kNoBlocks: return fail(PA_ERR_NO_BLOCKS, "prompt of %d tokens does not fit", n);
+    default: return fail(PA_ERR_INVALID, "invalid argument");
+  }
+}
+
 int pa_alloc(pa_pool* p, int32_t seq, int32_t n_tokens, int32_t* slots_out, int32_t* cow_out,
              void* stream) {
   if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
@@ -394,6 +406,10 @@ int pa_pool_stats(const pa_pool* p, pa_stats* out) {
   out->num_seqs = p->bm.live_seqs();
   out->cow_copies = p->bm.cow_copies();
   out->alloc_failures = p->bm.alloc_failures();
+  out->cache_hits = p->bm.cache_hits();
+  out->cache_misses = p->bm.cache_misses();
+  out->cache_evictions = p->bm.cache_evictions();
+  out->cached_blocks = p->bm.cached_blocks();
   return PA_OK;
 }
 

@@ -137,6 +137,16 @@ def pa_seq_create(h) -> int:
     return s.value
 
 
+def pa_seq_create_cached(h, tokens):
+    """Returns (seq, cached_tokens, slots of the uncached tokens)."""
+    t, tp = _i32_host(tokens)
+    slots = np.empty(max(len(t), 1), dtype=np.int32)
+    s, c = C.c_int32(), C.c_int32()
+    _check(_L().pa_seq_create_cached(C.c_void_p(h), tp, len(t), C.byref(s), C.byref(c),
+                                     slots.ctypes.data_as(C.POINTER(C.c_int32))))
+    return s.value, c.value, slots[:len(t) - c.value].copy()
+
+
 def pa_alloc(h, seq, n_tokens, stream=0):
     """Returns (slots int32[n_tokens], (src, dst) or None)."""
     slots = np.empty(max(int(n_tokens), 0), dtype=np.int32)
@@ -427,6 +437,9 @@ class PagedKVPool:
 
     def seq_create(self):
         return pa_seq_create(self.handle)
+
+    def seq_create_cached(self, tokens):
+        return pa_seq_create_cached(self.handle, tokens)
 
     def alloc(self, seq, n, stream=None):
         return pa_alloc(self.handle, seq, n, stream if self.buffer is not None else 0)

@@ -127,8 +127,11 @@ def test_free_order_must_be_permutation():
     pa.pa_pool_destroy(h)
 
 
+_PROMPTS = [list(range(100, 130)), list(range(100, 108)) + list(range(200, 222)), list(range(300, 330))]
+
+
 class DifferentialMachine(RuleBasedStateMachine):
-    """Random create/alloc/fork/free sequences on both implementations."""
+    """Random create/alloc/fork/free and prefix-cached creations on both implementations."""
 
     def __init__(self):
         super().__init__()
@@ -176,6 +179,20 @@ class DifferentialMachine(RuleBasedStateMachine):
         pa.pa_free(self.h, s)
         self.o.free_seq(s)
 
+    @rule(k=st.integers(0, 2), plen=st.integers(0, 28), slen=st.integers(0, 12), tag=st.integers(0, 3))
+    def create_cached(self, k, plen, slen, tag):
+        tokens = _PROMPTS[k][:plen] + [1000 + 7 * tag + j for j in range(slen)]
+        try:
+            os_, oc, oslots = self.o.seq_create_cached(tokens)
+        except NoBlocks:
+            with pytest.raises(pa.NoBlocksError):
+                pa.pa_seq_create_cached(self.h, tokens)
+            return
+        s, c, slots = pa.pa_seq_create_cached(self.h, tokens)
+        assert (s, c) == (os_, oc)
+        np.testing.assert_array_equal(slots, np.asarray(oslots, dtype=np.int32))
+        self.live.append(s)
+
     @rule(s=st.integers(-3, 200))
     def bad_seq(self, s):
         if s in self.o.tables:
@@ -202,3 +219,50 @@ def test_order_longest_first_is_a_stable_descending_sort():
         got = pa.pa_order_longest_first(lens)
         np.testing.assert_array_equal(got, np.argsort(-lens.astype(np.int64), kind="stable"))
     np.testing.assert_array_equal(pa.pa_order_longest_first([5, 9, 5, 9, 1]), [1, 3, 0, 2, 4])
+
+
+def test_prefix_cache_scripted_bit_exact():
+    """Shared system prompts, frees, evictions and revivals: library == oracle."""
+    rng = np.random.default_rng(11)
+    n, bs = 48, 8
+    order = list(rng.permutation(n))
+    h = _pool(n, bs, order)
+    o = OracleAllocator(n, bs, order)
+    system = [list(rng.integers(0, 50, 40)) for _ in range(3)]
+    live = []
+    for step in range(300):
+        r = rng.random()
+        if r < 0.5 or not live:
+            k = int(rng.integers(0, 3))
+            tokens = system[k][:int(rng.integers(0, 41))] + list(rng.integers(50, 60, int(rng.integers(0, 17))))
+            try:
+                os_, oc, oslots = o.seq_create_cached(tokens)
+            except NoBlocks:
+                with pytest.raises(pa.NoBlocksError):
+                    pa.pa_seq_create_cached(h, tokens)
+                continue
+            s, c, slots = pa.pa_seq_create_cached(h, tokens)
+            assert (s, c) == (os_, oc)
+            np.testing.assert_array_equal(slots, np.asarray(oslots, dtype=np.int32))
+            live.append(s)
+        elif r < 0.7:
+            s = live[int(rng.integers(0, len(live)))]
+            m = int(rng.integers(1, 6))
+            try:
+                oslots, ocow = o.alloc(s, m)
+            except NoBlocks:
+                with pytest.raises(pa.NoBlocksError):
+                    pa.pa_alloc(h, s, m)
+                continue
+            slots, cow = pa.pa_alloc(h, s, m)
+            np.testing.assert_array_equal(slots, np.asarray(oslots, dtype=np.int32))
+            assert cow == ocow
+        else:
+            s = live.pop(int(rng.integers(0, len(live))))
+            pa.pa_free(h, s)
+            o.free_seq(s)
+        o.check_invariants()
+        _same_state(h, o)
+    st_ = pa.pa_pool_stats(h)
+    assert st_["cache_hits"] > 50 and st_["cache_evictions"] > 10  # the script exercised both
+    pa.pa_pool_destroy(h)

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from oracle import attention
-from oracle.allocator import OracleAllocator
+from oracle.allocator import NoBlocks, OracleAllocator
 from oracle.kvstore import OracleKVStore
 from paged_kv_cache_464_amd import pa
 from tests.gpu_helpers import assert_close, build_case, oracle_decode, oracle_for, say
@@ -146,3 +146,64 @@ def test_fp8_sweep_sampled(name):
         out = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode)
         assert_close(out[sample], ref, "fp8", f"{name} P={mode}")
     assert c.pool.device_status() == 0
+
+
+def test_prefix_cached_sequences_decode_like_the_oracle():
+    """Sequences created through the prefix cache (hits, revivals of freed
+    blocks, evictions) write only their uncached tokens; every live sequence
+    then decodes like the oracle, whose store holds each sequence's whole
+    prompt written at its own slots."""
+    say("prefix cache decode")
+    bs, hq, hkv, nb = 16, 32, 8, 160
+    rng = np.random.default_rng(464_010)
+    systems = [list(rng.integers(0, 5000, 300)) for _ in range(3)]
+    table = normal_fp16((4096, hkv, 128), 464_010, 1, "cuda")
+    table_v = normal_fp16((4096, hkv, 128), 464_010, 2, "cuda")
+    order = free_order(464_010, nb)
+    pool = pa.PagedKVPool(1, hkv, 128, bs, nb, free_order=order)
+    pool.pool_bytes().fill_(0xFF)
+    orc = OracleAllocator(nb, bs, order)
+    st = OracleKVStore(1, nb, hkv, bs, 128)
+
+    def rows(toks, start):
+        idx = torch.tensor([(int(t) * 131 + start + i) % 4096 for i, t in enumerate(toks)], device="cuda")
+        return table[idx].contiguous(), table_v[idx].contiguous()
+
+    live, prompts = [], {}
+    for i in range(60):
+        toks = systems[i % 3][:int(rng.integers(0, 301))] + list(rng.integers(5000, 6000, int(rng.integers(1, 80))))
+        try:
+            os_, oc, oslots = orc.seq_create_cached(toks)
+        except NoBlocks:
+            with pytest.raises(pa.NoBlocksError):
+                pool.seq_create_cached(toks)
+            continue
+        s, c, slots = pool.seq_create_cached(toks)
+        assert (s, c) == (os_, oc) and list(slots) == list(oslots)
+        if len(slots):
+            k, v = rows(toks[c:], c)
+            pool.write_kv(0, k, v, torch.from_numpy(slots).cuda())
+        live.append(s)
+        prompts[s] = toks
+        if i % 4 == 3:  # free the oldest live sequence: its cached blocks join the free queue
+            old = live.pop(0)
+            pool.free(old)
+            orc.free_seq(old)
+    stats = pool.stats()
+    assert stats["cache_hits"] > 0 and stats["cache_evictions"] > 0
+    # oracle store: every live sequence's whole prompt at its own slots
+    for s in live:
+        toks = prompts[s]
+        t = np.arange(len(toks))
+        slots = np.asarray(orc.tables[s])[t // bs] * bs + t % bs
+        k, v = rows(toks, 0)
+        st.write(0, k.cpu().numpy(), v.cpu().numpy(), slots)
+    mb = max(len(orc.tables[s]) for s in live)
+    tables, lens = pool.block_tables(live, mb)
+    ot, ol = orc.block_tables(live, mb)
+    np.testing.assert_array_equal(tables, np.asarray(ot))
+    q = normal_fp16((len(live), hq, 128), 464_010, 3, "cuda")
+    out = pool.decode(0, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda())
+    ref = attention.decode(st, 0, q.cpu().numpy(), tables, lens)
+    assert_close(out, ref, "fp16", "prefix-cached decode")
+    assert pool.device_status() == 0

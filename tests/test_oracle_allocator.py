@@ -256,3 +256,96 @@ class AllocatorMachine(RuleBasedStateMachine):
 
 TestAllocatorMachine = AllocatorMachine.TestCase
 TestAllocatorMachine.settings = settings(max_examples=60, stateful_step_count=40, deadline=None)
+
+
+# ---- automatic prefix caching -------------------------------------------------
+
+def test_prefix_cache_savings_match_the_page_example():
+    """R = 100 prompts sharing a 200-token system prompt with 50-token suffixes
+    save 79.2% of the KV (iq-blog ch.4, "Prefix Caching"): with 2-token blocks
+    both lengths are block aligned, so the cached pool holds exactly the
+    formula's share."""
+    r, p, s_bar, bs = 100, 200, 50, 2
+    a = OracleAllocator(20000, bs)
+    system = list(range(7, 7 + p))
+    cached = []
+    for i in range(r):
+        _, c, slots = a.seq_create_cached(system + [10_000 + 1000 * i + j for j in range(s_bar)])
+        cached.append(c)
+        assert len(slots) == p + s_bar - c
+    assert cached == [0] + [p] * (r - 1)
+    used = a.stats()["used_blocks"]
+    assert used * bs == p + r * s_bar
+    savings = 1 - used * bs / (r * (p + s_bar))
+    assert abs(savings - formulas.prefix_savings(r, p, s_bar)) < 1e-15
+    assert round(100 * savings, 1) == 79.2
+    st_ = a.stats()
+    assert st_["cache_hits"] == (r - 1) * (p // bs) and st_["cache_evictions"] == 0
+    a.check_invariants()
+
+
+def test_prefix_cache_hits_stop_at_first_difference_and_skip_partial_blocks():
+    a = OracleAllocator(32, 8)
+    s0, c0, sl0 = a.seq_create_cached(list(range(20)))   # 2 full blocks + 4 tokens
+    assert c0 == 0 and len(sl0) == 20 and len(a.cache) == 2
+    s1, c1, sl1 = a.seq_create_cached(list(range(20)))   # same prompt: 2 blocks hit
+    assert c1 == 16 and len(sl1) == 4
+    assert a.tables[s1][:2] == a.tables[s0][:2] and a.tables[s1][2] != a.tables[s0][2]
+    s2, c2, _ = a.seq_create_cached(list(range(8)) + [99] + list(range(9, 20)))  # differs in block 1
+    assert c2 == 8 and a.tables[s2][0] == a.tables[s0][0] and a.tables[s2][1] != a.tables[s0][1]
+    s3, c3, _ = a.seq_create_cached([5] + list(range(1, 24)))  # differs in block 0: block 1 not looked up
+    assert c3 == 0
+    assert a.ref[a.tables[s0][0]] == 3 and a.ref[a.tables[s0][1]] == 2
+    a.check_invariants()
+
+
+def test_prefix_cache_lru_eviction_and_revival_through_the_free_queue():
+    """Freed cached blocks wait at the free-queue tail with their entries; a hit
+    revives one from the middle of the queue; allocation takes the head and
+    evicts the least recently freed first."""
+    a = OracleAllocator(6, 8, free_order=[0, 1, 2, 3, 4, 5])
+    s_a, _, _ = a.seq_create_cached([1] * 8)           # block 0, cached
+    s_b, _, _ = a.seq_create_cached([2] * 8)           # block 1, cached
+    s_c, _, _ = a.seq_create_cached([3] * 8)           # block 2, cached
+    a.free_seq(s_a)
+    a.free_seq(s_b)
+    a.free_seq(s_c)
+    assert list(a.free) == [3, 4, 5, 0, 1, 2] and len(a.cache) == 3
+    s_b2, c, _ = a.seq_create_cached([2] * 8)          # revival of block 1 from the middle
+    assert c == 8 and a.tables[s_b2] == [1] and list(a.free) == [3, 4, 5, 0, 2]
+    x = a.seq_create()
+    a.alloc(x, 32)                                      # takes 3, 4, 5, 0: evicts [1]*8's entry
+    assert a.tables[x] == [3, 4, 5, 0] and a.evictions == 1 and list(a.free) == [2]
+    _, c_a, _ = a.seq_create_cached([1] * 8)           # evicted: miss, takes block 2 (evicts [3]*8)
+    assert c_a == 0 and a.evictions == 2 and len(a.cache) == 2
+    with pytest.raises(NoBlocks):                        # nothing free: atomic failure, no id used
+        a.seq_create_cached([9] * 8)
+    nid = a.next_id
+    assert a.stats()["alloc_failures"] == 1 and a.next_id == nid
+    a.check_invariants()
+
+
+def test_prefix_cached_sequences_read_the_right_content():
+    """Content round trip: the K/V a cached sequence reads through its table
+    is its own prompt's, whichever sequence wrote the shared blocks."""
+    rng = np.random.default_rng(5)
+    bs, d = 8, 4
+    a = OracleAllocator(64, bs)
+    store = OracleKVStore(1, 64, 1, bs, d)
+    system = list(range(40))
+    value = lambda tok: np.full((1, d), float(tok), np.float16)  # K/V of a token = its id
+    seqs = {}
+    for i in range(12):
+        toks = system[:int(rng.integers(0, 41))] + [100 + i] * int(rng.integers(1, 9))
+        s, c, slots = a.seq_create_cached(toks)
+        kv = np.concatenate([value(t) for t in toks[c:]])[:, None, :] if len(toks) > c else np.zeros((0, 1, d), np.float16)
+        store.write(0, kv, kv, slots)
+        seqs[s] = toks
+        if i % 3 == 2:
+            a.free_seq(list(seqs)[0])
+            del seqs[list(seqs)[0]]
+    for s, toks in seqs.items():
+        t = np.arange(len(toks))
+        slots = np.asarray(a.tables[s])[t // bs] * bs + t % bs
+        k, _ = store.read_slots(0, slots)
+        np.testing.assert_array_equal(k[:, 0, 0], np.asarray(toks, np.float16))
