@@ -51,10 +51,11 @@ HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_464_amd", "csrc", f)
                   for f in ("decode_kernels.hip", "layout.hpp", "kernels.hpp", "token_store.hpp")]
 LLC_BYTES = 256 << 20  # MI355X Infinity Cache
+PREFIX_ROW_TABLE = 1 << 16  # distinct K/V rows of the prefix_cache workload
 CPU_SAMPLE_TOKENS = 1 << 18  # bound on the context tokens the CPU oracle is given
 BENCH_WORKLOADS = ["gqa_32x4096", "tiny", "cb_prefix", "long_ctx",
                    "fp8_gqa_bs8", "fp8_gqa_bs16", "fp8_gqa_bs32",
-                   "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32"]
+                   "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32", "prefix_cache"]
 
 
 def kernel_source_hash() -> str:
@@ -109,7 +110,8 @@ class DecodeBench:
         import torch
 
         from paged_kv_cache_464_amd import pa
-        from workloads import amax_scales, cb_prefix_script, free_order, normal_fp16, workload
+        from workloads import (amax_scales, cb_prefix_script, free_order, normal_fp16,
+                               prefix_cache_prompts, workload)
 
         self.torch, self.pa = torch, pa
         self.name = name
@@ -137,6 +139,11 @@ class DecodeBench:
         # Setup rows: every token whose K/V is generated before the timed steps.
         if name == "cb_prefix":
             self.script, self.n_rows = cb_prefix_script(w.seed)
+        elif name == "prefix_cache":
+            e = w.extra
+            self.prompts = prefix_cache_prompts(w.seed, w.num_seqs, e["systems"], e["system_tokens"],
+                                                e["suffix"])
+            self.n_rows = PREFIX_ROW_TABLE
         else:
             self.prefill = [t - 1 for t in w.context]  # the first step makes them T_i
             self.n_rows = int(sum(self.prefill))
@@ -217,6 +224,28 @@ class DecodeBench:
 
     def _setup_sequences(self, k0, v0):
         pool = self.pool
+        if self.name == "prefix_cache":
+            # K/V of token id x at position t is row (131 x + t) mod the row
+            # table, so equal prefixes carry equal K/V, as the cache assumes.
+            rows_all, slots_all, times = [], [], []
+            for toks in self.prompts:
+                t0 = time.perf_counter()
+                s, c, slots = pool.seq_create_cached(toks)
+                times.append(time.perf_counter() - t0)
+                rows = (np.asarray(toks, dtype=np.int64) * 131 + np.arange(len(toks))) % PREFIX_ROW_TABLE
+                self.seq_rows[s] = rows
+                rows_all.append(rows[c:])
+                slots_all.append(slots)
+            self._write_rows(k0, v0, np.concatenate(rows_all), np.concatenate(slots_all))
+            self.seqs = sorted(self.seq_rows)
+            st = pool.stats()
+            self.cache_info = {
+                "host_us_per_cached_create": float(np.mean(times)) * 1e6,
+                "cache_hits_blocks": st["cache_hits"], "cache_misses_blocks": st["cache_misses"],
+                "prompt_tokens": int(sum(len(t) for t in self.prompts)),
+                "stored_prompt_tokens": int(sum(len(r) for r in rows_all)),
+            }
+            return
         if self.name != "cb_prefix":
             self.seqs, slots = [], []
             base = 0
@@ -285,7 +314,7 @@ class DecodeBench:
         per_tok = 2 * self.hkv * 128 * self.elem
         scales = 2 * self.hkv * 4 if self.fp8 else 0
         self.kv_bytes_log.append(int(lens.astype(np.int64).sum()) * per_tok + scales)
-        if self.name == "cb_prefix":
+        if self.name in ("cb_prefix", "prefix_cache"):
             self.unique_bytes_log.append(self._unique_tokens(tables, lens) * per_tok + scales)
         self.lens_log.append(lens)
 
@@ -488,6 +517,7 @@ def main(argv=None):
             "step": (f"alloc 1 token/seq + {bench.R} x "
                      + ("(write_kv, then paged decode)" if bench.separate_write
                         else "fused (write_kv + paged decode) launch") + "; attention only"),
+            **({"prefix_cache": bench.cache_info} if hasattr(bench, "cache_info") else {}),
         },
         "kv_gbps": kv_gbps,
         "hbm_frac": kv_gbps / HBM_PEAK_GBPS,

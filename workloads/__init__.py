@@ -10,6 +10,7 @@ from .configs import (  # noqa: F401
     WORKLOADS,
     Workload,
     cb_prefix_script,
+    prefix_cache_prompts,
     workload,
 )
 from .generators import (  # noqa: F401

@@ -60,6 +60,10 @@ WORKLOADS = {
     "long_ctx": Workload(4, "long_ctx", 1, 64, 8, 128, 16, "fp16", 65536, 8,
                          context=(131072,) * 8, partition_tokens=512, repeats=80),
     **_fp8_variants(),
+    # Requests built through the prefix cache: 4 system prompts of 1024 tokens,
+    # request i takes system prompt i mod 4 plus its own U{64..1024} tokens.
+    "prefix_cache": Workload(6, "prefix_cache", 1, 32, 8, 128, 16, "fp16", 16384, 256, repeats=32,
+                             extra={"systems": 4, "system_tokens": 1024, "suffix": (64, 1024)}),
 }
 
 # The page's own worked example of a block table: free blocks handed out in
@@ -70,6 +74,20 @@ PAGE_EXAMPLE_FREE_ORDER = (0, 3, 5, 1, 2, 4, 6, 7)
 
 def workload(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+def prefix_cache_prompts(seed: int, n: int, systems: int, system_tokens: int, suffix):
+    """Token ids of ``n`` prompts: system prompt ``i % systems`` (ids below
+    100000) followed by the request's own ``U{suffix}`` tokens (ids unique to
+    it, from 100000 up)."""
+    sys_ids = [list(uniform_ints(seed, 10 + k, 0, 99_999, system_tokens)) for k in range(systems)]
+    lens = uniform_ints(seed, 20, suffix[0], suffix[1], n)
+    prompts, nxt = [], 100_000
+    for i in range(n):
+        own = list(range(nxt, nxt + int(lens[i])))
+        nxt += int(lens[i])
+        prompts.append([int(t) for t in sys_ids[i % systems]] + own)
+    return prompts
 
 
 def cb_prefix_script(seed: int, n_shared: int = 100, prefix: int = 200,
