@@ -55,7 +55,7 @@ PREFIX_ROW_TABLE = 1 << 16  # distinct K/V rows of the prefix_cache workload
 CPU_SAMPLE_TOKENS = 1 << 18  # bound on the context tokens the CPU oracle is given
 BENCH_WORKLOADS = ["gqa_32x4096", "tiny", "cb_prefix", "long_ctx",
                    "fp8_gqa_bs8", "fp8_gqa_bs16", "fp8_gqa_bs32",
-                   "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32", "prefix_cache"]
+                   "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32", "prefix_cache", "beam_k5"]
 
 
 def kernel_source_hash() -> str:
@@ -110,8 +110,9 @@ class DecodeBench:
         import torch
 
         from paged_kv_cache_464_amd import pa
-        from workloads import (amax_scales, cb_prefix_script, free_order, normal_fp16,
+        from workloads import (amax_scales, beam_parents, cb_prefix_script, free_order, normal_fp16,
                                prefix_cache_prompts, workload)
+        self.beam_parents = beam_parents
 
         self.torch, self.pa = torch, pa
         self.name = name
@@ -139,6 +140,9 @@ class DecodeBench:
         # Setup rows: every token whose K/V is generated before the timed steps.
         if name == "cb_prefix":
             self.script, self.n_rows = cb_prefix_script(w.seed)
+        elif name == "beam_k5":
+            e = w.extra
+            self.n_rows = e["groups"] * e["prompt"]
         elif name == "prefix_cache":
             e = w.extra
             self.prompts = prefix_cache_prompts(w.seed, w.num_seqs, e["systems"], e["system_tokens"],
@@ -168,6 +172,12 @@ class DecodeBench:
                 break
             self.sample_seqs.append(s)
             tok += n
+        # Their setup block tables, launch rows and lengths (beam search frees
+        # sequences during the steps, so these are taken now).
+        self.sample_pos = [self.seqs.index(s) for s in self.sample_seqs]
+        self.sample_lens = [int(self.setup_lens[i]) for i in self.sample_pos]
+        self.sample_tables, _ = self.pool.block_tables(
+            self.sample_seqs, int(-(-max(self.sample_lens) // self.bs)))
         self.sample = None
         if not args.no_cpu_baseline:
             idx = torch.from_numpy(np.concatenate([self.seq_rows[s] for s in self.sample_seqs])).to(self.dev)
@@ -224,6 +234,22 @@ class DecodeBench:
 
     def _setup_sequences(self, k0, v0):
         pool = self.pool
+        if self.name == "beam_k5":
+            # Every prompt, then k - 1 forks of it: the k beams start identical.
+            e = self.w.extra
+            self.beams, slots_all = [], []
+            for g in range(e["groups"]):
+                s = pool.seq_create()
+                slots_all.append(pool.alloc(s, e["prompt"])[0])
+                self.seq_rows[s] = np.arange(g * e["prompt"], (g + 1) * e["prompt"], dtype=np.int64)
+                kids = [s] + [pool.fork(s) for _ in range(e["k"] - 1)]
+                for c in kids[1:]:
+                    self.seq_rows[c] = self.seq_rows[s].copy()
+                self.beams.append(kids)
+            self._write_rows(k0, v0, np.arange(self.n_rows), np.concatenate(slots_all))
+            self.seqs = [s for b in self.beams for s in b]
+            self.beam_step = 0
+            return
         if self.name == "prefix_cache":
             # K/V of token id x at position t is row (131 x + t) mod the row
             # table, so equal prefixes carry equal K/V, as the cache assumes.
@@ -290,8 +316,10 @@ class DecodeBench:
         self.uploaded[k].synchronize()  # the upload that last read this pinned set is done
         meta = self.pinned[k].numpy()
         slots = meta[:self.S]
+        if self.name == "beam_k5":
+            self._beam_reselect()
         for i, s in enumerate(self.seqs):
-            slots[i] = self.pool.alloc(s, 1)[0][0]
+            slots[i] = self.pool.alloc(s, 1, stream=self.stream)[0][0]
         tables, lens = self.pool.block_tables(self.seqs, self.mb_cap)
         meta[self.S:2 * self.S] = lens
         meta[2 * self.S:3 * self.S] = pa.pa_order_longest_first(lens)
@@ -314,9 +342,32 @@ class DecodeBench:
         per_tok = 2 * self.hkv * 128 * self.elem
         scales = 2 * self.hkv * 4 if self.fp8 else 0
         self.kv_bytes_log.append(int(lens.astype(np.int64).sum()) * per_tok + scales)
-        if self.name in ("cb_prefix", "prefix_cache"):
+        if self.name in ("cb_prefix", "prefix_cache", "beam_k5"):
             self.unique_bytes_log.append(self._unique_tokens(tables, lens) * per_tok + scales)
         self.lens_log.append(lens)
+
+    def _beam_reselect(self):
+        """Beam survivors of one search step: new beam j descends from old beam
+        parents[j]; a beam's first child is the beam itself, the others are
+        forks (in j order); beams without a child are freed (in index order).
+        The appends that follow copy a shared partial last block (the copies go
+        on the stream ahead of the step's launches)."""
+        pool, k = self.pool, self.w.extra["k"]
+        choice = self.beam_parents(self.w.seed, self.beam_step, len(self.beams), k)
+        self.beam_step += 1
+        for g, parents in enumerate(choice):
+            old, new, used = self.beams[g], [], set()
+            for p in parents:
+                if p in used:
+                    new.append(pool.fork(old[p]))
+                else:
+                    used.add(p)
+                    new.append(old[p])
+            for b in range(k):
+                if b not in used:
+                    pool.free(old[b])
+            self.beams[g] = new
+        self.seqs = [s for b in self.beams for s in b]
 
     def _unique_tokens(self, tables, lens):
         """Tokens held in distinct physical blocks (a shared block counted once)."""
@@ -344,18 +395,14 @@ class DecodeBench:
         st = OracleKVStore(1, self.num_blocks, self.hkv, self.bs, 128, self.w.dtype,
                            None if sc is None else sc[0][None, :],
                            None if sc is None else sc[1][None, :])
-        sample = self.sample_seqs
-        pos = {s: i for i, s in enumerate(self.seqs)}
-        lens = [int(self.setup_lens[pos[s]]) for s in sample]
-        # Tables as they were at the end of setup (the steps only appended blocks).
-        tables, _ = self.pool.block_tables(sample, self.mb_cap)
+        sample, lens, tables = self.sample_seqs, self.sample_lens, self.sample_tables
         off = 0
         for i, n in enumerate(lens):
             t = np.arange(n)
             slots = tables[i][t // self.bs].astype(np.int64) * self.bs + t % self.bs
             st.write(0, k_all[off:off + n], v_all[off:off + n], slots)
             off += n
-        rows = [pos[s] for s in sample]
+        rows = self.sample_pos
         qs = {}
         done, t_total, tok = 0, 0.0, 0
         # Sequence i of launch r's queries, launch by launch, until the budget.
@@ -518,6 +565,10 @@ def main(argv=None):
                      + ("(write_kv, then paged decode)" if bench.separate_write
                         else "fused (write_kv + paged decode) launch") + "; attention only"),
             **({"prefix_cache": bench.cache_info} if hasattr(bench, "cache_info") else {}),
+            **({"beam": {**bench.w.extra, "search_steps": bench.beam_step,
+                         "cow_copies": bench.pool.stats()["cow_copies"],
+                         "shared_blocks_end": bench.pool.stats()["shared_blocks"]}}
+               if hasattr(bench, "beams") else {}),
         },
         "kv_gbps": kv_gbps,
         "hbm_frac": kv_gbps / HBM_PEAK_GBPS,

@@ -266,3 +266,60 @@ def test_prefix_cache_scripted_bit_exact():
     st_ = pa.pa_pool_stats(h)
     assert st_["cache_hits"] > 50 and st_["cache_evictions"] > 10  # the script exercised both
     pa.pa_pool_destroy(h)
+
+
+def _beam_step(alloc_like, beams, parents):
+    """One beam-search step on an allocator-like object (library or oracle):
+    new beam j descends from old beam parents[j]; the first child of a beam is
+    the beam itself, the others are forks (in j order); old beams without a
+    child are freed (in index order); then every new beam appends one token."""
+    fork, free, alloc = alloc_like
+    new, used = [], set()
+    for p in parents:
+        if p in used:
+            new.append(fork(beams[p]))
+        else:
+            used.add(p)
+            new.append(beams[p])
+    for b in range(len(beams)):
+        if b not in used:
+            free(beams[b])
+    return new, [alloc(s, 1) for s in new]
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_beam_search_fork_trees_bit_exact(bs):
+    """Width-5 beam search over 6 prompts for 40 steps: forks, frees and
+    copy-on-write appends on the library equal the oracle's, step by step."""
+    from workloads import beam_parents
+    groups, k, prompt = 6, 5, 37
+    n = 600
+    order = free_order(464_007, n)
+    h = _pool(n, bs, order)
+    o = OracleAllocator(n, bs, order)
+    lib = (lambda s: pa.pa_fork(h, s), lambda s: pa.pa_free(h, s), lambda s, m: pa.pa_alloc(h, s, m))
+    orc = (o.fork, o.free_seq, o.alloc)
+    beams_l, beams_o = [], []
+    for g in range(groups):
+        s = pa.pa_seq_create(h)
+        assert s == o.seq_create()
+        pa.pa_alloc(h, s, prompt)
+        o.alloc(s, prompt)
+        kids = [s] + [pa.pa_fork(h, s) for _ in range(k - 1)]
+        assert kids[1:] == [o.fork(s) for _ in range(k - 1)]
+        beams_l.append(kids)
+        beams_o.append(list(kids))
+    cows = 0
+    for step in range(40):
+        for g, parents in enumerate(beam_parents(464_007, step, groups, k)):
+            beams_l[g], res_l = _beam_step(lib, beams_l[g], parents)
+            beams_o[g], res_o = _beam_step(orc, beams_o[g], parents)
+            assert beams_l[g] == beams_o[g]
+            for (sl, cl), (so, co) in zip(res_l, res_o):
+                np.testing.assert_array_equal(sl, np.asarray(so, dtype=np.int32))
+                assert cl == co
+                cows += co is not None
+        o.check_invariants()
+        _same_state(h, o)
+    assert cows > 50 and o.stats()["shared_blocks"] > 0
+    pa.pa_pool_destroy(h)

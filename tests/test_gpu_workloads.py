@@ -207,3 +207,69 @@ def test_prefix_cached_sequences_decode_like_the_oracle():
     ref = attention.decode(st, 0, q.cpu().numpy(), tables, lens)
     assert_close(out, ref, "fp16", "prefix-cached decode")
     assert pool.device_status() == 0
+
+
+def test_beam_search_fork_trees_decode_like_the_oracle():
+    """Width-5 beam search (forks, frees, copy-on-write appends whose copies
+    the library enqueues on the stream) over 4 prompts for 24 steps, each new
+    token written by the fused step; then every beam decodes like the oracle."""
+    from workloads import beam_parents
+    say("beam fork trees")
+    bs, hq, hkv, nb, groups, k, prompt = 16, 32, 8, 400, 4, 5, 300
+    order = free_order(464_017, nb)
+    pool = pa.PagedKVPool(1, hkv, 128, bs, nb, free_order=order)
+    pool.pool_bytes().fill_(0xFF)
+    orc = OracleAllocator(nb, bs, order)
+    st = OracleKVStore(1, nb, hkv, bs, 128)
+    beams = []
+    for g in range(groups):
+        s = pool.seq_create()
+        assert s == orc.seq_create()
+        slots, _ = pool.alloc(s, prompt)
+        orc.alloc(s, prompt)
+        k0 = normal_fp16((prompt, hkv, 128), 464_017, 10 + g, "cuda")
+        v0 = normal_fp16((prompt, hkv, 128), 464_017, 20 + g, "cuda")
+        pool.write_kv(0, k0, v0, torch.from_numpy(slots).cuda())
+        st.write(0, k0.cpu().numpy(), v0.cpu().numpy(), slots)
+        kids = [s] + [pool.fork(s) for _ in range(k - 1)]
+        assert kids[1:] == [orc.fork(s) for _ in range(k - 1)]
+        beams.append(kids)
+    q = normal_fp16((groups * k, hq, 128), 464_017, 3, "cuda")
+    for step in range(24):
+        new_all, slots_all = [], []
+        for g, parents in enumerate(beam_parents(464_017, step, groups, k)):
+            old = beams[g]
+            new, used = [], set()
+            for p in parents:
+                if p in used:
+                    c = pool.fork(old[p])
+                    assert c == orc.fork(old[p])
+                    new.append(c)
+                else:
+                    used.add(p)
+                    new.append(old[p])
+            for b in range(k):
+                if b not in used:
+                    pool.free(old[b])
+                    orc.free_seq(old[b])
+            for s in new:
+                sl, cow = pool.alloc(s, 1)
+                osl, ocow = orc.alloc(s, 1)
+                assert list(sl) == list(osl) and cow == ocow
+                if cow is not None:
+                    st.copy_block(*cow)
+                slots_all.append(int(sl[0]))
+            beams[g] = new
+            new_all += new
+        kn = normal_fp16((groups * k, hkv, 128), 464_017, 1000 + step, "cuda")
+        vn = normal_fp16((groups * k, hkv, 128), 464_017, 2000 + step, "cuda")
+        st.write(0, kn.cpu().numpy(), vn.cpu().numpy(), np.asarray(slots_all))
+        mb = max(len(orc.tables[s]) for s in new_all)
+        tables, lens = pool.block_tables(new_all, mb)
+        out = pool.write_kv_decode(0, kn, vn, torch.tensor(slots_all, dtype=torch.int32, device="cuda"), q,
+                                   torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda())
+        if step % 8 == 7:
+            ref = attention.decode(st, 0, q.cpu().numpy(), tables, lens)
+            assert_close(out, ref, "fp16", f"beam step {step}")
+    assert pool.stats()["cow_copies"] == orc.stats()["cow_copies"] > 10
+    assert pool.device_status() == 0

@@ -349,3 +349,68 @@ def test_prefix_cached_sequences_read_the_right_content():
         slots = np.asarray(a.tables[s])[t // bs] * bs + t % bs
         k, _ = store.read_slots(0, slots)
         np.testing.assert_array_equal(k[:, 0, 0], np.asarray(toks, np.float16))
+
+
+# ---- beam-style fork trees ------------------------------------------------------
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+def test_beam_fork_tree_matches_an_explicit_token_tree(bs):
+    """Beam search keeps candidates that share their common prefix (opsoai
+    page, "KV 캐시는 왜 요청이 늘수록 서빙 병목이 되는가"; iq-blog ch.4,
+    "Prefix Caching").  Model the search as a tree of token nodes: every beam is
+    a root-to-leaf path.  Reading each beam back through its table (with the
+    copy-on-write copies applied to the stored contents) must give exactly its
+    path; with one-token blocks nothing is ever copied and the pool holds
+    exactly the tree's live nodes."""
+    from workloads import beam_parents
+    groups, k, prompt, steps = 3, 5, 21, 30
+    a = OracleAllocator(4000, bs)
+    content = {}  # slot -> token node held there
+
+    def append(s, node):
+        slots, cow = a.alloc(s, 1)
+        if cow is not None:
+            src, dst = cow
+            for o in range(bs):
+                if src * bs + o in content:
+                    content[dst * bs + o] = content[src * bs + o]
+        content[slots[0]] = node
+
+    beams, paths = [], []
+    for g in range(groups):
+        s = a.seq_create()
+        slots, _ = a.alloc(s, prompt)
+        for i, sl in enumerate(slots):
+            content[sl] = ("prompt", g, i)
+        kids = [s] + [a.fork(s) for _ in range(k - 1)]
+        beams.append(kids)
+        paths.append([[("prompt", g, i) for i in range(prompt)] for _ in range(k)])
+    for step in range(steps):
+        for g, parents in enumerate(beam_parents(464_021, step, groups, k)):
+            old, new, used = beams[g], [], set()
+            for p in parents:
+                if p in used:
+                    new.append(a.fork(old[p]))
+                else:
+                    used.add(p)
+                    new.append(old[p])
+            for b in range(k):
+                if b not in used:
+                    a.free_seq(old[b])
+            paths[g] = [paths[g][p] + [(step, g, j)] for j, p in enumerate(parents)]
+            for j, s in enumerate(new):
+                append(s, (step, g, j))
+            beams[g] = new
+        a.check_invariants()
+        live = set()
+        for g in range(groups):
+            for s, path in zip(beams[g], paths[g]):
+                t = a.tables[s]
+                got = [content[t[i // bs] * bs + i % bs] for i in range(a.lens[s])]
+                assert got == path
+                live.update(path)
+        if bs == 1:
+            assert not a.cow_log
+            assert a.stats()["used_blocks"] == len(live)
+    if bs > 1:
+        assert len(a.cow_log) > 0

@@ -9,6 +9,7 @@ from .configs import (  # noqa: F401
     PAGE_EXAMPLE_FREE_ORDER,
     WORKLOADS,
     Workload,
+    beam_parents,
     cb_prefix_script,
     prefix_cache_prompts,
     workload,

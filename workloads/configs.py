@@ -64,6 +64,10 @@ WORKLOADS = {
     # request i takes system prompt i mod 4 plus its own U{64..1024} tokens.
     "prefix_cache": Workload(6, "prefix_cache", 1, 32, 8, 128, 16, "fp16", 16384, 256, repeats=32,
                              extra={"systems": 4, "system_tokens": 1024, "suffix": (64, 1024)}),
+    # Beam search, width 5: 32 prompts of 2040 tokens, each with 5 beams that
+    # every step re-fork from the survivors (beam_parents) and append a token.
+    "beam_k5": Workload(7, "beam_k5", 1, 32, 8, 128, 16, "fp16", 8192, 160, repeats=32,
+                        extra={"groups": 32, "k": 5, "prompt": 2040}),
 }
 
 # The page's own worked example of a block table: free blocks handed out in
@@ -88,6 +92,16 @@ def prefix_cache_prompts(seed: int, n: int, systems: int, system_tokens: int, su
         nxt += int(lens[i])
         prompts.append([int(t) for t in sys_ids[i % systems]] + own)
     return prompts
+
+
+def beam_parents(seed: int, step: int, groups: int, k: int):
+    """Beam survivor choice of one search step: for every group, ``k`` sorted
+    indices (with repeats) of the old beams the new beams descend from."""
+    out = []
+    for g in range(groups):
+        draws = uniform_ints(seed, 100_000 + step * 4096 + g, 0, k - 1, k)
+        out.append(sorted(int(x) for x in draws))
+    return out
 
 
 def cb_prefix_script(seed: int, n_shared: int = 100, prefix: int = 200,
