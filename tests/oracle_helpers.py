@@ -8,7 +8,7 @@ from oracle.kvstore import OracleKVStore
 
 
 def build_paged(k_dense, v_dense, lens, block_size, num_blocks, free_order=None,
-                dtype="fp16", k_scales=None, v_scales=None):
+                dtype="fp16", k_scales=None, v_scales=None, k_zeros=None, v_zeros=None):
     """Allocate each sequence's tokens through the oracle allocator and write them.
 
     ``k_dense[i]``: ``[T_i][Hkv][d]`` fp16 for sequence i (one layer).
@@ -16,7 +16,8 @@ def build_paged(k_dense, v_dense, lens, block_size, num_blocks, free_order=None,
     """
     hkv, d = k_dense[0].shape[1], k_dense[0].shape[2]
     alloc = OracleAllocator(num_blocks, block_size, free_order)
-    store = OracleKVStore(1, num_blocks, hkv, block_size, d, dtype, k_scales, v_scales)
+    store = OracleKVStore(1, num_blocks, hkv, block_size, d, dtype, k_scales, v_scales,
+                          k_zeros, v_zeros)
     seqs, all_slots = [], []
     for i, t in enumerate(lens):
         s = alloc.seq_create()

@@ -93,3 +93,35 @@ def test_cow_without_copy_is_caught(monkeypatch):
             return slots, None  # forgets to report (so nobody copies) the shared block
     monkeypatch.setattr(ta, "OracleAllocator", Bad)
     _fails(ta.test_slot_mapping_content_round_trip_through_fork_and_cow)
+
+
+def test_int8_zero_point_with_wrong_sign_is_caught(monkeypatch):
+    from oracle import int8
+    from tests import test_oracle_int8 as ti
+    monkeypatch.setattr(int8, "decode", lambda c, s, z: (np.asarray(c, dtype=np.int8).astype(np.float64)
+                                                         + np.asarray(z, dtype=np.float64))
+                        * np.asarray(s, dtype=np.float32).astype(np.float64))
+    _fails(ti.test_grid_points_are_exact_and_round_trip)
+
+
+def test_truncating_int8_encode_is_caught(monkeypatch):
+    from oracle import int8
+    from tests import test_oracle_int8 as ti
+
+    def bad(y, zero):
+        y = np.nan_to_num(np.asarray(y, dtype=np.float64), nan=0.0, posinf=1e9, neginf=-1e9)
+        return np.clip(np.trunc(y) + np.asarray(zero), -128, 127).astype(np.int8)
+    monkeypatch.setattr(int8, "encode", bad)
+    _fails(ti.test_ties_to_even_saturation_and_nan)
+    _fails(ti.test_encode_matches_torch_qint8_away_from_ties, 0.02, 0)
+
+
+def test_int8_zero_point_after_saturation_is_caught(monkeypatch):
+    from oracle import int8
+    from tests import test_oracle_int8 as ti
+
+    def bad(y, zero):
+        y = np.nan_to_num(np.asarray(y, dtype=np.float64), nan=0.0, posinf=1e9, neginf=-1e9)
+        return np.clip(np.clip(np.rint(y), -128, 127) + np.asarray(zero), -128, 127).astype(np.int8)
+    monkeypatch.setattr(int8, "encode", bad)
+    _fails(ti.test_ties_to_even_saturation_and_nan)
