@@ -25,6 +25,11 @@
  *  - fp8 KV storage at one byte per element (youngju.dev page, section
  *    "KV 양자화: FP8과 INT8"), as OCP E4M3FN with one fp32 scale per
  *    (layer, KV head) for K and one for V.
+ *  - int8 KV storage at one byte per element with a scale and a zero point
+ *    (same section): code c in [-128, 127], value (c - z) * s, one fp32
+ *    scale s and one integer zero point z per (layer, KV head) for K and for
+ *    V; a new token is encoded as clamp(rint(x * f32(1/s)) + z, -128, 127)
+ *    (ties to even; NaN gives z).
  *
  * Conventions shared by every call:
  *  - Every call returns an int status: PA_OK (0) or a negative PA_ERR_*.
@@ -44,7 +49,8 @@
  *
  * Pool byte layout (device buffer given to pa_pool_bind, 256-byte aligned):
  *    [layers][2 (K, V)][num_blocks][kv_heads][tile]  then a metadata tail
- *    (fp32 scales and inverse scales, a device status word).
+ *    (fp32 scales, inverse scales and int8 zero points, a device status
+ *    word).
  *  A tile holds one (block, KV head): block_size x head_dim elements in a
  *  kernel-specific order (K in 16-byte chunks of consecutive dims, V with
  *  4-token x 16-dim sub-tiles).  Use pa_gather_kv to read tokens back in
@@ -71,6 +77,7 @@ extern "C" {
 /* ---- KV element types ---------------------------------------------------- */
 #define PA_DTYPE_FP16 0     /* IEEE binary16                                   */
 #define PA_DTYPE_FP8_E4M3 1 /* OCP E4M3FN: value = decode(code) * scale        */
+#define PA_DTYPE_INT8 2     /* int8 code c: value = (c - zero) * scale         */
 
 /* ---- device status bits (pa_device_status) -------------------------------- */
 #define PA_DEV_BAD_SLOT 1u  /* a slot >= num_blocks*block_size was skipped      */
@@ -82,7 +89,7 @@ typedef struct pa_pool pa_pool; /* opaque */
 
 typedef struct pa_pool_info {
   int32_t layers, kv_heads, head_dim, block_size, dtype, num_blocks;
-  int32_t elem_bytes; /* 2 (fp16) or 1 (fp8)                                  */
+  int32_t elem_bytes; /* 2 (fp16) or 1 (fp8, int8)                            */
   int32_t bound;      /* 1 once pa_pool_bind succeeded                        */
   uint64_t tile_bytes;  /* block_size * head_dim * elem_bytes                  */
   uint64_t kv_bytes;    /* 2 * layers * kv_heads * head_dim * elem_bytes *
@@ -129,6 +136,14 @@ int pa_pool_set_free_order(pa_pool* pool, const int32_t* perm, int32_t n);
  * (layer-major); fp16 pools pass NULL.  The library writes the scales, their
  * fp32 reciprocals and a zeroed status word into the tail (synchronously). */
 int pa_pool_bind(pa_pool* pool, void* dev_base, const float* k_scales, const float* v_scales);
+
+/* The same for int8 pools (pa_pool_bind refuses them): host fp32 scales and
+ * host int32 zero points in [-128, 127], each [layers*kv_heads] layer-major,
+ * for K and for V.  Scales must be positive and finite; otherwise, or for a
+ * zero point out of range, PA_ERR_INVALID and nothing is bound.  Inside the
+ * pool an int8 code c is kept as the byte c + 128; pa_gather_kv returns c. */
+int pa_pool_bind_int8(pa_pool* pool, void* dev_base, const float* k_scales, const float* v_scales,
+                      const int32_t* k_zeros, const int32_t* v_zeros);
 
 /* ---- block manager (host) ------------------------------------------------------ */
 
@@ -192,12 +207,14 @@ int pa_free_queue(const pa_pool* pool, int32_t* out, int32_t* n_out);
 /* Reshape-and-cache scatter: token t's K and V (device fp16 [n][kv_heads][head_dim],
  * 4-byte aligned) go to slot slot_mapping[t] (device int32[n]) of `layer`; negative slots are
  * skipped.  fp8 pools store encode(f32(x) * f32(1/scale)) with saturation to
- * +-448 and round-to-nearest-even. */
+ * +-448 and round-to-nearest-even; int8 pools store
+ * clamp(rint(f32(x) * f32(1/scale)) + zero, -128, 127). */
 int pa_write_kv(pa_pool* pool, int32_t layer, const void* k_new, const void* v_new,
                 const int32_t* slot_mapping, int32_t n_tokens, void* stream);
 
 /* Inverse of pa_write_kv: read the stored K/V of each slot into device
- * k_out/v_out [n][kv_heads][head_dim] (fp16 values, or raw uint8 codes for fp8).
+ * k_out/v_out [n][kv_heads][head_dim] (fp16 values, raw uint8 codes for fp8,
+ * int8 codes c for int8).
  * Negative slots leave their rows untouched. */
 int pa_gather_kv(const pa_pool* pool, int32_t layer, const int32_t* slot_mapping,
                  int32_t n_tokens, void* k_out, void* v_out, void* stream);
@@ -258,7 +275,7 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
  * included.  A negative slot skips the store (the pool's copy of token
  * T_i - 1 is used); any other slot sets PA_DEV_BAD_SLOT and is skipped too.
  * The wave that attends over token T_i - 1 takes it from k_new / v_new (as the
- * pool will hold it: fp16, or its E4M3FN code) and then stores it. */
+ * pool will hold it: fp16, or its E4M3FN or int8 code) and then stores it. */
 int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const void* v_new,
                        const int32_t* slot_mapping, const void* q, int32_t num_q_heads,
                        const int32_t* block_tables, int32_t max_blocks,

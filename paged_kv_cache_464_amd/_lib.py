@@ -19,6 +19,7 @@ PA_ERR_UNBOUND = -5
 
 PA_DTYPE_FP16 = 0
 PA_DTYPE_FP8_E4M3 = 1
+PA_DTYPE_INT8 = 2
 
 PA_DEV_BAD_SLOT = 1
 PA_DEV_BAD_BLOCK = 2
@@ -56,6 +57,7 @@ SIGNATURES = {
     "pa_pool_info_get": (C.c_int, [_P, C.POINTER(pa_pool_info)]),
     "pa_pool_set_free_order": (C.c_int, [_P, _PI32, _I32]),
     "pa_pool_bind": (C.c_int, [_P, _P, C.POINTER(C.c_float), C.POINTER(C.c_float)]),
+    "pa_pool_bind_int8": (C.c_int, [_P, _P, C.POINTER(C.c_float), C.POINTER(C.c_float), _PI32, _PI32]),
     "pa_seq_create": (C.c_int, [_P, _PI32]),
     "pa_seq_create_cached": (C.c_int, [_P, _PI32, _I32, _PI32, _PI32, _PI32]),
     "pa_alloc": (C.c_int, [_P, _I32, _I32, _PI32, _PI32, _P]),

@@ -1,5 +1,5 @@
 // Cache-side kernels: the reshape-and-cache scatter of new tokens' K/V into
-// their slots (fp16 copy or fp8 E4M3FN quantise), its inverse gather, and the
+// their slots (fp16 copy, fp8 E4M3FN or int8 quantise), its inverse gather, and the
 // whole-block copy used by copy-on-write.
 //
 // A slot is block * block_size + offset: the block table maps a sequence's
@@ -19,7 +19,7 @@ namespace {
 
 constexpr int kWaves = 4;  // waves per 256-thread workgroup
 
-template <int ELEM>
+template <int KIND>
 __global__ __launch_bounds__(256) void write_kv_kernel(PoolGeom g, int layer,
                                                        const _Float16* __restrict__ k_new,
                                                        const _Float16* __restrict__ v_new,
@@ -37,14 +37,16 @@ __global__ __launch_bounds__(256) void write_kv_kernel(PoolGeom g, int layer,
     return;
   }
   const int64_t src = (static_cast<int64_t>(tok) * g.kv_heads + h) * kHeadDim;
-  store_token<ELEM>(g, layer, h, slot, k_new + src, v_new + src, lane);
+  store_token<KIND>(g, layer, h, slot, k_new + src, v_new + src, lane);
 }
 
-template <int ELEM>
+// int8 pools return the codes c (two's complement), not the stored c + 128.
+template <int KIND>
 __global__ __launch_bounds__(256) void gather_kv_kernel(PoolGeom g, int layer,
                                                         const int32_t* __restrict__ slots,
                                                         int n_tokens, uint8_t* __restrict__ k_out,
                                                         uint8_t* __restrict__ v_out) {
+  constexpr int ELEM = kind_bytes(KIND);
   constexpr int X = 16 / ELEM;
   const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -72,11 +74,12 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(PoolGeom g, int layer,
     *reinterpret_cast<uint32_t*>(k_out + dst + 2 * d0) = kk;
     *reinterpret_cast<uint32_t*>(v_out + dst + 2 * d0) = v0 | (v1 << 16);
   } else {
-    const uint16_t kk = *reinterpret_cast<const uint16_t*>(kt + k_index(t, d0, bs, X, kHeadDim));
+    const uint32_t flip = KIND == kI8 ? 0x8080u : 0u;
+    const uint32_t kk = *reinterpret_cast<const uint16_t*>(kt + k_index(t, d0, bs, X, kHeadDim));
     const uint32_t v0 = vt[v_index(t, d0, bs, X)];
     const uint32_t v1 = vt[v_index(t, d0 + 1, bs, X)];
-    *reinterpret_cast<uint16_t*>(k_out + dst + d0) = kk;
-    *reinterpret_cast<uint16_t*>(v_out + dst + d0) = static_cast<uint16_t>(v0 | (v1 << 8));
+    *reinterpret_cast<uint16_t*>(k_out + dst + d0) = static_cast<uint16_t>(kk ^ flip);
+    *reinterpret_cast<uint16_t*>(v_out + dst + d0) = static_cast<uint16_t>((v0 | (v1 << 8)) ^ flip);
   }
 }
 
@@ -131,9 +134,16 @@ hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k_new, cons
   const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves));
   const auto* k = static_cast<const _Float16*>(k_new);
   const auto* v = static_cast<const _Float16*>(v_new);
-  if (g.elem_bytes == 2)
-    return launch_kernel(write_kv_kernel<2>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
-  return launch_kernel(write_kv_kernel<1>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
+  switch (g.kind) {
+    case kF16:
+      return launch_kernel(write_kv_kernel<kF16>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
+    case kF8:
+      return launch_kernel(write_kv_kernel<kF8>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
+    case kI8:
+      return launch_kernel(write_kv_kernel<kI8>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gather_kv(const PoolGeom& g, int layer, const int32_t* slots, int n_tokens,
@@ -143,9 +153,16 @@ hipError_t launch_gather_kv(const PoolGeom& g, int layer, const int32_t* slots, 
   const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves));
   auto* ko = static_cast<uint8_t*>(k_out);
   auto* vo = static_cast<uint8_t*>(v_out);
-  if (g.elem_bytes == 2)
-    return launch_kernel(gather_kv_kernel<2>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
-  return launch_kernel(gather_kv_kernel<1>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
+  switch (g.kind) {
+    case kF16:
+      return launch_kernel(gather_kv_kernel<kF16>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
+    case kF8:
+      return launch_kernel(gather_kv_kernel<kF8>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
+    case kI8:
+      return launch_kernel(gather_kv_kernel<kI8>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t stream) {

@@ -39,6 +39,9 @@ constexpr int kMinSplitTokens = 1024;  // shorter contexts always run in one pas
 
 }  // namespace
 
+static_assert(PA_DTYPE_FP16 == pa::kF16 && PA_DTYPE_FP8_E4M3 == pa::kF8 && PA_DTYPE_INT8 == pa::kI8,
+              "dtype codes are the kernels' element kinds");
+
 struct pa_pool {
   int32_t layers, kv_heads, head_dim, block_size, dtype, num_blocks, elem_bytes;
   uint64_t tile_bytes, kv_bytes, scales_offset, status_offset, total_bytes;
@@ -62,7 +65,7 @@ struct pa_pool {
     tile_bytes = static_cast<uint64_t>(B) * D * elem_bytes;
     kv_bytes = 2ull * L * N * H * tile_bytes;
     scales_offset = align_up(kv_bytes, 256);
-    status_offset = align_up(scales_offset + 16ull * L * H, 256);
+    status_offset = align_up(scales_offset + 24ull * L * H, 256);  // six fp32 per (layer, head)
     total_bytes = status_offset + 256;
   }
   ~pa_pool() {
@@ -243,7 +246,7 @@ int pa_pool_create(int32_t layers, int32_t kv_heads, int32_t head_dim, int32_t b
   if (head_dim != pa::kHeadDim) return fail(PA_ERR_INVALID, "head_dim %d unsupported (128 only)", head_dim);
   if (block_size != 8 && block_size != 16 && block_size != 32)
     return fail(PA_ERR_INVALID, "block_size %d unsupported (8, 16, 32)", block_size);
-  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_FP8_E4M3)
+  if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_FP8_E4M3 && dtype != PA_DTYPE_INT8)
     return fail(PA_ERR_INVALID, "unknown dtype %d", dtype);
   if (num_blocks < 1 || static_cast<int64_t>(num_blocks) * block_size > 0x7FFFFFFF)
     return fail(PA_ERR_INVALID, "num_blocks %d out of range", num_blocks);
@@ -284,14 +287,19 @@ int pa_pool_set_free_order(pa_pool* p, const int32_t* perm, int32_t n) {
   return PA_OK;
 }
 
-int pa_pool_bind(pa_pool* p, void* dev_base, const float* k_scales, const float* v_scales) {
+namespace {
+
+int bind_pool(pa_pool* p, void* dev_base, const float* k_scales, const float* v_scales,
+              const int32_t* k_zeros, const int32_t* v_zeros) {
   if (!p || !dev_base) return fail(PA_ERR_INVALID, "NULL argument");
   if (reinterpret_cast<uintptr_t>(dev_base) % 256 != 0)
     return fail(PA_ERR_INVALID, "device buffer must be 256-byte aligned");
   const size_t lh = static_cast<size_t>(p->layers) * p->kv_heads;
-  std::vector<float> sc(4 * lh, 1.0f);
-  if (p->dtype == PA_DTYPE_FP8_E4M3) {
-    if (!k_scales || !v_scales) return fail(PA_ERR_INVALID, "fp8 pools need k_scales and v_scales");
+  // [6][layers][kv_heads]: k_scale, v_scale, k_inv, v_inv, k_zero, v_zero
+  std::vector<float> sc(6 * lh, 1.0f);
+  std::fill(sc.begin() + 4 * lh, sc.end(), 0.0f);
+  if (p->dtype != PA_DTYPE_FP16) {
+    if (!k_scales || !v_scales) return fail(PA_ERR_INVALID, "fp8 and int8 pools need k_scales and v_scales");
     for (size_t i = 0; i < lh; ++i) {
       const float ks = k_scales[i], vs = v_scales[i];
       if (!(std::isfinite(ks) && ks > 0.0f && std::isfinite(vs) && vs > 0.0f))
@@ -300,6 +308,15 @@ int pa_pool_bind(pa_pool* p, void* dev_base, const float* k_scales, const float*
       sc[lh + i] = vs;
       sc[2 * lh + i] = 1.0f / ks;  // IEEE fp32 division, round to nearest even
       sc[3 * lh + i] = 1.0f / vs;
+    }
+  }
+  if (p->dtype == PA_DTYPE_INT8) {
+    if (!k_zeros || !v_zeros) return fail(PA_ERR_INVALID, "int8 pools need k_zeros and v_zeros");
+    for (size_t i = 0; i < lh; ++i) {
+      if (k_zeros[i] < -128 || k_zeros[i] > 127 || v_zeros[i] < -128 || v_zeros[i] > 127)
+        return fail(PA_ERR_INVALID, "zero point %zu outside [-128, 127]", i);
+      sc[4 * lh + i] = static_cast<float>(k_zeros[i]);
+      sc[5 * lh + i] = static_cast<float>(v_zeros[i]);
     }
   }
   int dev = 0;
@@ -321,6 +338,7 @@ int pa_pool_bind(pa_pool* p, void* dev_base, const float* k_scales, const float*
   g.block_size = p->block_size;
   g.num_blocks = p->num_blocks;
   g.elem_bytes = p->elem_bytes;
+  g.kind = p->dtype;  // PA_DTYPE_* values are the kernels' element kinds
   g.tile_bytes = p->tile_bytes;
   g.block_stride = p->tile_bytes * p->kv_heads;
   g.half_stride = g.block_stride * p->num_blocks;
@@ -329,6 +347,20 @@ int pa_pool_bind(pa_pool* p, void* dev_base, const float* k_scales, const float*
   p->device = dev;
   p->bound = true;
   return PA_OK;
+}
+
+}  // namespace
+
+int pa_pool_bind(pa_pool* p, void* dev_base, const float* k_scales, const float* v_scales) {
+  if (p && p->dtype == PA_DTYPE_INT8)
+    return fail(PA_ERR_INVALID, "int8 pools are bound with pa_pool_bind_int8 (they need zero points)");
+  return bind_pool(p, dev_base, k_scales, v_scales, nullptr, nullptr);
+}
+
+int pa_pool_bind_int8(pa_pool* p, void* dev_base, const float* k_scales, const float* v_scales,
+                      const int32_t* k_zeros, const int32_t* v_zeros) {
+  if (p && p->dtype != PA_DTYPE_INT8) return fail(PA_ERR_INVALID, "pa_pool_bind_int8 needs an int8 pool");
+  return bind_pool(p, dev_base, k_scales, v_scales, k_zeros, v_zeros);
 }
 
 int pa_seq_create(pa_pool* p, int32_t* seq_out) {

@@ -34,9 +34,10 @@
 //    writes each chunk's partials without any merge;
 // lse_reduce_kernel merges the partials.
 // fp8 (E4M3FN) tiles are widened to fp16 in registers with the hardware
-// packed converter (exact: every E4M3 value is an fp16 value); the
-// per-(layer, KV head) scales are folded into the score and output
-// multipliers.
+// packed converter (exact: every E4M3 value is an fp16 value); int8 tiles
+// become the fp16 integers c - z (exact, |c - z| <= 255) with a byte
+// shuffle and a packed fp16 subtraction.  The per-(layer, KV head) scales are
+// folded into the score and output multipliers.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -93,6 +94,18 @@ __device__ inline f16x4 e4m3x4_to_f16x4(uint32_t w) {
   return f16x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Four stored int8 bytes (c + 128 each, bytes 0..3 of w) -> four fp16 c - z
+// in byte order.  Each byte becomes the low byte of the fp16 bit pattern
+// 0x64XX, i.e. the value 1024 + c + 128 exactly; subtracting bias = 1152 + z
+// (an integer in [1024, 1279]) leaves c - z exactly.
+__device__ inline f16x4 i8x4_to_f16x4(uint32_t w, f16x2 bias) {
+  const uint32_t lo = (w & 0xFFu) | ((w & 0xFF00u) << 8) | 0x64006400u;
+  const uint32_t hi = ((w >> 16) & 0xFFu) | ((w >> 8) & 0xFF0000u) | 0x64006400u;
+  const f16x2 a = __builtin_bit_cast(f16x2, lo) - bias;
+  const f16x2 b = __builtin_bit_cast(f16x2, hi) - bias;
+  return f16x4{a[0], a[1], b[0], b[1]};
+}
+
 // Maximum / sum of x over the four 16-lane rows of the wave (lanes n, n+16,
 // n+32, n+48 end up with the same value), with two VALU row swaps:
 // permlane16_swap pairs rows 0-1 and 2-3, permlane32_swap the two halves.
@@ -120,8 +133,9 @@ struct StepRegs {
 // 16-token step of one (sequence, KV head).  Lane (gq, n): gq = lane / 16 is
 // its row group, n = lane % 16 its head column.  FUSE: the launch also
 // stores each unit's new token (the fused scatter).
-template <int ELEM, int BS, int NT, bool FUSE>
+template <int KIND, int BS, int NT, bool FUSE>
 struct WaveDecoder {
+  static constexpr int ELEM = kind_bytes(KIND);
   static constexpr int kElem = ELEM;
   static constexpr bool kFuse = FUSE;
   static constexpr int kNT = NT;
@@ -139,14 +153,16 @@ struct WaveDecoder {
   // null; owns_new marks the wave whose step holds that token.
   const _Float16* knew;
   const _Float16* vnew;
-  float new_kinv, new_vinv;  // fp8: inverse scales of this (layer, KV head)
+  float new_kinv, new_vinv;  // fp8 / int8: inverse scales of this (layer, KV head)
+  float new_kz, new_vz;      // int8: its zero points
+  f16x2 kbias, vbias;        // int8: 1152 + zero point, twice (see i8x4_to_f16x4)
   int new_slot, new_blk;     // slot given for the new token; table entry of token T - 1
   bool owns_new;
   int new_tr;
   u32x4 newk[NLD][1];         // fp16: the new token's K chunks
   _Float16 newv[NLD][X / 4];  // fp16: its V elements
   uint32_t new_kh, new_vh;    // fp8: its K and V dims 2*lane, 2*lane+1 (fp16)
-  uint8_t* lds_new;           // fp8: this wave's 256-byte LDS scratch for its codes
+  uint8_t* lds_new;           // fp8 / int8: this wave's 256-byte LDS scratch for its codes
   f16x8 qop[NT][4];
   f32x4 oacc[NT][8];
   // Online-softmax state per head column: accumulators relative to the
@@ -178,6 +194,7 @@ struct WaveDecoder {
     bad = 0;
     knew = vnew = nullptr;
     new_kinv = new_vinv = 1.0f;
+    new_kz = new_vz = 0.0f;
     new_slot = -1;
     new_blk = 0;
     owns_new = false;
@@ -204,6 +221,12 @@ struct WaveDecoder {
       const int lh = p.layer * g.kv_heads + kvh;
       qk_mul *= g.scales[lh];
       out_mul = g.scales[lhs + lh];
+      if constexpr (KIND == kI8) {
+        const _Float16 kb = static_cast<_Float16>(1152.0f + g.scales[4 * lhs + lh]);
+        const _Float16 vb = static_cast<_Float16>(1152.0f + g.scales[5 * lhs + lh]);
+        kbias = f16x2{kb, kb};
+        vbias = f16x2{vb, vb};
+      }
     }
     const _Float16* qs = static_cast<const _Float16*>(p.q) + static_cast<int64_t>(seq) * p.num_q_heads * kD;
 #pragma unroll
@@ -262,16 +285,16 @@ struct WaveDecoder {
 
   __device__ int lane_id() const { return gq * 16 + n; }
 
-  // fp8: the wave encodes the new token (two dims of K and of V per lane,
-  // lane-parallel) into its LDS scratch: K codes at bytes 0..127, V codes at
-  // 128..255, both in dim order; inject_k / inject_v read them back in the
-  // tile layout.  DS operations of one wave run in order.
+  // fp8 / int8: the wave encodes the new token (two dims of K and of V per
+  // lane, lane-parallel) into its LDS scratch: K codes at bytes 0..127, V
+  // codes at 128..255, both in dim order; inject_k / inject_v read them back
+  // in the tile layout.  DS operations of one wave run in order.
   __device__ void encode_new_to_lds() {
     const int d0 = 2 * lane_id();
-    const uint32_t k0 = e4m3_encode(half_bits_to_float(new_kh) * new_kinv);
-    const uint32_t k1 = e4m3_encode(half_bits_to_float(new_kh >> 16) * new_kinv);
-    const uint32_t v0 = e4m3_encode(half_bits_to_float(new_vh) * new_vinv);
-    const uint32_t v1 = e4m3_encode(half_bits_to_float(new_vh >> 16) * new_vinv);
+    const uint32_t k0 = encode_byte<KIND>(half_bits_to_float(new_kh) * new_kinv, new_kz);
+    const uint32_t k1 = encode_byte<KIND>(half_bits_to_float(new_kh >> 16) * new_kinv, new_kz);
+    const uint32_t v0 = encode_byte<KIND>(half_bits_to_float(new_vh) * new_vinv, new_vz);
+    const uint32_t v1 = encode_byte<KIND>(half_bits_to_float(new_vh >> 16) * new_vinv, new_vz);
     *reinterpret_cast<uint16_t*>(lds_new + d0) = static_cast<uint16_t>(k0 | (k1 << 8));
     *reinterpret_cast<uint16_t*>(lds_new + kD + d0) = static_cast<uint16_t>(v0 | (v1 << 8));
   }
@@ -350,8 +373,14 @@ struct WaveDecoder {
         kop = __builtin_bit_cast(f16x8, kr[u]);
       } else {
         const u32x4 raw = kr[u >> 1];
-        const f16x4 a = e4m3x4_to_f16x4((u & 1) ? raw[2] : raw[0]);
-        const f16x4 b = e4m3x4_to_f16x4((u & 1) ? raw[3] : raw[1]);
+        f16x4 a, b;
+        if constexpr (KIND == kI8) {
+          a = i8x4_to_f16x4((u & 1) ? raw[2] : raw[0], kbias);
+          b = i8x4_to_f16x4((u & 1) ? raw[3] : raw[1], kbias);
+        } else {
+          a = e4m3x4_to_f16x4((u & 1) ? raw[2] : raw[0]);
+          b = e4m3x4_to_f16x4((u & 1) ? raw[3] : raw[1]);
+        }
         kop = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
       }
 #pragma unroll
@@ -549,7 +578,8 @@ struct WaveDecoder {
         vop = __builtin_bit_cast(f16x4, (rr & 1) ? u32x2{raw[2], raw[3]} : u32x2{raw[0], raw[1]});
       } else {
         const u32x4 raw = r.v[rr >> 2];
-        vop = e4m3x4_to_f16x4(raw[rr & 3]);
+        if constexpr (KIND == kI8) vop = i8x4_to_f16x4(raw[rr & 3], vbias);
+        else vop = e4m3x4_to_f16x4(raw[rr & 3]);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -728,9 +758,10 @@ __device__ inline int context_len(const PoolGeom& g, const DecodeLaunch& p, int 
 // two-tile (G > 16) variants 340 VGPR+AGPR registers and one wave per SIMD,
 // though they fit in 256 without spills; with two, MQA decode ran 10-13%
 // faster on MI355X (one-tile variants measured the same either way).
-template <int ELEM, int BS, int NT, int MODE, bool FUSE>
+template <int KIND, int BS, int NT, int MODE, bool FUSE>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(PoolGeom g, DecodeLaunch p) {
+  constexpr int ELEM = kind_bytes(KIND);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int group = p.num_q_heads / g.kv_heads;
@@ -774,7 +805,7 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
     else return static_cast<int64_t>(c_begin) * P + 16ll * j;
   };
 
-  using Dec = WaveDecoder<ELEM, BS, NT, FUSE>;
+  using Dec = WaveDecoder<KIND, BS, NT, FUSE>;
   Dec dec;
   if constexpr (FUSE && ELEM == 1) {
     __shared__ __attribute__((aligned(16))) uint8_t new_codes[kWaves][2 * kD];
@@ -818,6 +849,10 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
         const int lh = p.layer * g.kv_heads + kvh;
         dec.new_kinv = g.scales[2 * lhs + lh];
         dec.new_vinv = g.scales[3 * lhs + lh];
+        if constexpr (KIND == kI8) {
+          dec.new_kz = g.scales[4 * lhs + lh];
+          dec.new_vz = g.scales[5 * lhs + lh];
+        }
       }
     }
   }
@@ -1050,20 +1085,20 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_small_kernel(PoolGe
 // Kernels are launched with hipExtLaunchKernel (launch_kernel): its start/stop
 // events (null when not timing) are stamped by the dispatch itself, so timing a
 // launch adds no barrier packets to the stream.
-template <int ELEM, int BS, int NT, bool FUSE>
+template <int KIND, int BS, int NT, bool FUSE>
 hipError_t launch_decode_nt(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
                             hipEvent_t t1) {
   const dim3 block(kWaves * 64);
   const int64_t units = static_cast<int64_t>(d.num_seqs) * g.kv_heads;
   switch (d.mode) {
     case kSingle:
-      return launch_kernel(decode_kernel<ELEM, BS, NT, kSingle, FUSE>, dim3(static_cast<unsigned>(units)), block, s,
+      return launch_kernel(decode_kernel<KIND, BS, NT, kSingle, FUSE>, dim3(static_cast<unsigned>(units)), block, s,
                            t0, t1, g, d);
     case kSplit4:
-      return launch_kernel(decode_kernel<ELEM, BS, NT, kSplit4, FUSE>,
+      return launch_kernel(decode_kernel<KIND, BS, NT, kSplit4, FUSE>,
                            dim3(static_cast<unsigned>(units * d.waves_per_unit)), block, s, t0, t1, g, d);
     case kSplit1:
-      return launch_kernel(decode_kernel<ELEM, BS, NT, kSplit1, FUSE>,
+      return launch_kernel(decode_kernel<KIND, BS, NT, kSplit1, FUSE>,
                            dim3(static_cast<unsigned>((units * d.waves_per_unit + kWaves - 1) / kWaves)), block,
                            s, t0, t1, g, d);
     default:
@@ -1071,23 +1106,23 @@ hipError_t launch_decode_nt(const PoolGeom& g, const DecodeLaunch& d, hipStream_
   }
 }
 
-template <int ELEM, int BS>
+template <int KIND, int BS>
 hipError_t launch_decode_bs(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s,
                             hipEvent_t t0, hipEvent_t t1) {
   if (d.new_slots)
-    return nt == 1 ? launch_decode_nt<ELEM, BS, 1, true>(g, d, s, t0, t1)
-                   : launch_decode_nt<ELEM, BS, 2, true>(g, d, s, t0, t1);
-  return nt == 1 ? launch_decode_nt<ELEM, BS, 1, false>(g, d, s, t0, t1)
-                 : launch_decode_nt<ELEM, BS, 2, false>(g, d, s, t0, t1);
+    return nt == 1 ? launch_decode_nt<KIND, BS, 1, true>(g, d, s, t0, t1)
+                   : launch_decode_nt<KIND, BS, 2, true>(g, d, s, t0, t1);
+  return nt == 1 ? launch_decode_nt<KIND, BS, 1, false>(g, d, s, t0, t1)
+                 : launch_decode_nt<KIND, BS, 2, false>(g, d, s, t0, t1);
 }
 
-template <int ELEM>
-hipError_t launch_decode_elem(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s,
+template <int KIND>
+hipError_t launch_decode_kind(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s,
                               hipEvent_t t0, hipEvent_t t1) {
   switch (g.block_size) {
-    case 8: return launch_decode_bs<ELEM, 8>(g, d, nt, s, t0, t1);
-    case 16: return launch_decode_bs<ELEM, 16>(g, d, nt, s, t0, t1);
-    case 32: return launch_decode_bs<ELEM, 32>(g, d, nt, s, t0, t1);
+    case 8: return launch_decode_bs<KIND, 8>(g, d, nt, s, t0, t1);
+    case 16: return launch_decode_bs<KIND, 16>(g, d, nt, s, t0, t1);
+    case 32: return launch_decode_bs<KIND, 32>(g, d, nt, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1106,8 +1141,12 @@ hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s
         d.partition_tokens % quantum != 0)
       return hipErrorInvalidValue;
   }
-  if (g.elem_bytes == 2) return launch_decode_elem<2>(g, d, nt, s, t0, t1);
-  return launch_decode_elem<1>(g, d, nt, s, t0, t1);
+  switch (g.kind) {
+    case kF16: return launch_decode_kind<kF16>(g, d, nt, s, t0, t1);
+    case kF8: return launch_decode_kind<kF8>(g, d, nt, s, t0, t1);
+    case kI8: return launch_decode_kind<kI8>(g, d, nt, s, t0, t1);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s,

@@ -26,6 +26,13 @@ namespace pa {
 
 constexpr int kHeadDim = 128;
 
+// Element kinds of a pool (the values of PA_DTYPE_*): fp16, fp8 E4M3FN codes,
+// and int8 codes with a scale and a zero point.  The pool keeps an int8 code
+// c as the byte c + 128 (offset binary), which the decode kernel widens to
+// fp16 without a sign step; the gather returns c itself.
+constexpr int kF16 = 0, kF8 = 1, kI8 = 2;
+__host__ __device__ constexpr int kind_bytes(int kind) { return kind == kF16 ? 2 : 1; }
+
 __host__ __device__ constexpr int chunk_elems(int elem_bytes) { return 16 / elem_bytes; }
 
 __host__ __device__ inline int k_index(int t, int dim, int block_size, int x, int head_dim) {
@@ -43,10 +50,12 @@ __host__ __device__ inline int v_index(int t, int dim, int block_size, int x) {
 struct PoolGeom {
   uint8_t* base;           // device base of the pool
   int32_t layers, kv_heads, head_dim, block_size, num_blocks, elem_bytes;
+  int32_t kind;            // kF16, kF8 or kI8
   uint64_t tile_bytes;     // block_size * head_dim * elem_bytes
   uint64_t block_stride;   // kv_heads * tile_bytes (one block of one layer's K or V)
   uint64_t half_stride;    // num_blocks * block_stride (one layer's K pool)
-  float* scales;           // [4][layers][kv_heads]: k_scale, v_scale, k_inv, v_inv
+  float* scales;           // [6][layers][kv_heads]: k_scale, v_scale, k_inv, v_inv,
+                           // k_zero, v_zero (int8 zero points, exact in fp32)
   uint32_t* status;        // PA_DEV_* bits
 
   __host__ __device__ uint8_t* k_layer(int layer) const {

@@ -1,8 +1,9 @@
 // Device helpers shared by the cache kernels and the decode kernel: the fp8
-// E4M3FN encoder and the store of one new token's K/V (one KV head) into its
-// slot, i.e. the reshape-and-cache scatter (youngju.dev "KV cache and paged
-// attention", section "PagedAttention: OS 가상 메모리식 관리" for slots; section
-// "KV 양자화: FP8과 INT8" for the one-byte element).
+// E4M3FN and int8 encoders and the store of one new token's K/V (one KV head)
+// into its slot, i.e. the reshape-and-cache scatter (youngju.dev "KV cache and
+// paged attention", section "PagedAttention: OS 가상 메모리식 관리" for slots;
+// section "KV 양자화: FP8과 INT8" for the one-byte elements, int8 with a scale
+// and a zero point).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,16 +34,36 @@ __device__ inline uint32_t e4m3_encode(float y) {
   return sign | keep;
 }
 
+// int8 code of y = x * inv_scale: y rounded to the nearest integer (ties to
+// even), plus the zero point, saturated to [-128, 127]; NaN gives the zero
+// point and infinities saturate.  Returned as the stored byte c + 128.
+__device__ inline uint32_t i8_encode_stored(float y, float zero) {
+  float r = rintf(y);
+  r = (r == r) ? r : 0.0f;
+  const float c = fminf(fmaxf(r + zero, -128.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int>(c) + 128);
+}
+
+// The stored byte of y = x * inv_scale in a pool of the given one-byte kind.
+template <int KIND>
+__device__ inline uint32_t encode_byte(float y, float zero) {
+  if constexpr (KIND == kI8) return i8_encode_stored(y, zero);
+  (void)zero;
+  return e4m3_encode(y);
+}
+
 __device__ inline float half_bits_to_float(uint32_t bits) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }
 
 // One wave stores token `slot` of KV head h of `layer`: lane l takes dims 2l
-// and 2l+1 of k_src / v_src (fp16 [head_dim] each).  fp8 pools quantise with
-// the (layer, head) inverse scales.  The slot must be inside the pool.
-template <int ELEM>
+// and 2l+1 of k_src / v_src (fp16 [head_dim] each).  fp8 and int8 pools
+// quantise with the (layer, head) inverse scales (and int8 zero points).  The
+// slot must be inside the pool.
+template <int KIND>
 __device__ inline void store_token(const PoolGeom& g, int layer, int h, int slot,
                                    const _Float16* k_src, const _Float16* v_src, int lane) {
+  constexpr int ELEM = kind_bytes(KIND);
   constexpr int X = 16 / ELEM;
   const int blk = slot / g.block_size, t = slot % g.block_size;
   uint8_t* kt = g.k_layer(layer) + static_cast<uint64_t>(blk) * g.block_stride +
@@ -63,10 +84,12 @@ __device__ inline void store_token(const PoolGeom& g, int layer, int h, int slot
     const int lhs = g.layers * g.kv_heads;
     const float k_inv = g.scales[2 * lhs + lh];
     const float v_inv = g.scales[3 * lhs + lh];
-    const uint32_t k0 = e4m3_encode(half_bits_to_float(kk) * k_inv);
-    const uint32_t k1 = e4m3_encode(half_bits_to_float(kk >> 16) * k_inv);
-    const uint32_t v0 = e4m3_encode(half_bits_to_float(vv) * v_inv);
-    const uint32_t v1 = e4m3_encode(half_bits_to_float(vv >> 16) * v_inv);
+    const float k_z = g.scales[4 * lhs + lh];
+    const float v_z = g.scales[5 * lhs + lh];
+    const uint32_t k0 = encode_byte<KIND>(half_bits_to_float(kk) * k_inv, k_z);
+    const uint32_t k1 = encode_byte<KIND>(half_bits_to_float(kk >> 16) * k_inv, k_z);
+    const uint32_t v0 = encode_byte<KIND>(half_bits_to_float(vv) * v_inv, v_z);
+    const uint32_t v1 = encode_byte<KIND>(half_bits_to_float(vv >> 16) * v_inv, v_z);
     *reinterpret_cast<uint16_t*>(kt + k_index(t, d0, bs, X, kHeadDim)) = static_cast<uint16_t>(k0 | (k1 << 8));
     vt[v_index(t, d0, bs, X)] = static_cast<uint8_t>(v0);
     vt[v_index(t, d0 + 1, bs, X)] = static_cast<uint8_t>(v1);

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import (PA_DTYPE_FP16, PA_DTYPE_FP8_E4M3, PA_ERR_BAD_SEQ, PA_ERR_NO_BLOCKS,  # noqa: F401
+from ._lib import (PA_DTYPE_FP16, PA_DTYPE_FP8_E4M3, PA_DTYPE_INT8, PA_ERR_BAD_SEQ, PA_ERR_NO_BLOCKS,  # noqa: F401
                    PA_DEV_BAD_BLOCK, PA_DEV_BAD_LEN, PA_DEV_BAD_ORDER, PA_DEV_BAD_SLOT)
 
 
@@ -129,6 +129,16 @@ def pa_pool_bind(h, dev_ptr: int, k_scales=None, v_scales=None):
     _check(_L().pa_pool_bind(C.c_void_p(h), C.c_void_p(dev_ptr), kp, vp))
 
 
+def pa_pool_bind_int8(h, dev_ptr: int, k_scales, v_scales, k_zeros, v_zeros):
+    """Bind an int8 pool: fp32 scales and int32 zero points, each [layers*kv_heads]."""
+    arrs = [np.ascontiguousarray(np.asarray(a, dtype=dt).reshape(-1))
+            for a, dt in ((k_scales, np.float32), (v_scales, np.float32),
+                          (k_zeros, np.int32), (v_zeros, np.int32))]
+    ptrs = [a.ctypes.data_as(C.POINTER(C.c_float if a.dtype == np.float32 else C.c_int32)) for a in arrs]
+    _forget(h)
+    _check(_L().pa_pool_bind_int8(C.c_void_p(h), C.c_void_p(dev_ptr), *ptrs))
+
+
 # ---- block manager ---------------------------------------------------------
 
 def pa_seq_create(h) -> int:
@@ -220,7 +230,7 @@ def pa_write_kv(h, layer, k_new, v_new, slot_mapping, stream=None):
 def pa_gather_kv(h, layer, slot_mapping, k_out, v_out, stream=None):
     info = _info(h)
     n = slot_mapping.numel()
-    dt = torch.float16 if info["dtype"] == PA_DTYPE_FP16 else torch.uint8
+    dt = {PA_DTYPE_FP16: torch.float16, PA_DTYPE_FP8_E4M3: torch.uint8, PA_DTYPE_INT8: torch.int8}[info["dtype"]]
     shape = (n, info["kv_heads"], info["head_dim"])
     sp = _dev(slot_mapping, torch.int32, (n,), "slot_mapping")
     kp = _dev(k_out, dt, shape, "k_out")
@@ -396,8 +406,9 @@ class PagedKVPool:
     """A pool descriptor plus the torch-allocated device buffer it is bound to."""
 
     def __init__(self, layers, kv_heads, head_dim, block_size, num_blocks, dtype="fp16",
-                 device="cuda", free_order=None, k_scales=None, v_scales=None, bind=True):
-        code = {"fp16": PA_DTYPE_FP16, "fp8": PA_DTYPE_FP8_E4M3}[dtype]
+                 device="cuda", free_order=None, k_scales=None, v_scales=None, bind=True,
+                 k_zeros=None, v_zeros=None):
+        code = {"fp16": PA_DTYPE_FP16, "fp8": PA_DTYPE_FP8_E4M3, "int8": PA_DTYPE_INT8}[dtype]
         self.handle = pa_pool_create(layers, kv_heads, head_dim, block_size, code, num_blocks)
         self.dtype = dtype
         self.buffer = None
@@ -411,7 +422,10 @@ class PagedKVPool:
                 base = self.buffer.data_ptr()
                 aligned = (base + 255) // 256 * 256
                 self.base_ptr = aligned
-                pa_pool_bind(self.handle, aligned, k_scales, v_scales)
+                if dtype == "int8":
+                    pa_pool_bind_int8(self.handle, aligned, k_scales, v_scales, k_zeros, v_zeros)
+                else:
+                    pa_pool_bind(self.handle, aligned, k_scales, v_scales)
                 self.info = pa_pool_info_get(self.handle)
         except Exception:
             pa_pool_destroy(self.handle)
@@ -469,7 +483,7 @@ class PagedKVPool:
         pa_write_kv(self.handle, layer, k_new, v_new, slot_mapping, stream)
 
     def gather_kv(self, layer, slot_mapping, stream=None):
-        dt = torch.float16 if self.dtype == "fp16" else torch.uint8
+        dt = {"fp16": torch.float16, "fp8": torch.uint8, "int8": torch.int8}[self.dtype]
         n = slot_mapping.numel()
         shape = (n, self.info["kv_heads"], self.info["head_dim"])
         k = torch.zeros(shape, dtype=dt, device=slot_mapping.device)

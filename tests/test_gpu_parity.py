@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention, fp8
+from oracle import attention, fp8, int8
 from oracle.allocator import OracleAllocator
 from oracle.kvstore import OracleKVStore
 from paged_kv_cache_464_amd import pa
@@ -29,7 +29,7 @@ def _need_gpu():
 
 # ---- scatter / gather -------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_write_kv_bit_exact(dtype, bs):
     say("write_kv", dtype, bs)
@@ -68,6 +68,47 @@ def test_fp8_encode_exhaustive_over_fp16_inputs():
         np.testing.assert_array_equal(v.cpu().numpy(), fp8.quantize(vt.cpu().numpy(), inv_v))
 
 
+def test_int8_encode_exhaustive_over_fp16_inputs():
+    """Every finite fp16 value through the GPU int8 quantiser, for several
+    scales and zero points (saturation, ties and the zero-point shift)."""
+    say("int8 exhaustive")
+    x = np.arange(65536, dtype=np.uint16).view(np.float16)
+    x = x[np.isfinite(x)]
+    n_tok = len(x) // 128
+    x = x[:n_tok * 128]
+    for scale, kz, vz in ((1.0, 0, 0), (0.0123, -128, 127), (3.7, 5, -77), (2.0 ** -6, 100, -3)):
+        pool = pa.PagedKVPool(1, 1, 128, 16, -(-n_tok // 16), "int8", k_scales=[scale],
+                              v_scales=[scale * 0.5], k_zeros=[kz], v_zeros=[vz])
+        kt = torch.from_numpy(x.reshape(n_tok, 1, 128)).cuda()
+        vt = kt.flip(0).contiguous()
+        sl = torch.arange(n_tok, dtype=torch.int32, device="cuda")
+        pool.write_kv(0, kt, vt, sl)
+        k, v = pool.gather_kv(0, sl)
+        inv_k = int8.inverse_scale(np.float32(scale))
+        inv_v = int8.inverse_scale(np.float32(scale * 0.5))
+        np.testing.assert_array_equal(k.cpu().numpy(), int8.quantize(kt.cpu().numpy(), inv_k, kz))
+        np.testing.assert_array_equal(v.cpu().numpy(), int8.quantize(vt.cpu().numpy(), inv_v, vz))
+    nan = torch.full((1, 1, 128), float("nan"), dtype=torch.float16, device="cuda")
+    pool.write_kv(0, nan, nan, sl[:1])
+    k, v = pool.gather_kv(0, sl[:1])
+    assert (k == 100).all() and (v == -3).all()  # NaN encodes as the zero point
+
+
+def test_int8_bind_rules():
+    say("int8 bind")
+    with pytest.raises(pa.PAError):
+        pa.PagedKVPool(1, 2, 128, 16, 4, "int8", k_scales=[1, 1], v_scales=[1, 1],
+                       k_zeros=[0, 128], v_zeros=[0, 0])
+    with pytest.raises(pa.PAError):
+        pa.PagedKVPool(1, 2, 128, 16, 4, "int8", k_scales=[1, 0], v_scales=[1, 1],
+                       k_zeros=[0, 0], v_zeros=[0, 0])
+    h = pa.pa_pool_create(1, 2, 128, 16, pa.PA_DTYPE_INT8, 4)
+    buf = torch.empty(pa.pa_pool_info_get(h)["total_bytes"], dtype=torch.uint8, device="cuda")
+    with pytest.raises(pa.PAError):
+        pa.pa_pool_bind(h, buf.data_ptr(), [1, 1], [1, 1])  # int8 needs the zero points
+    pa.pa_pool_destroy(h)
+
+
 def test_negative_slots_are_skipped():
     say("negative slots")
     c = build_case([20], 4, 1, 16, 4, 7)
@@ -104,11 +145,11 @@ def _lens(seed, n, hi):
     return x
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
 @pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (32, 1), (8, 8), (16, 2)])
 def test_decode_matrix(dtype, bs, hq, hkv):
-    seed = 1000 + bs * 7 + hq * 3 + hkv + (500 if dtype == "fp8" else 0)
+    seed = 1000 + bs * 7 + hq * 3 + hkv + {"fp16": 0, "fp8": 500, "int8": 800}[dtype]
     lens = _lens(seed, 6, 700)
     nb = int(sum(-(-int(t) // bs) for t in lens)) + 5
     say("matrix", dtype, bs, hq, hkv, list(lens))
@@ -122,7 +163,7 @@ def test_decode_matrix(dtype, bs, hq, hkv):
     assert c.pool.device_status() == 0
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
 def test_partials_match_oracle_split(dtype):
     say("partials", dtype)
     lens = [1, 300, 1000, 513]
@@ -139,7 +180,7 @@ def test_partials_match_oracle_split(dtype):
         # base-2 max -> natural units; l is invariant to the base change
         np.testing.assert_allclose(m[i, :, :nc] * ln2, om, rtol=0, atol=2e-3)
         np.testing.assert_allclose(l[i, :, :nc], ol, rtol=5e-3, atol=0)
-        tol = 2e-3 if dtype == "fp16" else 2e-2 * np.abs(oo).max()
+        tol = {"fp16": 2e-3, "fp8": 2e-2 * np.abs(oo).max(), "int8": 4e-3 * np.abs(oo).max()}[dtype]
         np.testing.assert_allclose(o[i, :, :nc], oo, rtol=0, atol=tol)
     out = torch.empty_like(c.q)
     ws = torch.empty(pa.pa_decode_workspace_bytes(c.pool.handle, 4, 16, c.max_blocks, P),
@@ -248,7 +289,7 @@ def test_kernel_timing_samples_every_nth_launch():
         pa.pa_profile_begin(c.pool.handle, 4, 0)
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
 def test_seq_order_changes_nothing_but_the_schedule(dtype):
     """seq_order only reorders the workgroups: outputs and partials are bitwise
     those of the natural order, in every schedule."""
@@ -297,14 +338,14 @@ def _poison_last(c, last_slots):
     c.pool.write_kv(0, nan, nan, last_slots)
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
 @pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("hq,hkv", [(32, 8), (32, 1)])
 def test_write_kv_decode_equals_write_then_decode(dtype, bs, hq, hkv):
     """The fused step gives bit for bit the output and the pool of pa_write_kv
     followed by pa_decode, in every schedule, with the new token's slot holding
     NaN before the launch."""
-    seed = 3000 + bs + hq + hkv + (7 if dtype == "fp8" else 0)
+    seed = 3000 + bs + hq + hkv + {"fp16": 0, "fp8": 7, "int8": 11}[dtype]
     lens = [1, 16, 17, 700, 33, 1000, 64, 5]
     nb = int(sum(-(-t // bs) for t in lens)) + 4
     say("write_kv_decode", dtype, bs, hq, hkv)

@@ -18,6 +18,8 @@ from .generators import (  # noqa: F401
     FP8_E4M3_MAX,
     SEED_BASE,
     amax_scales,
+    head_offsets,
+    minmax_int8_params,
     free_order,
     normal_fp16,
     seed_for,

@@ -60,6 +60,12 @@ WORKLOADS = {
     "long_ctx": Workload(4, "long_ctx", 1, 64, 8, 128, 16, "fp16", 65536, 8,
                          context=(131072,) * 8, partition_tokens=512, repeats=80),
     **_fp8_variants(),
+    # The fp8 shapes with int8 codes (per-(layer, KV head) scale and zero
+    # point from each head's min/max; keys shifted by a per-head mean).
+    "int8_gqa_bs16": Workload(8, "int8_gqa_bs16", 1, 32, 8, 128, 16, "int8", 64 * 8192 // 16, 64,
+                              context=(8192,) * 64, repeats=32),
+    "int8_mqa_bs16": Workload(8, "int8_mqa_bs16", 1, 32, 1, 128, 16, "int8", 64 * 8192 // 16, 64,
+                              context=(8192,) * 64, repeats=32),
     # Requests built through the prefix cache: 4 system prompts of 1024 tokens,
     # request i takes system prompt i mod 4 plus its own U{64..1024} tokens.
     "prefix_cache": Workload(6, "prefix_cache", 1, 32, 8, 128, 16, "fp16", 16384, 256, repeats=32,

@@ -64,3 +64,27 @@ def amax_scales(x: torch.Tensor) -> np.ndarray:
     a = x.reshape(-1, hkv, x.shape[-1]).abs().amax(dim=(0, 2)).to(torch.float32).cpu().numpy()
     a = np.maximum(a, np.float32(1e-6))
     return (a / np.float32(FP8_E4M3_MAX)).astype(np.float32)
+
+
+def minmax_int8_params(x: torch.Tensor):
+    """Per-KV-head int8 calibration of ``x[..., Hkv, d]``: the scale maps the
+    head's [min, max] onto the 255 steps of [-128, 127] and the zero point is
+    the code of 0, ``s = (max - min) / 255``, ``z = clamp(rint(-128 - min / s))``.
+
+    Returned on the host: float32 scales and int32 zero points of shape [Hkv].
+    This is how the synthetic int8 workloads pick their per-(layer, kv_head)
+    parameters (an input convention, like ``amax_scales`` for fp8).
+    """
+    hkv = x.shape[-2]
+    y = x.reshape(-1, hkv, x.shape[-1]).to(torch.float32)
+    lo = y.amin(dim=(0, 2)).cpu().numpy().astype(np.float64)
+    hi = y.amax(dim=(0, 2)).cpu().numpy().astype(np.float64)
+    s = np.maximum((hi - lo) / 255.0, 1e-6).astype(np.float32)
+    z = np.clip(np.rint(-128.0 - lo / s.astype(np.float64)), -128, 127).astype(np.int32)
+    return s, z
+
+
+def head_offsets(hkv: int) -> np.ndarray:
+    """Per-KV-head mean shifts for the int8 workloads' keys (-1 .. 1.5), so
+    that zero points differ from head to head."""
+    return np.linspace(-1.0, 1.5, hkv).astype(np.float32)
