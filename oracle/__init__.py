@@ -16,6 +16,8 @@ follows:
   quantise).
 * ``attention.decode``           exact softmax(q K^T / sqrt(d)) V per query head
   over the K/V rebuilt contiguously from each block table.
+* ``attention.multi_token``      causal attention for several new query tokens
+  per sequence (prefill chunks mixed with decode tokens) through the tables.
 * ``attention.split_partials`` / ``attention.lse_merge``  per-chunk
   (max, sum, normalised output) and their log-sum-exp merge.
 * ``fp8``                        OCP E4M3FN decode / saturating RNE encode.

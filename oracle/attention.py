@@ -113,3 +113,41 @@ def lse_merge(m, lsum, o):
     m = np.asarray(m, dtype=np.float64)
     w = np.asarray(lsum, dtype=np.float64) * np.exp(m - np.max(m))
     return (w[:, None] * np.asarray(o, dtype=np.float64)).sum(axis=0) / w.sum()
+
+
+def multi_token(store, layer, q, query_start, block_tables, context_lens, scale=None):
+    """Paged attention for several new query tokens per sequence (a prefill
+    chunk, or one decode token), output ``[N][Hq][d]`` float64.
+
+    Attention is causal: a token attends to itself and the tokens before it
+    (youngju.dev page, section "핵심 원리: KV 캐시란 무엇인가"); batches may mix
+    prefill chunks and decode tokens (iq-blog ch.4, the scheduler described
+    in its vLLM architecture section).  Sequence i owns query rows
+    ``query_start[i] .. query_start[i+1] - 1``: its last n_i tokens, whose K/V
+    are already in the cache, so that row j (0-based within the sequence)
+    sits at position ``T_i - n_i + j`` and attends to the first
+    ``T_i - n_i + j + 1`` tokens through the block table.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_rows, n_q_heads, d = q.shape
+    g = n_q_heads // store.kv_heads
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qs = [int(x) for x in query_start]
+    if qs[0] != 0 or qs[-1] != n_rows or any(b < a for a, b in zip(qs, qs[1:])):
+        raise ValueError("query_start must rise from 0 to the number of query rows")
+    out = np.zeros((n_rows, n_q_heads, d), dtype=np.float64)
+    for i in range(len(qs) - 1):
+        n_i = qs[i + 1] - qs[i]
+        if n_i == 0:
+            continue
+        length = int(context_lens[i])
+        if length < n_i:
+            raise ValueError(f"sequence {i}: {n_i} query tokens but a context of {length}")
+        for kvh in range(store.kv_heads):
+            k, v = gather_context(store, layer, block_tables[i], length, kvh)
+            for j in range(n_i):
+                visible = length - n_i + j + 1
+                for h in range(kvh * g, (kvh + 1) * g):
+                    out[qs[i] + j, h] = _attend(q[qs[i] + j, h], k[:visible], v[:visible], scale)
+    return out

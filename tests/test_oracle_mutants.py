@@ -125,3 +125,38 @@ def test_int8_zero_point_after_saturation_is_caught(monkeypatch):
         return np.clip(np.clip(np.rint(y), -128, 127) + np.asarray(zero), -128, 127).astype(np.int8)
     monkeypatch.setattr(int8, "encode", bad)
     _fails(ti.test_ties_to_even_saturation_and_nan)
+
+
+def _multi_token_with(visible_of):
+    """A copy of the oracle's multi-token attention with the causal limit replaced."""
+    import math
+
+    def bad(store, layer, q, query_start, block_tables, context_lens, scale=None):
+        q = np.asarray(q, dtype=np.float64)
+        n_rows, hq, d = q.shape
+        g = hq // store.kv_heads
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        qs = [int(x) for x in query_start]
+        out = np.zeros((n_rows, hq, d))
+        for i in range(len(qs) - 1):
+            n_i, length = qs[i + 1] - qs[i], int(context_lens[i])
+            for kvh in range(store.kv_heads):
+                k, v = attention.gather_context(store, layer, block_tables[i], length, kvh)
+                for j in range(n_i):
+                    vis = max(1, min(length, visible_of(length, n_i, j)))
+                    for h in range(kvh * g, (kvh + 1) * g):
+                        out[qs[i] + j, h] = attention._attend(q[qs[i] + j, h], k[:vis], v[:vis], scale)
+        return out
+    return bad
+
+
+def test_causal_limit_off_by_one_is_caught(monkeypatch):
+    from tests import test_oracle_multi_token as tm
+    monkeypatch.setattr(attention, "multi_token", _multi_token_with(lambda t, n, j: t - n + j))
+    _fails(tm.test_full_prefill_is_causal_sdpa, 8, 2, 16)
+
+
+def test_chunk_positions_from_the_start_are_caught(monkeypatch):
+    from tests import test_oracle_multi_token as tm
+    monkeypatch.setattr(attention, "multi_token", _multi_token_with(lambda t, n, j: j + 1))
+    _fails(tm.test_chunk_after_cached_context_matches_masked_sdpa)
