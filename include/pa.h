@@ -283,6 +283,33 @@ int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const vo
                        float scale, int32_t partition_tokens, void* out, void* workspace,
                        uint64_t workspace_bytes, void* stream);
 
+/* Multi-token paged attention: causal attention for several new query
+ * tokens per sequence, i.e. prefill chunks and decode tokens mixed in one
+ * batch (youngju.dev page, section "핵심 원리: KV 캐시란 무엇인가": a token's
+ * query meets the keys and values of itself and all earlier tokens; iq-blog
+ * ch.4: the scheduler mixes prefill and decode requests in one batch).
+ *   query_start  HOST int32 [num_seqs + 1], query_start[0] = 0, non-decreasing:
+ *                sequence i owns query rows query_start[i] .. query_start[i+1]-1,
+ *                its last n_i = query_start[i+1] - query_start[i] tokens
+ *                (n_i = 0: nothing; 1: a decode token; more: a prefill chunk)
+ *   q, out       device fp16 [query_start[num_seqs]][num_q_heads][head_dim]
+ *                (16- and 8-byte aligned)
+ *   block_tables, max_blocks, context_lens, scale  as in pa_decode; the K/V
+ *                of every query token must already be in the pool
+ *                (pa_write_kv), and T_i >= n_i
+ * Row j of sequence i (0-based) sits at position T_i - n_i + j and attends
+ * to tokens 0 .. T_i - n_i + j through the block table.  A sequence with
+ * T_i < n_i or T_i > max_blocks*block_size sets PA_DEV_BAD_LEN and its rows
+ * are zeros.  workspace: device memory of pa_multi_token_workspace_bytes()
+ * bytes (16 per tile of query tokens), 16-byte aligned; the library uploads
+ * its work list there on `stream` from pinned host memory it owns. */
+int pa_multi_token_workspace_bytes(const pa_pool* pool, const int32_t* query_start, int32_t num_seqs,
+                                   int32_t num_q_heads, uint64_t* bytes_out);
+int pa_multi_token_attention(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                             const int32_t* query_start, const int32_t* block_tables, int32_t max_blocks,
+                             const int32_t* context_lens, int32_t num_seqs, float scale, void* out,
+                             void* workspace, uint64_t workspace_bytes, void* stream);
+
 /* Host helper: order_out[0..n) = indices of lens[0..n) by decreasing length,
  * equal lengths in increasing index (a stable sort), for pa_decode's seq_order. */
 int pa_order_longest_first(const int32_t* lens, int32_t n, int32_t* order_out);

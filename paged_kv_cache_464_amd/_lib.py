@@ -58,6 +58,9 @@ SIGNATURES = {
     "pa_pool_set_free_order": (C.c_int, [_P, _PI32, _I32]),
     "pa_pool_bind": (C.c_int, [_P, _P, C.POINTER(C.c_float), C.POINTER(C.c_float)]),
     "pa_pool_bind_int8": (C.c_int, [_P, _P, C.POINTER(C.c_float), C.POINTER(C.c_float), _PI32, _PI32]),
+    "pa_multi_token_workspace_bytes": (C.c_int, [_P, _PI32, _I32, _I32, C.POINTER(C.c_uint64)]),
+    "pa_multi_token_attention": (C.c_int, [_P, _I32, _P, _I32, _PI32, _P, _I32, _P, _I32, C.c_float, _P, _P,
+                                           C.c_uint64, _P]),
     "pa_seq_create": (C.c_int, [_P, _PI32]),
     "pa_seq_create_cached": (C.c_int, [_P, _PI32, _I32, _PI32, _PI32, _PI32]),
     "pa_alloc": (C.c_int, [_P, _I32, _I32, _PI32, _PI32, _P]),

@@ -58,6 +58,11 @@ struct pa_pool {
   std::vector<hipEvent_t> ev;  // 4 per record: decode start/end, reduce start/end (if any)
   std::vector<int8_t> has_reduce;
   int32_t n_records = 0;
+  // multi-token work items: pinned host staging (reused once the event of
+  // the upload that last read it has completed)
+  int32_t* mt_host = nullptr;
+  size_t mt_cap = 0;  // int32 entries
+  hipEvent_t mt_done = nullptr;
 
   pa_pool(int32_t L, int32_t H, int32_t D, int32_t B, int32_t dt, int32_t N)
       : layers(L), kv_heads(H), head_dim(D), block_size(B), dtype(dt), num_blocks(N),
@@ -70,6 +75,11 @@ struct pa_pool {
   }
   ~pa_pool() {
     for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    if (mt_done) {
+      (void)hipEventSynchronize(mt_done);
+      (void)hipEventDestroy(mt_done);
+    }
+    if (mt_host) (void)hipHostFree(mt_host);
   }
 };
 
@@ -575,6 +585,126 @@ int pa_write_kv_decode(pa_pool* p, int32_t layer, const void* k_new, const void*
   nt.slots = slot_mapping;
   return run_decode(p, layer, q, num_q_heads, block_tables, max_blocks, context_lens, num_seqs,
                     seq_order, scale, partition_tokens, out, workspace, workspace_bytes, stream, 0, nt);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Work items of a multi-token launch: for every sequence with query tokens,
+// tiles of multi_token_tile(G) tokens, the later tiles (which see more keys)
+// first.  Returns the number of items, or -1 after fail() for a bad
+// query_start.
+int64_t multi_token_items(const pa_pool* p, const int32_t* query_start, int32_t num_seqs, int32_t group,
+                          std::vector<int32_t>* items) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID, "num_seqs %d < 0", num_seqs), -1;
+  if (num_seqs > 0 && !query_start) return fail(PA_ERR_INVALID, "query_start is NULL"), -1;
+  if (num_seqs > 0 && query_start[0] != 0) return fail(PA_ERR_INVALID, "query_start[0] must be 0"), -1;
+  const int tq = pa::multi_token_tile(group);
+  int64_t n_items = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t n_i = static_cast<int64_t>(query_start[i + 1]) - query_start[i];
+    if (n_i < 0) return fail(PA_ERR_INVALID, "query_start decreases at sequence %d", i), -1;
+    n_items += (n_i + tq - 1) / tq;
+  }
+  if (items) {
+    items->clear();
+    items->reserve(static_cast<size_t>(4 * n_items));
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int32_t n_i = query_start[i + 1] - query_start[i];
+      for (int32_t t = (n_i + tq - 1) / tq - 1; t >= 0; --t) {
+        items->push_back(i);
+        items->push_back(t * tq);
+        items->push_back(query_start[i] + t * tq);
+        items->push_back(n_i);
+      }
+    }
+  }
+  (void)p;
+  return n_items;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_multi_token_workspace_bytes(const pa_pool* p, const int32_t* query_start, int32_t num_seqs,
+                                   int32_t num_q_heads, uint64_t* bytes_out) {
+  if (!p || !bytes_out) return fail(PA_ERR_INVALID, "NULL argument");
+  if (num_q_heads < 1 || num_q_heads % p->kv_heads != 0 || num_q_heads / p->kv_heads > 32)
+    return fail(PA_ERR_INVALID, "num_q_heads %d must be a multiple of kv_heads %d with a group of at most 32",
+                num_q_heads, p->kv_heads);
+  const int64_t n = multi_token_items(p, query_start, num_seqs, num_q_heads / p->kv_heads, nullptr);
+  if (n < 0) return PA_ERR_INVALID;
+  *bytes_out = static_cast<uint64_t>(n) * 16;
+  return PA_OK;
+}
+
+int pa_multi_token_attention(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
+                             const int32_t* query_start, const int32_t* block_tables, int32_t max_blocks,
+                             const int32_t* context_lens, int32_t num_seqs, float scale, void* out,
+                             void* workspace, uint64_t workspace_bytes, void* stream) {
+  int rc = check_decode_args(p, layer, q, block_tables, context_lens, num_seqs, scale);
+  if (rc) return rc;
+  if (num_q_heads < 1 || num_q_heads % p->kv_heads != 0 || num_q_heads / p->kv_heads > 32)
+    return fail(PA_ERR_INVALID, "num_q_heads %d must be a multiple of kv_heads %d with a group of at most 32",
+                num_q_heads, p->kv_heads);
+  if (max_blocks < 1 || static_cast<int64_t>(max_blocks) * p->block_size > 0x7FFFFFFF)
+    return fail(PA_ERR_INVALID, "max_blocks %d out of range", max_blocks);
+  std::vector<int32_t> items;
+  const int64_t n_items = multi_token_items(p, query_start, num_seqs, num_q_heads / p->kv_heads, &items);
+  if (n_items < 0) return PA_ERR_INVALID;
+  if (n_items == 0) return PA_OK;
+  if (!out) return fail(PA_ERR_INVALID, "out is NULL");
+  if (misaligned(out, 8)) return fail(PA_ERR_INVALID, "out must be 8-byte aligned");
+  const uint64_t need = static_cast<uint64_t>(n_items) * 16;
+  if (!workspace || workspace_bytes < need || misaligned(workspace, 16))
+    return fail(PA_ERR_INVALID, "a 16-byte aligned workspace of %llu bytes is needed",
+                static_cast<unsigned long long>(need));
+  if (n_items * p->kv_heads > 0x7FFFFFFF) return fail(PA_ERR_INVALID, "too many query tiles");
+  auto s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p->mt_done) {
+    e = hipEventSynchronize(p->mt_done);  // the staging buffer's last upload has been read
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  } else {
+    e = hipEventCreateWithFlags(&p->mt_done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  if (p->mt_cap < items.size()) {
+    if (p->mt_host) (void)hipHostFree(p->mt_host);
+    p->mt_host = nullptr;
+    p->mt_cap = 0;
+    e = hipHostMalloc(reinterpret_cast<void**>(&p->mt_host), items.size() * sizeof(int32_t), hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(work items)");
+    p->mt_cap = items.size();
+  }
+  std::memcpy(p->mt_host, items.data(), items.size() * sizeof(int32_t));
+  e = hipMemcpyAsync(workspace, p->mt_host, need, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work items)");
+  e = hipEventRecord(p->mt_done, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  pa::DecodeLaunch d{};
+  d.layer = layer;
+  d.q = q;
+  d.tables = block_tables;
+  d.lens = context_lens;
+  d.out = out;
+  d.num_seqs = num_seqs;
+  d.num_q_heads = num_q_heads;
+  d.max_blocks = max_blocks;
+  d.scale = scale;
+  d.work = static_cast<const int32_t*>(workspace);
+  d.num_items = static_cast<int>(n_items);
+  const bool rec = p->profiling && p->launches++ % p->every == 0 && p->n_records < p->max_records;
+  hipEvent_t* ev = rec ? &p->ev[4 * static_cast<size_t>(p->n_records)] : nullptr;
+  e = pa::launch_multi_token(p->geom, d, s, rec ? ev[0] : nullptr, rec ? ev[1] : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "multi-token launch");
+  if (rec) {
+    p->has_reduce[p->n_records] = 0;
+    ++p->n_records;
+  }
+  return PA_OK;
 }
 
 int pa_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream) {

@@ -132,8 +132,10 @@ struct StepRegs {
 // The per-wave engine: operands, softmax state and the load / compute of one
 // 16-token step of one (sequence, KV head).  Lane (gq, n): gq = lane / 16 is
 // its row group, n = lane % 16 its head column.  FUSE: the launch also
-// stores each unit's new token (the fused scatter).
-template <int KIND, int BS, int NT, bool FUSE>
+// stores each unit's new token (the fused scatter).  MULTI: the columns are
+// (query token, head) pairs of several new tokens of one sequence, each with
+// its own causal limit (multi-token attention).
+template <int KIND, int BS, int NT, bool FUSE, bool MULTI = false>
 struct WaveDecoder {
   static constexpr int ELEM = kind_bytes(KIND);
   static constexpr int kElem = ELEM;
@@ -143,6 +145,11 @@ struct WaveDecoder {
   static constexpr int NLD = StepRegs<ELEM>::kLoads;
 
   int gq, n, T, max_blocks, num_blocks;
+  // MULTI: keys visible to this lane's column of each tile (its position + 1)
+  // and the smallest limit of the wave's columns; the query rows of the
+  // columns start at mt_row0 (column c: token c / group, head c % group) and
+  // columns at or past mt_ncols are padding.
+  int lim[NT], lim_min, mt_row0, mt_ncols;
   uint64_t block_stride;
   const ConstI32* trow;
   const uint8_t* kbase;
@@ -232,8 +239,14 @@ struct WaveDecoder {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int col = nt * 16 + n;
-      const bool valid = col < group;
+      bool valid = col < group;
       const _Float16* qh = qs + static_cast<int64_t>(kvh * group + (valid ? col : 0)) * kD;
+      if constexpr (MULTI) {
+        valid = col < mt_ncols;
+        const int c = valid ? col : 0;
+        qh = static_cast<const _Float16*>(p.q) +
+             ((static_cast<int64_t>(mt_row0) + c / group) * p.num_q_heads + kvh * group + c % group) * kD;
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int dim0 = (ELEM == 2) ? (u * 4 + gq) * 8 : ((u >> 1) * 4 + gq) * 16 + (u & 1) * 8;
@@ -471,6 +484,8 @@ struct WaveDecoder {
 
   // Moves column tile nt's reference to m_new, rescaling what it holds.
   __device__ void rescale(int nt, float m_new) {
+    // MULTI: a column with nothing visible yet keeps its empty state.
+    if (MULTI && m_new == -__builtin_inff()) return;
     const float alpha = fast_exp2(m_run[nt] - m_new);
     l_part[nt] *= alpha;
 #pragma unroll
@@ -495,9 +510,13 @@ struct WaveDecoder {
     // S^T = K Q^T
     f32x4 s[NT];
     raw_scores(r.k, s);
-    // Scores of tokens tb + 4*gq + e for head column n; mask the tail.
-    const bool tail = tb + 16 > T;
-    const int valid_here = T - (tb + 4 * gq);  // tokens of this lane's 4 that exist
+    // Scores of tokens tb + 4*gq + e for head column n; mask the tail (MULTI:
+    // each column's causal limit).  vtail / valid_here: tokens of this lane's
+    // 4 that exist (for the V mask).
+    const bool vtail = tb + 16 > T;
+    const int valid_here = T - (tb + 4 * gq);
+    const bool tail = MULTI ? tb + 16 > lim_min : vtail;
+    auto valid_col = [&](int nt) { return MULTI ? lim[nt] - (tb + 4 * gq) : valid_here; };
     if constexpr (kLazy) {
       // The reference moves only when a score exceeds it by kRescaleSlack or
       // more, so exponentials stay below 2^kRescaleSlack (exact in fp16 and
@@ -506,7 +525,7 @@ struct WaveDecoder {
       bool need = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float m = scale_mask(s[nt], tail, valid_here);
+        const float m = scale_mask(s[nt], tail, valid_col(nt));
         m_true[nt] = fmaxf(m_true[nt], m);
         need |= m - m_run[nt] >= kRescaleSlack;
       }
@@ -526,7 +545,7 @@ struct WaveDecoder {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float x = s[nt][e] * qk_mul;
-          if (tail && e >= valid_here) x = -__builtin_inff();
+          if (tail && e >= valid_col(nt)) x = -__builtin_inff();
           s[nt][e] = x;
         }
         const float m = max_across_rows(fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3])));
@@ -542,8 +561,11 @@ struct WaveDecoder {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float pe[4];
+      // MULTI: a column may have seen only masked keys so far (reference
+      // -inf); its scores here are all -inf too and must give 0, not NaN.
+      const float mref = (MULTI && m_run[nt] == -__builtin_inff()) ? 0.0f : m_run[nt];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(s[nt][e] - m_run[nt]);
+      for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(s[nt][e] - mref);
       l_part[nt] += (pe[0] + pe[1]) + (pe[2] + pe[3]);
       pop[nt] = f16x4{(_Float16)pe[0], (_Float16)pe[1], (_Float16)pe[2], (_Float16)pe[3]};
     }
@@ -555,7 +577,7 @@ struct WaveDecoder {
     }
     // Unused slots of the last block may hold anything (NaN included): zero them,
     // since 0 * NaN would poison the product.
-    if (tail) {
+    if (vtail) {
       const int vc = valid_here < 0 ? 0 : (valid_here > 4 ? 4 : valid_here);
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
@@ -966,6 +988,87 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
   }
 }
 
+// Causal attention of a tile of new query tokens of one sequence over its
+// paged context, for one KV head (youngju.dev "KV cache and paged
+// attention", section "핵심 원리: KV 캐시란 무엇인가": a token's query meets
+// the keys and values of itself and every earlier token; iq-blog ch.4: the
+// scheduler mixes prefill chunks and decode tokens in one batch).
+// Workgroup = (work item, KV head): the item's nq <= multi_token_tile(G)
+// tokens j0 .. j0+nq-1 of its sequence, whose n_i query tokens are the last
+// n_i of its T_i; token j sits at position T_i - n_i + j and sees that many
+// keys plus one.  Columns are (token, head) pairs, 32 per wave (two MFMA
+// tiles); the four waves take key steps w, w+4, ... of the keys the tile's
+// last token sees and merge as in a single-pass decode.  Every key tile is
+// loaded once per workgroup; tiles of one sequence re-read the same keys
+// through the caches.
+template <int KIND, int BS>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
+  constexpr int NT = 2;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = p.num_q_heads / g.kv_heads;
+  const int tq = multi_token_tile(group);
+  const int item = static_cast<int>(blockIdx.x / g.kv_heads);
+  const int kvh = static_cast<int>(blockIdx.x % g.kv_heads);
+  const ConstI32* wk = (const ConstI32*)(p.work + 4 * static_cast<int64_t>(item));
+  const int seq = wk[0], j0 = wk[1], row0 = wk[2], n_i = wk[3];
+  auto raw_tok = [&](int j) -> int64_t { return 16ll * (w + kWaves * j); };
+  using Dec = WaveDecoder<KIND, BS, NT, false, true>;
+  Dec dec;
+  dec.bind(g, p, seq, kvh, lane);
+  FirstIds first;
+#pragma unroll
+  for (int j = 0; j < 2 * kDepth - 1; ++j) dec.fetch_ids(raw_tok(j), first.lo[j], first.hi[j]);
+  const int nq = (n_i - j0) < tq ? (n_i - j0) : tq;
+  const int ncols = nq * group;
+  int T = p.lens[seq];
+  if (T < n_i || T > p.max_blocks * BS) {
+    // The context must hold the sequence's query tokens: flag it and give
+    // the tile's rows a defined output of zeros.
+    if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
+    for (int i = threadIdx.x; i < ncols * kD; i += kWaves * 64) {
+      const int col = i / kD;
+      static_cast<_Float16*>(p.out)[((static_cast<int64_t>(row0) + col / group) * p.num_q_heads + kvh * group +
+                                     col % group) * kD + i % kD] = 0;
+    }
+    return;
+  }
+  const int base = T - n_i + j0;  // position of token j0
+  const int kmax = base + nq;     // keys the tile's last token sees
+  dec.T = kmax;
+  dec.lim_min = base + 1;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = nt * 16 + dec.n;
+    dec.lim[nt] = col < ncols ? base + col / group + 1 : kmax;
+  }
+  dec.mt_row0 = row0;
+  dec.mt_ncols = ncols;
+  const int n = (kmax + 16 * kWaves - 1) / (16 * kWaves);
+  const int last_tok = ((kmax - 1) >> 4) << 4;
+  auto real = [&](int j) { return raw_tok(j) < kmax; };
+  auto tok_of = [&](int j) -> int { return real(j) ? static_cast<int>(raw_tok(j)) : last_tok; };
+  dec.load_q(g, p, seq, kvh, group);
+  dec.reset();
+  const int gq = dec.gq;
+  __shared__ MergeLds<NT> sm;
+  stream_steps(dec, n, tok_of, real, first, [](int) {});
+  if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
+  merge_waves(dec, sm, w, ncols, [&](int nt, int col, f32x4* acc, float, float L, float) {
+    (void)nt;
+    const float inv_l = dec.out_mul / L;
+    _Float16* po = static_cast<_Float16*>(p.out) +
+                   ((static_cast<int64_t>(row0) + col / group) * p.num_q_heads + kvh * group + col % group) * kD +
+                   4 * gq;
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const f32x4 a = acc[rr] * inv_l;
+      *reinterpret_cast<f16x4*>(po + rr * 16) = f16x4{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
+    }
+  });
+}
+
 // Log-sum-exp merge of the chunk partials of one (sequence, query head):
 // out = sum_c w_c o_c / sum_c w_c with w_c = l_c * 2^(m_c - max_c m_c).
 // One 256-thread workgroup per row: the four waves take every fourth chunk
@@ -1145,6 +1248,32 @@ hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s
     case kF16: return launch_decode_kind<kF16>(g, d, nt, s, t0, t1);
     case kF8: return launch_decode_kind<kF8>(g, d, nt, s, t0, t1);
     case kI8: return launch_decode_kind<kI8>(g, d, nt, s, t0, t1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int KIND>
+hipError_t launch_multi_token_kind(const PoolGeom& g, const DecodeLaunch& d, const dim3& grid, hipStream_t s,
+                                   hipEvent_t t0, hipEvent_t t1) {
+  const dim3 block(kWaves * 64);
+  switch (g.block_size) {
+    case 8: return launch_kernel(multi_token_kernel<KIND, 8>, grid, block, s, t0, t1, g, d);
+    case 16: return launch_kernel(multi_token_kernel<KIND, 16>, grid, block, s, t0, t1, g, d);
+    case 32: return launch_kernel(multi_token_kernel<KIND, 32>, grid, block, s, t0, t1, g, d);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_multi_token(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
+                              hipEvent_t t1) {
+  const int64_t wgs = static_cast<int64_t>(d.num_items) * g.kv_heads;
+  if (wgs <= 0) return hipSuccess;
+  if (!d.work || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(wgs));
+  switch (g.kind) {
+    case kF16: return launch_multi_token_kind<kF16>(g, d, grid, s, t0, t1);
+    case kF8: return launch_multi_token_kind<kF8>(g, d, grid, s, t0, t1);
+    case kI8: return launch_multi_token_kind<kI8>(g, d, grid, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }

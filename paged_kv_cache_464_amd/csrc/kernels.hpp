@@ -48,6 +48,11 @@ struct DecodeLaunch {
   const int32_t* tables;
   const int32_t* lens;
   const int32_t* order;  // optional [S]: workgroup order of the sequences (null: 0..S-1)
+  // Multi-token attention only: work items of four int32 (sequence, first
+  // query token j0 of the tile, its query row, the sequence's query count),
+  // one per workgroup and KV head.
+  const int32_t* work;
+  int num_items;
   // Optional fused scatter of each sequence's new token (null: none):
   // fp16 [S][Hkv][D] K and V of token T_i - 1, stored at new_slots[i].
   const void* k_new;
@@ -71,5 +76,11 @@ hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s
                          hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
                              hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// Causal attention of several query tokens per sequence (d.work, d.num_items;
+// d.q and d.out are [query rows][Hq][D]).
+hipError_t launch_multi_token(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
+                              hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// Query tokens per multi-token work item for a query-head group of `group`.
+__host__ __device__ inline int multi_token_tile(int group) { return group > 16 ? 1 : 32 / group; }
 
 }  // namespace pa

@@ -340,6 +340,42 @@ def pa_write_kv_decode(h, layer, k_new, v_new, slot_mapping, q, block_tables, co
     return out
 
 
+def pa_multi_token_workspace_bytes(h, query_start, num_q_heads):
+    qs, qsp = _i32_host(query_start)
+    b = C.c_uint64()
+    _check(_L().pa_multi_token_workspace_bytes(C.c_void_p(h), qsp, len(qs) - 1, int(num_q_heads), C.byref(b)))
+    return b.value
+
+
+def pa_multi_token_attention(h, layer, q, query_start, block_tables, context_lens, out=None, scale=None,
+                             workspace=None, stream=None):
+    """Causal attention of query rows q [N][Hq][d]: sequence i owns rows
+    query_start[i] .. query_start[i+1]-1 (host ints), its last tokens."""
+    info = _info(h)
+    qs, qsp = _i32_host(query_start)
+    s = len(qs) - 1
+    if q.dim() != 3 or q.shape[2] != info["head_dim"] or q.shape[0] != int(qs[-1]):
+        raise ValueError(f"q must be [query_start[-1]][num_q_heads][{info['head_dim']}]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    hq, mb = int(q.shape[1]), int(block_tables.shape[1])
+    qp = _dev(q, torch.float16, None, "q")
+    tp = _dev(block_tables, torch.int32, None, "block_tables")
+    lp = _dev(context_lens, torch.int32, (s,), "context_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    op = _dev(out, torch.float16, tuple(q.shape), "out")
+    need = pa_multi_token_workspace_bytes(h, qs, hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wp = _dev(workspace, torch.uint8, None, "workspace")
+    if scale is None:
+        scale = 1.0 / math.sqrt(info["head_dim"])
+    _check(_L().pa_multi_token_attention(C.c_void_p(h), int(layer), qp, hq, qsp, tp, mb, lp, s, float(scale),
+                                         op, wp, workspace.numel(), _stream(stream)))
+    return out
+
+
 def pa_decode_partials(h, layer, q, block_tables, context_lens, partition_tokens, scale=None,
                        workspace=None, stream=None, seq_order=None):
     """Returns (m, l, o) views into the workspace: [S][Hq][C], [S][Hq][C], [S][Hq][C][d]."""
@@ -496,6 +532,9 @@ class PagedKVPool:
 
     def decode(self, layer, q, block_tables, context_lens, **kw):
         return pa_decode(self.handle, layer, q, block_tables, context_lens, **kw)
+
+    def multi_token_attention(self, layer, q, query_start, block_tables, context_lens, **kw):
+        return pa_multi_token_attention(self.handle, layer, q, query_start, block_tables, context_lens, **kw)
 
     def write_kv_decode(self, layer, k_new, v_new, slot_mapping, q, block_tables, context_lens, **kw):
         return pa_write_kv_decode(self.handle, layer, k_new, v_new, slot_mapping, q, block_tables,
