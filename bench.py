@@ -58,7 +58,9 @@ CPU_SAMPLE_TOKENS = 1 << 18  # bound on the context tokens the CPU oracle is giv
 BENCH_WORKLOADS = ["gqa_32x4096", "tiny", "cb_prefix", "long_ctx",
                    "fp8_gqa_bs8", "fp8_gqa_bs16", "fp8_gqa_bs32",
                    "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32", "int8_gqa_bs16", "int8_mqa_bs16",
-                   "prefix_cache", "beam_k5"]
+                   "prefix_cache", "beam_k5", "prefill_chunks", "mixed_batch"]
+MULTI_TOKEN_WORKLOADS = ("prefill_chunks", "mixed_batch")
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 
 
 def kernel_source_hash() -> str:
@@ -450,6 +452,187 @@ class DecodeBench:
         }
 
 
+class MultiTokenBench:
+    """Multi-token attention over a fixed batch: sequence i's last n_i tokens
+    are queries (a prefill chunk, or one decode token).  A step runs, R times
+    over rotating pool copies, the scatter of the query tokens' K/V
+    (pa_write_kv; the same values each step, so the contexts stay fixed) and
+    one multi-token attention launch."""
+
+    def __init__(self, name, args):
+        import torch
+
+        from paged_kv_cache_464_amd import pa
+        from workloads import free_order, normal_fp16, workload
+
+        self.torch, self.pa = torch, pa
+        self.name = name
+        w = self.w = workload(name)
+        self.dev = "cuda"
+        self.S, self.hq, self.hkv, self.bs = w.num_seqs, w.q_heads, w.kv_heads, w.block_size
+        self.fp8 = self.int8 = False
+        self.elem = 2
+        self.separate_write = True
+        self.partition = 0
+        self.R = w.repeats
+        self.lens = np.asarray(w.context, dtype=np.int64)
+        self.nq = np.asarray(w.extra["queries"], dtype=np.int64)
+        layer_bytes = 2 * w.num_blocks * self.hkv * self.bs * 128 * self.elem
+        self.copies = max(1, -(-(4 * LLC_BYTES) // layer_bytes))
+        self.num_blocks = w.num_blocks
+        self.pool = pa.PagedKVPool(self.copies, self.hkv, 128, self.bs, self.num_blocks, "fp16",
+                                   free_order=free_order(w.seed, self.num_blocks))
+        self.seqs, slots = [], []
+        for t in self.lens:
+            s = self.pool.seq_create()
+            slots.append(self.pool.alloc(s, int(t))[0])
+            self.seqs.append(s)
+        n_rows = int(self.lens.sum())
+        k0 = normal_fp16((n_rows, self.hkv, 128), w.seed, 10_000, self.dev)
+        v0 = normal_fp16((n_rows, self.hkv, 128), w.seed, 10_001, self.dev)
+        slot_all = torch.from_numpy(np.concatenate(slots).astype(np.int32)).to(self.dev)
+        for c in range(self.copies):
+            self.pool.write_kv(c, k0, v0, slot_all)
+        offs = np.concatenate([[0], np.cumsum(self.lens)])
+        new_idx = np.concatenate([np.arange(offs[i] + self.lens[i] - self.nq[i], offs[i + 1])
+                                  for i in range(self.S)]).astype(np.int64)
+        idx = torch.from_numpy(new_idx).to(self.dev)
+        self.new_slots = slot_all[idx].contiguous()
+        self.k_new, self.v_new = k0[idx].contiguous(), v0[idx].contiguous()
+        self.qs = np.concatenate([[0], np.cumsum(self.nq)]).astype(np.int32)
+        n_q = int(self.qs[-1])
+        self.q = normal_fp16((self.R, n_q, self.hq, 128), w.seed, 1, self.dev)
+        self.out = torch.empty_like(self.q)
+        mb = int(-(-self.lens.max() // self.bs))
+        tables, lens = self.pool.block_tables(self.seqs, mb)
+        self.tables_np = tables
+        self.tables_d = torch.from_numpy(tables).to(self.dev)
+        self.lens_d = torch.from_numpy(lens).to(self.dev)
+        need = pa.pa_multi_token_workspace_bytes(self.pool.handle, self.qs, self.hq)
+        self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=self.dev)
+        # Algorithmic work of one launch: every (query row, head) meets the
+        # keys up to its position (QK^T and PV: 4 d flops per key); every
+        # sequence's visible K and V are read once.
+        visible = sum(int(((self.lens[i] - self.nq[i] + 1) + self.lens[i]) * self.nq[i] // 2)
+                      for i in range(self.S))
+        self.flops = float(visible) * self.hq * 4 * 128
+        self.kv_bytes = int(self.lens.sum()) * 2 * self.hkv * 128 * self.elem
+        # Host copies of the first sequences' K/V for the CPU oracle.
+        self.sample_n = min(self.S, 4)
+        self.sample = (k0[:offs[self.sample_n]].cpu().numpy(), v0[:offs[self.sample_n]].cpu().numpy())
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.kv_bytes_log, self.unique_bytes_log, self.lens_log = [], [], []
+        del k0, v0
+        torch.cuda.synchronize()
+
+    def step(self):
+        pa, h, st = self.pa, self.pool.handle, self.stream
+        for r in range(self.R):
+            layer = r % self.copies
+            pa.pa_write_kv(h, layer, self.k_new, self.v_new, self.new_slots, stream=st)
+            pa.pa_multi_token_attention(h, layer, self.q[r], self.qs, self.tables_d, self.lens_d,
+                                        out=self.out[r], workspace=self.workspace, stream=st)
+        self.kv_bytes_log.append(self.kv_bytes)
+        self.lens_log.append(self.lens)
+
+    def cpu_baseline(self, budget_s):
+        """fp64 oracle multi-token attention (as it stands) on the first
+        sequences of pool copy 0, one sequence at a time until about
+        ``budget_s`` seconds, scaled by algorithmic flops to one step."""
+        from oracle import attention
+        from oracle.kvstore import OracleKVStore
+
+        k_all, v_all = self.sample
+        st = OracleKVStore(1, self.num_blocks, self.hkv, self.bs, 128, "fp16")
+        off = 0
+        for i in range(self.sample_n):
+            t = np.arange(self.lens[i])
+            slots = self.tables_np[i][t // self.bs].astype(np.int64) * self.bs + t % self.bs
+            st.write(0, k_all[off:off + len(t)], v_all[off:off + len(t)], slots)
+            off += len(t)
+        q0 = self.q[0].cpu().numpy()
+        done, t_total, work = 0, 0.0, 0.0
+        while t_total < budget_s and done < self.sample_n:
+            i = done
+            rows = slice(int(self.qs[i]), int(self.qs[i + 1]))
+            t0 = time.perf_counter()
+            attention.multi_token(st, 0, q0[rows], [0, int(self.nq[i])], self.tables_np[i:i + 1],
+                                  [int(self.lens[i])])
+            t_total += time.perf_counter() - t0
+            work += float(((self.lens[i] - self.nq[i] + 1) + self.lens[i]) * self.nq[i] // 2) * self.hq * 4 * 128
+            done += 1
+        step_s = t_total * (self.flops * self.R / work)
+        return {
+            "value": int(self.qs[-1]) / step_s,
+            "unit": "query tokens/s",
+            "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": (f"pool copy 0, the first {done} sequences' query rows ({work / 1e9:.1f} GFLOP of "
+                       f"attention, {t_total:.1f} s of fp64 numpy), scaled by algorithmic flops to all "
+                       f"{self.S} sequences and x{self.R} launches per step"),
+            "gflops": work / t_total / 1e9,
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model(),
+        }
+
+
+def multi_token_result(bench, args, elapsed, prof, stream_gbps, cpu):
+    """The JSON line of a multi-token workload.  The roofline is priced on
+    whichever of MFMA flops and HBM bytes bounds the launch at peak."""
+    n_launch = max(prof["decode_launches"], 1)
+    launch_s = prof["decode_ms"] / 1e3 / n_launch
+    tflops = bench.flops / launch_s / 1e12
+    gbps = bench.kv_bytes / launch_s / 1e9
+    t_mfma = bench.flops / (MFMA_FP16_PEAK_TFLOPS * 1e12)
+    t_hbm = bench.kv_bytes / (HBM_PEAK_GBPS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / MFMA_FP16_PEAK_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS}
+    w = bench.w
+    n_q = int(bench.qs[-1])
+    roof.update({
+        "traffic": None,
+        "kernel": (f"multi-token paged attention (per launch: {n_q} query rows x {bench.hq} heads, "
+                   f"causal over {int(bench.lens.sum())} context tokens of {bench.S} sequences)"),
+        "algorithmic_flops_per_launch": bench.flops,
+        "algorithmic_bytes_per_launch": bench.kv_bytes,
+        "timed_launches": prof["decode_launches"],
+        "kernel_source": kernel_source_hash(),
+    })
+    return {
+        "metric": METRIC,
+        "value": n_q * args.steps / elapsed,
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": bench.name, "layers": w.layers, "launches_per_step": bench.R,
+            "pool_copies": bench.copies, "num_seqs": bench.S, "q_heads": bench.hq, "kv_heads": bench.hkv,
+            "head_dim": 128, "block_size": bench.bs, "kv_dtype": "fp16", "accumulate": "fp32",
+            "context_lens": sorted(set(int(t) for t in bench.lens)),
+            "query_tokens": {str(k): int((bench.nq == k).sum()) for k in sorted(set(bench.nq.tolist()))},
+            "step": f"{bench.R} x (write_kv of the {n_q} query tokens + multi-token attention)",
+        },
+        "attention_us": launch_s * 1e6,
+        "tflops": tflops,
+        "kv_gbps": gbps,
+        "stream_read_gbps": stream_gbps,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+
+
 def stream_read_gbps(torch, pa, gib=2, reps=5):
     """Rate of the library's streaming-read reference kernel over a fresh
     ``gib`` GiB buffer (beyond the 256 MB last-level cache): the practical
@@ -508,7 +691,8 @@ def main(argv=None):
         return 1
     torch.cuda.set_device(0)
 
-    bench = DecodeBench(args.workload, args)
+    multi = args.workload in MULTI_TOKEN_WORKLOADS
+    bench = MultiTokenBench(args.workload, args) if multi else DecodeBench(args.workload, args)
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
@@ -536,6 +720,9 @@ def main(argv=None):
     # The CPU oracle runs after the timed steps so that its BLAS threads cannot
     # compete with the host side of the step.
     cpu = None if args.no_cpu_baseline else bench.cpu_baseline(args.cpu_budget)
+    if multi:
+        print(json.dumps(multi_token_result(bench, args, elapsed, prof, stream_gbps, cpu)), flush=True)
+        return 0
 
     w = bench.w
     n_launch = max(prof["decode_launches"], 1)

@@ -302,7 +302,9 @@ int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const vo
  * T_i < n_i or T_i > max_blocks*block_size sets PA_DEV_BAD_LEN and its rows
  * are zeros.  workspace: device memory of pa_multi_token_workspace_bytes()
  * bytes (16 per tile of query tokens), 16-byte aligned; the library uploads
- * its work list there on `stream` from pinned host memory it owns. */
+ * its work list there on `stream` from pinned host memory it owns (a ring of
+ * 16 buffers: a call waits only for the upload made 16 calls earlier).  Calls
+ * that share a workspace must be on the same stream. */
 int pa_multi_token_workspace_bytes(const pa_pool* pool, const int32_t* query_start, int32_t num_seqs,
                                    int32_t num_q_heads, uint64_t* bytes_out);
 int pa_multi_token_attention(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,

@@ -58,11 +58,17 @@ struct pa_pool {
   std::vector<hipEvent_t> ev;  // 4 per record: decode start/end, reduce start/end (if any)
   std::vector<int8_t> has_reduce;
   int32_t n_records = 0;
-  // multi-token work items: pinned host staging (reused once the event of
-  // the upload that last read it has completed)
-  int32_t* mt_host = nullptr;
-  size_t mt_cap = 0;  // int32 entries
-  hipEvent_t mt_done = nullptr;
+  // multi-token work items: a ring of pinned host staging buffers, each
+  // reused once the event of the upload that last read it has completed (so
+  // the host can run several launches ahead of the device)
+  struct Staging {
+    int32_t* host = nullptr;
+    size_t cap = 0;  // int32 entries
+    hipEvent_t done = nullptr;
+  };
+  static constexpr int kStagingRing = 16;
+  Staging mt_ring[kStagingRing];
+  int mt_next = 0;
 
   pa_pool(int32_t L, int32_t H, int32_t D, int32_t B, int32_t dt, int32_t N)
       : layers(L), kv_heads(H), head_dim(D), block_size(B), dtype(dt), num_blocks(N),
@@ -75,11 +81,13 @@ struct pa_pool {
   }
   ~pa_pool() {
     for (hipEvent_t e : ev) (void)hipEventDestroy(e);
-    if (mt_done) {
-      (void)hipEventSynchronize(mt_done);
-      (void)hipEventDestroy(mt_done);
+    for (Staging& st : mt_ring) {
+      if (st.done) {
+        (void)hipEventSynchronize(st.done);
+        (void)hipEventDestroy(st.done);
+      }
+      if (st.host) (void)hipHostFree(st.host);
     }
-    if (mt_host) (void)hipHostFree(mt_host);
   }
 };
 
@@ -664,25 +672,27 @@ int pa_multi_token_attention(pa_pool* p, int32_t layer, const void* q, int32_t n
   if (n_items * p->kv_heads > 0x7FFFFFFF) return fail(PA_ERR_INVALID, "too many query tiles");
   auto s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (p->mt_done) {
-    e = hipEventSynchronize(p->mt_done);  // the staging buffer's last upload has been read
+  pa_pool::Staging& st = p->mt_ring[p->mt_next];
+  p->mt_next = (p->mt_next + 1) % pa_pool::kStagingRing;
+  if (st.done) {
+    e = hipEventSynchronize(st.done);  // this buffer's last upload has been read
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
   } else {
-    e = hipEventCreateWithFlags(&p->mt_done, hipEventDisableTiming);
+    e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
   }
-  if (p->mt_cap < items.size()) {
-    if (p->mt_host) (void)hipHostFree(p->mt_host);
-    p->mt_host = nullptr;
-    p->mt_cap = 0;
-    e = hipHostMalloc(reinterpret_cast<void**>(&p->mt_host), items.size() * sizeof(int32_t), hipHostMallocDefault);
+  if (st.cap < items.size()) {
+    if (st.host) (void)hipHostFree(st.host);
+    st.host = nullptr;
+    st.cap = 0;
+    e = hipHostMalloc(reinterpret_cast<void**>(&st.host), items.size() * sizeof(int32_t), hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(work items)");
-    p->mt_cap = items.size();
+    st.cap = items.size();
   }
-  std::memcpy(p->mt_host, items.data(), items.size() * sizeof(int32_t));
-  e = hipMemcpyAsync(workspace, p->mt_host, need, hipMemcpyHostToDevice, s);
+  std::memcpy(st.host, items.data(), items.size() * sizeof(int32_t));
+  e = hipMemcpyAsync(workspace, st.host, need, hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work items)");
-  e = hipEventRecord(p->mt_done, s);
+  e = hipEventRecord(st.done, s);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   pa::DecodeLaunch d{};
   d.layer = layer;

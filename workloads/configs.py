@@ -70,6 +70,13 @@ WORKLOADS = {
     # request i takes system prompt i mod 4 plus its own U{64..1024} tokens.
     "prefix_cache": Workload(6, "prefix_cache", 1, 32, 8, 128, 16, "fp16", 16384, 256, repeats=32,
                              extra={"systems": 4, "system_tokens": 1024, "suffix": (64, 1024)}),
+    # Multi-token attention: 16 prompts of 2048 tokens whose last 512 form a
+    # prefill chunk (positions 1536..2047); and a mixed batch of 4 such chunks
+    # with 60 decode tokens at 2048-token contexts.
+    "prefill_chunks": Workload(9, "prefill_chunks", 1, 32, 8, 128, 16, "fp16", 16 * 2048 // 16, 16,
+                               context=(2048,) * 16, repeats=32, extra={"queries": (512,) * 16}),
+    "mixed_batch": Workload(10, "mixed_batch", 1, 32, 8, 128, 16, "fp16", 64 * 2048 // 16, 64,
+                            context=(2048,) * 64, repeats=32, extra={"queries": (512,) * 4 + (1,) * 60}),
     # Beam search, width 5: 32 prompts of 2040 tokens, each with 5 beams that
     # every step re-fork from the survivors (beam_parents) and append a token.
     "beam_k5": Workload(7, "beam_k5", 1, 32, 8, 128, 16, "fp16", 8192, 160, repeats=32,
