@@ -432,7 +432,10 @@ struct WaveDecoder {
     return b;
   }
 
+  // Nontemporal in decode (every tile is read once); plain loads in
+  // multi-token attention, whose waves re-read each other's key tiles.
   static __device__ u32x4 ld16(const uint8_t* a) {
+    if constexpr (MULTI) return *reinterpret_cast<const u32x4*>(a);
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
   }
 
@@ -993,80 +996,117 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
 // attention", section "핵심 원리: KV 캐시란 무엇인가": a token's query meets
 // the keys and values of itself and every earlier token; iq-blog ch.4: the
 // scheduler mixes prefill chunks and decode tokens in one batch).
-// Workgroup = (work item, KV head): the item's nq <= multi_token_tile(G)
-// tokens j0 .. j0+nq-1 of its sequence, whose n_i query tokens are the last
-// n_i of its T_i; token j sits at position T_i - n_i + j and sees that many
-// keys plus one.  Columns are (token, head) pairs, 32 per wave (two MFMA
-// tiles); the four waves take key steps w, w+4, ... of the keys the tile's
-// last token sees and merge as in a single-pass decode.  Every key tile is
-// loaded once per workgroup; tiles of one sequence re-read the same keys
-// through the caches.
+// Workgroup = (work item, KV head): up to multi_token_tile(G) tokens
+// j0, j0+1, ... of its sequence, whose n_i query tokens are the last n_i of
+// its T_i; token j sits at position T_i - n_i + j and sees that many keys
+// plus one.  Columns are (token, head) pairs, 32 per wave (two MFMA tiles),
+// i.e. tq = multi_token_wave_tile(G) tokens per wave.
+//  * wide (the item holds more than tq tokens): wave w takes tokens
+//    j0 + w*tq ... and streams every key they see on its own; the four
+//    waves read the same key tiles at about the same time, so three of the
+//    four reads hit the CU's cache (plain loads, not nontemporal ones);
+//  * split (at most tq tokens, e.g. a decode token): the four waves take key
+//    steps w, w+4, ... and merge in LDS, as the single-pass decode does.
+template <class Dec>
+__device__ inline void multi_token_setup(Dec& dec, int base, int nq, int group, int row0, int& kmax) {
+  const int ncols = nq * group;
+  kmax = base + nq;  // keys the last token sees
+  dec.T = kmax;
+  dec.lim_min = base + 1;
+#pragma unroll
+  for (int nt = 0; nt < Dec::kNT; ++nt) {
+    const int col = nt * 16 + dec.n;
+    dec.lim[nt] = col < ncols ? base + col / group + 1 : kmax;
+  }
+  dec.mt_row0 = row0;
+  dec.mt_ncols = ncols;
+}
+
+// fp16 output of a wave's (or a merge's) accumulators for column col.
+template <class Dec>
+__device__ inline void multi_token_store(const DecodeLaunch& p, const Dec& dec, const f32x4* acc, float inv_l,
+                                         int row0, int col, int kvh, int group) {
+  _Float16* po = static_cast<_Float16*>(p.out) +
+                 ((static_cast<int64_t>(row0) + col / group) * p.num_q_heads + kvh * group + col % group) * kD +
+                 4 * dec.gq;
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    const f32x4 a = acc[rr] * inv_l;
+    *reinterpret_cast<f16x4*>(po + rr * 16) = f16x4{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
+  }
+}
+
 template <int KIND, int BS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
   constexpr int NT = 2;
+  using Dec = WaveDecoder<KIND, BS, NT, false, true>;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = p.num_q_heads / g.kv_heads;
-  const int tq = multi_token_tile(group);
+  const int tq = multi_token_wave_tile(group);
   const int item = static_cast<int>(blockIdx.x / g.kv_heads);
   const int kvh = static_cast<int>(blockIdx.x % g.kv_heads);
   const ConstI32* wk = (const ConstI32*)(p.work + 4 * static_cast<int64_t>(item));
   const int seq = wk[0], j0 = wk[1], row0 = wk[2], n_i = wk[3];
-  auto raw_tok = [&](int j) -> int64_t { return 16ll * (w + kWaves * j); };
-  using Dec = WaveDecoder<KIND, BS, NT, false, true>;
-  Dec dec;
-  dec.bind(g, p, seq, kvh, lane);
-  FirstIds first;
-#pragma unroll
-  for (int j = 0; j < 2 * kDepth - 1; ++j) dec.fetch_ids(raw_tok(j), first.lo[j], first.hi[j]);
-  const int nq = (n_i - j0) < tq ? (n_i - j0) : tq;
-  const int ncols = nq * group;
+  const int nq_item = (n_i - j0) < kWaves * tq ? (n_i - j0) : kWaves * tq;
+  const bool wide = nq_item > tq;  // uniform over the workgroup
   int T = p.lens[seq];
   if (T < n_i || T > p.max_blocks * BS) {
     // The context must hold the sequence's query tokens: flag it and give
-    // the tile's rows a defined output of zeros.
+    // the item's rows a defined output of zeros.
     if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
-    for (int i = threadIdx.x; i < ncols * kD; i += kWaves * 64) {
+    for (int i = threadIdx.x; i < nq_item * group * kD; i += kWaves * 64) {
       const int col = i / kD;
       static_cast<_Float16*>(p.out)[((static_cast<int64_t>(row0) + col / group) * p.num_q_heads + kvh * group +
                                      col % group) * kD + i % kD] = 0;
     }
     return;
   }
-  const int base = T - n_i + j0;  // position of token j0
-  const int kmax = base + nq;     // keys the tile's last token sees
-  dec.T = kmax;
-  dec.lim_min = base + 1;
+  Dec dec;
+  dec.bind(g, p, seq, kvh, lane);
+  FirstIds first;
+  int kmax;
+  if (wide) {
+    const int jw = w * tq;  // this wave's first token within the item
+    if (jw >= nq_item) return;  // no tokens for this wave (no barrier on this path)
+    const int nq = (nq_item - jw) < tq ? (nq_item - jw) : tq;
+    auto raw_tok = [](int j) -> int64_t { return 16ll * j; };
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int col = nt * 16 + dec.n;
-    dec.lim[nt] = col < ncols ? base + col / group + 1 : kmax;
-  }
-  dec.mt_row0 = row0;
-  dec.mt_ncols = ncols;
-  const int n = (kmax + 16 * kWaves - 1) / (16 * kWaves);
-  const int last_tok = ((kmax - 1) >> 4) << 4;
-  auto real = [&](int j) { return raw_tok(j) < kmax; };
-  auto tok_of = [&](int j) -> int { return real(j) ? static_cast<int>(raw_tok(j)) : last_tok; };
-  dec.load_q(g, p, seq, kvh, group);
-  dec.reset();
-  const int gq = dec.gq;
-  __shared__ MergeLds<NT> sm;
-  stream_steps(dec, n, tok_of, real, first, [](int) {});
-  if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
-  merge_waves(dec, sm, w, ncols, [&](int nt, int col, f32x4* acc, float, float L, float) {
-    (void)nt;
-    const float inv_l = dec.out_mul / L;
-    _Float16* po = static_cast<_Float16*>(p.out) +
-                   ((static_cast<int64_t>(row0) + col / group) * p.num_q_heads + kvh * group + col % group) * kD +
-                   4 * gq;
+    for (int j = 0; j < 2 * kDepth - 1; ++j) dec.fetch_ids(raw_tok(j), first.lo[j], first.hi[j]);
+    multi_token_setup(dec, T - n_i + j0 + jw, nq, group, row0 + jw, kmax);
+    const int n = (kmax + 15) >> 4;
+    const int last_tok = ((kmax - 1) >> 4) << 4;
+    auto real = [&](int j) { return raw_tok(j) < kmax; };
+    auto tok_of = [&](int j) -> int { return real(j) ? static_cast<int>(raw_tok(j)) : last_tok; };
+    dec.load_q(g, p, seq, kvh, group);
+    dec.reset();
+    stream_steps(dec, n, tok_of, real, first, [](int) {});
+    if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const f32x4 a = acc[rr] * inv_l;
-      *reinterpret_cast<f16x4*>(po + rr * 16) = f16x4{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
+    for (int nt = 0; nt < NT; ++nt) {
+      const float l = sum_across_rows(dec.l_part[nt]);
+      const int col = nt * 16 + dec.n;
+      if (col < nq * group) multi_token_store(p, dec, dec.oacc[nt], dec.out_mul / l, row0 + jw, col, kvh, group);
     }
-  });
+  } else {
+    auto raw_tok = [&](int j) -> int64_t { return 16ll * (w + kWaves * j); };
+#pragma unroll
+    for (int j = 0; j < 2 * kDepth - 1; ++j) dec.fetch_ids(raw_tok(j), first.lo[j], first.hi[j]);
+    multi_token_setup(dec, T - n_i + j0, nq_item, group, row0, kmax);
+    const int n = (kmax + 16 * kWaves - 1) / (16 * kWaves);
+    const int last_tok = ((kmax - 1) >> 4) << 4;
+    auto real = [&](int j) { return raw_tok(j) < kmax; };
+    auto tok_of = [&](int j) -> int { return real(j) ? static_cast<int>(raw_tok(j)) : last_tok; };
+    dec.load_q(g, p, seq, kvh, group);
+    dec.reset();
+    __shared__ MergeLds<NT> sm;
+    stream_steps(dec, n, tok_of, real, first, [](int) {});
+    if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
+    merge_waves(dec, sm, w, nq_item * group, [&](int, int col, f32x4* acc, float, float L, float) {
+      multi_token_store(p, dec, acc, dec.out_mul / L, row0, col, kvh, group);
+    });
+  }
 }
 
 // Log-sum-exp merge of the chunk partials of one (sequence, query head):

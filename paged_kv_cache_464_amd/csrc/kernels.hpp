@@ -80,7 +80,10 @@ hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream
 // d.q and d.out are [query rows][Hq][D]).
 hipError_t launch_multi_token(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
                               hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
-// Query tokens per multi-token work item for a query-head group of `group`.
-__host__ __device__ inline int multi_token_tile(int group) { return group > 16 ? 1 : 32 / group; }
+// Query tokens of one multi-token wave (32 (token, head) columns) and of one
+// work item (a workgroup of four such waves), for a query-head group of
+// `group`.
+__host__ __device__ inline int multi_token_wave_tile(int group) { return group > 16 ? 1 : 32 / group; }
+__host__ __device__ inline int multi_token_tile(int group) { return 4 * multi_token_wave_tile(group); }
 
 }  // namespace pa
