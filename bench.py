@@ -72,12 +72,14 @@ def kernel_source_hash() -> str:
 
 
 def traffic_profile_path(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.txt")
+    kernel = "multi_token" if workload in MULTI_TOKEN_WORKLOADS else "decode"
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
 
 
 def stored_traffic(workload: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary
-    of this workload, if it was taken on the current kernel sources; else None."""
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary of this workload, if it was taken on the current kernel sources;
+    else None."""
     path = traffic_profile_path(workload)
     if not os.path.exists(path):
         return None
@@ -595,7 +597,7 @@ def multi_token_result(bench, args, elapsed, prof, stream_gbps, cpu):
     w = bench.w
     n_q = int(bench.qs[-1])
     roof.update({
-        "traffic": None,
+        "traffic": stored_traffic(bench.name),
         "kernel": (f"multi-token paged attention (per launch: {n_q} query rows x {bench.hq} heads, "
                    f"causal over {int(bench.lens.sum())} context tokens of {bench.S} sequences)"),
         "algorithmic_flops_per_launch": bench.flops,
@@ -720,10 +722,16 @@ def main(argv=None):
     # The CPU oracle runs after the timed steps so that its BLAS threads cannot
     # compete with the host side of the step.
     cpu = None if args.no_cpu_baseline else bench.cpu_baseline(args.cpu_budget)
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
     if multi:
         print(json.dumps(multi_token_result(bench, args, elapsed, prof, stream_gbps, cpu)), flush=True)
         return 0
-
     w = bench.w
     n_launch = max(prof["decode_launches"], 1)
     # Every launch of a step reads the same bytes; steps differ by one token
@@ -733,13 +741,6 @@ def main(argv=None):
     reduce_s = prof["reduce_ms"] / 1e3 / max(prof["reduce_launches"], 1)
     achieved = bytes_per_launch / decode_s / 1e9
     kv_gbps = bytes_per_launch / (decode_s + reduce_s) / 1e9
-    if args.calibrate_copy_mib:
-        n = args.calibrate_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
     first, last = bench.lens_log[0], bench.lens_log[-1]
     result = {
         "metric": METRIC,
