@@ -133,18 +133,42 @@ def test_long_context_sampled():
 
 
 @pytest.mark.parametrize("name", ["fp8_gqa_bs8", "fp8_gqa_bs16", "fp8_gqa_bs32",
-                                  "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32"])
-def test_fp8_sweep_sampled(name):
-    """64 x 8192 tokens, fp8 E4M3 K/V with per-KV-head scales, B in {8, 16, 32}."""
+                                  "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32",
+                                  "int8_gqa_bs16", "int8_mqa_bs16"])
+def test_quantized_sweep_sampled(name):
+    """64 x 8192 tokens, fp8 E4M3 K/V with per-KV-head scales (B in {8, 16,
+    32}) or int8 K/V with per-KV-head scales and zero points."""
     w = workload(name)
     say(name)
-    c = build_case(w.context, w.q_heads, w.kv_heads, w.block_size, w.num_blocks, w.seed, "fp8",
+    c = build_case(w.context, w.q_heads, w.kv_heads, w.block_size, w.num_blocks, w.seed, w.dtype,
                    poison=False)
     sample = [0, 40, 63]
     ref = oracle_decode(c, sample)
     for mode in (0, -1):
         out = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode)
-        assert_close(out[sample], ref, "fp8", f"{name} P={mode}")
+        assert_close(out[sample], ref, w.dtype, f"{name} P={mode}")
+    assert c.pool.device_status() == 0
+
+
+def test_prefill_chunks_full_size_sampled():
+    """16 prompts of 2048 tokens whose last 512 are one multi-token launch,
+    as the benchmark runs it; sampled rows against the oracle's decode of
+    their prefixes."""
+    w = workload("prefill_chunks")
+    say("prefill_chunks")
+    n = list(w.extra["queries"])
+    c = build_case(w.context, w.q_heads, w.kv_heads, w.block_size, w.num_blocks, w.seed, poison=False)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = normal_fp16((int(qs[-1]), w.q_heads, 128), w.seed, 1, "cuda")
+    out = c.pool.multi_token_attention(0, q, qs, c.tables, c.lens_dev)
+    rows = [0, 31, 32, 511, 512 * 7 + 100, 512 * 15, int(qs[-1]) - 1]
+    seq_of = np.searchsorted(qs, rows, side="right") - 1
+    st = oracle_for(c, sorted(set(seq_of.tolist())))
+    qh = q.cpu().numpy()
+    for r, i in zip(rows, seq_of):
+        pos = w.context[i] - n[i] + (r - qs[i])
+        ref = attention.decode(st, 0, qh[r:r + 1], c.tables_np[i:i + 1], [pos + 1])
+        assert_close(out[r:r + 1], ref, "fp16", f"row {r} (seq {i}, position {pos})")
     assert c.pool.device_status() == 0
 
 
