@@ -323,3 +323,22 @@ def test_beam_search_fork_trees_bit_exact(bs):
         _same_state(h, o)
     assert cows > 50 and o.stats()["shared_blocks"] > 0
     pa.pa_pool_destroy(h)
+
+
+def test_multi_token_work_list_size_and_checks():
+    """Host side of multi-token attention (no GPU): one 16-byte work item per
+    tile of up to 4 * 32 / G query tokens of a sequence (4 tokens when G > 16),
+    and the query_start checks."""
+    h = pa.pa_pool_create(1, 8, 128, 16, pa.PA_DTYPE_FP16, 64)
+    qs = [0, 1, 33, 33, 100]  # 1, 32, 0 and 67 query tokens
+    assert pa.pa_multi_token_workspace_bytes(h, qs, 32) == 16 * (1 + 1 + 0 + 3)   # G = 4: 32 per tile
+    assert pa.pa_multi_token_workspace_bytes(h, qs, 8) == 16 * (1 + 1 + 0 + 1)    # G = 1: 128 per tile
+    assert pa.pa_multi_token_workspace_bytes(h, qs, 256) == 16 * (1 + 8 + 0 + 17)  # G = 32: 4 per tile
+    assert pa.pa_multi_token_workspace_bytes(h, [0], 32) == 0
+    for bad_qs, hq in (([0, 5, 3], 32), ([1, 5], 32), ([0, 5], 12), ([0, 5], 8 * 33)):
+        with pytest.raises(pa.PAError):
+            pa.pa_multi_token_workspace_bytes(h, bad_qs, hq)
+    pa.pa_pool_destroy(h)
+    h1 = pa.pa_pool_create(1, 1, 128, 16, pa.PA_DTYPE_FP16, 64)
+    assert pa.pa_multi_token_workspace_bytes(h1, [0, 24, 25], 24) == 16 * (6 + 1)  # G = 24: 4 per tile
+    pa.pa_pool_destroy(h1)
