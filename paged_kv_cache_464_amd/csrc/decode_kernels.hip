@@ -441,6 +441,8 @@ struct WaveDecoder {
 
   // Loads of the step starting at token tb, whose blocks are id_lo (and
   // id_hi, the block of its second 8 tokens when blocks hold 8).
+  // DO_K / DO_V: load only the K or only the V tile (multi-token pairs).
+  template <bool DO_K = true, bool DO_V = true>
   __device__ void issue(StepRegs<ELEM>& r, int tb, int id_lo, int id_hi) {
     if constexpr (BS == 8) {
       const int b0 = phys_ok(id_lo);
@@ -450,8 +452,8 @@ struct WaveDecoder {
       const uint8_t* vp = vbase + static_cast<uint64_t>(gq < 2 ? b0 : b1) * block_stride;
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        r.k[j] = ld16(kp + koff[j]);
-        r.v[j] = ld16(vp + voff[j]);
+        if constexpr (DO_K) r.k[j] = ld16(kp + koff[j]);
+        if constexpr (DO_V) r.v[j] = ld16(vp + voff[j]);
       }
     } else {
       (void)id_hi;
@@ -466,9 +468,111 @@ struct WaveDecoder {
       const uint8_t* vp = vbase + static_cast<uint64_t>(b) * block_stride + voff_sub;
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        r.k[j] = ld16(kp + koff[j]);
-        r.v[j] = ld16(vp + voff[j]);
+        if constexpr (DO_K) r.k[j] = ld16(kp + koff[j]);
+        if constexpr (DO_V) r.v[j] = ld16(vp + voff[j]);
       }
+    }
+  }
+
+  // ---- MULTI: two steps at a time ------------------------------------------
+  // The P.V product of two 16-token steps runs as one v_mfma_f32_16x16x32_f16
+  // per (dim tile, column tile), twice the rate of two 16x16x16 products on
+  // gfx950: the K index of lane group gq is tokens 4gq..4gq+3 of the first
+  // step, then of the second, the same order for V^T and P^T.
+
+  // Base-2 logits of one step, masked by each column's causal limit (all
+  // masked when the step is padding).
+  __device__ void pair_scores(const u32x4 (&kr)[NLD], int tb, bool is_real, f32x4 (&s)[NT]) const {
+    raw_scores(kr, s);
+    const bool tail = !is_real || tb + 16 > lim_min;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int vh = is_real ? lim[nt] - (tb + 4 * gq) : 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = s[nt][e] * qk_mul;
+        if (tail && e >= vh) x = -__builtin_inff();
+        s[nt][e] = x;
+      }
+    }
+  }
+
+  // Zeroes the V elements of tokens at or past the keys in use (NaN-safe);
+  // a padding step is zeroed whole.
+  __device__ void pair_mask_v(u32x4 (&v)[NLD], int tb, bool is_real) const {
+    if (is_real && tb + 16 <= T) return;
+    const int vh = is_real ? T - (tb + 4 * gq) : 0;
+    const int vc = vh < 0 ? 0 : (vh > 4 ? 4 : vh);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      if constexpr (ELEM == 2) {
+        const uint32_t m01 = (vc > 0 ? 0x0000FFFFu : 0u) | (vc > 1 ? 0xFFFF0000u : 0u);
+        const uint32_t m23 = (vc > 2 ? 0x0000FFFFu : 0u) | (vc > 3 ? 0xFFFF0000u : 0u);
+        v[j] &= u32x4{m01, m23, m01, m23};
+      } else {
+        const uint32_t mb = vc >= 4 ? 0xFFFFFFFFu : ((1u << (8 * vc)) - 1u);
+        v[j] &= u32x4{mb, mb, mb, mb};
+      }
+    }
+  }
+
+  // Online softmax over the 32 tokens of a pair (lazy rescaling), and the
+  // probabilities as the P^T operands.
+  __device__ void pair_softmax(f32x4 (&sa)[NT], f32x4 (&sb)[NT], f16x8 (&pop)[NT]) {
+    static_assert(kLazy, "pairs use the lazy reference");
+    bool need = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float ma = fmaxf(fmaxf(sa[nt][0], sa[nt][1]), fmaxf(sa[nt][2], sa[nt][3]));
+      const float mb = fmaxf(fmaxf(sb[nt][0], sb[nt][1]), fmaxf(sb[nt][2], sb[nt][3]));
+      const float m = max_across_rows(fmaxf(ma, mb));
+      m_true[nt] = fmaxf(m_true[nt], m);
+      need |= m - m_run[nt] >= kRescaleSlack;
+    }
+    if (fresh) {
+      fresh = false;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) m_run[nt] = m_true[nt];
+    } else if (__any(need)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) rescale(nt, m_true[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mref = (m_run[nt] == -__builtin_inff()) ? 0.0f : m_run[nt];
+      float pe[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pe[e] = fast_exp2(sa[nt][e] - mref);
+        pe[4 + e] = fast_exp2(sb[nt][e] - mref);
+      }
+      l_part[nt] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+      pop[nt] = f16x8{(_Float16)pe[0], (_Float16)pe[1], (_Float16)pe[2], (_Float16)pe[3],
+                      (_Float16)pe[4], (_Float16)pe[5], (_Float16)pe[6], (_Float16)pe[7]};
+    }
+  }
+
+  // The four tokens x 16 dims V^T operand of dim tile rr of one step.
+  __device__ f16x4 v_operand(const u32x4 (&v)[NLD], int rr) const {
+    if constexpr (ELEM == 2) {
+      const u32x4 raw = v[rr >> 1];
+      return __builtin_bit_cast(f16x4, (rr & 1) ? u32x2{raw[2], raw[3]} : u32x2{raw[0], raw[1]});
+    } else {
+      const u32x4 raw = v[rr >> 2];
+      if constexpr (KIND == kI8) return i8x4_to_f16x4(raw[rr & 3], vbias);
+      else return e4m3x4_to_f16x4(raw[rr & 3]);
+    }
+  }
+
+  __device__ void pair_pv(const u32x4 (&va)[NLD], const u32x4 (&vb)[NLD], const f16x8 (&pop)[NT]) {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const f16x4 a = v_operand(va, rr);
+      const f16x4 b = v_operand(vb, rr);
+      const f16x8 vop{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        oacc[nt][rr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[nt], oacc[nt][rr], 0, 0, 0);
     }
   }
 
@@ -671,6 +775,50 @@ __device__ inline void stream_steps(Dec& dec, int n, TokOf tok_of, Real real, Fi
     block(n_pad - D, std::true_type{});
   } else {
     for (int j = 0; j < n_pad; j += D) block(j, std::false_type{});
+  }
+}
+
+// MULTI: runs steps j = 0 .. n-1 (padded to pairs) two at a time.  tok_of
+// and real as for stream_steps.  Loads are split so that each has about one
+// pair of work to hide behind: the first step of the next pair is loaded as
+// soon as this pair's first K tile has been used (its V tile kept in
+// registers), the second step's K tile after this pair's second scores, and
+// its V tile after the P.V product.  Block ids are fetched a pair ahead.
+template <class Dec, class TokOf, class Real>
+__device__ inline void stream_pairs(Dec& dec, int n, TokOf tok_of, Real real) {
+  constexpr int NT = Dec::kNT;
+  const int pairs = (n + 1) >> 1;
+  auto tok_at = [&](int j) { return tok_of(j < n ? j : n - 1); };
+  auto real_at = [&](int j) { return j < n && real(j); };
+  int lo[4], hi[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dec.fetch_ids(tok_at(j), lo[j], hi[j]);
+  StepRegs<Dec::kElem> a, b;
+  u32x4 vkeep[Dec::NLD];
+  dec.issue(a, tok_at(0), lo[0], hi[0]);
+  dec.issue(b, tok_at(1), lo[1], hi[1]);
+  for (int pr = 0; pr < pairs; ++pr) {
+    const int j = 2 * pr;
+    int nlo[2], nhi[2];
+    dec.fetch_ids(tok_at(j + 4), nlo[0], nhi[0]);
+    dec.fetch_ids(tok_at(j + 5), nlo[1], nhi[1]);
+    const int ta = tok_at(j), tb = tok_at(j + 1);
+    const bool ra = real_at(j), rb = real_at(j + 1);
+    f32x4 sa[NT], sb[NT];
+    dec.pair_scores(a.k, ta, ra, sa);
+#pragma unroll
+    for (int q = 0; q < Dec::NLD; ++q) vkeep[q] = a.v[q];
+    dec.issue(a, tok_at(j + 2), lo[2], hi[2]);
+    dec.pair_scores(b.k, tb, rb, sb);
+    dec.template issue<true, false>(b, tok_at(j + 3), lo[3], hi[3]);
+    f16x8 pop[NT];
+    dec.pair_softmax(sa, sb, pop);
+    dec.pair_mask_v(vkeep, ta, ra);
+    dec.pair_mask_v(b.v, tb, rb);
+    dec.pair_pv(vkeep, b.v, pop);
+    dec.template issue<false, true>(b, tok_at(j + 3), lo[3], hi[3]);
+    lo[0] = lo[2]; hi[0] = hi[2]; lo[1] = lo[3]; hi[1] = hi[3];
+    lo[2] = nlo[0]; hi[2] = nhi[0]; lo[3] = nlo[1]; hi[3] = nhi[1];
   }
 }
 
@@ -1065,15 +1213,12 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
   }
   Dec dec;
   dec.bind(g, p, seq, kvh, lane);
-  FirstIds first;
   int kmax;
   if (wide) {
     const int jw = w * tq;  // this wave's first token within the item
     if (jw >= nq_item) return;  // no tokens for this wave (no barrier on this path)
     const int nq = (nq_item - jw) < tq ? (nq_item - jw) : tq;
     auto raw_tok = [](int j) -> int64_t { return 16ll * j; };
-#pragma unroll
-    for (int j = 0; j < 2 * kDepth - 1; ++j) dec.fetch_ids(raw_tok(j), first.lo[j], first.hi[j]);
     multi_token_setup(dec, T - n_i + j0 + jw, nq, group, row0 + jw, kmax);
     const int n = (kmax + 15) >> 4;
     const int last_tok = ((kmax - 1) >> 4) << 4;
@@ -1081,7 +1226,7 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
     auto tok_of = [&](int j) -> int { return real(j) ? static_cast<int>(raw_tok(j)) : last_tok; };
     dec.load_q(g, p, seq, kvh, group);
     dec.reset();
-    stream_steps(dec, n, tok_of, real, first, [](int) {});
+    stream_pairs(dec, n, tok_of, real);
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1091,8 +1236,6 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
     }
   } else {
     auto raw_tok = [&](int j) -> int64_t { return 16ll * (w + kWaves * j); };
-#pragma unroll
-    for (int j = 0; j < 2 * kDepth - 1; ++j) dec.fetch_ids(raw_tok(j), first.lo[j], first.hi[j]);
     multi_token_setup(dec, T - n_i + j0, nq_item, group, row0, kmax);
     const int n = (kmax + 16 * kWaves - 1) / (16 * kWaves);
     const int last_tok = ((kmax - 1) >> 4) << 4;
@@ -1101,7 +1244,7 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
     dec.load_q(g, p, seq, kvh, group);
     dec.reset();
     __shared__ MergeLds<NT> sm;
-    stream_steps(dec, n, tok_of, real, first, [](int) {});
+    stream_pairs(dec, n, tok_of, real);
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
     merge_waves(dec, sm, w, nq_item * group, [&](int, int col, f32x4* acc, float, float L, float) {
       multi_token_store(p, dec, acc, dec.out_mul / L, row0, col, kvh, group);
