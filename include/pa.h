@@ -294,9 +294,9 @@ int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const vo
  *                (n_i = 0: nothing; 1: a decode token; more: a prefill chunk)
  *   q, out       device fp16 [query_start[num_seqs]][num_q_heads][head_dim]
  *                (16- and 8-byte aligned)
- *   block_tables, max_blocks, context_lens, scale  as in pa_decode; the K/V
- *                of every query token must already be in the pool
- *                (pa_write_kv), and T_i >= n_i
+ *   block_tables, max_blocks, context_lens, scale  as in pa_decode (scale
+ *                nonzero); the K/V of every query token must already be in
+ *                the pool (pa_write_kv), and T_i >= n_i
  * Row j of sequence i (0-based) sits at position T_i - n_i + j and attends
  * to tokens 0 .. T_i - n_i + j through the block table.  A sequence with
  * T_i < n_i or T_i > max_blocks*block_size sets PA_DEV_BAD_LEN and its rows

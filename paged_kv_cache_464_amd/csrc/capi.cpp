@@ -654,6 +654,7 @@ int pa_multi_token_attention(pa_pool* p, int32_t layer, const void* q, int32_t n
                              void* workspace, uint64_t workspace_bytes, void* stream) {
   int rc = check_decode_args(p, layer, q, block_tables, context_lens, num_seqs, scale);
   if (rc) return rc;
+  if (scale == 0.0f) return fail(PA_ERR_INVALID, "scale must be nonzero");
   if (num_q_heads < 1 || num_q_heads % p->kv_heads != 0 || num_q_heads / p->kv_heads > 32)
     return fail(PA_ERR_INVALID, "num_q_heads %d must be a multiple of kv_heads %d with a group of at most 32",
                 num_q_heads, p->kv_heads);

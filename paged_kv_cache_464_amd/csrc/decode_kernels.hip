@@ -254,6 +254,17 @@ struct WaveDecoder {
         qop[nt][u] = valid ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
+    if constexpr (MULTI) {
+      // The pair softmax needs qk_mul > 0: a negative scale's sign moves into
+      // q (exact in fp16).  A zero scale is refused by the host.
+      if (qk_mul < 0.0f) {
+        qk_mul = -qk_mul;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) qop[nt][u] = -qop[nt][u];
+      }
+    }
   }
 
   // Fused scatter (owner wave only).  Before the stream, the lanes that will
@@ -480,19 +491,18 @@ struct WaveDecoder {
   // gfx950: the K index of lane group gq is tokens 4gq..4gq+3 of the first
   // step, then of the second, the same order for V^T and P^T.
 
-  // Base-2 logits of one step, masked by each column's causal limit (all
-  // masked when the step is padding).
+  // Raw scores of one step (the scale is applied with the exponent), masked
+  // by each column's causal limit (all masked when the step is padding);
+  // only the steps at the limits take the masking branch.
   __device__ void pair_scores(const u32x4 (&kr)[NLD], int tb, bool is_real, f32x4 (&s)[NT]) const {
     raw_scores(kr, s);
-    const bool tail = !is_real || tb + 16 > lim_min;
+    if (!is_real || tb + 16 > lim_min) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int vh = is_real ? lim[nt] - (tb + 4 * gq) : 0;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int vh = is_real ? lim[nt] - (tb + 4 * gq) : 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = s[nt][e] * qk_mul;
-        if (tail && e >= vh) x = -__builtin_inff();
-        s[nt][e] = x;
+        for (int e = 0; e < 4; ++e)
+          if (e >= vh) s[nt][e] = -__builtin_inff();
       }
     }
   }
@@ -500,7 +510,7 @@ struct WaveDecoder {
   // Zeroes the V elements of tokens at or past the keys in use (NaN-safe);
   // a padding step is zeroed whole.
   __device__ void pair_mask_v(u32x4 (&v)[NLD], int tb, bool is_real) const {
-    if (is_real && tb + 16 <= T) return;
+    if (__builtin_expect(is_real && tb + 16 <= T, 1)) return;
     const int vh = is_real ? T - (tb + 4 * gq) : 0;
     const int vc = vh < 0 ? 0 : (vh > 4 ? 4 : vh);
 #pragma unroll
@@ -517,7 +527,10 @@ struct WaveDecoder {
   }
 
   // Online softmax over the 32 tokens of a pair (lazy rescaling), and the
-  // probabilities as the P^T operands.
+  // probabilities as the P^T operands.  Scores arrive unscaled: qk_mul > 0
+  // (load_q folds a negative scale's sign into q), so the largest raw score
+  // times qk_mul is the largest logit, and each probability is one
+  // exp2(fma(s, qk_mul, -reference)).
   __device__ void pair_softmax(f32x4 (&sa)[NT], f32x4 (&sb)[NT], f16x8 (&pop)[NT]) {
     static_assert(kLazy, "pairs use the lazy reference");
     bool need = false;
@@ -525,7 +538,7 @@ struct WaveDecoder {
     for (int nt = 0; nt < NT; ++nt) {
       const float ma = fmaxf(fmaxf(sa[nt][0], sa[nt][1]), fmaxf(sa[nt][2], sa[nt][3]));
       const float mb = fmaxf(fmaxf(sb[nt][0], sb[nt][1]), fmaxf(sb[nt][2], sb[nt][3]));
-      const float m = max_across_rows(fmaxf(ma, mb));
+      const float m = max_across_rows(fmaxf(ma, mb)) * qk_mul;
       m_true[nt] = fmaxf(m_true[nt], m);
       need |= m - m_run[nt] >= kRescaleSlack;
     }
@@ -543,8 +556,8 @@ struct WaveDecoder {
       float pe[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pe[e] = fast_exp2(sa[nt][e] - mref);
-        pe[4 + e] = fast_exp2(sb[nt][e] - mref);
+        pe[e] = fast_exp2(__builtin_fmaf(sa[nt][e], qk_mul, -mref));
+        pe[4 + e] = fast_exp2(__builtin_fmaf(sb[nt][e], qk_mul, -mref));
       }
       l_part[nt] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
       pop[nt] = f16x8{(_Float16)pe[0], (_Float16)pe[1], (_Float16)pe[2], (_Float16)pe[3],
@@ -780,10 +793,9 @@ __device__ inline void stream_steps(Dec& dec, int n, TokOf tok_of, Real real, Fi
 
 // MULTI: runs steps j = 0 .. n-1 (padded to pairs) two at a time.  tok_of
 // and real as for stream_steps.  Loads are split so that each has about one
-// pair of work to hide behind: the first step of the next pair is loaded as
-// soon as this pair's first K tile has been used (its V tile kept in
-// registers), the second step's K tile after this pair's second scores, and
-// its V tile after the P.V product.  Block ids are fetched a pair ahead.
+// pair of work to hide behind: the next pair's K tiles are loaded as soon as
+// this pair's scores have used each K tile, its V tiles after the P.V
+// product.  Block ids are fetched a pair ahead.
 template <class Dec, class TokOf, class Real>
 __device__ inline void stream_pairs(Dec& dec, int n, TokOf tok_of, Real real) {
   constexpr int NT = Dec::kNT;
@@ -794,7 +806,6 @@ __device__ inline void stream_pairs(Dec& dec, int n, TokOf tok_of, Real real) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) dec.fetch_ids(tok_at(j), lo[j], hi[j]);
   StepRegs<Dec::kElem> a, b;
-  u32x4 vkeep[Dec::NLD];
   dec.issue(a, tok_at(0), lo[0], hi[0]);
   dec.issue(b, tok_at(1), lo[1], hi[1]);
   for (int pr = 0; pr < pairs; ++pr) {
@@ -806,16 +817,15 @@ __device__ inline void stream_pairs(Dec& dec, int n, TokOf tok_of, Real real) {
     const bool ra = real_at(j), rb = real_at(j + 1);
     f32x4 sa[NT], sb[NT];
     dec.pair_scores(a.k, ta, ra, sa);
-#pragma unroll
-    for (int q = 0; q < Dec::NLD; ++q) vkeep[q] = a.v[q];
-    dec.issue(a, tok_at(j + 2), lo[2], hi[2]);
+    dec.template issue<true, false>(a, tok_at(j + 2), lo[2], hi[2]);
     dec.pair_scores(b.k, tb, rb, sb);
     dec.template issue<true, false>(b, tok_at(j + 3), lo[3], hi[3]);
     f16x8 pop[NT];
     dec.pair_softmax(sa, sb, pop);
-    dec.pair_mask_v(vkeep, ta, ra);
+    dec.pair_mask_v(a.v, ta, ra);
     dec.pair_mask_v(b.v, tb, rb);
-    dec.pair_pv(vkeep, b.v, pop);
+    dec.pair_pv(a.v, b.v, pop);
+    dec.template issue<false, true>(a, tok_at(j + 2), lo[2], hi[2]);
     dec.template issue<false, true>(b, tok_at(j + 3), lo[3], hi[3]);
     lo[0] = lo[2]; hi[0] = hi[2]; lo[1] = lo[3]; hi[1] = hi[3];
     lo[2] = nlo[0]; hi[2] = nhi[0]; lo[3] = nlo[1]; hi[3] = nhi[1];

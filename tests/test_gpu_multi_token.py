@@ -95,3 +95,20 @@ def test_prefill_chunks_at_full_size_sampled():
         ref = attention.decode(st, 0, qh[r:r + 1], c.tables_np[i:i + 1], [pos + 1])
         assert_close(out[r:r + 1], ref, "fp16", f"row {r} (seq {i}, position {pos})")
     assert c.pool.device_status() == 0
+
+
+def test_negative_scale_and_zero_scale():
+    """A negative softmax temperature is exact (its sign moves into q); a zero
+    scale is refused."""
+    say("multi_token scale sign")
+    lens, n = [300, 40, 9], [45, 40, 1]
+    c = build_case(lens, 32, 8, 16, 40, 5400)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = normal_fp16((int(qs[-1]), 32, 128), 5400, 7, "cuda")
+    out = c.pool.multi_token_attention(0, q, qs, c.tables, c.lens_dev, scale=-0.05)
+    st = oracle_for(c, range(len(lens)))
+    ref = attention.multi_token(st, 0, q.cpu().numpy(), qs, c.tables_np, lens, scale=-0.05)
+    assert_close(out, ref, "fp16", "scale -0.05")
+    with pytest.raises(pa.PAError):
+        c.pool.multi_token_attention(0, q, qs, c.tables, c.lens_dev, scale=0.0)
+    assert c.pool.device_status() == 0
