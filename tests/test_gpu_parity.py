@@ -155,11 +155,32 @@ def test_decode_matrix(dtype, bs, hq, hkv):
     say("matrix", dtype, bs, hq, hkv, list(lens))
     c = build_case(lens, hq, hkv, bs, nb, seed, dtype)
     ref = oracle_decode(c, list(range(len(lens))))
-    for mode in (-1, 0, 64, 512):
+    # P = 64 gives one step per wave and chunk (an odd count: wide groups pad
+    # each chunk's steps to a pair); P = 32 and 48 run one wave per chunk run
+    # (two and three steps per chunk).
+    for mode in (-1, 0, 32, 48, 64, 512):
         if mode > 0 and mode % bs:
             continue
         out = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode)
         assert_close(out, ref, dtype, f"{dtype}/B{bs}/{hq}x{hkv}/P={mode}")
+    assert c.pool.device_status() == 0
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("hq,hkv", [(32, 1), (32, 8)])
+@pytest.mark.parametrize("scale", [-0.05, 0.0])
+def test_decode_negative_and_zero_scale(dtype, hq, hkv, scale):
+    """A negative softmax scale and a zero one (uniform weights: the mean of
+    the values) in every schedule."""
+    seed = 4100 + hq + hkv + (0 if dtype == "fp16" else 50)
+    lens = [1, 45, 700, 16, 300]
+    nb = int(sum(-(-t // 16) for t in lens)) + 4
+    say("scale", dtype, hq, hkv, scale)
+    c = build_case(lens, hq, hkv, 16, nb, seed, dtype)
+    ref = oracle_decode(c, list(range(len(lens))), scale=scale)
+    for mode in (-1, 32, 48, 64, 256):
+        out = c.pool.decode(0, c.q, c.tables, c.lens_dev, scale=scale, partition_tokens=mode)
+        assert_close(out, ref, dtype, f"{dtype}/{hq}x{hkv}/scale={scale}/P={mode}")
     assert c.pool.device_status() == 0
 
 
