@@ -185,11 +185,13 @@ def test_decode_negative_and_zero_scale(dtype, hq, hkv, scale):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
-def test_partials_match_oracle_split(dtype):
-    say("partials", dtype)
+@pytest.mark.parametrize("P", [128, 48])
+def test_partials_match_oracle_split(dtype, P):
+    """Chunk partials (max, sum, normalised O) against the oracle's, with four
+    waves per chunk (P = 128) and one wave per chunk run (P = 48)."""
+    say("partials", dtype, P)
     lens = [1, 300, 1000, 513]
     c = build_case(lens, 16, 2, 16, 200, 77, dtype)
-    P = 128
     m, l, o = pa.pa_decode_partials(c.pool.handle, 0, c.q, c.tables, c.lens_dev, P)
     m, l, o = m.cpu().numpy(), l.cpu().numpy(), o.cpu().numpy()
     st = oracle_for(c, range(len(lens)))
