@@ -39,7 +39,9 @@ __device__ inline uint32_t e4m3_encode(float y) {
 // point and infinities saturate.  Returned as the stored byte c + 128.
 __device__ inline uint32_t i8_encode_stored(float y, float zero) {
   float r = rintf(y);
-  r = (r == r) ? r : 0.0f;
+  // NaN test on the bit pattern: it must hold where the compiler may assume
+  // that no value is NaN (the decode kernels are built so).
+  r = (__float_as_uint(r) & 0x7FFFFFFFu) > 0x7F800000u ? 0.0f : r;
   const float c = fminf(fmaxf(r + zero, -128.0f), 127.0f);
   return static_cast<uint32_t>(static_cast<int>(c) + 128);
 }
