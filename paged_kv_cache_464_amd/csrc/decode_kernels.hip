@@ -1264,9 +1264,12 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
 
 // Log-sum-exp merge of the chunk partials of one (sequence, query head):
 // out = sum_c w_c o_c / sum_c w_c with w_c = l_c * 2^(m_c - max_c m_c).
-// One 256-thread workgroup per row: the four waves take every fourth chunk
-// (eight chunks' loads in flight per wave), each lane two of the 128 dims;
-// the waves' sums meet in LDS.
+// One 256-thread workgroup per row.  The chunks go in blocks of 256: thread
+// t computes the weight of chunk t of the block into LDS (one exponential
+// per chunk, lane-parallel loads of m and l), then wave w accumulates the
+// block's chunks w, w + 4, ... with every lane taking two of the 128 dims
+// and reading each weight as an LDS broadcast (eight chunks' loads in flight
+// per wave); the waves' sums meet in LDS.
 constexpr int kReduceThreads = 256;
 constexpr int kReduceUnroll = 8;
 
@@ -1286,6 +1289,7 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(PoolGeom g, 
   const float* o = p.part_o + base * kD + 2 * lane;
 
   __shared__ float sm_red[4];
+  __shared__ float sm_w[kReduceThreads];
   __shared__ float sm_acc[4][kD];
   __shared__ float sm_den[4];
   // 1. M = max_c m_c
@@ -1295,24 +1299,33 @@ __global__ __launch_bounds__(kReduceThreads) void lse_reduce_kernel(PoolGeom g, 
   if (lane == 0) sm_red[w] = M;
   __syncthreads();
   M = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
-  // 2. this wave's chunks c = w, w + 4, ...
+  // 2. blocks of 256 chunks
   float a0 = 0.0f, a1 = 0.0f, den = 0.0f;
-  for (int c0 = w; c0 < cv; c0 += 4 * kReduceUnroll) {
-    float2 ov[kReduceUnroll];
-    float wt[kReduceUnroll];
-#pragma unroll
-    for (int u = 0; u < kReduceUnroll; ++u) {
-      const int c = c0 + 4 * u;
-      const bool ok = c < cv;
-      ov[u] = ok ? *reinterpret_cast<const float2*>(o + static_cast<int64_t>(c) * kD) : float2{0.0f, 0.0f};
-      wt[u] = ok ? l[c] * exp2f(m[c] - M) : 0.0f;
+  for (int cb = 0; cb < cv; cb += kReduceThreads) {
+    const int nb = (cv - cb) < kReduceThreads ? (cv - cb) : kReduceThreads;
+    {
+      const int c = cb + static_cast<int>(threadIdx.x);
+      sm_w[threadIdx.x] = c < cv ? l[c] * exp2f(m[c] - M) : 0.0f;
     }
+    __syncthreads();
+    for (int i0 = w; i0 < nb; i0 += 4 * kReduceUnroll) {
+      float2 ov[kReduceUnroll];
 #pragma unroll
-    for (int u = 0; u < kReduceUnroll; ++u) {
-      den += wt[u];
-      a0 += wt[u] * ov[u].x;
-      a1 += wt[u] * ov[u].y;
+      for (int u = 0; u < kReduceUnroll; ++u) {
+        const int i = i0 + 4 * u;
+        ov[u] = i < nb ? *reinterpret_cast<const float2*>(o + static_cast<int64_t>(cb + i) * kD)
+                       : float2{0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < kReduceUnroll; ++u) {
+        const int i = i0 + 4 * u;
+        const float wt = i < nb ? sm_w[i] : 0.0f;
+        den += wt;
+        a0 += wt * ov[u].x;
+        a1 += wt * ov[u].y;
+      }
     }
+    __syncthreads();  // sm_w is rewritten by the next block
   }
   sm_acc[w][2 * lane] = a0;
   sm_acc[w][2 * lane + 1] = a1;

@@ -213,6 +213,22 @@ def test_partials_match_oracle_split(dtype, P):
     assert_close(out, oracle_decode(c, range(len(lens))), dtype, "reduce")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+def test_reduce_over_many_chunks(dtype):
+    """More than 64 chunks per row (the blocked log-sum-exp reduce), with 257
+    chunks at P = 16: a second block of one chunk."""
+    lens = [1, 300, 4112, 2000]
+    nb = int(sum(-(-t // 16) for t in lens)) + 4
+    say("reduce many chunks", dtype)
+    c = build_case(lens, 32, 8, 16, nb, 5150 + (7 if dtype == "fp8" else 0), dtype)
+    assert c.max_blocks * 16 // 16 > 256
+    ref = oracle_decode(c, list(range(len(lens))))
+    for mode in (16, 32, 48):
+        out = c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode)
+        assert_close(out, ref, dtype, f"{dtype}/P={mode}")
+    assert c.pool.device_status() == 0
+
+
 def test_output_bitwise_invariant_under_placement():
     say("placement invariance")
     lens = [77, 301, 16, 1000]
