@@ -544,7 +544,8 @@ static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_he
   if (mode == 0 && num_seqs > 0 && !out) return fail(PA_ERR_INVALID, "out is NULL");
   if (mode == 0 && misaligned(out, 8)) return fail(PA_ERR_INVALID, "out must be 8-byte aligned");
   if (pl.partial && misaligned(workspace, 16)) return fail(PA_ERR_INVALID, "workspace must be 16-byte aligned");
-  if (pl.partial && (!workspace || workspace_bytes < pl.ws_bytes))
+  // An empty batch needs no workspace (0 bytes, which may be NULL).
+  if (pl.partial && pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes))
     return fail(PA_ERR_INVALID, "workspace of %llu bytes needed", static_cast<unsigned long long>(pl.ws_bytes));
   if (num_seqs == 0) return PA_OK;
   pa::DecodeLaunch d = make_launch(layer, q, num_q_heads, tables, max_blocks, lens, num_seqs,
