@@ -239,13 +239,14 @@ pa::DecodeLaunch make_launch(int32_t layer, const void* q, int32_t num_q_heads,
 
 bool misaligned(const void* ptr, uintptr_t bytes) { return reinterpret_cast<uintptr_t>(ptr) % bytes != 0; }
 
+// has_q: the call reads q (false when a multi-token batch has no query rows).
 int check_decode_args(pa_pool* pool, int32_t layer, const void* q, const int32_t* tables,
-                      const int32_t* lens, int32_t num_seqs, float scale) {
+                      const int32_t* lens, int32_t num_seqs, float scale, bool has_q = true) {
   int rc = check_bound(pool);
   if (rc) return rc;
   if ((rc = check_layer(pool, layer))) return rc;
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "scale is not finite");
-  if (num_seqs > 0 && (!q || !tables || !lens)) return fail(PA_ERR_INVALID, "NULL device pointer");
+  if (num_seqs > 0 && ((has_q && !q) || !tables || !lens)) return fail(PA_ERR_INVALID, "NULL device pointer");
   if (misaligned(q, 16)) return fail(PA_ERR_INVALID, "q must be 16-byte aligned");
   return PA_OK;
 }
@@ -653,7 +654,10 @@ int pa_multi_token_attention(pa_pool* p, int32_t layer, const void* q, int32_t n
                              const int32_t* query_start, const int32_t* block_tables, int32_t max_blocks,
                              const int32_t* context_lens, int32_t num_seqs, float scale, void* out,
                              void* workspace, uint64_t workspace_bytes, void* stream) {
-  int rc = check_decode_args(p, layer, q, block_tables, context_lens, num_seqs, scale);
+  // With no query rows at all (every n_i = 0) q and out hold nothing and
+  // may be NULL.
+  const bool no_rows = num_seqs > 0 && query_start && query_start[num_seqs] == 0;
+  int rc = check_decode_args(p, layer, q, block_tables, context_lens, num_seqs, scale, !no_rows);
   if (rc) return rc;
   if (scale == 0.0f) return fail(PA_ERR_INVALID, "scale must be nonzero");
   if (num_q_heads < 1 || num_q_heads % p->kv_heads != 0 || num_q_heads / p->kv_heads > 32)

@@ -26,6 +26,14 @@ def test_empty_batch_writes_and_decodes_nothing():
         out = c.pool.decode(0, c.q[:0].contiguous(), c.tables[:0].contiguous(), c.lens_dev[:0].contiguous(),
                             partition_tokens=mode)
         assert tuple(out.shape) == (0, 8, 128)
+        out = c.pool.write_kv_decode(0, c.k[:0].contiguous(), c.v[:0].contiguous(), slots0,
+                                     c.q[:0].contiguous(), c.tables[:0].contiguous(),
+                                     c.lens_dev[:0].contiguous(), partition_tokens=mode)
+        assert tuple(out.shape) == (0, 8, 128)
+    # Multi-token attention with no query rows at all (every n_i = 0).
+    q0 = c.q[:0].contiguous()
+    out = c.pool.multi_token_attention(0, q0, [0, 0, 0], c.tables, c.lens_dev)
+    assert tuple(out.shape) == (0, 8, 128)
     torch.cuda.synchronize()
     assert c.pool.device_status() == 0
     # The pool is unchanged by the empty calls.
