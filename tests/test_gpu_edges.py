@@ -41,7 +41,7 @@ def test_empty_batch_writes_and_decodes_nothing():
     assert_close(c.pool.decode(0, c.q, c.tables, c.lens_dev), ref, "fp16", "after empty calls")
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
 @pytest.mark.parametrize("t", [1, 9, 16])
 def test_one_block_pool(dtype, t):
     say("one-block pool", dtype, t)
@@ -98,4 +98,41 @@ def test_out_of_range_table_entry_is_flagged_and_read_as_block_zero():
         torch.cuda.synchronize()
         assert c.pool.device_status(clear=True) & pa.PA_DEV_BAD_BLOCK, mode
         assert np.abs(out[0].double().cpu().numpy() - ref[0]).max() <= 2e-3, mode
+    assert c.pool.device_status() == 0
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (12, 2), (24, 2), (20, 1), (24, 1)])
+def test_decode_group_sizes_that_are_not_powers_of_two(dtype, hq, hkv):
+    """Groups of 3, 6, 12, 20 and 24 query heads per KV head: the column tile
+    is padded (and a second tile partly filled above 16) in every schedule."""
+    seed = 6500 + 7 * hq + hkv + {"fp16": 0, "fp8": 1, "int8": 2}[dtype]
+    lens = [1, 37, 700, 16, 1100]
+    nb = int(sum(-(-t // 16) for t in lens)) + 4
+    say("odd group", dtype, hq, hkv)
+    c = build_case(lens, hq, hkv, 16, nb, seed, dtype)
+    ref = oracle_decode(c, list(range(len(lens))))
+    for mode in (-1, 0, 32, 64, 256):
+        assert_close(c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode), ref, dtype,
+                     f"{dtype}/{hq}x{hkv}/P={mode}")
+    assert c.pool.device_status() == 0
+
+
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (12, 2), (20, 1)])
+def test_multi_token_group_sizes_that_are_not_powers_of_two(hq, hkv):
+    from oracle import attention
+    from tests.gpu_helpers import oracle_for
+    from workloads import normal_fp16
+
+    lens = [1, 37, 300, 1000, 129, 700]
+    n = [1, 37, 45, 1, 17, 64]
+    nb = int(sum(-(-t // 16) for t in lens)) + 4
+    say("odd group multi-token", hq, hkv)
+    c = build_case(lens, hq, hkv, 16, nb, 6600 + hq + hkv)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = normal_fp16((int(qs[-1]), hq, 128), 6600 + hq, 77, "cuda")
+    out = c.pool.multi_token_attention(0, q, qs, c.tables, c.lens_dev)
+    st = oracle_for(c, range(len(lens)))
+    ref = attention.multi_token(st, 0, q.cpu().numpy(), qs, c.tables_np, lens)
+    assert_close(out, ref, "fp16", f"multi {hq}x{hkv}")
     assert c.pool.device_status() == 0
