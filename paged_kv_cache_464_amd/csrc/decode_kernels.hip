@@ -178,6 +178,11 @@ struct WaveDecoder {
   // with nothing accumulated; otherwise m_run is the running maximum itself.
   static constexpr bool kLazy = NT > 1;
   float m_run[NT], m_true[NT], l_part[NT];
+  // MULTI: the softmax denominators accumulate on the matrix cores (one
+  // 16x16x32 MFMA of an all-ones operand with P per pair and column tile),
+  // so every lane holds its column's whole sum; finish_l turns them into
+  // l_part for the merges.
+  f32x4 lacc[NT];
   bool fresh;
   uint32_t bad;
 
@@ -420,6 +425,7 @@ struct WaveDecoder {
       m_run[nt] = -__builtin_inff();
       m_true[nt] = -__builtin_inff();
       l_part[nt] = 0.0f;
+      lacc[nt] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int r = 0; r < 8; ++r) oacc[nt][r] = f32x4{0, 0, 0, 0};
     }
@@ -559,7 +565,6 @@ struct WaveDecoder {
         pe[e] = fast_exp2(__builtin_fmaf(sa[nt][e], qk_mul, -mref));
         pe[4 + e] = fast_exp2(__builtin_fmaf(sb[nt][e], qk_mul, -mref));
       }
-      l_part[nt] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
       pop[nt] = f16x8{(_Float16)pe[0], (_Float16)pe[1], (_Float16)pe[2], (_Float16)pe[3],
                       (_Float16)pe[4], (_Float16)pe[5], (_Float16)pe[6], (_Float16)pe[7]};
     }
@@ -578,6 +583,9 @@ struct WaveDecoder {
   }
 
   __device__ void pair_pv(const u32x4 (&va)[NLD], const u32x4 (&vb)[NLD], const f16x8 (&pop)[NT]) {
+    const f16x8 ones{1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[nt], lacc[nt], 0, 0, 0);
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
       const f16x4 a = v_operand(va, rr);
@@ -608,9 +616,17 @@ struct WaveDecoder {
     if (MULTI && m_new == -__builtin_inff()) return;
     const float alpha = fast_exp2(m_run[nt] - m_new);
     l_part[nt] *= alpha;
+    if constexpr (MULTI) lacc[nt] *= alpha;
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) oacc[nt][rr] *= alpha;
     m_run[nt] = m_new;
+  }
+
+  // MULTI: the denominators as per-row parts (a quarter of the whole sum in
+  // each of the four rows, exact), the form the merges sum across rows.
+  __device__ void finish_l() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) l_part[nt] = lacc[nt][0] * 0.25f;
   }
 
   // INJ: the step may hold the fused new token (only the last scheduled
@@ -1237,6 +1253,7 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
     dec.load_q(g, p, seq, kvh, group);
     dec.reset();
     stream_pairs(dec, n, tok_of, real);
+    dec.finish_l();
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1255,6 +1272,7 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
     dec.reset();
     __shared__ MergeLds<NT> sm;
     stream_pairs(dec, n, tok_of, real);
+    dec.finish_l();
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
     merge_waves(dec, sm, w, nq_item * group, [&](int, int col, f32x4* acc, float, float L, float) {
       multi_token_store(p, dec, acc, dec.out_mul / L, row0, col, kvh, group);
