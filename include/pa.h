@@ -187,6 +187,8 @@ int pa_fork(pa_pool* pool, int32_t parent, int32_t* child_out);
  * reference count reaches zero is appended to the free-queue tail. */
 int pa_free(pa_pool* pool, int32_t seq);
 
+/* Tokens and blocks of `seq` (either out pointer may be NULL); PA_ERR_BAD_SEQ
+ * for an unknown or freed sequence. */
 int pa_seq_len(const pa_pool* pool, int32_t seq, int32_t* len_out, int32_t* num_blocks_out);
 
 /* Export block tables: tables_out host int32[n][max_blocks] (rows padded with
@@ -194,6 +196,7 @@ int pa_seq_len(const pa_pool* pool, int32_t seq, int32_t* len_out, int32_t* num_
 int pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n, int32_t max_blocks,
                     int32_t* tables_out, int32_t* lens_out);
 
+/* The pool's block, sequence, copy-on-write and prefix-cache counters (pa_stats). */
 int pa_pool_stats(const pa_pool* pool, pa_stats* out);
 
 /* Allocator state for inspection: reference count of every block (host
@@ -259,7 +262,8 @@ int pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num
  * leaves some sequence's output unwritten.
  * workspace: device memory of pa_decode_workspace_bytes() bytes, 16-byte
  * aligned (may be NULL when that is 0).  Out-of-range table entries or lengths never cause an
- * out-of-bounds access; they set PA_DEV_* bits instead. */
+ * out-of-bounds access; they set PA_DEV_* bits instead.  num_seqs = 0 launches
+ * nothing (q, block_tables, context_lens, out and workspace may then be NULL). */
 int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
               int32_t num_seqs, const int32_t* seq_order, float scale, int32_t partition_tokens,
@@ -304,7 +308,9 @@ int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const vo
  * bytes (16 per tile of query tokens), 16-byte aligned; the library uploads
  * its work list there on `stream` from pinned host memory it owns (a ring of
  * 16 buffers: a call waits only for the upload made 16 calls earlier).  Calls
- * that share a workspace must be on the same stream. */
+ * that share a workspace must be on the same stream.  With no query rows
+ * (query_start[num_seqs] = 0) nothing is launched, and q, out and workspace
+ * may be NULL. */
 int pa_multi_token_workspace_bytes(const pa_pool* pool, const int32_t* query_start, int32_t num_seqs,
                                    int32_t num_q_heads, uint64_t* bytes_out);
 int pa_multi_token_attention(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
