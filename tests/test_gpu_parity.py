@@ -293,19 +293,31 @@ def test_shared_prefix_cow_and_decode():
     assert pool.stats()["cow_copies"] == 1
 
 
-def test_copy_blocks_all_layers():
-    say("copy_blocks")
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
+def test_copy_blocks_all_layers(dtype):
+    """Whole-block copies (all layers, K and V) are byte copies in every pool
+    type: the destination gathers exactly what the source holds."""
+    say("copy_blocks", dtype)
     layers, n, bs = 4, 16, 8
-    pool = pa.PagedKVPool(layers, 2, 128, bs, n)
+    kw = {}
+    if dtype != "fp16":
+        kw = {"k_scales": np.full((layers, 2), 0.03), "v_scales": np.full((layers, 2), 0.05)}
+        if dtype == "int8":
+            kw.update(k_zeros=np.full((layers, 2), 3.0), v_zeros=np.full((layers, 2), -2.0))
+    pool = pa.PagedKVPool(layers, 2, 128, bs, n, dtype, **kw)
     k = normal_fp16((layers, bs, 2, 128), 5, 1, "cuda")
+    v = normal_fp16((layers, bs, 2, 128), 5, 2, "cuda")
     src_slots = torch.arange(3 * bs, 4 * bs, dtype=torch.int32, device="cuda")  # block 3
-    for ly in range(layers):
-        pool.write_kv(ly, k[ly], k[ly], src_slots)
-    pool.copy_blocks([3], [11])
     dst_slots = torch.arange(11 * bs, 12 * bs, dtype=torch.int32, device="cuda")
     for ly in range(layers):
-        kk, vv = pool.gather_kv(ly, dst_slots)
-        assert torch.equal(kk, k[ly]) and torch.equal(vv, k[ly])
+        pool.write_kv(ly, k[ly], v[ly], src_slots)
+    pool.copy_blocks([3], [11])
+    for ly in range(layers):
+        ks, vs = pool.gather_kv(ly, src_slots)
+        kd, vd = pool.gather_kv(ly, dst_slots)
+        assert torch.equal(kd, ks) and torch.equal(vd, vs), ly
+        if dtype == "fp16":
+            assert torch.equal(kd, k[ly]) and torch.equal(vd, v[ly])
 
 
 def test_kernel_timing_samples_every_nth_launch():
