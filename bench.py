@@ -336,8 +336,9 @@ class DecodeBench:
         slots = meta[:self.S]
         if self.name == "beam_k5":
             self._beam_reselect()
-        for i, s in enumerate(self.seqs):
-            slots[i] = self.pool.alloc(s, 1, stream=self.stream)[0][0]
+        # One append per sequence; the step's copy-on-write copies (beam
+        # forks) go to the stream in one launch.
+        slots[:] = self.pool.alloc_batch(self.seqs, [1] * len(self.seqs), stream=self.stream)[0]
         tables, lens = self.pool.block_tables(self.seqs, self.mb_cap)
         meta[self.S:2 * self.S] = lens
         meta[2 * self.S:3 * self.S] = pa.pa_order_longest_first(lens)

@@ -180,6 +180,20 @@ int pa_seq_create_cached(pa_pool* pool, const int32_t* tokens, int32_t n, int32_
 int pa_alloc(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* slots_out,
              int32_t* cow_out, void* stream);
 
+/* Batched appends: for k = 0 .. count-1 in order, append n_tokens[k] >= 0
+ * tokens to seqs[k] exactly as pa_alloc would (the same allocator state and
+ * slots), the slots back to back in slots_out (host int32[sum of n_tokens]).
+ * The copy-on-write copies of the whole batch are enqueued on `stream` in one
+ * launch (per 64 copies) after the appends, instead of one launch per copy:
+ * every copy's destination is a fresh block private to its sequence, so the
+ * copies do not depend on one another.  cow_out (host int32[2*count], may be
+ * NULL): each append's {src, dst} or {-1, -1}.  done_out (may be NULL): the
+ * number of appends made.  On a failing append k the appends before it stay
+ * made (their copies enqueued), append k changes nothing, and its status is
+ * returned (PA_ERR_NO_BLOCKS when the pool runs out). */
+int pa_alloc_batch(pa_pool* pool, const int32_t* seqs, const int32_t* n_tokens, int32_t count,
+                   int32_t* slots_out, int32_t* cow_out, int32_t* done_out, void* stream);
+
 /* New sequence sharing every block of `parent` (each reference count + 1). */
 int pa_fork(pa_pool* pool, int32_t parent, int32_t* child_out);
 

@@ -417,6 +417,50 @@ int pa_alloc(pa_pool* p, int32_t seq, int32_t n_tokens, int32_t* slots_out, int3
   return PA_OK;
 }
 
+int pa_alloc_batch(pa_pool* p, const int32_t* seqs, const int32_t* n_tokens, int32_t count,
+                   int32_t* slots_out, int32_t* cow_out, int32_t* done_out, void* stream) {
+  if (done_out) *done_out = 0;
+  if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (count < 0 || (count > 0 && (!seqs || !n_tokens)))
+    return fail(PA_ERR_INVALID, "bad arguments to pa_alloc_batch");
+  int64_t total = 0;
+  for (int32_t k = 0; k < count; ++k) {
+    if (n_tokens[k] < 0) return fail(PA_ERR_INVALID, "n_tokens[%d] = %d < 0", k, n_tokens[k]);
+    total += n_tokens[k];
+  }
+  if (total > 0 && !slots_out) return fail(PA_ERR_INVALID, "slots_out is NULL");
+  // The appends in order, as pa_alloc does them; the copies of the whole
+  // batch go to the device together afterwards.  Their order does not
+  // matter: every copy's destination is a fresh block private to the
+  // appending sequence, so no copy of the batch reads another's destination,
+  // and no append frees a block.
+  std::vector<int32_t> src, dst;
+  int rc = PA_OK;
+  int32_t k = 0;
+  int64_t off = 0;
+  for (; k < count; ++k) {
+    int32_t s = -1, d = -1;
+    rc = bm_status(p->bm.alloc(seqs[k], n_tokens[k], slots_out ? slots_out + off : nullptr, &s, &d), seqs[k]);
+    if (cow_out) {
+      cow_out[2 * k] = s;
+      cow_out[2 * k + 1] = d;
+    }
+    if (rc) break;
+    off += n_tokens[k];
+    if (s >= 0) {
+      src.push_back(s);
+      dst.push_back(d);
+    }
+  }
+  if (done_out) *done_out = k;
+  if (!src.empty() && p->bound) {
+    const hipError_t e = pa::launch_copy_blocks(p->geom, src.data(), dst.data(), static_cast<int>(src.size()),
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "copy-on-write block copies");
+  }
+  return rc;
+}
+
 int pa_fork(pa_pool* p, int32_t parent, int32_t* child_out) {
   if (!p || !child_out) return fail(PA_ERR_INVALID, "NULL argument");
   return bm_status(p->bm.fork(parent, child_out), parent);

@@ -168,6 +168,24 @@ def pa_alloc(h, seq, n_tokens, stream=0):
     return slots, (None if cow[0] < 0 else (int(cow[0]), int(cow[1])))
 
 
+def pa_alloc_batch(h, seqs, n_tokens, stream=0):
+    """Appends n_tokens[k] tokens to seqs[k] for every k in order, with one
+    launch for all copy-on-write copies.  Returns (slots int32[sum n_tokens],
+    cow int32[count][2] with -1 where an append copied nothing)."""
+    s_arr, s_ptr = _i32_host(seqs)
+    n_arr, n_ptr = _i32_host(n_tokens)
+    if len(s_arr) != len(n_arr):
+        raise ValueError("seqs and n_tokens differ in length")
+    slots = np.empty(max(int(n_arr.sum()) if len(n_arr) else 0, 0), dtype=np.int32)
+    cow = np.full((len(s_arr), 2), -1, dtype=np.int32)
+    done = C.c_int32()
+    st = C.c_void_p(0) if stream == 0 else _stream(stream)
+    _check(_L().pa_alloc_batch(C.c_void_p(h), s_ptr, n_ptr, len(s_arr),
+                               slots.ctypes.data_as(C.POINTER(C.c_int32)),
+                               cow.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(done), st))
+    return slots, cow
+
+
 def pa_fork(h, parent) -> int:
     c = C.c_int32()
     _check(_L().pa_fork(C.c_void_p(h), int(parent), C.byref(c)))
@@ -493,6 +511,9 @@ class PagedKVPool:
 
     def alloc(self, seq, n, stream=None):
         return pa_alloc(self.handle, seq, n, stream if self.buffer is not None else 0)
+
+    def alloc_batch(self, seqs, n_tokens, stream=None):
+        return pa_alloc_batch(self.handle, seqs, n_tokens, stream if self.buffer is not None else 0)
 
     def fork(self, parent):
         return pa_fork(self.handle, parent)

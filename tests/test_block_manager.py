@@ -342,3 +342,65 @@ def test_multi_token_work_list_size_and_checks():
     h1 = pa.pa_pool_create(1, 1, 128, 16, pa.PA_DTYPE_FP16, 64)
     assert pa.pa_multi_token_workspace_bytes(h1, [0, 24, 25], 24) == 16 * (6 + 1)  # G = 24: 4 per tile
     pa.pa_pool_destroy(h1)
+
+
+@pytest.mark.parametrize("bs", [8, 16])
+def test_alloc_batch_equals_appends_one_by_one(bs):
+    """pa_alloc_batch leaves the allocator exactly as the same pa_alloc calls
+    in order (slots, copy-on-write pairs, tables, refcounts, free queue), also
+    when a shared partial block is appended to by several sharers and when the
+    pool runs out part way (the appends before the failing one stay made)."""
+    rng = np.random.default_rng(4646 + bs)
+    order = free_order(4646 + bs, 96)
+    h1, h2 = _pool(96, bs, order), _pool(96, bs, order)
+    o = OracleAllocator(96, bs, order)
+
+    def both(fn, *a):
+        r1, r2 = fn(h1, *a), fn(h2, *a)
+        assert r1 == r2
+        return r1
+
+    roots = []
+    for t in (5, 2 * bs + 3, bs):
+        s = both(pa.pa_seq_create)
+        os_ = o.seq_create()
+        assert s == os_
+        pa.pa_alloc(h1, s, t)
+        pa.pa_alloc(h2, s, t)
+        o.alloc(s, t)
+        roots.append(s)
+    seqs = list(roots)
+    for r in roots:  # sharers of every root, partial last blocks included
+        for _ in range(2):
+            c = both(pa.pa_fork, r)
+            assert c == o.fork(r)
+            seqs.append(c)
+    for step in range(6):
+        batch = [int(x) for x in rng.permutation(seqs)]
+        n = [int(x) for x in rng.integers(0, 2 * bs, len(batch))]
+        slots, cow = pa.pa_alloc_batch(h1, batch, n)
+        exp_slots, exp_cow = [], []
+        for s, k in zip(batch, n):
+            sl, c = pa.pa_alloc(h2, s, k)
+            exp_slots.append(sl)
+            exp_cow.append(c if c is not None else (-1, -1))
+            osl, ocow = o.alloc(s, k)
+            np.testing.assert_array_equal(sl, np.asarray(osl, dtype=np.int32))
+        np.testing.assert_array_equal(slots, np.concatenate(exp_slots).astype(np.int32))
+        np.testing.assert_array_equal(cow, np.asarray(exp_cow, dtype=np.int32).reshape(-1, 2))
+        _same_state(h1, o)
+        _same_state(h2, o)
+    # Exhaust the pool part way through a batch.
+    big = [seqs[0], seqs[1], seqs[2]]
+    free_now = pa.pa_pool_stats(h1)["free_blocks"]
+    n = [bs, (free_now + 4) * bs, bs]
+    with pytest.raises(pa.NoBlocksError):
+        pa.pa_alloc_batch(h1, big, n)
+    pa.pa_alloc(h2, big[0], n[0])
+    with pytest.raises(pa.NoBlocksError):
+        pa.pa_alloc(h2, big[1], n[1])
+    o.alloc(big[0], n[0])
+    with pytest.raises(NoBlocks):
+        o.alloc(big[1], n[1])
+    _same_state(h1, o)
+    _same_state(h2, o)

@@ -276,13 +276,16 @@ def test_beam_search_fork_trees_decode_like_the_oracle():
                 if b not in used:
                     pool.free(old[b])
                     orc.free_seq(old[b])
-            for s in new:
-                sl, cow = pool.alloc(s, 1)
+            # The group's appends in one batch: its copy-on-write copies go
+            # to the device in one launch.
+            sl_b, cow_b = pool.alloc_batch(new, [1] * len(new))
+            for j, s in enumerate(new):
                 osl, ocow = orc.alloc(s, 1)
-                assert list(sl) == list(osl) and cow == ocow
+                cow = None if cow_b[j][0] < 0 else (int(cow_b[j][0]), int(cow_b[j][1]))
+                assert [int(sl_b[j])] == list(osl) and cow == ocow
                 if cow is not None:
                     st.copy_block(*cow)
-                slots_all.append(int(sl[0]))
+                slots_all.append(int(sl_b[j]))
             beams[g] = new
             new_all += new
         kn = normal_fp16((groups * k, hkv, 128), 464_017, 1000 + step, "cuda")
