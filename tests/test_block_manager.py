@@ -404,3 +404,18 @@ def test_alloc_batch_equals_appends_one_by_one(bs):
         o.alloc(big[1], n[1])
     _same_state(h1, o)
     _same_state(h2, o)
+
+
+def test_alloc_batch_argument_edges():
+    h = _pool(8, 16)
+    s = pa.pa_seq_create(h)
+    slots, cow = pa.pa_alloc_batch(h, [], [])
+    assert slots.size == 0 and cow.shape == (0, 2)
+    slots, cow = pa.pa_alloc_batch(h, [s, s], [0, 0])  # zero-token appends change nothing
+    assert slots.size == 0 and (cow == -1).all()
+    assert pa.pa_seq_len(h, s)[0] == 0
+    with pytest.raises(pa.PAError):
+        pa.pa_alloc_batch(h, [s], [-1])
+    with pytest.raises(pa.BadSeqError):
+        pa.pa_alloc_batch(h, [s, 99], [3, 1])
+    assert pa.pa_seq_len(h, s)[0] == 3  # the append before the failing one stays made
