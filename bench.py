@@ -22,13 +22,16 @@ the bandwidth figure is HBM's and not the cache's.
 
 Prints one JSON line.  ``roofline`` is for the decode attention kernel: its
 algorithmic KV bytes per launch (each sequence's K and V, every KV head once,
-plus the fp8 scales or int8 scales and zero points) divided by its average
-duration, from HIP events that
+plus the fp8 scales or int8 scales and zero points; where sequences share
+physical blocks -- ``cb_prefix``, ``prefix_cache``, ``beam_k5`` -- each block
+once, the bytes that must come from HBM, with the per-sequence "logical"
+bytes reported beside them) divided by its average duration, from HIP events that
 the dispatches themselves stamp on the launch stream for every decode launch
 of the last ``--stamp-steps`` (default 1) timed steps.  Event-stamped launches
 slow the stream down (on MI355X one stamped launch per step cost about
 0.09 ms of a 2.7 ms step, one in four 0.19 ms, all 0.32 ms), so only the
-final step carries them.  ``cpu_baseline`` is the fp64 CPU oracle timed on
+final step carries them.  ``ms_per_step_stats`` gives the median, minimum and
+maximum of the timed steps (HIP events at the step boundaries).  ``cpu_baseline`` is the fp64 CPU oracle timed on
 this host on a bounded sample of the same workload, after the timed steps.
 """
 from __future__ import annotations
@@ -61,6 +64,9 @@ BENCH_WORKLOADS = ["gqa_32x4096", "tiny", "cb_prefix", "long_ctx",
                    "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32", "int8_gqa_bs16", "int8_mqa_bs16",
                    "prefix_cache", "beam_k5", "prefill_chunks", "mixed_batch"]
 MULTI_TOKEN_WORKLOADS = ("prefill_chunks", "mixed_batch")
+# Workloads whose sequences share physical blocks: their roofline is priced on
+# the bytes that must come from HBM, each shared block once.
+SHARING_WORKLOADS = ("cb_prefix", "prefix_cache", "beam_k5")
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 
 
@@ -222,7 +228,7 @@ class DecodeBench:
         self.tables_d = self.meta_d[3 * self.S:].view(self.S, self.mb_cap)
         self.n_step = 0
         self.stream = torch.cuda.current_stream().cuda_stream  # every launch goes here
-        self.kv_bytes_log, self.unique_bytes_log, self.lens_log = [], [], []
+        self.kv_bytes_log, self.tables_log, self.lens_log = [], [], []
         torch.cuda.synchronize()
 
     # ---- setup ------------------------------------------------------------------
@@ -361,9 +367,17 @@ class DecodeBench:
         per_tok = 2 * self.hkv * 128 * self.elem
         scales = 2 * self.hkv * 4 if self.fp8 else (4 * self.hkv * 4 if self.int8 else 0)
         self.kv_bytes_log.append(int(lens.astype(np.int64).sum()) * per_tok + scales)
-        if self.name in ("cb_prefix", "prefix_cache", "beam_k5"):
-            self.unique_bytes_log.append(self._unique_tokens(tables, lens) * per_tok + scales)
+        if self.name in SHARING_WORKLOADS:
+            # Counted after the timed region (a host loop over every block).
+            self.tables_log.append(tables)
         self.lens_log.append(lens)
+
+    def unique_bytes(self, i):
+        """Bytes that step i's launches must read from HBM: each physical
+        block once, however many sequences share it (plus the scales)."""
+        per_tok = 2 * self.hkv * 128 * self.elem
+        scales = 2 * self.hkv * 4 if self.fp8 else (4 * self.hkv * 4 if self.int8 else 0)
+        return self._unique_tokens(self.tables_log[i], self.lens_log[i]) * per_tok + scales
 
     def _beam_reselect(self):
         """Beam survivors of one search step: new beam j descends from old beam
@@ -525,7 +539,7 @@ class MultiTokenBench:
         self.sample_n = min(self.S, 4)
         self.sample = (k0[:offs[self.sample_n]].cpu().numpy(), v0[:offs[self.sample_n]].cpu().numpy())
         self.stream = torch.cuda.current_stream().cuda_stream
-        self.kv_bytes_log, self.unique_bytes_log, self.lens_log = [], [], []
+        self.kv_bytes_log, self.tables_log, self.lens_log = [], [], []
         del k0, v0
         torch.cuda.synchronize()
 
@@ -731,20 +745,29 @@ def main(argv=None):
         bench.step()
     torch.cuda.synchronize()
     bench.kv_bytes_log.clear()
-    bench.unique_bytes_log.clear()
+    bench.tables_log.clear()
     bench.lens_log.clear()
     stamp = min(max(args.stamp_steps, 1), args.steps)
     gc.collect()
     gc.disable()  # no collector pauses inside the timed steps
+    # One event per step boundary on the launch stream: per-step GPU-timeline
+    # durations for the median / min / max, with no synchronisation inside.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    marks[0].record()
     for i in range(args.steps):
         if i == args.steps - stamp:  # host-side switch, no synchronisation
             pa.pa_profile_begin(bench.pool.handle, stamp * bench.R, args.time_every)
         bench.step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gc.enable()
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    step_stats = {"median": float(np.median(step_ms)), "min": float(step_ms.min()),
+                  "max": float(step_ms.max()), "steps": args.steps,
+                  "clock": "HIP events at the step boundaries on the launch stream"}
     prof = pa.pa_profile_end(bench.pool.handle)
     status = bench.pool.device_status()
     if status:
@@ -762,13 +785,22 @@ def main(argv=None):
         b.copy_(a)
         torch.cuda.synchronize()
     if multi:
-        print(json.dumps(multi_token_result(bench, args, elapsed, prof, stream_gbps, cpu)), flush=True)
+        res = multi_token_result(bench, args, elapsed, prof, stream_gbps, cpu)
+        res["ms_per_step_stats"] = step_stats
+        print(json.dumps(res), flush=True)
         return 0
     w = bench.w
     n_launch = max(prof["decode_launches"], 1)
     # Every launch of a step reads the same bytes; steps differ by one token
     # per sequence.  Durations are averaged over the stamped launches.
-    bytes_per_launch = float(sum(bench.kv_bytes_log[-stamp:])) / stamp  # the stamped steps
+    logical_per_launch = float(sum(bench.kv_bytes_log[-stamp:])) / stamp  # the stamped steps
+    sharing = bool(bench.tables_log)
+    if sharing:
+        # Shared blocks need to come from HBM once per launch: price on those.
+        n_log = len(bench.lens_log)
+        bytes_per_launch = float(sum(bench.unique_bytes(i) for i in range(n_log - stamp, n_log))) / stamp
+    else:
+        bytes_per_launch = logical_per_launch
     decode_s = prof["decode_ms"] / 1e3 / n_launch
     reduce_s = prof["reduce_ms"] / 1e3 / max(prof["reduce_launches"], 1)
     achieved = bytes_per_launch / decode_s / 1e9
@@ -783,6 +815,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": elapsed * 1e3 / args.steps,
+        "ms_per_step_stats": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -825,19 +858,21 @@ def main(argv=None):
             "traffic": stored_traffic(bench.name),
             "kernel": (f"paged decode attention (per launch: {bench.S} seqs x T_i tokens x "
                        f"{bench.hkv} KV heads x 128 x {bench.elem} B x K,V"
-                       + (" + fp8 scales)" if bench.fp8 else " + int8 scales and zero points)" if bench.int8
-                          else ")")),
+                       + (" + fp8 scales" if bench.fp8 else " + int8 scales and zero points" if bench.int8
+                          else "")
+                       + ("; each physical block counted once however many sequences share it)"
+                          if sharing else ")")),
             "algorithmic_bytes_per_launch": bytes_per_launch,
+            "logical_bytes_per_launch": logical_per_launch,
+            "logical_gbps": logical_per_launch / decode_s / 1e9,
             "timed_launches": prof["decode_launches"],
             "timed_steps": f"last {stamp} of {args.steps}",
             "kernel_source": kernel_source_hash(),
         },
         "cpu_baseline": cpu,
     }
-    if bench.unique_bytes_log:
-        ub = float(sum(bench.unique_bytes_log[-stamp:])) / stamp
-        result["unique_kv_gbps"] = ub / (decode_s + reduce_s) / 1e9
-        result["unique_bytes_per_launch"] = ub
+    if sharing:
+        result["logical_kv_gbps"] = logical_per_launch / (decode_s + reduce_s) / 1e9
     print(json.dumps(result), flush=True)
     return 0
 

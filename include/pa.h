@@ -97,6 +97,11 @@ typedef struct pa_pool_info {
                            (openakashic note, Key Points; youngju.dev page,
                            section "KV 캐시는 왜 메모리를 먹는가") at full pool */
   uint64_t total_bytes; /* kv_bytes + metadata tail: what pa_pool_bind needs   */
+  float softmax_scale;  /* 1/sqrt(head_dim) in fp32, the temperature of
+                           softmax(q K^T / sqrt(d)) V (youngju.dev page, section
+                           "핵심 원리: KV 캐시란 무엇인가"): the scale to pass to
+                           the attention calls when the caller has no other   */
+  int32_t reserved;     /* 0                                                    */
 } pa_pool_info;
 
 typedef struct pa_stats {
@@ -116,28 +121,41 @@ typedef struct pa_profile {
 /* ---- pool ------------------------------------------------------------------ */
 
 /* Create a pool descriptor: per layer, K and V pools of `num_blocks` blocks of
- * `block_size` tokens x `kv_heads` x `head_dim`.  Supported: head_dim 128,
- * block_size 8/16/32, dtype PA_DTYPE_*, num_blocks*block_size < 2^31.
+ * `block_size` tokens x `kv_heads` x `head_dim` (the fixed-size blocks of one
+ * physical pool: youngju.dev page, section "PagedAttention: OS 가상 메모리식
+ * 관리"; their bytes are the KV-size formula of section "KV 캐시는 왜 메모리를
+ * 먹는가").  Supported: head_dim 128, block_size 8/16/32, dtype PA_DTYPE_*,
+ * num_blocks*block_size < 2^31.  Anything else: PA_ERR_INVALID, *out = NULL.
  * No device memory is touched; host-side block management works unbound. */
 int pa_pool_create(int32_t layers, int32_t kv_heads, int32_t head_dim, int32_t block_size,
                    int32_t dtype, int32_t num_blocks, pa_pool** out);
 
-/* Release the host metadata (the caller frees the device buffer). NULL is a no-op. */
+/* Release the host metadata (the caller frees the device buffer). NULL is a no-op.
+ * (Library housekeeping; not a step of the method.) */
 int pa_pool_destroy(pa_pool* pool);
 
+/* Geometry, byte sizes and default softmax scale of a pool (pa_pool_info);
+ * PA_ERR_INVALID for NULL arguments. */
 int pa_pool_info_get(const pa_pool* pool, pa_pool_info* out);
 
 /* Replace the initial free-queue order by a permutation of 0..num_blocks-1
- * (host int32[n], n == num_blocks).  Only valid before the first allocation. */
+ * (host int32[n], n == num_blocks).  Only valid before the first allocation,
+ * else PA_ERR_INVALID.  The queue is the pool's free list (openakashic note,
+ * Key Points: "free queue"; iq-blog ch.4, section "OS Paging에서 가져온 해법");
+ * a seeded permutation places blocks at random physical positions. */
 int pa_pool_set_free_order(pa_pool* pool, const int32_t* perm, int32_t n);
 
-/* Attach caller-owned device memory of info.total_bytes, 256-byte aligned.
+/* Attach caller-owned device memory of info.total_bytes, 256-byte aligned
+ * (the physical pool of youngju.dev page, section "PagedAttention: OS 가상
+ * 메모리식 관리"; fp8 scales: section "KV 양자화: FP8과 INT8").
  * fp8 pools need host fp32 scales k_scales[layers*kv_heads] and v_scales[...]
  * (layer-major); fp16 pools pass NULL.  The library writes the scales, their
  * fp32 reciprocals and a zeroed status word into the tail (synchronously). */
 int pa_pool_bind(pa_pool* pool, void* dev_base, const float* k_scales, const float* v_scales);
 
-/* The same for int8 pools (pa_pool_bind refuses them): host fp32 scales and
+/* The same for int8 pools (pa_pool_bind refuses them; youngju.dev page,
+ * section "KV 양자화: FP8과 INT8": one byte per element needs a scale and a
+ * zero point): host fp32 scales and
  * host int32 zero points in [-128, 127], each [layers*kv_heads] layer-major,
  * for K and for V.  Scales must be positive and finite; otherwise, or for a
  * zero point out of range, PA_ERR_INVALID and nothing is bound.  Inside the
@@ -147,7 +165,9 @@ int pa_pool_bind_int8(pa_pool* pool, void* dev_base, const float* k_scales, cons
 
 /* ---- block manager (host) ------------------------------------------------------ */
 
-/* New empty sequence; ids are 0, 1, 2, ... in creation order, never reused. */
+/* New empty sequence with an empty block table (youngju.dev page, section
+ * "PagedAttention: OS 가상 메모리식 관리": one block table per request); ids
+ * are 0, 1, 2, ... in creation order, never reused.  PA_ERR_INVALID for NULL. */
 int pa_seq_create(pa_pool* pool, int32_t* seq_out);
 
 /* Automatic prefix caching (iq-blog ch.4, section "Prefix Caching";
@@ -167,7 +187,10 @@ int pa_seq_create(pa_pool* pool, int32_t* seq_out);
 int pa_seq_create_cached(pa_pool* pool, const int32_t* tokens, int32_t n, int32_t* seq_out,
                          int32_t* cached_out, int32_t* slots_out);
 
-/* Append n_tokens >= 0 tokens to `seq`.  slots_out (host int32[n_tokens]):
+/* Blocks on demand as a sequence grows (youngju.dev page, section
+ * "PagedAttention: OS 가상 메모리식 관리"; copy-on-write: section "prefix 공유와
+ * copy-on-write"; failure: openakashic note, Key Points).
+ * Append n_tokens >= 0 tokens to `seq`.  slots_out (host int32[n_tokens]):
  * slot of the j-th new token = table[t / B] * B + t % B, t = old_len + j.
  * If the append lands in a partly filled last block shared with another
  * sequence, that block is copied first into a fresh block which replaces it
@@ -180,7 +203,8 @@ int pa_seq_create_cached(pa_pool* pool, const int32_t* tokens, int32_t n, int32_
 int pa_alloc(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* slots_out,
              int32_t* cow_out, void* stream);
 
-/* Batched appends: for k = 0 .. count-1 in order, append n_tokens[k] >= 0
+/* Batched appends (the same pages as pa_alloc): for k = 0 .. count-1 in order,
+ * append n_tokens[k] >= 0
  * tokens to seqs[k] exactly as pa_alloc would (the same allocator state and
  * slots), the slots back to back in slots_out (host int32[sum of n_tokens]).
  * The copy-on-write copies of the whole batch are enqueued on `stream` in one
@@ -194,26 +218,39 @@ int pa_alloc(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* slots_out,
 int pa_alloc_batch(pa_pool* pool, const int32_t* seqs, const int32_t* n_tokens, int32_t count,
                    int32_t* slots_out, int32_t* cow_out, int32_t* done_out, void* stream);
 
-/* New sequence sharing every block of `parent` (each reference count + 1). */
+/* New sequence sharing every block of `parent` (each reference count + 1):
+ * sequences with a common prefix point at the same physical blocks
+ * (youngju.dev page, section "prefix 공유와 copy-on-write"; opsoai page,
+ * section "KV 캐시는 왜 요청이 늘수록 서빙 병목이 되는가": beams share their
+ * prefix).  PA_ERR_BAD_SEQ for an unknown or freed parent. */
 int pa_fork(pa_pool* pool, int32_t parent, int32_t* child_out);
 
 /* Drop `seq`: its blocks are visited last to first, and each one whose
- * reference count reaches zero is appended to the free-queue tail. */
+ * reference count reaches zero is appended to the free-queue tail (blocks
+ * return to the free list when a request ends: iq-blog ch.4, section "OS
+ * Paging에서 가져온 해법"; openakashic note, Key Points).  PA_ERR_BAD_SEQ for an
+ * unknown or freed sequence. */
 int pa_free(pa_pool* pool, int32_t seq);
 
 /* Tokens and blocks of `seq` (either out pointer may be NULL); PA_ERR_BAD_SEQ
  * for an unknown or freed sequence. */
 int pa_seq_len(const pa_pool* pool, int32_t seq, int32_t* len_out, int32_t* num_blocks_out);
 
-/* Export block tables: tables_out host int32[n][max_blocks] (rows padded with
- * -1), lens_out host int32[n].  PA_ERR_INVALID if a table is longer than max_blocks. */
+/* Export block tables (logical block -> physical block, youngju.dev page,
+ * section "PagedAttention: OS 가상 메모리식 관리"; int32 entries, iq-blog ch.4,
+ * section "vLLM의 4-Layer 통합 아키텍처"): tables_out host int32[n][max_blocks]
+ * (rows padded with -1), lens_out host int32[n].  PA_ERR_INVALID if a table is
+ * longer than max_blocks, PA_ERR_BAD_SEQ for an unknown sequence. */
 int pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n, int32_t max_blocks,
                     int32_t* tables_out, int32_t* lens_out);
 
-/* The pool's block, sequence, copy-on-write and prefix-cache counters (pa_stats). */
+/* The pool's block, sequence, copy-on-write and prefix-cache counters
+ * (pa_stats; inspection, not a step of the method). */
 int pa_pool_stats(const pa_pool* pool, pa_stats* out);
 
-/* Allocator state for inspection: reference count of every block (host
+/* Allocator state for inspection (the reference counts of youngju.dev page,
+ * section "prefix 공유와 copy-on-write", and the free queue of the openakashic
+ * note, Key Points): reference count of every block (host
  * int32[num_blocks]); the free queue head to tail (host int32[num_blocks],
  * *n_out = number of free blocks). */
 int pa_refcounts(const pa_pool* pool, int32_t* out);
@@ -221,7 +258,9 @@ int pa_free_queue(const pa_pool* pool, int32_t* out, int32_t* n_out);
 
 /* ---- device operations ---------------------------------------------------------- */
 
-/* Reshape-and-cache scatter: token t's K and V (device fp16 [n][kv_heads][head_dim],
+/* Reshape-and-cache scatter (slot = block * block_size + offset: youngju.dev
+ * page, section "PagedAttention: OS 가상 메모리식 관리"; one-byte elements:
+ * section "KV 양자화: FP8과 INT8"): token t's K and V (device fp16 [n][kv_heads][head_dim],
  * 4-byte aligned) go to slot slot_mapping[t] (device int32[n]) of `layer`; negative slots are
  * skipped.  fp8 pools store encode(f32(x) * f32(1/scale)) with saturation to
  * +-448 and round-to-nearest-even; int8 pools store
@@ -229,7 +268,8 @@ int pa_free_queue(const pa_pool* pool, int32_t* out, int32_t* n_out);
 int pa_write_kv(pa_pool* pool, int32_t layer, const void* k_new, const void* v_new,
                 const int32_t* slot_mapping, int32_t n_tokens, void* stream);
 
-/* Inverse of pa_write_kv: read the stored K/V of each slot into device
+/* Inverse of pa_write_kv (for tests and inspection; slot arithmetic as there):
+ * read the stored K/V of each slot into device
  * k_out/v_out [n][kv_heads][head_dim] (fp16 values, raw uint8 codes for fp8,
  * int8 codes c for int8).
  * Negative slots leave their rows untouched. */
@@ -243,15 +283,23 @@ int pa_gather_kv(const pa_pool* pool, int32_t layer, const int32_t* slot_mapping
  * ceiling the decode kernel is compared with. */
 int pa_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, void* stream);
 
-/* Copy whole blocks src[i] -> dst[i] (host int32[n]) across all layers, K and V. */
+/* Copy whole blocks src[i] -> dst[i] (host int32[n]) across all layers, K and V:
+ * the copy of copy-on-write (youngju.dev page, section "prefix 공유와
+ * copy-on-write").  PA_ERR_INVALID for a block id outside the pool. */
 int pa_copy_blocks(pa_pool* pool, const int32_t* src, const int32_t* dst, int32_t n, void* stream);
 
 /* Device bytes of the workspace pa_decode needs for this launch shape
- * (0 when it runs in a single pass).  partition_tokens as in pa_decode. */
+ * (0 when it runs in a single pass).  partition_tokens as in pa_decode.
+ * (Split-context partials are not on the pages: a softmax over a union of
+ * disjoint chunks, merged by log-sum-exp.) */
 int pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                               int32_t max_blocks, int32_t partition_tokens, uint64_t* bytes_out);
 
-/* Paged decode attention for one layer.
+/* Paged decode attention for one layer: softmax(q K^T * scale) V over each
+ * sequence's cached tokens (youngju.dev page, section "핵심 원리: KV 캐시란
+ * 무엇인가"), K/V gathered through the block table (iq-blog ch.4, section
+ * "PagedAttention 알고리즘"), query heads grouped onto KV heads (youngju.dev
+ * page, section "GQA와 MQA").
  *   q            device fp16 [num_seqs][num_q_heads][head_dim], 16-byte aligned
  *   block_tables device int32 [num_seqs][max_blocks] (entries past a sequence's
  *                last block are ignored)
@@ -283,8 +331,8 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
               int32_t num_seqs, const int32_t* seq_order, float scale, int32_t partition_tokens,
               void* out, void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* One decode step fused: the scatter of pa_write_kv and the attention of
- * pa_decode in one launch.  k_new, v_new: device fp16 [num_seqs][kv_heads]
+/* One decode step fused (passages as for pa_write_kv and pa_decode): the
+ * scatter of pa_write_kv and the attention of pa_decode in one launch.  k_new, v_new: device fp16 [num_seqs][kv_heads]
  * [head_dim], 16-byte aligned, the new token of every sequence; slot_mapping: device int32
  * [num_seqs].  Each sequence's new token must be its last one, T_i - 1, at
  * the slot its block table gives that token (what pa_alloc returned for it);
@@ -332,11 +380,13 @@ int pa_multi_token_attention(pa_pool* pool, int32_t layer, const void* q, int32_
                              const int32_t* context_lens, int32_t num_seqs, float scale, void* out,
                              void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* Host helper: order_out[0..n) = indices of lens[0..n) by decreasing length,
+/* Host helper (scheduling, not a step of the method): order_out[0..n) =
+ * indices of lens[0..n) by decreasing length,
  * equal lengths in increasing index (a stable sort), for pa_decode's seq_order. */
 int pa_order_longest_first(const int32_t* lens, int32_t n, int32_t* order_out);
 
-/* The two halves of a partitioned pa_decode, callable separately.
+/* The two halves of a partitioned pa_decode, callable separately (not on the
+ * pages: the chunked softmax and its log-sum-exp merge).
  * pa_decode_partials writes, for chunk c of every (sequence, query head), into
  * the workspace laid out as three consecutive fp32 arrays of C = ceil(max_blocks
  * * block_size / P) chunks each:
@@ -356,10 +406,12 @@ int pa_lse_reduce(pa_pool* pool, const void* workspace, uint64_t workspace_bytes
                   const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                   int32_t max_blocks, int32_t partition_tokens, void* out, void* stream);
 
-/* Read (and optionally clear) the pool's device status word; synchronises `stream`. */
+/* Read (and optionally clear) the pool's device status word (PA_DEV_* bits:
+ * contract violations the kernels detected and skipped); synchronises `stream`. */
 int pa_device_status(pa_pool* pool, uint32_t* flags_out, int32_t clear, void* stream);
 
-/* Kernel timing: while enabled, the pa_decode / pa_decode_partials launches
+/* Kernel timing (measurement, not a step of the method): while enabled, the
+ * pa_decode / pa_decode_partials launches
  * numbered 0, every, 2*every, ... since pa_profile_begin (up to max_launches of
  * them; every >= 1, 1 = all) are dispatched with HIP start/stop events that
  * the dispatch itself stamps at the kernel's start and end on the launch

@@ -31,7 +31,8 @@ class pa_pool_info(C.Structure):
     _fields_ = [("layers", C.c_int32), ("kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("block_size", C.c_int32), ("dtype", C.c_int32), ("num_blocks", C.c_int32),
                 ("elem_bytes", C.c_int32), ("bound", C.c_int32),
-                ("tile_bytes", C.c_uint64), ("kv_bytes", C.c_uint64), ("total_bytes", C.c_uint64)]
+                ("tile_bytes", C.c_uint64), ("kv_bytes", C.c_uint64), ("total_bytes", C.c_uint64),
+                ("softmax_scale", C.c_float), ("reserved", C.c_int32)]
 
 
 class pa_stats(C.Structure):

@@ -295,6 +295,9 @@ int pa_pool_info_get(const pa_pool* p, pa_pool_info* out) {
   out->tile_bytes = p->tile_bytes;
   out->kv_bytes = p->kv_bytes;
   out->total_bytes = p->total_bytes;
+  // 1/sqrt(d): the square root and the division each rounded to fp32.
+  out->softmax_scale = 1.0f / std::sqrt(static_cast<float>(p->head_dim));
+  out->reserved = 0;
   return PA_OK;
 }
 

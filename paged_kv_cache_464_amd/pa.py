@@ -9,7 +9,6 @@ non-zero status.  All computation happens in libpa.so.
 from __future__ import annotations
 
 import ctypes as C
-import math
 
 import numpy as np
 import torch
@@ -331,7 +330,7 @@ def pa_decode(h, layer, q, block_tables, context_lens, out=None, scale=None, par
     op = _dev(out, torch.float16, tuple(q.shape), "out")
     wp, wb, workspace = _workspace(h, s, hq, mb, partition_tokens, workspace, q.device)
     if scale is None:
-        scale = 1.0 / math.sqrt(info["head_dim"])
+        scale = info["softmax_scale"]
     _check(_L().pa_decode(C.c_void_p(h), int(layer), qp, hq, tp, mb, lp, s, orp, float(scale),
                           int(partition_tokens), op, wp, wb, _stream(stream)))
     return out
@@ -352,7 +351,7 @@ def pa_write_kv_decode(h, layer, k_new, v_new, slot_mapping, q, block_tables, co
     op = _dev(out, torch.float16, tuple(q.shape), "out")
     wp, wb, workspace = _workspace(h, s, hq, mb, partition_tokens, workspace, q.device)
     if scale is None:
-        scale = 1.0 / math.sqrt(info["head_dim"])
+        scale = info["softmax_scale"]
     _check(_L().pa_write_kv_decode(C.c_void_p(h), int(layer), kp, vp, sp, qp, hq, tp, mb, lp, s, orp,
                                    float(scale), int(partition_tokens), op, wp, wb, _stream(stream)))
     return out
@@ -388,7 +387,7 @@ def pa_multi_token_attention(h, layer, q, query_start, block_tables, context_len
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     wp = _dev(workspace, torch.uint8, None, "workspace")
     if scale is None:
-        scale = 1.0 / math.sqrt(info["head_dim"])
+        scale = info["softmax_scale"]
     _check(_L().pa_multi_token_attention(C.c_void_p(h), int(layer), qp, hq, qsp, tp, mb, lp, s, float(scale),
                                          op, wp, workspace.numel(), _stream(stream)))
     return out
@@ -401,7 +400,7 @@ def pa_decode_partials(h, layer, q, block_tables, context_lens, partition_tokens
     orp = _order_arg(seq_order, s)
     wp, wb, workspace = _workspace(h, s, hq, mb, partition_tokens, workspace, q.device)
     if scale is None:
-        scale = 1.0 / math.sqrt(info["head_dim"])
+        scale = info["softmax_scale"]
     _check(_L().pa_decode_partials(C.c_void_p(h), int(layer), qp, hq, tp, mb, lp, s, orp, float(scale),
                                    int(partition_tokens), wp, wb, _stream(stream)))
     return workspace_views(workspace, s, hq, mb * info["block_size"], partition_tokens, info["head_dim"])

@@ -12,9 +12,7 @@ from oracle.kvstore import OracleKVStore
 from paged_kv_cache_464_amd import pa
 from workloads import amax_scales, free_order, head_offsets, minmax_int8_params, normal_fp16
 
-FP16_ATOL = 2e-3  # max-abs error vs the fp64 oracle, fp16 K/V
-FP8_RTOL = 2e-2   # per (seq, head) row: max|err| <= 2e-2 * max|ref|, fp8 K/V
-INT8_RTOL = 4e-3  # per (seq, head) row: max|err| <= 4e-3 * max|ref|, int8 K/V
+from tests import parity
 
 
 def say(*a):
@@ -100,17 +98,21 @@ def oracle_decode(c, seq_idx, scale=None):
 
 
 def assert_close(gpu_out, ref, dtype, what=""):
+    """GPU output against the fp64 oracle under the criteria of tests/parity.py
+    (stated: 2e-3 max-abs for fp16, 2e-2 row-relative for fp8; derived: 4e-3
+    row-relative for every kind); the observed errors go to the margins file."""
     got = gpu_out.double().cpu().numpy() if isinstance(gpu_out, torch.Tensor) else gpu_out
-    assert np.isfinite(got).all(), f"{what}: non-finite output"
-    err = np.abs(got - ref)
-    if dtype == "fp16":
-        worst = err.max()
-        say(what, f"max_abs_err={worst:.3e} (tol {FP16_ATOL})")
-        assert worst <= FP16_ATOL, f"{what}: max abs err {worst}"
-    else:
-        tol = FP8_RTOL if dtype == "fp8" else INT8_RTOL
-        row_err = err.max(axis=-1)
-        row_ref = np.abs(ref).max(axis=-1)
-        ratio = (row_err / np.maximum(row_ref, 1e-30)).max()
-        say(what, f"max_row_rel_err={ratio:.3e} (tol {tol})")
-        assert ratio <= tol, f"{what}: row-relative err {ratio}"
+    bad, max_abs, row_rel = parity.failures(got, ref, dtype)
+    say(what, f"{dtype} max_abs_err={max_abs:.3e} max_row_rel_err={row_rel:.3e}")
+    parity.record(what, dtype, max_abs, row_rel)
+    assert not bad, f"{what}: " + "; ".join(bad)
+
+
+def assert_partials(m, l, o, om, ol, oo, dtype, what=""):
+    """Chunk partials of one sequence, every query head, against the oracle's:
+    m (the GPU keeps base-2 units) within 2e-3, l within 5e-3 relative, and
+    each chunk's normalised o under the output criteria (row = one chunk of
+    one head)."""
+    np.testing.assert_allclose(np.asarray(m) * np.log(2.0), om, rtol=0, atol=2e-3, err_msg=f"{what}: m")
+    np.testing.assert_allclose(np.asarray(l), ol, rtol=5e-3, atol=0, err_msg=f"{what}: l")
+    assert_close(np.asarray(o, dtype=np.float64), oo, dtype, f"{what}: chunk o")

@@ -81,7 +81,7 @@ def test_out_of_contract_lengths_are_flagged_and_read_safely():
         flags = c.pool.device_status(clear=True)
         assert flags & pa.PA_DEV_BAD_LEN, (mode, flags)
         got = out.double().cpu().numpy()
-        assert np.abs(got[0] - ref[0]).max() <= 2e-3, mode
+        assert_close(got[:1], ref[:1], "fp16", f"bad lengths, valid row, P={mode}")
         assert (got[1] == 0).all(), mode
     assert c.pool.device_status() == 0
 
@@ -97,7 +97,7 @@ def test_out_of_range_table_entry_is_flagged_and_read_as_block_zero():
         out = c.pool.decode(0, c.q, tables, c.lens_dev, partition_tokens=mode)
         torch.cuda.synchronize()
         assert c.pool.device_status(clear=True) & pa.PA_DEV_BAD_BLOCK, mode
-        assert np.abs(out[0].double().cpu().numpy() - ref[0]).max() <= 2e-3, mode
+        assert_close(out[:1], ref[:1], "fp16", f"bad table entry, valid row, P={mode}")
     assert c.pool.device_status() == 0
 
 
