@@ -85,6 +85,9 @@ extern "C" {
 #define PA_DEV_BAD_LEN 4u   /* a context length < 1 or > max_blocks*block_size  */
 #define PA_DEV_BAD_ORDER 8u /* a seq_order entry outside [0, num_seqs) was skipped */
 
+/* ---- pa_decode_noalloc ------------------------------------------------------ */
+#define PA_NOALLOC_SCRATCH_BYTES 33554432 /* 32 MiB of static device scratch per GPU */
+
 typedef struct pa_pool pa_pool; /* opaque */
 
 typedef struct pa_pool_info {
@@ -330,6 +333,23 @@ int pa_decode(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
               const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
               int32_t num_seqs, const int32_t* seq_order, float scale, int32_t partition_tokens,
               void* out, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): pa_decode
+ * with the same arguments and results, minus the workspace.  When the plan
+ * splits contexts, the chunk partials go to a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; a launch whose partials need more
+ * (pa_decode_workspace_bytes > PA_NOALLOC_SCRATCH_BYTES) fails with
+ * PA_ERR_INVALID and launches nothing.  The call allocates nothing (no
+ * hipMalloc, no host allocation).  Every call on one GPU shares that array,
+ * written before it is read within a call (nothing needs clearing): calls
+ * that overlap on one GPU (several streams or host threads at once) race.
+ * The current device must be the pool's. */
+int pa_decode_noalloc(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                      const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                      int32_t num_seqs, const int32_t* seq_order, float scale, int32_t partition_tokens,
+                      void* out, void* stream);
 
 /* One decode step fused (passages as for pa_write_kv and pa_decode): the
  * scatter of pa_write_kv and the attention of pa_decode in one launch.  k_new, v_new: device fp16 [num_seqs][kv_heads]

@@ -26,6 +26,8 @@ PA_DEV_BAD_BLOCK = 2
 PA_DEV_BAD_LEN = 4
 PA_DEV_BAD_ORDER = 8
 
+PA_NOALLOC_SCRATCH_BYTES = 33554432
+
 
 class pa_pool_info(C.Structure):
     _fields_ = [("layers", C.c_int32), ("kv_heads", C.c_int32), ("head_dim", C.c_int32),
@@ -79,6 +81,7 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (C.c_int, [_P, _I32, _I32, _I32, _I32, C.POINTER(C.c_uint64)]),
     "pa_decode": (C.c_int, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _P, C.c_float, _I32, _P, _P,
                             C.c_uint64, _P]),
+    "pa_decode_noalloc": (C.c_int, [_P, _I32, _P, _I32, _P, _I32, _P, _I32, _P, C.c_float, _I32, _P, _P]),
     "pa_order_longest_first": (C.c_int, [_PI32, _I32, _PI32]),
     "pa_stream_read": (C.c_int, [_P, C.c_uint64, _P, _P]),
     "pa_write_kv_decode": (C.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _P,

@@ -7,8 +7,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
-#include <string>
 #include <vector>
 
 #include "../../include/pa.h"
@@ -17,15 +17,14 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+// A fixed buffer, so that reporting a failure allocates nothing.
+thread_local char g_last_error[512];
 
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return code;
 }
 
@@ -39,6 +38,39 @@ constexpr int kMinSplitTokens = 1024;  // shorter contexts always run in one pas
 
 }  // namespace
 
+// Split-context partials of pa_decode_noalloc: a fixed device array, one copy
+// per GPU, held until the process ends.  Host code never uses its name as an
+// address (on the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_err[kMaxDevices] = {};
+
+// Looks up (once per device) the device address of `scratch` on device `dev`,
+// which must be current.  Returns null if the lookup failed.
+void* scratch_on_current_device(int dev, hipError_t* err) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev] && g_scratch_err[dev] == hipSuccess) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && ptr) g_scratch_ptr[dev] = ptr;
+    else g_scratch_err[dev] = e != hipSuccess ? e : hipErrorInvalidSymbol;
+  }
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 static_assert(PA_DTYPE_FP16 == pa::kF16 && PA_DTYPE_FP8_E4M3 == pa::kF8 && PA_DTYPE_INT8 == pa::kI8,
               "dtype codes are the kernels' element kinds");
 
@@ -49,6 +81,8 @@ struct pa_pool {
   bool bound = false;
   int device = -1;
   int num_cus = 256;
+  void* scratch = nullptr;           // device address of `scratch` on `device`
+  hipError_t scratch_err = hipSuccess;
   pa::PoolGeom geom{};
   // kernel timing
   bool profiling = false;
@@ -255,7 +289,7 @@ int check_decode_args(pa_pool* pool, int32_t layer, const void* q, const int32_t
 
 extern "C" {
 
-const char* pa_last_error(void) { return g_last_error.c_str(); }
+const char* pa_last_error(void) { return g_last_error; }
 
 int pa_pool_create(int32_t layers, int32_t kv_heads, int32_t head_dim, int32_t block_size,
                    int32_t dtype, int32_t num_blocks, pa_pool** out) {
@@ -367,6 +401,9 @@ int bind_pool(pa_pool* p, void* dev_base, const float* k_scales, const float* v_
   g.scales = reinterpret_cast<float*>(base + p->scales_offset);
   g.status = reinterpret_cast<uint32_t*>(base + p->status_offset);
   p->device = dev;
+  // Set-up of pa_decode_noalloc's partials on this device (once per device;
+  // a failure is reported by that call, not by the bind).
+  p->scratch = scratch_on_current_device(dev, &p->scratch_err);
   p->bound = true;
   return PA_OK;
 }
@@ -624,6 +661,36 @@ int pa_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
               void* out, void* workspace, uint64_t workspace_bytes, void* stream) {
   return run_decode(p, layer, q, num_q_heads, block_tables, max_blocks, context_lens, num_seqs,
                     seq_order, scale, partition_tokens, out, workspace, workspace_bytes, stream, 0);
+}
+
+int pa_decode_noalloc(pa_pool* p, int32_t layer, const void* q, int32_t num_q_heads,
+                      const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                      int32_t num_seqs, const int32_t* seq_order, float scale, int32_t partition_tokens,
+                      void* out, void* stream) {
+  int rc = check_bound(p);
+  if (rc) return rc;
+  Plan pl;
+  if ((rc = make_plan(p, num_seqs, num_q_heads, max_blocks, partition_tokens, &pl))) return rc;
+  void* ws = nullptr;
+  uint64_t ws_bytes = 0;
+  if (pl.partial && num_seqs > 0) {
+    if (pl.ws_bytes > PA_NOALLOC_SCRATCH_BYTES)
+      return fail(PA_ERR_INVALID,
+                  "this launch needs %llu bytes of split-context partials, more than the %llu-byte "
+                  "static scratch of pa_decode_noalloc (use pa_decode with a workspace, or fewer chunks)",
+                  static_cast<unsigned long long>(pl.ws_bytes),
+                  static_cast<unsigned long long>(PA_NOALLOC_SCRATCH_BYTES));
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != p->device)
+      return fail(PA_ERR_INVALID, "current device %d is not the pool's device %d", dev, p->device);
+    if (!p->scratch) return hip_fail(p->scratch_err, "device address of the static scratch");
+    ws = p->scratch;
+    ws_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
+  return run_decode(p, layer, q, num_q_heads, block_tables, max_blocks, context_lens, num_seqs,
+                    seq_order, scale, partition_tokens, out, ws, ws_bytes, stream, 0);
 }
 
 int pa_write_kv_decode(pa_pool* p, int32_t layer, const void* k_new, const void* v_new,

@@ -15,7 +15,8 @@ import torch
 
 from . import _lib
 from ._lib import (PA_DTYPE_FP16, PA_DTYPE_FP8_E4M3, PA_DTYPE_INT8, PA_ERR_BAD_SEQ, PA_ERR_NO_BLOCKS,  # noqa: F401
-                   PA_DEV_BAD_BLOCK, PA_DEV_BAD_LEN, PA_DEV_BAD_ORDER, PA_DEV_BAD_SLOT)
+                   PA_DEV_BAD_BLOCK, PA_DEV_BAD_LEN, PA_DEV_BAD_ORDER, PA_DEV_BAD_SLOT,
+                   PA_NOALLOC_SCRATCH_BYTES)
 
 
 class PAError(RuntimeError):
@@ -336,6 +337,20 @@ def pa_decode(h, layer, q, block_tables, context_lens, out=None, scale=None, par
     return out
 
 
+def pa_decode_noalloc(h, layer, q, block_tables, context_lens, out, scale=None, partition_tokens=0,
+                      stream=None, seq_order=None):
+    """pa_decode without a workspace: split-context partials live in the
+    library's static device scratch.  ``out`` is required (no allocation)."""
+    info, s, hq, mb, qp, tp, lp = _decode_args(h, q, block_tables, context_lens)
+    orp = _order_arg(seq_order, s)
+    op = _dev(out, torch.float16, tuple(q.shape), "out")
+    if scale is None:
+        scale = info["softmax_scale"]
+    _check(_L().pa_decode_noalloc(C.c_void_p(h), int(layer), qp, hq, tp, mb, lp, s, orp, float(scale),
+                                  int(partition_tokens), op, _stream(stream)))
+    return out
+
+
 def pa_write_kv_decode(h, layer, k_new, v_new, slot_mapping, q, block_tables, context_lens,
                        out=None, scale=None, partition_tokens=0, workspace=None, stream=None,
                        seq_order=None):
@@ -552,6 +567,9 @@ class PagedKVPool:
 
     def decode(self, layer, q, block_tables, context_lens, **kw):
         return pa_decode(self.handle, layer, q, block_tables, context_lens, **kw)
+
+    def decode_noalloc(self, layer, q, block_tables, context_lens, out, **kw):
+        return pa_decode_noalloc(self.handle, layer, q, block_tables, context_lens, out, **kw)
 
     def multi_token_attention(self, layer, q, query_start, block_tables, context_lens, **kw):
         return pa_multi_token_attention(self.handle, layer, q, query_start, block_tables, context_lens, **kw)
