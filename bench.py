@@ -54,7 +54,8 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: KV GB/s read + % HBM peak; tokens/s at 32×4096 GQA"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_464_amd", "csrc", f)
-                  for f in ("decode_kernels.hip", "layout.hpp", "kernels.hpp", "token_store.hpp")]
+                  for f in ("decode_engine.hpp", "decode_inst.hip", "decode_kernels.hip", "layout.hpp",
+                            "kernels.hpp", "token_store.hpp")]
 KERNEL_SOURCES.append(os.path.join(ROOT, "paged_kv_cache_464_amd", "build.py"))  # compiler flags
 LLC_BYTES = 256 << 20  # MI355X Infinity Cache
 PREFIX_ROW_TABLE = 1 << 16  # distinct K/V rows of the prefix_cache workload

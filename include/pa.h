@@ -127,7 +127,7 @@ typedef struct pa_profile {
  * `block_size` tokens x `kv_heads` x `head_dim` (the fixed-size blocks of one
  * physical pool: youngju.dev page, section "PagedAttention: OS 가상 메모리식
  * 관리"; their bytes are the KV-size formula of section "KV 캐시는 왜 메모리를
- * 먹는가").  Supported: head_dim 128, block_size 8/16/32, dtype PA_DTYPE_*,
+ * 먹는가").  Supported: head_dim 64 or 128, block_size 8/16/32, dtype PA_DTYPE_*,
  * num_blocks*block_size < 2^31.  Anything else: PA_ERR_INVALID, *out = NULL.
  * No device memory is touched; host-side block management works unbound. */
 int pa_pool_create(int32_t layers, int32_t kv_heads, int32_t head_dim, int32_t block_size,
@@ -264,7 +264,7 @@ int pa_free_queue(const pa_pool* pool, int32_t* out, int32_t* n_out);
 /* Reshape-and-cache scatter (slot = block * block_size + offset: youngju.dev
  * page, section "PagedAttention: OS 가상 메모리식 관리"; one-byte elements:
  * section "KV 양자화: FP8과 INT8"): token t's K and V (device fp16 [n][kv_heads][head_dim],
- * 4-byte aligned) go to slot slot_mapping[t] (device int32[n]) of `layer`; negative slots are
+ * 16-byte aligned) go to slot slot_mapping[t] (device int32[n]) of `layer`; negative slots are
  * skipped.  fp8 pools store encode(f32(x) * f32(1/scale)) with saturation to
  * +-448 and round-to-nearest-even; int8 pools store
  * clamp(rint(f32(x) * f32(1/scale)) + zero, -128, 127). */

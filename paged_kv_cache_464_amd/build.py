@@ -21,6 +21,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libpa.so")
 
 HIP_SOURCES = ["cache_kernels.hip", "decode_kernels.hip", "capi.cpp"]
+# decode_inst.hip is compiled once per (element kind, head_dim): the decode and
+# multi-token kernel instantiations of each pair build in parallel.
+INST_SOURCE = "decode_inst.hip"
+INSTANCES = [(kind, d) for kind in (0, 1, 2) for d in (64, 128)]
 HOST_SOURCES = ["block_manager.cpp"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
@@ -34,7 +38,7 @@ HIP_FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature"
 # not by tests on values; the encoders test NaN on bit patterns), so they are
 # built without NaN semantics: fmaxf then needs no quieting of its inputs,
 # which took two of every three v_max_f32 in the softmax maxima.
-FILE_FLAGS = {"decode_kernels.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"decode_kernels.hip": ["-fno-honor-nans"], INST_SOURCE: ["-fno-honor-nans"]}
 
 
 def _hipcc() -> str:
@@ -64,6 +68,11 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         obj = os.path.join(BUILD_DIR, src + ".o")
         jobs.append([hipcc, *HIP_FLAGS, *COMMON, *FILE_FLAGS.get(src, []), *extra_flags, "-c",
                      os.path.join(CSRC, src), "-o", obj])
+    for kind, d in INSTANCES:
+        obj = os.path.join(BUILD_DIR, f"decode_inst_k{kind}_d{d}.o")
+        jobs.append([hipcc, *HIP_FLAGS, *COMMON, *FILE_FLAGS[INST_SOURCE], *extra_flags,
+                     f"-DPA_INST_KIND={kind}", f"-DPA_INST_D={d}", "-c",
+                     os.path.join(CSRC, INST_SOURCE), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         jobs.append([hipcc, *COMMON, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])

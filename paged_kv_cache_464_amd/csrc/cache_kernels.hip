@@ -19,29 +19,196 @@ namespace {
 
 constexpr int kWaves = 4;  // waves per 256-thread workgroup
 
-template <int KIND>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Reshape-and-cache scatter.  A workgroup takes a window of kWin consecutive
+// input tokens of one KV head:
+//  1. their slots and their K and V rows (coalesced 16-byte loads), already
+//     in the pool's element form (fp16 bits, E4M3FN or int8 codes), go to LDS;
+//  2. K: each token's D / X chunks of X consecutive dims are 16-byte pieces
+//     of the tile (chunk-major, token-minor inside a run of min(B, 16) slots),
+//     so lane (token, chunk) stores one piece and the tokens of consecutive
+//     slots fill contiguous 16-byte runs;
+//  3. V: a 16-byte piece of the tile holds 4 slots (4t .. 4t+3) x X/4 dims.
+//     Where four consecutive tokens of the window go to such an aligned
+//     group of four slots (a prefill, at any input offset) the piece is
+//     assembled from LDS and stored whole; the remaining tokens (a decode
+//     token, the ends of a window or of a sequence) store element by element.
+// Every slot is written by at most one token of a call (the caller's
+// contract); tokens with a negative slot are skipped, slots past the pool set
+// PA_DEV_BAD_SLOT and are skipped.
+constexpr int kWin = 64;
+
+template <int KIND, int D>
 __global__ __launch_bounds__(256) void write_kv_kernel(PoolGeom g, int layer,
                                                        const _Float16* __restrict__ k_new,
                                                        const _Float16* __restrict__ v_new,
                                                        const int32_t* __restrict__ slots,
                                                        int n_tokens) {
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wave >= static_cast<int64_t>(n_tokens) * g.kv_heads) return;
-  const int tok = static_cast<int>(wave / g.kv_heads);
-  const int h = static_cast<int>(wave % g.kv_heads);
-  const int slot = slots[tok];
-  if (slot < 0) return;
-  if (slot >= g.num_blocks * g.block_size) {
-    if (lane == 0) atomicOr(g.status, kDevBadSlot);
-    return;
+  constexpr int ELEM = kind_bytes(KIND);
+  constexpr int X = 16 / ELEM;          // elements per 16-byte piece
+  constexpr int R = X / 4;              // 16-dim groups per V piece
+  constexpr int ROW = D * ELEM + 16;    // LDS row of one token (padded against bank conflicts)
+  constexpr int NRP = D * ELEM / 64;    // V pieces per (slot group of 4, lane n)
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[kWin * ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kWin * ROW];
+  __shared__ int32_t s_slot[kWin];
+  __shared__ int32_t s_flag[kWin];             // 1: token leads a complete group of four slots
+  __shared__ int32_t s_lead[kWin], s_rest[kWin];  // compacted token lists
+  __shared__ int32_t s_n[2];
+
+  const int tid = threadIdx.x;
+  // The KV head varies fastest over the grid: the workgroups that run
+  // together read every head of the same input rows (whole rows of
+  // kv_heads * D values) and write the neighbouring tiles of the same blocks.
+  const int h = static_cast<int>(blockIdx.x % g.kv_heads);
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x / g.kv_heads) * kWin;
+  const int nw = static_cast<int>((n_tokens - i0) < kWin ? (n_tokens - i0) : kWin);
+  const int bs = g.block_size;
+  const int cap = g.num_blocks * bs;
+  if (tid < kWin) {
+    int s = tid < nw ? slots[i0 + tid] : -1;
+    if (s >= cap) {
+      atomicOr(g.status, kDevBadSlot);
+      s = -1;
+    }
+    s_slot[tid] = s;
   }
-  const int64_t src = (static_cast<int64_t>(tok) * g.kv_heads + h) * kHeadDim;
-  store_token<KIND>(g, layer, h, slot, k_new + src, v_new + src, lane);
+  // 1. rows into LDS in the pool's form
+  float k_inv = 1.0f, v_inv = 1.0f, k_z = 0.0f, v_z = 0.0f;
+  if constexpr (ELEM == 1) {
+    const int lh = layer * g.kv_heads + h;
+    const int lhs = g.layers * g.kv_heads;
+    k_inv = g.scales[2 * lhs + lh];
+    v_inv = g.scales[3 * lhs + lh];
+    k_z = g.scales[4 * lhs + lh];
+    v_z = g.scales[5 * lhs + lh];
+  }
+  constexpr int kPieces = D / 8;                 // 16-byte input pieces (8 fp16) per row
+  constexpr int kPer = kWin * kPieces / 256;      // pieces of K (and of V) per thread
+  // Every load of the thread is issued before any is used.
+  u32x4 kk[kPer], vv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int idx = tid + 256 * u;
+    const int t = idx / kPieces, c = idx % kPieces;
+    if (t < nw) {
+      const int64_t src = ((i0 + t) * g.kv_heads + h) * D + c * 8;
+      kk[u] = *reinterpret_cast<const u32x4*>(k_new + src);
+      vv[u] = *reinterpret_cast<const u32x4*>(v_new + src);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int idx = tid + 256 * u;
+    const int t = idx / kPieces, c = idx % kPieces;
+    if (t >= nw) continue;
+    if constexpr (ELEM == 2) {
+      *reinterpret_cast<u32x4*>(s_k + t * ROW + c * 16) = kk[u];
+      *reinterpret_cast<u32x4*>(s_v + t * ROW + c * 16) = vv[u];
+    } else {
+      u32x2 kc, vc;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        uint32_t kw = 0, vw = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t kh = kk[u][2 * w + (e >> 1)] >> (16 * (e & 1));
+          const uint32_t vh = vv[u][2 * w + (e >> 1)] >> (16 * (e & 1));
+          kw |= encode_byte<KIND>(half_bits_to_float(kh & 0xFFFFu) * k_inv, k_z) << (8 * e);
+          vw |= encode_byte<KIND>(half_bits_to_float(vh & 0xFFFFu) * v_inv, v_z) << (8 * e);
+        }
+        kc[w] = kw;
+        vc[w] = vw;
+      }
+      *reinterpret_cast<u32x2*>(s_k + t * ROW + c * 8) = kc;
+      *reinterpret_cast<u32x2*>(s_v + t * ROW + c * 8) = vc;
+    }
+  }
+  __syncthreads();
+  const uint64_t head_off = static_cast<uint64_t>(h) * g.tile_bytes;
+  uint8_t* kl = g.k_layer(layer) + head_off;
+  uint8_t* vl = g.v_layer(layer) + head_off;
+  // Groups of four slots filled whole by four consecutive tokens: the
+  // leading token of each, and the tokens outside every such group.
+  if (tid < kWin) {
+    const int s = s_slot[tid];
+    bool lead = s >= 0 && (s & 3) == 0 && tid + 3 < nw;
+    if (lead) {
+#pragma unroll
+      for (int k = 1; k < 4; ++k) lead = lead && s_slot[tid + k] == s + k;
+    }
+    s_flag[tid] = lead ? 1 : 0;
+  }
+  __syncthreads();
+  if (tid < kWin) {  // wave 0: compact the two lists
+    const int s = s_slot[tid];
+    const int back = s >= 0 ? (s & 3) : 0;
+    const bool covered = s >= 0 && tid - back >= 0 && s_flag[tid - back] != 0;
+    const bool lead = s_flag[tid] != 0;
+    const bool rest = s >= 0 && !covered;
+    const uint64_t lm = __ballot(lead), rm = __ballot(rest);
+    const uint64_t below = (tid == 0) ? 0ull : (~0ull >> (64 - tid));
+    if (lead) s_lead[__popcll(lm & below)] = tid;
+    if (rest) s_rest[__popcll(rm & below)] = tid;
+    if (tid == 0) {
+      s_n[0] = __popcll(lm);
+      s_n[1] = __popcll(rm);
+    }
+  }
+  // 2. K pieces (independent of the lists)
+  for (int idx = tid; idx < kWin * (D / X); idx += 256) {
+    const int t = idx % kWin, c = idx / kWin;
+    const int s = t < nw ? s_slot[t] : -1;
+    if (s < 0) continue;
+    const int blk = s / bs, off = s % bs;
+    uint8_t* dst = kl + static_cast<uint64_t>(blk) * g.block_stride + k_index(off, c * X, bs, X, D) * ELEM;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(s_k + t * ROW + c * 16);
+  }
+  __syncthreads();
+  // 3. whole V pieces of the complete slot groups
+  const int n_lead = s_n[0], n_rest = s_n[1];
+  for (int idx = tid; idx < n_lead * 16 * NRP; idx += 256) {
+    const int n = idx % 16;
+    const int l = (idx / 16) % n_lead;
+    const int rp = idx / (16 * n_lead);
+    const int t = s_lead[l];
+    const int s = s_slot[t];
+    const int blk = s / bs, off = s % bs;
+    uint8_t* dst = vl + static_cast<uint64_t>(blk) * g.block_stride + v_index(off, rp * R * 16 + n, bs, X) * ELEM;
+    uint32_t wd[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int dim = (rp * R + r) * 16 + n;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int e = r * 4 + tt;  // element of the piece
+        uint32_t val;
+        if constexpr (ELEM == 2) val = *reinterpret_cast<const uint16_t*>(s_v + (t + tt) * ROW + 2 * dim);
+        else val = s_v[(t + tt) * ROW + dim];
+        wd[(e * ELEM) >> 2] |= val << (8 * ((e * ELEM) & 3));
+      }
+    }
+    *reinterpret_cast<u32x4*>(dst) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+  }
+  // ... and element by element for the other tokens.
+  for (int idx = tid; idx < n_rest * D; idx += 256) {
+    const int t = s_rest[idx / D], dim = idx % D;
+    const int s = s_slot[t];
+    const int blk = s / bs, off = s % bs;
+    uint8_t* dst = vl + static_cast<uint64_t>(blk) * g.block_stride + v_index(off, dim, bs, X) * ELEM;
+    if constexpr (ELEM == 2) {
+      *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(s_v + t * ROW + 2 * dim);
+    } else {
+      *dst = s_v[t * ROW + dim];
+    }
+  }
 }
 
 // int8 pools return the codes c (two's complement), not the stored c + 128.
-template <int KIND>
+// One wave per (token, KV head); lane l reads dims 2l and 2l + 1.
+template <int KIND, int D>
 __global__ __launch_bounds__(256) void gather_kv_kernel(PoolGeom g, int layer,
                                                         const int32_t* __restrict__ slots,
                                                         int n_tokens, uint8_t* __restrict__ k_out,
@@ -59,23 +226,24 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(PoolGeom g, int layer,
     if (lane == 0) atomicOr(g.status, kDevBadSlot);
     return;
   }
+  const int d0 = 2 * lane;
+  if (d0 >= D) return;
   const int blk = slot / g.block_size, t = slot % g.block_size;
   const uint8_t* kt = g.k_layer(layer) + static_cast<uint64_t>(blk) * g.block_stride +
                       static_cast<uint64_t>(h) * g.tile_bytes;
   const uint8_t* vt = g.v_layer(layer) + static_cast<uint64_t>(blk) * g.block_stride +
                       static_cast<uint64_t>(h) * g.tile_bytes;
-  const int64_t dst = (static_cast<int64_t>(tok) * g.kv_heads + h) * kHeadDim * ELEM;
-  const int d0 = 2 * lane;
+  const int64_t dst = (static_cast<int64_t>(tok) * g.kv_heads + h) * D * ELEM;
   const int bs = g.block_size;
   if constexpr (ELEM == 2) {
-    const uint32_t kk = *reinterpret_cast<const uint32_t*>(kt + 2 * k_index(t, d0, bs, X, kHeadDim));
+    const uint32_t kk = *reinterpret_cast<const uint32_t*>(kt + 2 * k_index(t, d0, bs, X, D));
     const uint32_t v0 = *reinterpret_cast<const uint16_t*>(vt + 2 * v_index(t, d0, bs, X));
     const uint32_t v1 = *reinterpret_cast<const uint16_t*>(vt + 2 * v_index(t, d0 + 1, bs, X));
     *reinterpret_cast<uint32_t*>(k_out + dst + 2 * d0) = kk;
     *reinterpret_cast<uint32_t*>(v_out + dst + 2 * d0) = v0 | (v1 << 16);
   } else {
     const uint32_t flip = KIND == kI8 ? 0x8080u : 0u;
-    const uint32_t kk = *reinterpret_cast<const uint16_t*>(kt + k_index(t, d0, bs, X, kHeadDim));
+    const uint32_t kk = *reinterpret_cast<const uint16_t*>(kt + k_index(t, d0, bs, X, D));
     const uint32_t v0 = vt[v_index(t, d0, bs, X)];
     const uint32_t v1 = vt[v_index(t, d0 + 1, bs, X)];
     *reinterpret_cast<uint16_t*>(k_out + dst + d0) = static_cast<uint16_t>(kk ^ flip);
@@ -88,13 +256,12 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(PoolGeom g, int layer,
 // it equals a value no input produces in practice (so the loads stay live).
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, uint64_t n16,
                                                           uint32_t* __restrict__ sink) {
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
   uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * 256;
   uint32_t acc = 0;
   for (; i < n16; i += stride) {
-    const u32x4_t v = __builtin_nontemporal_load(q + i);
+    const u32x4 v = __builtin_nontemporal_load(q + i);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
@@ -125,43 +292,69 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(PoolGeom g, CopyPairs 
   }
 }
 
+template <int D>
+hipError_t launch_write_kv_d(const PoolGeom& g, int layer, const _Float16* k, const _Float16* v,
+                             const int32_t* slots, int n_tokens, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(n_tokens) + kWin - 1) / kWin * g.kv_heads));
+  switch (g.kind) {
+    case kF16:
+      return launch_kernel(write_kv_kernel<kF16, D>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots,
+                           n_tokens);
+    case kF8:
+      return launch_kernel(write_kv_kernel<kF8, D>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots,
+                           n_tokens);
+    case kI8:
+      return launch_kernel(write_kv_kernel<kI8, D>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots,
+                           n_tokens);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_gather_kv_d(const PoolGeom& g, int layer, const int32_t* slots, int n_tokens, uint8_t* ko,
+                              uint8_t* vo, hipStream_t stream) {
+  const int64_t waves = static_cast<int64_t>(n_tokens) * g.kv_heads;
+  const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves));
+  switch (g.kind) {
+    case kF16:
+      return launch_kernel(gather_kv_kernel<kF16, D>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots,
+                           n_tokens, ko, vo);
+    case kF8:
+      return launch_kernel(gather_kv_kernel<kF8, D>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots,
+                           n_tokens, ko, vo);
+    case kI8:
+      return launch_kernel(gather_kv_kernel<kI8, D>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots,
+                           n_tokens, ko, vo);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k_new, const void* v_new,
                            const int32_t* slots, int n_tokens, hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
-  const int64_t waves = static_cast<int64_t>(n_tokens) * g.kv_heads;
-  const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves));
+  if ((static_cast<int64_t>(n_tokens) + kWin - 1) / kWin * g.kv_heads > 0x7FFFFFFF) return hipErrorInvalidValue;
   const auto* k = static_cast<const _Float16*>(k_new);
   const auto* v = static_cast<const _Float16*>(v_new);
-  switch (g.kind) {
-    case kF16:
-      return launch_kernel(write_kv_kernel<kF16>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
-    case kF8:
-      return launch_kernel(write_kv_kernel<kF8>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
-    case kI8:
-      return launch_kernel(write_kv_kernel<kI8>, grid, dim3(256), stream, nullptr, nullptr, g, layer, k, v, slots, n_tokens);
-    default:
-      return hipErrorInvalidValue;
+  switch (g.head_dim) {
+    case 64: return launch_write_kv_d<64>(g, layer, k, v, slots, n_tokens, stream);
+    case 128: return launch_write_kv_d<128>(g, layer, k, v, slots, n_tokens, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gather_kv(const PoolGeom& g, int layer, const int32_t* slots, int n_tokens,
                             void* k_out, void* v_out, hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
-  const int64_t waves = static_cast<int64_t>(n_tokens) * g.kv_heads;
-  const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves));
   auto* ko = static_cast<uint8_t*>(k_out);
   auto* vo = static_cast<uint8_t*>(v_out);
-  switch (g.kind) {
-    case kF16:
-      return launch_kernel(gather_kv_kernel<kF16>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
-    case kF8:
-      return launch_kernel(gather_kv_kernel<kF8>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
-    case kI8:
-      return launch_kernel(gather_kv_kernel<kI8>, grid, dim3(256), stream, nullptr, nullptr, g, layer, slots, n_tokens, ko, vo);
-    default:
-      return hipErrorInvalidValue;
+  switch (g.head_dim) {
+    case 64: return launch_gather_kv_d<64>(g, layer, slots, n_tokens, ko, vo, stream);
+    case 128: return launch_gather_kv_d<128>(g, layer, slots, n_tokens, ko, vo, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -296,7 +296,8 @@ int pa_pool_create(int32_t layers, int32_t kv_heads, int32_t head_dim, int32_t b
   if (!out) return fail(PA_ERR_INVALID, "out is NULL");
   *out = nullptr;
   if (layers < 1 || kv_heads < 1) return fail(PA_ERR_INVALID, "layers and kv_heads must be >= 1");
-  if (head_dim != pa::kHeadDim) return fail(PA_ERR_INVALID, "head_dim %d unsupported (128 only)", head_dim);
+  if (head_dim != pa::kHeadDimSmall && head_dim != pa::kHeadDimLarge)
+    return fail(PA_ERR_INVALID, "head_dim %d unsupported (64 or 128)", head_dim);
   if (block_size != 8 && block_size != 16 && block_size != 32)
     return fail(PA_ERR_INVALID, "block_size %d unsupported (8, 16, 32)", block_size);
   if (dtype != PA_DTYPE_FP16 && dtype != PA_DTYPE_FP8_E4M3 && dtype != PA_DTYPE_INT8)
@@ -568,7 +569,8 @@ int pa_write_kv(pa_pool* p, int32_t layer, const void* k_new, const void* v_new,
   if ((rc = check_layer(p, layer))) return rc;
   if (n_tokens < 0) return fail(PA_ERR_INVALID, "n_tokens %d < 0", n_tokens);
   if (n_tokens > 0 && (!k_new || !v_new || !slot_mapping)) return fail(PA_ERR_INVALID, "NULL device pointer");
-  if (misaligned(k_new, 4) || misaligned(v_new, 4)) return fail(PA_ERR_INVALID, "k_new and v_new must be 4-byte aligned");
+  if (misaligned(k_new, 16) || misaligned(v_new, 16))
+    return fail(PA_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
   const hipError_t e = pa::launch_write_kv(p->geom, layer, k_new, v_new, slot_mapping, n_tokens,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : hip_fail(e, "write_kv launch");

@@ -1,10 +1,10 @@
 // Byte layout of the KV block pool in HBM.
 //
 // Pool: [layer][K|V][block][kv_head][tile].  A tile is one (block, KV head):
-// B tokens x D dims, stored in the order the decode kernel's 64-lane loads
-// consume it, so that every 16-byte lane load of one wave lands in a
-// contiguous 1 KiB run (512 B for block_size 8) and the registers it fills
-// are already the MFMA operand fragments:
+// B tokens x D dims (D = head_dim, 64 or 128), stored in the order the decode
+// kernel's 64-lane loads consume it, so that every 16-byte lane load of one
+// wave lands in a contiguous 1 KiB run (512 B for block_size 8) and the
+// registers it fills are already the MFMA operand fragments:
 //
 //  K tile: 16-byte chunks of X consecutive dims (X = 8 fp16 / 16 fp8) of one
 //    token; for a run of TR = min(B, 16) tokens the chunk index is the outer
@@ -24,7 +24,9 @@
 
 namespace pa {
 
-constexpr int kHeadDim = 128;
+// head_dim values the kernels are built for (a template parameter of every
+// kernel that touches a tile).
+constexpr int kHeadDimSmall = 64, kHeadDimLarge = 128;
 
 // Element kinds of a pool (the values of PA_DTYPE_*): fp16, fp8 E4M3FN codes,
 // and int8 codes with a scale and a zero point.  The pool keeps an int8 code

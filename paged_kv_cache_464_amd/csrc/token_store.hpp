@@ -1,9 +1,7 @@
-// Device helpers shared by the cache kernels and the decode kernel: the fp8
-// E4M3FN and int8 encoders and the store of one new token's K/V (one KV head)
-// into its slot, i.e. the reshape-and-cache scatter (youngju.dev "KV cache and
-// paged attention", section "PagedAttention: OS 가상 메모리식 관리" for slots;
-// section "KV 양자화: FP8과 INT8" for the one-byte elements, int8 with a scale
-// and a zero point).
+// Device helpers shared by the reshape-and-cache scatter and the fused decode
+// step: the fp8 E4M3FN and int8 encoders of a new token's K/V (youngju.dev
+// "KV cache and paged attention", section "KV 양자화: FP8과 INT8": one byte
+// per element, int8 with a scale and a zero point).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,46 +54,6 @@ __device__ inline uint32_t encode_byte(float y, float zero) {
 
 __device__ inline float half_bits_to_float(uint32_t bits) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
-}
-
-// One wave stores token `slot` of KV head h of `layer`: lane l takes dims 2l
-// and 2l+1 of k_src / v_src (fp16 [head_dim] each).  fp8 and int8 pools
-// quantise with the (layer, head) inverse scales (and int8 zero points).  The
-// slot must be inside the pool.
-template <int KIND>
-__device__ inline void store_token(const PoolGeom& g, int layer, int h, int slot,
-                                   const _Float16* k_src, const _Float16* v_src, int lane) {
-  constexpr int ELEM = kind_bytes(KIND);
-  constexpr int X = 16 / ELEM;
-  const int blk = slot / g.block_size, t = slot % g.block_size;
-  uint8_t* kt = g.k_layer(layer) + static_cast<uint64_t>(blk) * g.block_stride +
-                static_cast<uint64_t>(h) * g.tile_bytes;
-  uint8_t* vt = g.v_layer(layer) + static_cast<uint64_t>(blk) * g.block_stride +
-                static_cast<uint64_t>(h) * g.tile_bytes;
-  const int d0 = 2 * lane;  // this lane's two dims
-  const uint32_t kk = *reinterpret_cast<const uint32_t*>(k_src + d0);
-  const uint32_t vv = *reinterpret_cast<const uint32_t*>(v_src + d0);
-  const int bs = g.block_size;
-  if constexpr (ELEM == 2) {
-    // d0, d0+1 are adjacent inside one K chunk.
-    *reinterpret_cast<uint32_t*>(kt + 2 * k_index(t, d0, bs, X, kHeadDim)) = kk;
-    *reinterpret_cast<uint16_t*>(vt + 2 * v_index(t, d0, bs, X)) = static_cast<uint16_t>(vv);
-    *reinterpret_cast<uint16_t*>(vt + 2 * v_index(t, d0 + 1, bs, X)) = static_cast<uint16_t>(vv >> 16);
-  } else {
-    const int lh = layer * g.kv_heads + h;
-    const int lhs = g.layers * g.kv_heads;
-    const float k_inv = g.scales[2 * lhs + lh];
-    const float v_inv = g.scales[3 * lhs + lh];
-    const float k_z = g.scales[4 * lhs + lh];
-    const float v_z = g.scales[5 * lhs + lh];
-    const uint32_t k0 = encode_byte<KIND>(half_bits_to_float(kk) * k_inv, k_z);
-    const uint32_t k1 = encode_byte<KIND>(half_bits_to_float(kk >> 16) * k_inv, k_z);
-    const uint32_t v0 = encode_byte<KIND>(half_bits_to_float(vv) * v_inv, v_z);
-    const uint32_t v1 = encode_byte<KIND>(half_bits_to_float(vv >> 16) * v_inv, v_z);
-    *reinterpret_cast<uint16_t*>(kt + k_index(t, d0, bs, X, kHeadDim)) = static_cast<uint16_t>(k0 | (k1 << 8));
-    vt[v_index(t, d0, bs, X)] = static_cast<uint8_t>(v0);
-    vt[v_index(t, d0 + 1, bs, X)] = static_cast<uint8_t>(v1);
-  }
 }
 
 }  // namespace pa

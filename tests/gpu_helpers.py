@@ -25,16 +25,16 @@ class Case:
 
 
 def build_case(lens, hq, hkv, bs, num_blocks, seed, dtype="fp16", layers=1, layer=0,
-               order=None, poison=True, device="cuda"):
+               order=None, poison=True, device="cuda", head_dim=128):
     """Allocate sequences of the given lengths (in order), write their K/V into
     ``layer`` of a fresh pool, and return everything needed for checks."""
     lens = [int(t) for t in lens]
     c = Case()
-    c.lens, c.hq, c.hkv, c.bs, c.layer, c.dtype = lens, hq, hkv, bs, layer, dtype
+    c.lens, c.hq, c.hkv, c.bs, c.layer, c.dtype, c.head_dim = lens, hq, hkv, bs, layer, dtype, head_dim
     total = sum(lens)
-    c.k = normal_fp16((total, hkv, 128), seed, 1, device)
-    c.v = normal_fp16((total, hkv, 128), seed, 2, device)
-    c.q = normal_fp16((len(lens), hq, 128), seed, 3, device)
+    c.k = normal_fp16((total, hkv, head_dim), seed, 1, device)
+    c.v = normal_fp16((total, hkv, head_dim), seed, 2, device)
+    c.q = normal_fp16((len(lens), hq, head_dim), seed, 3, device)
     c.offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     ks = vs = kz = vz = None
     if dtype == "fp8":
@@ -53,7 +53,7 @@ def build_case(lens, hq, hkv, bs, num_blocks, seed, dtype="fp16", layers=1, laye
     if order is None:
         order = free_order(seed, num_blocks)
     c.order = np.asarray(order, dtype=np.int32)
-    c.pool = pa.PagedKVPool(layers, hkv, 128, bs, num_blocks, dtype, device=device,
+    c.pool = pa.PagedKVPool(layers, hkv, head_dim, bs, num_blocks, dtype, device=device,
                             free_order=c.order, k_scales=ks, v_scales=vs, k_zeros=kz, v_zeros=vz)
     if poison:
         c.pool.pool_bytes().fill_(0xFF)  # NaN everywhere not written (0x7F/0xFF codes for fp8)
@@ -80,7 +80,7 @@ def oracle_for(c, seq_idx):
     """Oracle store holding only the sequences ``seq_idx`` (one layer), and the inputs."""
     kh = c.k.cpu().numpy()
     vh = c.v.cpu().numpy()
-    st = OracleKVStore(1, c.pool.info["num_blocks"], c.hkv, c.bs, 128, c.dtype,
+    st = OracleKVStore(1, c.pool.info["num_blocks"], c.hkv, c.bs, c.head_dim, c.dtype,
                        None if c.dtype == "fp16" else c.k_scales[None, :],
                        None if c.dtype == "fp16" else c.v_scales[None, :],
                        c.k_zeros[None, :] if c.dtype == "int8" else None,

@@ -111,8 +111,22 @@ def test_error_codes_and_atomic_failure():
     pa.pa_pool_destroy(h)
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_create_accepts_both_head_dims(head_dim):
+    """head_dim 64 and 128 are the create-time domain; the pool's byte sizes
+    follow the KV-size formula and the default scale is 1/sqrt(head_dim)."""
+    h = pa.pa_pool_create(2, 4, head_dim, 16, 0, 10)
+    info = pa.pa_pool_info_get(h)
+    assert info["head_dim"] == head_dim
+    assert info["tile_bytes"] == 16 * head_dim * 2
+    assert info["kv_bytes"] == 2 * 2 * 4 * head_dim * 2 * 10 * 16
+    assert info["softmax_scale"] == np.float32(1.0) / np.sqrt(np.float32(head_dim))
+    pa.pa_pool_destroy(h)
+
+
 @pytest.mark.parametrize("args", [
-    (0, 2, 128, 16, 0, 8), (1, 0, 128, 16, 0, 8), (1, 2, 64, 16, 0, 8), (1, 2, 128, 12, 0, 8),
+    (0, 2, 128, 16, 0, 8), (1, 0, 128, 16, 0, 8), (1, 2, 96, 16, 0, 8), (1, 2, 256, 16, 0, 8),
+    (1, 2, 32, 16, 0, 8), (1, 2, 128, 12, 0, 8),
     (1, 2, 128, 16, 7, 8), (1, 2, 128, 16, 0, 0), (1, 2, 128, 32, 0, 1 << 26)])
 def test_create_rejects_bad_arguments(args):
     with pytest.raises(pa.PAError):

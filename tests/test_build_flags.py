@@ -9,12 +9,13 @@ import re
 from paged_kv_cache_464_amd import build
 
 CSRC = build.CSRC
-NO_NAN_SOURCES = ["decode_kernels.hip", "token_store.hpp", "layout.hpp", "kernels.hpp"]
+NO_NAN_SOURCES = ["decode_kernels.hip", "decode_inst.hip", "decode_engine.hpp", "token_store.hpp", "layout.hpp",
+                  "kernels.hpp"]
 
 
 def test_attention_kernels_are_built_without_nan_semantics_and_nothing_else_is():
-    assert build.FILE_FLAGS == {"decode_kernels.hip": ["-fno-honor-nans"]}
-    for src in build.HIP_SOURCES + build.HOST_SOURCES:
+    assert build.FILE_FLAGS == {"decode_kernels.hip": ["-fno-honor-nans"], "decode_inst.hip": ["-fno-honor-nans"]}
+    for src in build.HIP_SOURCES + build.HOST_SOURCES + [build.INST_SOURCE]:
         assert os.path.exists(os.path.join(CSRC, src)), src
 
 

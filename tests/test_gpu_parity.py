@@ -48,6 +48,61 @@ def test_write_kv_bit_exact(dtype, bs):
     assert c.pool.device_status() == 0
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_write_kv_slot_patterns(dtype, bs):
+    """The scatter stores whole V pieces where four consecutive tokens fill an
+    aligned group of four slots and element by element elsewhere: prefills at
+    every input offset mod 4 (groups cut by the 64-token window edges),
+    descending and shuffled slots, and skipped (negative) slots inside runs;
+    the pool must equal the oracle's bit for bit in every case."""
+    from workloads import amax_scales, minmax_int8_params
+    say("write_kv patterns", dtype, bs)
+    n_blocks = 96
+    rng = np.random.default_rng(4242 + bs)
+    order = free_order(777 + bs, n_blocks)
+    k = normal_fp16((n_blocks * bs, 2, 128), 4243, 1, "cuda")
+    v = normal_fp16((n_blocks * bs, 2, 128), 4243, 2, "cuda")
+    ks = vs = kz = vz = None
+    if dtype == "fp8":
+        ks, vs = amax_scales(k)[None], amax_scales(v)[None]
+    if dtype == "int8":
+        (ks, kz), (vs, vz) = minmax_int8_params(k), minmax_int8_params(v)
+        ks, kz, vs, vz = ks[None], kz[None], vs[None], vz[None]
+    pool = pa.PagedKVPool(1, 2, 128, bs, n_blocks, dtype, free_order=order, k_scales=ks, v_scales=vs,
+                          k_zeros=kz, v_zeros=vz)
+    st = OracleKVStore(1, n_blocks, 2, bs, 128, dtype, ks, vs, kz, vz)
+    # Sequences whose prefills start at input offsets 0, 1, 2, 3 (mod 4) of one call.
+    lens = [61, 130, 7, 255, 66, 3, 200]
+    seqs, slot_lists = [], []
+    for t in lens:
+        s = pool.seq_create()
+        seqs.append(s)
+        slot_lists.append(pool.alloc(s, t)[0])
+    used = sum(lens)
+    slots_prefill = np.concatenate(slot_lists).astype(np.int32)
+    patterns = {
+        "prefill": slots_prefill,
+        "descending": slots_prefill[::-1].copy(),
+        "shuffled": rng.permutation(slots_prefill).astype(np.int32),
+        "holes": np.where(rng.random(used) < 0.1, -1, slots_prefill).astype(np.int32),
+    }
+    for name, sl in patterns.items():
+        rows = rng.permutation(n_blocks * bs)[:used]  # fresh values for every pattern
+        kk, vv = k[rows].contiguous(), v[rows].contiguous()
+        pool.write_kv(0, kk, vv, torch.from_numpy(sl).cuda())
+        st.write(0, kk.cpu().numpy(), vv.cpu().numpy(), sl)
+        kg, vg = pool.gather_kv(0, torch.from_numpy(slots_prefill).cuda())
+        ok, ov = st.read_slots(0, slots_prefill)
+        if dtype == "fp16":
+            kg, vg, ok, ov = (a.view(np.uint16) for a in (kg.cpu().numpy(), vg.cpu().numpy(), ok, ov))
+        else:
+            kg, vg = kg.cpu().numpy(), vg.cpu().numpy()
+        np.testing.assert_array_equal(kg, ok, err_msg=name)
+        np.testing.assert_array_equal(vg, ov, err_msg=name)
+    assert pool.device_status() == 0
+
+
 def test_fp8_encode_exhaustive_over_fp16_inputs():
     """Every finite fp16 value through the GPU quantiser with three scales."""
     say("fp8 exhaustive")
