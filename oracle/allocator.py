@@ -36,9 +36,16 @@ reuse blocks, old prefixes are evicted least recently used first; openakashic
 note, Key Points: a cached block taken from the free queue for a new
 allocation loses its prefix entry).  Readings:
 
-* Only full blocks of a prompt given at creation are cached; the key of a
-  block is the whole token prefix up to its end (here the tuple itself, so the
-  oracle is exact; the library hashes it).
+* A sequence's token ids are known when it was created with a prompt (or
+  empty) and every append gave its token ids; a tokenless append makes them
+  unknown for good.  Every full block of a sequence with known ids is
+  cached: the prompt's full blocks at creation, and each block an append
+  fills, when it fills (so a later turn of a conversation hits on the blocks
+  generated in an earlier one: youngju.dev page, section "prefix 공유와
+  copy-on-write", names multi-turn history as a shared prefix).  A fork
+  inherits its parent's ids.  The key of a block is the whole token prefix
+  up to its end (here the tuple itself, so the oracle is exact; the library
+  compares the same prefixes exactly, block by block).
 * Lookup walks the prompt's full blocks in order and stops at the first miss;
   a hit takes the block (count + 1), out of the free queue if it sat there.
 * The rest of the prompt is allocated like an append; its full blocks are then
@@ -72,6 +79,7 @@ class OracleAllocator:
         self.ref = [0] * self.num_blocks
         self.tables = {}  # seq id -> list of physical block ids
         self.lens = {}  # seq id -> number of tokens
+        self.tokens = {}  # seq id -> its token ids, or None when unknown
         self.next_id = 0
         self.cow_log = []  # (src, dst) in the order they happened
         self.failures = 0
@@ -87,21 +95,28 @@ class OracleAllocator:
         self.next_id += 1
         self.tables[sid] = []
         self.lens[sid] = 0
+        self.tokens[sid] = []
         return sid
 
     def _check(self, sid):
         if sid not in self.tables:
             raise BadSeq(sid)
 
-    def alloc(self, sid: int, n: int):
+    def alloc(self, sid: int, n: int, tokens=None):
         """Append ``n`` tokens to ``sid``; return (slots, cow) where cow is (src, dst) or None.
 
         Slot of logical token t is table[t // B] * B + t % B (the block table maps
         the logical block to its physical block; the offset within the block is kept).
+        ``tokens``: the appended token ids (``n`` of them), or None; with ids,
+        every block the append fills is entered in the prefix cache.
         """
         self._check(sid)
         if n < 0:
             raise ValueError("n must be >= 0")
+        if tokens is not None:
+            tokens = [int(t) for t in tokens]
+            if len(tokens) != n:
+                raise ValueError("tokens must hold n ids")
         bs = self.block_size
         table = self.tables[sid]
         length = self.lens[sid]
@@ -125,7 +140,23 @@ class OracleAllocator:
             table.append(b)
         slots = [table[(length + j) // bs] * bs + (length + j) % bs for j in range(n)]
         self.lens[sid] = length + n
+        if n > 0:
+            if tokens is None or self.tokens[sid] is None:
+                self.tokens[sid] = None
+            else:
+                ids = self.tokens[sid]
+                ids.extend(tokens)
+                for i in range(length // bs, (length + n) // bs):  # the blocks this append filled
+                    self._register(tuple(ids[:(i + 1) * bs]), table[i])
         return slots, cow_pair
+
+    def _register(self, key, b):
+        """Enter block ``b`` under the prefix ``key`` (replacing an entry with the same key)."""
+        old = self.cache.get(key)
+        if old is not None:
+            self.block_key[old] = None
+        self.cache[key] = b
+        self.block_key[b] = key
 
     def _take_free(self) -> int:
         """Pop the free-queue head; a cached block loses its prefix entry."""
@@ -174,14 +205,9 @@ class OracleAllocator:
             self.ref[b] = 1
             table.append(b)
         for i in range(h, full):
-            key = tuple(tokens[:(i + 1) * bs])
-            old = self.cache.get(key)
-            if old is not None:
-                self.block_key[old] = None
-            b = table[i]
-            self.cache[key] = b
-            self.block_key[b] = key
+            self._register(tuple(tokens[:(i + 1) * bs]), table[i])
         self.lens[sid] = n
+        self.tokens[sid] = list(tokens)
         slots = [table[t // bs] * bs + t % bs for t in range(h * bs, n)]
         return sid, h * bs, slots
 
@@ -191,6 +217,7 @@ class OracleAllocator:
         sid = self.seq_create()
         self.tables[sid] = list(self.tables[parent])
         self.lens[sid] = self.lens[parent]
+        self.tokens[sid] = None if self.tokens[parent] is None else list(self.tokens[parent])
         for b in self.tables[sid]:
             self.ref[b] += 1
         return sid
@@ -204,6 +231,7 @@ class OracleAllocator:
                 self.free.append(b)
         del self.tables[sid]
         del self.lens[sid]
+        del self.tokens[sid]
 
     # -- views ---------------------------------------------------------------
     def block_tables(self, seqs, max_blocks: int):

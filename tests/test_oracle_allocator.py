@@ -351,6 +351,87 @@ def test_prefix_cached_sequences_read_the_right_content():
         np.testing.assert_array_equal(k[:, 0, 0], np.asarray(toks, np.float16))
 
 
+def test_a_second_turn_hits_on_the_blocks_generated_in_the_first():
+    """Multi-turn history is a shared prefix (youngju.dev page, "prefix 공유와
+    copy-on-write"): appends with token ids enter every block they fill, so
+    the next turn's prompt (first prompt + answer + new question) is served
+    from the cache up to the last full block of prompt + answer."""
+    bs = 8
+    a = OracleAllocator(64, bs)
+    prompt = list(range(100, 120))                      # 2 full blocks + 4 tokens
+    s, c, _ = a.seq_create_cached(prompt)
+    assert c == 0 and len(a.cache) == 2
+    answer = list(range(500, 513))                      # 13 generated tokens, one at a time
+    for t in answer:
+        a.alloc(s, 1, [t])
+    assert a.lens[s] == 33 and len(a.cache) == 4       # blocks 2 and 3 filled and entered
+    turn1_blocks = list(a.tables[s][:4])
+    a.free_seq(s)
+    s2, c2, slots2 = a.seq_create_cached(prompt + answer + list(range(900, 910)))
+    assert c2 == 32 and a.tables[s2][:4] == turn1_blocks and len(slots2) == 43 - 32
+    st_ = a.stats()
+    assert st_["cache_hits"] == 4 and st_["cache_misses"] == 2 + 1
+    a.check_invariants()
+
+
+def test_a_tokenless_append_ends_caching_for_its_sequence():
+    bs = 4
+    a = OracleAllocator(32, bs)
+    s, _, _ = a.seq_create_cached([1, 2, 3, 4, 5, 6])  # 1 full block cached
+    a.alloc(s, 2, [7, 8])                               # fills block 1: cached
+    a.alloc(s, 3)                                       # no ids: the sequence's ids are unknown now
+    a.alloc(s, 5, [1, 1, 1, 1, 1])                      # fills blocks: not cached
+    assert a.tokens[s] is None and len(a.cache) == 2
+    t = a.seq_create()                                  # empty sequence, appends with ids
+    a.alloc(t, 4, [9, 9, 9, 9])
+    assert len(a.cache) == 3 and a.cache[(9, 9, 9, 9)] == a.tables[t][0]
+    _, c, _ = a.seq_create_cached([1, 2, 3, 4, 5, 6, 7, 8, 0])
+    assert c == 8
+    a.check_invariants()
+
+
+def test_forks_inherit_token_ids_and_cache_their_own_continuations():
+    """Two forks of a prompt with a partial last block: each append copies the
+    shared block (copy-on-write) and, when the copy fills, enters it under
+    that fork's own prefix."""
+    bs = 4
+    a = OracleAllocator(32, bs)
+    p, _, _ = a.seq_create_cached([1, 2, 3, 4, 5, 6])
+    f = a.fork(p)
+    _, cow_f = a.alloc(f, 2, [7, 8])                    # f copies the shared block, fills it
+    _, cow_p = a.alloc(p, 2, [70, 80])                  # p is now the block's only owner: no copy
+    assert cow_f is not None and cow_p is None
+    assert a.cache[(1, 2, 3, 4, 5, 6, 7, 8)] == a.tables[f][1] == cow_f[1]
+    assert a.cache[(1, 2, 3, 4, 5, 6, 70, 80)] == a.tables[p][1] == cow_f[0]
+    _, c1, _ = a.seq_create_cached([1, 2, 3, 4, 5, 6, 7, 8, 11])
+    _, c2, _ = a.seq_create_cached([1, 2, 3, 4, 5, 6, 70, 80])
+    assert c1 == 8 and c2 == 8
+    a.check_invariants()
+
+
+def test_evictions_take_the_entries_of_reused_blocks_only():
+    """Freed cached blocks keep their entries until the free queue hands them
+    out (child block first: a freed sequence's blocks join the queue last to
+    first); then the prefixes miss and are entered again."""
+    bs = 2
+    a = OracleAllocator(4, bs, free_order=[0, 1, 2, 3])
+    x, _, _ = a.seq_create_cached([1, 1, 2, 2])        # blocks 0 ([1,1]) and 1 ([1,1,2,2]) cached
+    a.free_seq(x)                                       # free queue: 2, 3, 1, 0
+    assert list(a.free) == [2, 3, 1, 0]
+    y = a.seq_create()
+    a.alloc(y, 6)                                       # takes 2, 3, 1: evicts [1,1,2,2]'s entry
+    assert a.evictions == 1 and len(a.cache) == 1
+    a.free_seq(y)                                       # free queue: 0, 1, 3, 2
+    z = a.seq_create()
+    a.alloc(z, 2)                                       # takes 0: evicts [1,1]
+    assert a.evictions == 2 and len(a.cache) == 0
+    a.free_seq(z)
+    w, _, _ = a.seq_create_cached([5, 5, 6, 6])        # misses; enters two new blocks
+    v, c, _ = a.seq_create_cached([5, 5, 6, 6, 7])
+    assert c == 4 and len(a.cache) == 2
+    a.check_invariants()
+
+
 # ---- beam-style fork trees ------------------------------------------------------
 
 @pytest.mark.parametrize("bs", [1, 4, 16])
