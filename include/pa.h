@@ -180,12 +180,13 @@ int pa_seq_create(pa_pool* pool, int32_t* seq_out);
  * prompt matches a cached prefix block by block (reference count + 1; a block
  * that sat in the free queue leaves it), the rest is allocated like
  * pa_alloc, and the prompt's newly allocated full blocks are entered in the
- * cache.  *cached_out = tokens whose K/V the pool already holds (a multiple
+ * cache (later appends with ids enter the blocks they fill: pa_alloc_tokens).  *cached_out = tokens whose K/V the pool already holds (a multiple
  * of block_size); slots_out (host int32[n]) receives the slots of tokens
  * cached_out .. n-1, which the caller writes with pa_write_kv.  Freed cached
  * blocks keep their entry at the free-queue tail and lose it when the queue
- * hands them out again (least recently freed first).  Keys are 64-bit hashes
- * chained over the prompt's blocks; a hit also compares the block's tokens.
+ * hands them out again (least recently freed first).  The key of a block is
+ * the whole token prefix up to its end, compared exactly (a trie of blocks:
+ * the parent prefix and the block's ids), so different prefixes never share.
  * PA_ERR_NO_BLOCKS if the rest does not fit: nothing changes, no id is used. */
 int pa_seq_create_cached(pa_pool* pool, const int32_t* tokens, int32_t n, int32_t* seq_out,
                          int32_t* cached_out, int32_t* slots_out);
@@ -206,10 +207,23 @@ int pa_seq_create_cached(pa_pool* pool, const int32_t* tokens, int32_t n, int32_
 int pa_alloc(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* slots_out,
              int32_t* cow_out, void* stream);
 
+/* pa_alloc with the appended tokens' ids (host int32[n_tokens]; NULL makes it
+ * pa_alloc).  While a sequence's ids are known (it was created empty or with
+ * a prompt, and every append gave ids; a fork inherits its parent's), every
+ * block an append fills is entered in the prefix cache under the sequence's
+ * whole token prefix, so a later prompt that extends it (the next turn of a
+ * conversation: youngju.dev page, section "prefix 공유와 copy-on-write") is
+ * served from the cache (pa_seq_create_cached).  An append without ids ends
+ * that for the sequence.  Errors as pa_alloc. */
+int pa_alloc_tokens(pa_pool* pool, int32_t seq, int32_t n_tokens, const int32_t* tokens,
+                    int32_t* slots_out, int32_t* cow_out, void* stream);
+
 /* Batched appends (the same pages as pa_alloc): for k = 0 .. count-1 in order,
  * append n_tokens[k] >= 0
- * tokens to seqs[k] exactly as pa_alloc would (the same allocator state and
- * slots), the slots back to back in slots_out (host int32[sum of n_tokens]).
+ * tokens to seqs[k] exactly as pa_alloc_tokens would (the same allocator state
+ * and slots), the slots back to back in slots_out (host int32[sum of n_tokens]).
+ * tokens: the appended ids back to back (host int32[sum of n_tokens]), or NULL
+ * for appends without ids.
  * The copy-on-write copies of the whole batch are enqueued on `stream` in one
  * launch (per 64 copies) after the appends, instead of one launch per copy:
  * every copy's destination is a fresh block private to its sequence, so the
@@ -219,7 +233,8 @@ int pa_alloc(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* slots_out,
  * made (their copies enqueued), append k changes nothing, and its status is
  * returned (PA_ERR_NO_BLOCKS when the pool runs out). */
 int pa_alloc_batch(pa_pool* pool, const int32_t* seqs, const int32_t* n_tokens, int32_t count,
-                   int32_t* slots_out, int32_t* cow_out, int32_t* done_out, void* stream);
+                   const int32_t* tokens, int32_t* slots_out, int32_t* cow_out, int32_t* done_out,
+                   void* stream);
 
 /* New sequence sharing every block of `parent` (each reference count + 1):
  * sequences with a common prefix point at the same physical blocks

@@ -67,7 +67,8 @@ SIGNATURES = {
     "pa_seq_create": (C.c_int, [_P, _PI32]),
     "pa_seq_create_cached": (C.c_int, [_P, _PI32, _I32, _PI32, _PI32, _PI32]),
     "pa_alloc": (C.c_int, [_P, _I32, _I32, _PI32, _PI32, _P]),
-    "pa_alloc_batch": (C.c_int, [_P, _PI32, _PI32, _I32, _PI32, _PI32, _PI32, _P]),
+    "pa_alloc_tokens": (C.c_int, [_P, _I32, _I32, _PI32, _PI32, _PI32, _P]),
+    "pa_alloc_batch": (C.c_int, [_P, _PI32, _PI32, _I32, _PI32, _PI32, _PI32, _PI32, _P]),
     "pa_fork": (C.c_int, [_P, _I32, _PI32]),
     "pa_free": (C.c_int, [_P, _I32]),
     "pa_seq_len": (C.c_int, [_P, _I32, _PI32, _PI32]),

@@ -10,10 +10,7 @@ BlockManager::BlockManager(int32_t num_blocks, int32_t block_size)
       next_(static_cast<size_t>(num_blocks), -1),
       prev_(static_cast<size_t>(num_blocks), -1),
       in_free_(static_cast<size_t>(num_blocks), 0),
-      key_(static_cast<size_t>(num_blocks), 0),
-      parent_key_(static_cast<size_t>(num_blocks), 0),
-      has_key_(static_cast<size_t>(num_blocks), 0),
-      key_tokens_(static_cast<size_t>(num_blocks) * block_size, 0),
+      block_node_(static_cast<size_t>(num_blocks), -1),
       ref_(static_cast<size_t>(num_blocks), 0) {
   for (int32_t b = 0; b < num_blocks; ++b) push_free(b);
 }
@@ -44,10 +41,8 @@ void BlockManager::unlink_free(int32_t b) {
 int32_t BlockManager::pop_free() {
   const int32_t b = head_;
   unlink_free(b);
-  if (has_key_[b]) {  // the cached prefix block is reused: its entry goes
-    auto it = cache_.find(key_[b]);
-    if (it != cache_.end() && it->second == b) cache_.erase(it);
-    has_key_[b] = 0;
+  if (block_node_[b] >= 0) {  // the cached prefix block is reused: its entry goes
+    clear_entry(b);
     ++cache_evictions_;
   }
   return b;
@@ -62,10 +57,19 @@ void BlockManager::push_free(int32_t b) {
   ++free_count_;
 }
 
-// 64-bit key of a full block given its parent's key: FNV-1a over the token
-// ids, then the splitmix64 finalizer to spread the bits.
-uint64_t BlockManager::block_key(uint64_t parent, const int32_t* tokens) const {
-  uint64_t h = parent ^ 0xCBF29CE484222325ull;
+// Bucket of a trie node: FNV-1a over the parent node and the block's token
+// ids, then the splitmix64 finalizer.  Only the bucket depends on it: a lookup
+// compares the parent and the ids exactly.  Tests build a variant whose hash
+// is constant (every key in one bucket) to show that.
+uint64_t BlockManager::node_hash(int32_t parent, const int32_t* tokens) const {
+#ifdef PA_PREFIX_HASH_CONSTANT
+  (void)parent;
+  (void)tokens;
+  return 0;
+#else
+  uint64_t h = 0xCBF29CE484222325ull;
+  h ^= static_cast<uint32_t>(parent);
+  h *= 0x100000001B3ull;
   for (int32_t i = 0; i < block_size_; ++i) {
     h ^= static_cast<uint32_t>(tokens[i]);
     h *= 0x100000001B3ull;
@@ -76,16 +80,104 @@ uint64_t BlockManager::block_key(uint64_t parent, const int32_t* tokens) const {
   h *= 0x94D049BB133111EBull;
   h ^= h >> 31;
   return h;
+#endif
 }
 
-void BlockManager::register_block(int32_t b, uint64_t key, uint64_t parent, const int32_t* tokens) {
-  auto it = cache_.find(key);
-  if (it != cache_.end()) has_key_[it->second] = 0;  // replaced entry
-  cache_[key] = b;
-  key_[b] = key;
-  parent_key_[b] = parent;
-  has_key_[b] = 1;
-  std::copy(tokens, tokens + block_size_, key_tokens_.begin() + static_cast<int64_t>(b) * block_size_);
+int32_t BlockManager::find_node(int32_t parent, const int32_t* tokens) const {
+  const auto range = index_.equal_range(node_hash(parent, tokens));
+  for (auto it = range.first; it != range.second; ++it) {
+    const int32_t id = it->second;
+    if (nodes_[id].parent == parent &&
+        std::equal(tokens, tokens + block_size_, node_tokens_.begin() + static_cast<int64_t>(id) * block_size_))
+      return id;
+  }
+  return -1;
+}
+
+// The node (parent, tokens), created if absent (a new node holds a reference
+// on its parent).
+int32_t BlockManager::get_node(int32_t parent, const int32_t* tokens) {
+  int32_t id = find_node(parent, tokens);
+  if (id >= 0) return id;
+  if (!free_nodes_.empty()) {
+    id = free_nodes_.back();
+    free_nodes_.pop_back();
+  } else {
+    id = static_cast<int32_t>(nodes_.size());
+    nodes_.emplace_back();
+    node_tokens_.resize(node_tokens_.size() + block_size_);
+  }
+  PrefixNode& nd = nodes_[id];
+  nd.parent = parent;
+  nd.block = -1;
+  nd.refs = 0;
+  nd.hash = node_hash(parent, tokens);
+  std::copy(tokens, tokens + block_size_, node_tokens_.begin() + static_cast<int64_t>(id) * block_size_);
+  index_.emplace(nd.hash, id);
+  if (parent >= 0) ++nodes_[parent].refs;
+  return id;
+}
+
+void BlockManager::pin(int32_t node) {
+  if (node >= 0) ++nodes_[node].refs;
+}
+
+// Drops one reference; a node left with none leaves the trie and releases its
+// parent in turn.
+void BlockManager::release(int32_t node) {
+  while (node >= 0) {
+    PrefixNode& nd = nodes_[node];
+    if (--nd.refs > 0) return;
+    const auto range = index_.equal_range(nd.hash);
+    for (auto it = range.first; it != range.second; ++it) {
+      if (it->second == node) {
+        index_.erase(it);
+        break;
+      }
+    }
+    free_nodes_.push_back(node);
+    node = nd.parent;
+  }
+}
+
+// Enters block b under the node's prefix, replacing an entry with the same key.
+void BlockManager::set_entry(int32_t node, int32_t b) {
+  PrefixNode& nd = nodes_[node];
+  if (nd.block >= 0) {
+    block_node_[nd.block] = -1;  // replaced entry
+  } else {
+    ++nd.refs;
+    ++cached_count_;
+  }
+  nd.block = b;
+  block_node_[b] = node;
+}
+
+void BlockManager::clear_entry(int32_t b) {
+  const int32_t node = block_node_[b];
+  block_node_[b] = -1;
+  nodes_[node].block = -1;
+  --cached_count_;
+  release(node);
+}
+
+// Token ids of n tokens appended to s from position first_token (the table
+// already holds their blocks): each block they fill is entered under the
+// sequence's prefix.
+void BlockManager::append_ids(Seq& s, int64_t first_token, int32_t n, const int32_t* tokens) {
+  const int64_t bs = block_size_;
+  for (int32_t j = 0; j < n; ++j) {
+    s.tail.push_back(tokens[j]);
+    if (static_cast<int64_t>(s.tail.size()) == bs) {
+      const int64_t i = (first_token + j) / bs;  // the block this token fills
+      const int32_t nd = get_node(s.node, s.tail.data());
+      set_entry(nd, s.table[i]);
+      pin(nd);
+      release(s.node);
+      s.node = nd;
+      s.tail.clear();
+    }
+  }
 }
 
 BmStatus BlockManager::seq_create_cached(const int32_t* tokens, int32_t n, int32_t* seq,
@@ -96,20 +188,12 @@ BmStatus BlockManager::seq_create_cached(const int32_t* tokens, int32_t n, int32
   const int64_t full = n / bs;
   // Look up the prompt's full blocks until the first miss.
   std::vector<int32_t> hits;
-  std::vector<uint64_t> keys;
-  uint64_t parent = 0;
+  int32_t parent = -1;
   for (int64_t i = 0; i < full; ++i) {
-    const int32_t* tk = tokens + i * bs;
-    const uint64_t k = block_key(parent, tk);
-    keys.push_back(k);
-    auto it = cache_.find(k);
-    if (it == cache_.end()) break;
-    const int32_t b = it->second;
-    if (!has_key_[b] || key_[b] != k || parent_key_[b] != parent ||
-        !std::equal(tk, tk + bs, key_tokens_.begin() + static_cast<int64_t>(b) * bs))
-      break;
-    hits.push_back(b);
-    parent = k;
+    const int32_t nd = find_node(parent, tokens + i * bs);
+    if (nd < 0 || nodes_[nd].block < 0) break;
+    hits.push_back(nodes_[nd].block);
+    parent = nd;
   }
   const int64_t h = static_cast<int64_t>(hits.size());
   const int64_t need = (n - h * bs + bs - 1) / bs;
@@ -129,15 +213,17 @@ BmStatus BlockManager::seq_create_cached(const int32_t* tokens, int32_t n, int32
   }
   cache_hits_ += h;
   cache_misses_ += full - h;
+  // The hit chain's last node holds its ancestors; it stays in the trie while
+  // the allocations below evict other entries.
+  pin(parent);
   for (int64_t i = 0; i < need; ++i) {
     const int32_t b = pop_free();
     ref_[b] = 1;
     s.table.push_back(b);
   }
-  for (int64_t i = h; i < full; ++i) {
-    if (i >= static_cast<int64_t>(keys.size())) keys.push_back(block_key(keys[i - 1], tokens + i * bs));
-    register_block(s.table[i], keys[i], i == 0 ? 0 : keys[i - 1], tokens + i * bs);
-  }
+  s.node = parent;  // pinned above
+  s.len = static_cast<int32_t>(h * bs);
+  append_ids(s, h * bs, static_cast<int32_t>(n - h * bs), tokens + h * bs);
   s.len = n;
   for (int64_t t = h * bs; t < n; ++t)
     slots[t - h * bs] = static_cast<int32_t>(static_cast<int64_t>(s.table[t / bs]) * bs + t % bs);
@@ -154,7 +240,7 @@ int32_t BlockManager::seq_create() {
 }
 
 BmStatus BlockManager::alloc(int32_t seq, int32_t n, int32_t* slots, int32_t* cow_src,
-                             int32_t* cow_dst) {
+                             int32_t* cow_dst, const int32_t* tokens) {
   if (cow_src) *cow_src = -1;
   if (cow_dst) *cow_dst = -1;
   if (!valid_seq(seq)) return BmStatus::kBadSeq;
@@ -190,6 +276,16 @@ BmStatus BlockManager::alloc(int32_t seq, int32_t n, int32_t* slots, int32_t* co
     slots[j] = static_cast<int32_t>(static_cast<int64_t>(s.table[t / bs]) * bs + t % bs);
   }
   s.len = static_cast<int32_t>(new_len);
+  if (n > 0 && s.known) {
+    if (tokens) {
+      append_ids(s, len, n, tokens);
+    } else {  // ids unknown from here on: nothing more of this sequence is cached
+      release(s.node);
+      s.node = -1;
+      s.known = false;
+      s.tail.clear();
+    }
+  }
   return BmStatus::kOk;
 }
 
@@ -198,9 +294,14 @@ BmStatus BlockManager::fork(int32_t parent, int32_t* child) {
   if (child == nullptr) return BmStatus::kInvalid;
   const int32_t c = seq_create();
   Seq& p = seqs_[parent];  // seq_create may reallocate seqs_: take the reference after it
-  seqs_[c].table = p.table;
-  seqs_[c].len = p.len;
-  for (int32_t b : seqs_[c].table) ++ref_[b];
+  Seq& k = seqs_[c];
+  k.table = p.table;
+  k.len = p.len;
+  k.known = p.known;
+  k.node = p.node;
+  k.tail = p.tail;
+  if (k.known) pin(k.node);
+  for (int32_t b : k.table) ++ref_[b];
   *child = c;
   return BmStatus::kOk;
 }
@@ -213,6 +314,10 @@ BmStatus BlockManager::free_seq(int32_t seq) {
   }
   s.table.clear();
   s.table.shrink_to_fit();
+  if (s.known) release(s.node);
+  s.node = -1;
+  s.tail.clear();
+  s.tail.shrink_to_fit();
   s.len = 0;
   s.alive = false;
   --live_seqs_;

@@ -23,17 +23,25 @@
 // prefixes found by a hash and shared by reference count; youngju.dev page,
 // section "prefix 캐시의 수명과 무효화": hits reuse blocks, least recently used
 // prefixes are evicted first; openakashic note, Key Points: a cached block
-// taken from the free queue for a new allocation loses its entry):
-//  * only full blocks of a prompt given at creation are cached, keyed by a
-//    64-bit hash chained over the prompt's blocks (the key of block i covers
-//    tokens 0 .. (i+1)B-1); a hit also checks the block's own tokens and its
-//    parent key;
+// taken from the free queue for a new allocation loses its entry; section
+// "prefix 공유와 copy-on-write": multi-turn history is a shared prefix):
+//  * the key of a cached block is its sequence's whole token prefix up to the
+//    block's end, held exactly in a trie: node = (node of the prefix one
+//    block shorter, the block's B token ids).  Lookup compares the ids and
+//    the parent node, so two different prefixes never share a block whatever
+//    the hash does (the hash only picks the bucket);
+//  * every full block of a sequence whose token ids are known is cached: a
+//    prompt's full blocks at creation, and each block an append with token
+//    ids fills; a tokenless append makes the sequence's ids unknown for good;
+//    forks inherit the ids;
 //  * lookup stops at the first miss; hits leave the free queue if they sat
 //    there; the rest of the prompt is allocated like an append and its full
 //    blocks are registered (replacing an entry with the same key);
 //  * freed cached blocks keep their entry at the free-queue tail, so the least
 //    recently freed is evicted first; the free queue is a doubly linked list
-//    so that a hit can take a block out of its middle.
+//    so that a hit can take a block out of its middle;
+//  * a trie node lives while it has an entry, a child node or a sequence
+//    whose prefix ends there.
 #pragma once
 
 #include <cstdint>
@@ -57,8 +65,9 @@ class BlockManager {
   int32_t seq_create();
 
   // Append n tokens.  slots[n] receive the new tokens' slots; *cow_src/*cow_dst the
-  // copied block pair or -1.
-  BmStatus alloc(int32_t seq, int32_t n, int32_t* slots, int32_t* cow_src, int32_t* cow_dst);
+  // copied block pair or -1.  tokens: the n appended token ids, or null.
+  BmStatus alloc(int32_t seq, int32_t n, int32_t* slots, int32_t* cow_src, int32_t* cow_dst,
+                 const int32_t* tokens = nullptr);
   // New sequence holding the prompt tokens[n]: *cached leading tokens come from
   // the prefix cache; slots[0 .. n - *cached) receive the rest's slots.
   BmStatus seq_create_cached(const int32_t* tokens, int32_t n, int32_t* seq, int32_t* cached,
@@ -78,7 +87,8 @@ class BlockManager {
   int64_t cache_hits() const { return cache_hits_; }
   int64_t cache_misses() const { return cache_misses_; }
   int64_t cache_evictions() const { return cache_evictions_; }
-  int64_t cached_blocks() const { return static_cast<int64_t>(cache_.size()); }
+  int64_t cached_blocks() const { return cached_count_; }
+  int64_t prefix_nodes() const { return static_cast<int64_t>(nodes_.size() - free_nodes_.size()); }
   const std::vector<int32_t>& refcounts() const { return ref_; }
   void free_queue(int32_t* out) const;  // head to tail, free_count() entries
 
@@ -87,6 +97,16 @@ class BlockManager {
     std::vector<int32_t> table;
     int32_t len = 0;
     bool alive = false;
+    bool known = true;          // its token ids are known (prefix caching)
+    int32_t node = -1;          // trie node of its full blocks' prefix (-1: empty prefix)
+    std::vector<int32_t> tail;  // ids of the tokens in its partly filled last block
+  };
+  // A trie node: the prefix of its parent plus one block of B token ids.
+  struct PrefixNode {
+    int32_t parent = -1;  // -1: the empty prefix
+    int32_t block = -1;   // cached block whose key this prefix is, or -1
+    int32_t refs = 0;     // child nodes + sequences ending here + (block >= 0)
+    uint64_t hash = 0;
   };
   bool valid_seq(int32_t s) const {
     return s >= 0 && s < static_cast<int32_t>(seqs_.size()) && seqs_[s].alive;
@@ -94,8 +114,14 @@ class BlockManager {
   int32_t pop_free();  // head of the free queue; drops its cache entry, if any
   void push_free(int32_t b);
   void unlink_free(int32_t b);
-  uint64_t block_key(uint64_t parent, const int32_t* tokens) const;
-  void register_block(int32_t b, uint64_t key, uint64_t parent, const int32_t* tokens);
+  uint64_t node_hash(int32_t parent, const int32_t* tokens) const;
+  int32_t find_node(int32_t parent, const int32_t* tokens) const;
+  int32_t get_node(int32_t parent, const int32_t* tokens);
+  void pin(int32_t node);
+  void release(int32_t node);
+  void set_entry(int32_t node, int32_t b);
+  void clear_entry(int32_t b);
+  void append_ids(Seq& s, int64_t first_token, int32_t n, const int32_t* tokens);
 
   int32_t num_blocks_;
   int32_t block_size_;
@@ -104,11 +130,13 @@ class BlockManager {
   std::vector<char> in_free_;
   int32_t head_ = -1, tail_ = -1;
   int64_t free_count_ = 0;
-  // Prefix cache.
-  std::unordered_map<uint64_t, int32_t> cache_;
-  std::vector<uint64_t> key_, parent_key_;
-  std::vector<char> has_key_;
-  std::vector<int32_t> key_tokens_;  // B tokens per cached block
+  // Prefix cache: the trie, its index by (parent, ids) hash, and each block's entry.
+  std::vector<PrefixNode> nodes_;
+  std::vector<int32_t> node_tokens_;  // B token ids per node
+  std::vector<int32_t> free_nodes_;
+  std::unordered_multimap<uint64_t, int32_t> index_;
+  std::vector<int32_t> block_node_;  // node whose entry the block is, or -1
+  int64_t cached_count_ = 0;
   int64_t cache_hits_ = 0, cache_misses_ = 0, cache_evictions_ = 0;
   std::vector<int32_t> ref_;
   std::vector<Seq> seqs_;

@@ -441,11 +441,11 @@ int pa_seq_create_cached(pa_pool* p, const int32_t* tokens, int32_t n, int32_t* 
   }
 }
 
-int pa_alloc(pa_pool* p, int32_t seq, int32_t n_tokens, int32_t* slots_out, int32_t* cow_out,
-             void* stream) {
+int pa_alloc_tokens(pa_pool* p, int32_t seq, int32_t n_tokens, const int32_t* tokens, int32_t* slots_out,
+                    int32_t* cow_out, void* stream) {
   if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
   int32_t src = -1, dst = -1;
-  const int rc = bm_status(p->bm.alloc(seq, n_tokens, slots_out, &src, &dst), seq);
+  const int rc = bm_status(p->bm.alloc(seq, n_tokens, slots_out, &src, &dst, tokens), seq);
   if (cow_out) {
     cow_out[0] = src;
     cow_out[1] = dst;
@@ -458,8 +458,14 @@ int pa_alloc(pa_pool* p, int32_t seq, int32_t n_tokens, int32_t* slots_out, int3
   return PA_OK;
 }
 
+int pa_alloc(pa_pool* p, int32_t seq, int32_t n_tokens, int32_t* slots_out, int32_t* cow_out,
+             void* stream) {
+  return pa_alloc_tokens(p, seq, n_tokens, nullptr, slots_out, cow_out, stream);
+}
+
 int pa_alloc_batch(pa_pool* p, const int32_t* seqs, const int32_t* n_tokens, int32_t count,
-                   int32_t* slots_out, int32_t* cow_out, int32_t* done_out, void* stream) {
+                   const int32_t* tokens, int32_t* slots_out, int32_t* cow_out, int32_t* done_out,
+                   void* stream) {
   if (done_out) *done_out = 0;
   if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
   if (count < 0 || (count > 0 && (!seqs || !n_tokens)))
@@ -481,7 +487,9 @@ int pa_alloc_batch(pa_pool* p, const int32_t* seqs, const int32_t* n_tokens, int
   int64_t off = 0;
   for (; k < count; ++k) {
     int32_t s = -1, d = -1;
-    rc = bm_status(p->bm.alloc(seqs[k], n_tokens[k], slots_out ? slots_out + off : nullptr, &s, &d), seqs[k]);
+    rc = bm_status(p->bm.alloc(seqs[k], n_tokens[k], slots_out ? slots_out + off : nullptr, &s, &d,
+                               tokens ? tokens + off : nullptr),
+                   seqs[k]);
     if (cow_out) {
       cow_out[2 * k] = s;
       cow_out[2 * k + 1] = d;

@@ -157,32 +157,57 @@ def pa_seq_create_cached(h, tokens):
     return s.value, c.value, slots[:len(t) - c.value].copy()
 
 
-def pa_alloc(h, seq, n_tokens, stream=0):
-    """Returns (slots int32[n_tokens], (src, dst) or None)."""
+def pa_alloc(h, seq, n_tokens, stream=0, tokens=None):
+    """Returns (slots int32[n_tokens], (src, dst) or None).  ``tokens``: the
+    appended token ids (pa_alloc_tokens), or None."""
     slots = np.empty(max(int(n_tokens), 0), dtype=np.int32)
     cow = np.full(2, -1, dtype=np.int32)
     st = C.c_void_p(0) if stream == 0 else _stream(stream)
-    _check(_L().pa_alloc(C.c_void_p(h), int(seq), int(n_tokens),
-                         slots.ctypes.data_as(C.POINTER(C.c_int32)),
-                         cow.ctypes.data_as(C.POINTER(C.c_int32)), st))
+    tp = None
+    if tokens is not None:
+        t_arr, tp = _i32_host(tokens)
+        if len(t_arr) != int(n_tokens):
+            raise ValueError("tokens must hold n_tokens ids")
+    _check(_L().pa_alloc_tokens(C.c_void_p(h), int(seq), int(n_tokens), tp,
+                                slots.ctypes.data_as(C.POINTER(C.c_int32)),
+                                cow.ctypes.data_as(C.POINTER(C.c_int32)), st))
     return slots, (None if cow[0] < 0 else (int(cow[0]), int(cow[1])))
 
 
-def pa_alloc_batch(h, seqs, n_tokens, stream=0):
+def pa_alloc_batch(h, seqs, n_tokens, stream=0, tokens=None):
     """Appends n_tokens[k] tokens to seqs[k] for every k in order, with one
     launch for all copy-on-write copies.  Returns (slots int32[sum n_tokens],
-    cow int32[count][2] with -1 where an append copied nothing)."""
+    cow int32[count][2] with -1 where an append copied nothing).  ``tokens``:
+    the appended ids back to back, or None.
+
+    If append k fails, appends 0 .. k-1 stay made (their copies enqueued): the
+    raised error carries ``done`` = k and the ``slots`` and ``cow`` of those
+    appends, so that the caller can still write their K/V."""
     s_arr, s_ptr = _i32_host(seqs)
     n_arr, n_ptr = _i32_host(n_tokens)
     if len(s_arr) != len(n_arr):
         raise ValueError("seqs and n_tokens differ in length")
-    slots = np.empty(max(int(n_arr.sum()) if len(n_arr) else 0, 0), dtype=np.int32)
+    total = int(n_arr.sum()) if len(n_arr) else 0
+    slots = np.empty(max(total, 0), dtype=np.int32)
     cow = np.full((len(s_arr), 2), -1, dtype=np.int32)
+    tp = None
+    if tokens is not None:
+        t_arr, tp = _i32_host(tokens)
+        if len(t_arr) != total:
+            raise ValueError("tokens must hold sum(n_tokens) ids")
     done = C.c_int32()
     st = C.c_void_p(0) if stream == 0 else _stream(stream)
-    _check(_L().pa_alloc_batch(C.c_void_p(h), s_ptr, n_ptr, len(s_arr),
-                               slots.ctypes.data_as(C.POINTER(C.c_int32)),
-                               cow.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(done), st))
+    rc = _L().pa_alloc_batch(C.c_void_p(h), s_ptr, n_ptr, len(s_arr), tp,
+                             slots.ctypes.data_as(C.POINTER(C.c_int32)),
+                             cow.ctypes.data_as(C.POINTER(C.c_int32)), C.byref(done), st)
+    try:
+        _check(rc)
+    except PAError as e:
+        k = done.value
+        e.done = k
+        e.slots = slots[:int(n_arr[:k].sum()) if k else 0].copy()
+        e.cow = cow[:k].copy()
+        raise
     return slots, cow
 
 
@@ -523,11 +548,11 @@ class PagedKVPool:
     def seq_create_cached(self, tokens):
         return pa_seq_create_cached(self.handle, tokens)
 
-    def alloc(self, seq, n, stream=None):
-        return pa_alloc(self.handle, seq, n, stream if self.buffer is not None else 0)
+    def alloc(self, seq, n, stream=None, tokens=None):
+        return pa_alloc(self.handle, seq, n, stream if self.buffer is not None else 0, tokens)
 
-    def alloc_batch(self, seqs, n_tokens, stream=None):
-        return pa_alloc_batch(self.handle, seqs, n_tokens, stream if self.buffer is not None else 0)
+    def alloc_batch(self, seqs, n_tokens, stream=None, tokens=None):
+        return pa_alloc_batch(self.handle, seqs, n_tokens, stream if self.buffer is not None else 0, tokens)
 
     def fork(self, parent):
         return pa_fork(self.handle, parent)

@@ -179,6 +179,26 @@ class DifferentialMachine(RuleBasedStateMachine):
         assert cow == ocow
 
     @precondition(lambda self: self.live)
+    @rule(i=st.integers(0, 1000), n=st.integers(0, 11), k=st.integers(0, 2), tag=st.integers(0, 2))
+    def alloc_tokens(self, i, n, k, tag):
+        """Appends with token ids: drawn from the shared prompts (so that the
+        blocks they fill collide with prompt blocks and with each other) or
+        from a few tags."""
+        s = self.live[i % len(self.live)]
+        ln = self.o.lens[s]
+        toks = (_PROMPTS[k] * 2)[ln:ln + n] if tag == 0 else [2000 + 5 * tag + j % 3 for j in range(n)]
+        toks = (toks + [7] * n)[:n]
+        try:
+            oslots, ocow = self.o.alloc(s, n, toks)
+        except NoBlocks:
+            with pytest.raises(pa.NoBlocksError):
+                pa.pa_alloc(self.h, s, n, tokens=toks)
+            return
+        slots, cow = pa.pa_alloc(self.h, s, n, tokens=toks)
+        np.testing.assert_array_equal(slots, np.asarray(oslots, dtype=np.int32))
+        assert cow == ocow
+
+    @precondition(lambda self: self.live)
     @rule(i=st.integers(0, 1000))
     def fork(self, i):
         p = self.live[i % len(self.live)]
@@ -430,6 +450,10 @@ def test_alloc_batch_argument_edges():
     assert pa.pa_seq_len(h, s)[0] == 0
     with pytest.raises(pa.PAError):
         pa.pa_alloc_batch(h, [s], [-1])
-    with pytest.raises(pa.BadSeqError):
+    with pytest.raises(pa.BadSeqError) as err:
         pa.pa_alloc_batch(h, [s, 99], [3, 1])
     assert pa.pa_seq_len(h, s)[0] == 3  # the append before the failing one stays made
+    # ... and the error hands back what was made, so its K/V can still be written.
+    first_block = int(pa.pa_block_tables(h, [s], 1)[0][0][0])
+    assert err.value.done == 1 and err.value.slots.tolist() == [first_block * 16 + j for j in range(3)]
+    assert err.value.cow.tolist() == [[-1, -1]]

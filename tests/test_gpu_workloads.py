@@ -234,6 +234,83 @@ def test_prefix_cached_sequences_decode_like_the_oracle():
     assert pool.device_status() == 0
 
 
+def test_conversation_turns_hit_on_generated_blocks_and_decode_like_the_oracle():
+    """Multi-turn conversations: each turn's prompt is the previous turns'
+    prompts and answers plus a new question; answers are generated one token
+    per step with the fused write + decode call and appended with their token
+    ids, so the blocks they fill enter the cache and the next turn hits on
+    them.  Cached counts and tables equal the oracle's; at the end of each
+    turn, decode over every conversation (the answers' K/V written by the
+    fused steps) matches the oracle, whose store holds each sequence's tokens
+    at its own slots (K/V of token id x at position t: row (131 x + t) of a
+    seeded table, so equal prefixes carry equal K/V)."""
+    say("conversation turns")
+    bs, hq, hkv, nb = 16, 32, 8, 400
+    rng = np.random.default_rng(464_011)
+    table = normal_fp16((4096, hkv, 128), 464_011, 1, "cuda")
+    table_v = normal_fp16((4096, hkv, 128), 464_011, 2, "cuda")
+    order = free_order(464_011, nb)
+    pool = pa.PagedKVPool(1, hkv, 128, bs, nb, free_order=order)
+    pool.pool_bytes().fill_(0xFF)
+    orc = OracleAllocator(nb, bs, order)
+
+    def rows(toks, start):
+        idx = torch.tensor([(int(t) * 131 + start + i) % 4096 for i, t in enumerate(toks)], device="cuda")
+        return table[idx].contiguous(), table_v[idx].contiguous()
+
+    def check_decode(seqs, hist):
+        st = OracleKVStore(1, nb, hkv, bs, 128)
+        for s in seqs:
+            t = np.arange(len(hist[s]))
+            k, v = rows(hist[s], 0)
+            st.write(0, k.cpu().numpy(), v.cpu().numpy(), np.asarray(orc.tables[s])[t // bs] * bs + t % bs)
+        mb = max(len(orc.tables[s]) for s in seqs)
+        tables, lens = pool.block_tables(seqs, mb)
+        np.testing.assert_array_equal(tables, np.asarray(orc.block_tables(seqs, mb)[0]))
+        q = normal_fp16((len(seqs), hq, 128), 464_011, 3 + sum(lens), "cuda")
+        out = pool.decode(0, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda())
+        assert_close(out, attention.decode(st, 0, q.cpu().numpy(), tables, lens), "fp16", f"turns T={sum(lens)}")
+
+    convs = 6
+    hist = {}
+    prev = [[] for _ in range(convs)]
+    for turn in range(3):
+        seqs = []
+        for c in range(convs):
+            prompt = prev[c] + [int(x) for x in rng.integers(0, 3000, int(rng.integers(5, 40)))]
+            os_, oc, oslots = orc.seq_create_cached(prompt)
+            s, cached, slots = pool.seq_create_cached(prompt)
+            assert (s, cached) == (os_, oc) and list(slots) == list(oslots)
+            if turn > 0:  # everything up to the last full block of the previous turn is cached
+                assert cached == len(prev[c]) // bs * bs
+            k, v = rows(prompt[cached:], cached)
+            pool.write_kv(0, k, v, torch.from_numpy(slots).cuda())
+            hist[s] = list(prompt)
+            seqs.append(s)
+        for step in range(int(rng.integers(10, 30))):  # the answer, one token per step
+            toks = [int(x) for x in rng.integers(0, 3000, len(seqs))]
+            slots, cow = pool.alloc_batch(seqs, [1] * len(seqs), tokens=toks)
+            for s, t in zip(seqs, toks):
+                orc.alloc(s, 1, [t])
+                hist[s].append(t)
+            pos = [len(hist[s]) - 1 for s in seqs]
+            kn = torch.stack([rows([t], p)[0][0] for t, p in zip(toks, pos)]).contiguous()
+            vn = torch.stack([rows([t], p)[1][0] for t, p in zip(toks, pos)]).contiguous()
+            mb = max(len(orc.tables[s]) for s in seqs)
+            tables, lens = pool.block_tables(seqs, mb)
+            q = normal_fp16((len(seqs), hq, 128), 464_011, 1000 + 97 * turn + step, "cuda")
+            pool.write_kv_decode(0, kn, vn, torch.from_numpy(slots).cuda(), q, torch.from_numpy(tables).cuda(),
+                                 torch.from_numpy(lens).cuda())
+        check_decode(seqs, hist)
+        for c, s in enumerate(seqs):
+            prev[c] = list(hist[s])
+            pool.free(s)
+            orc.free_seq(s)
+    st_, ost = pool.stats(), orc.stats()
+    assert all(st_[k] == ost[k] for k in ost) and st_["cache_hits"] > 0
+    assert pool.device_status() == 0
+
+
 def test_beam_search_fork_trees_decode_like_the_oracle():
     """Width-5 beam search (forks, frees, copy-on-write appends whose copies
     the library enqueues on the stream) over 4 prompts for 24 steps, each new
