@@ -836,6 +836,7 @@ def main(argv=None):
             "step": (f"alloc 1 token/seq + {bench.R} x "
                      + ("(write_kv, then paged decode)" if bench.separate_write
                         else "fused (write_kv + paged decode) launch") + "; attention only"),
+            "kv_loads": "ordinary (cached)" if pa.pa_pool_load_policy(bench.pool.handle)[1] else "nontemporal",
             **({"prefix_cache": bench.cache_info} if hasattr(bench, "cache_info") else {}),
             **({"beam": {**bench.w.extra, "search_steps": bench.beam_step,
                          "cow_copies": bench.pool.stats()["cow_copies"],

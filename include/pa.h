@@ -85,6 +85,11 @@ extern "C" {
 #define PA_DEV_BAD_LEN 4u   /* a context length < 1 or > max_blocks*block_size  */
 #define PA_DEV_BAD_ORDER 8u /* a seq_order entry outside [0, num_seqs) was skipped */
 
+/* ---- K/V load policy of the decode kernels (pa_pool_set_load_policy) -------- */
+#define PA_LOADS_AUTO 0      /* cached when used blocks average >= 1.5 holders    */
+#define PA_LOADS_STREAMING 1 /* nontemporal loads: every tile read once            */
+#define PA_LOADS_CACHED 2    /* ordinary loads: sharers' reads of a tile hit in L2 */
+
 /* ---- pa_decode_noalloc ------------------------------------------------------ */
 #define PA_NOALLOC_SCRATCH_BYTES 33554432 /* 32 MiB of static device scratch per GPU */
 
@@ -140,6 +145,19 @@ int pa_pool_destroy(pa_pool* pool);
 /* Geometry, byte sizes and default softmax scale of a pool (pa_pool_info);
  * PA_ERR_INVALID for NULL arguments. */
 int pa_pool_info_get(const pa_pool* pool, pa_pool_info* out);
+
+/* How the decode kernels load K/V tiles (not a step of the method; results do
+ * not depend on it).  Sequences that share a prefix read identical blocks
+ * (youngju.dev page, section "prefix 공유와 copy-on-write"): with ordinary
+ * loads their reads of a shared tile are served by L2, with nontemporal
+ * loads a tile read once streams past the caches at a higher rate.
+ * PA_LOADS_AUTO (the default) takes ordinary loads when the pool's used
+ * blocks are named by at least 1.5 block-table entries on average, else
+ * nontemporal ones.  PA_ERR_INVALID for an unknown policy.
+ * pa_pool_load_policy returns the policy and (cached_now_out, may be NULL)
+ * whether a decode launched now would use ordinary loads. */
+int pa_pool_set_load_policy(pa_pool* pool, int32_t policy);
+int pa_pool_load_policy(const pa_pool* pool, int32_t* policy_out, int32_t* cached_now_out);
 
 /* Replace the initial free-queue order by a permutation of 0..num_blocks-1
  * (host int32[n], n == num_blocks).  Only valid before the first allocation,

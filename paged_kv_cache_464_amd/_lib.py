@@ -26,6 +26,10 @@ PA_DEV_BAD_BLOCK = 2
 PA_DEV_BAD_LEN = 4
 PA_DEV_BAD_ORDER = 8
 
+PA_LOADS_AUTO = 0
+PA_LOADS_STREAMING = 1
+PA_LOADS_CACHED = 2
+
 PA_NOALLOC_SCRATCH_BYTES = 33554432
 
 
@@ -59,6 +63,8 @@ SIGNATURES = {
     "pa_pool_destroy": (C.c_int, [_P]),
     "pa_pool_info_get": (C.c_int, [_P, C.POINTER(pa_pool_info)]),
     "pa_pool_set_free_order": (C.c_int, [_P, _PI32, _I32]),
+    "pa_pool_set_load_policy": (C.c_int, [_P, _I32]),
+    "pa_pool_load_policy": (C.c_int, [_P, _PI32, _PI32]),
     "pa_pool_bind": (C.c_int, [_P, _P, C.POINTER(C.c_float), C.POINTER(C.c_float)]),
     "pa_pool_bind_int8": (C.c_int, [_P, _P, C.POINTER(C.c_float), C.POINTER(C.c_float), _PI32, _PI32]),
     "pa_multi_token_workspace_bytes": (C.c_int, [_P, _PI32, _I32, _I32, C.POINTER(C.c_uint64)]),

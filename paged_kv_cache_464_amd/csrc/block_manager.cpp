@@ -221,6 +221,7 @@ BmStatus BlockManager::seq_create_cached(const int32_t* tokens, int32_t n, int32
     ref_[b] = 1;
     s.table.push_back(b);
   }
+  table_entries_ += static_cast<int64_t>(s.table.size());
   s.node = parent;  // pinned above
   s.len = static_cast<int32_t>(h * bs);
   append_ids(s, h * bs, static_cast<int32_t>(n - h * bs), tokens + h * bs);
@@ -271,6 +272,7 @@ BmStatus BlockManager::alloc(int32_t seq, int32_t n, int32_t* slots, int32_t* co
     ref_[b] = 1;
     s.table.push_back(b);
   }
+  table_entries_ += need;
   for (int64_t j = 0; j < n; ++j) {
     const int64_t t = len + j;
     slots[j] = static_cast<int32_t>(static_cast<int64_t>(s.table[t / bs]) * bs + t % bs);
@@ -302,6 +304,7 @@ BmStatus BlockManager::fork(int32_t parent, int32_t* child) {
   k.tail = p.tail;
   if (k.known) pin(k.node);
   for (int32_t b : k.table) ++ref_[b];
+  table_entries_ += static_cast<int64_t>(k.table.size());
   *child = c;
   return BmStatus::kOk;
 }
@@ -312,6 +315,7 @@ BmStatus BlockManager::free_seq(int32_t seq) {
   for (auto it = s.table.rbegin(); it != s.table.rend(); ++it) {
     if (--ref_[*it] == 0) push_free(*it);
   }
+  table_entries_ -= static_cast<int64_t>(s.table.size());
   s.table.clear();
   s.table.shrink_to_fit();
   if (s.known) release(s.node);

@@ -84,6 +84,9 @@ class BlockManager {
   int64_t cow_copies() const { return cow_copies_; }
   int64_t alloc_failures() const { return alloc_failures_; }
   int64_t shared_blocks() const;
+  // Block-table entries of the live sequences (the sum of all reference
+  // counts): over the used blocks, the mean number of holders of a block.
+  int64_t table_entries() const { return table_entries_; }
   int64_t cache_hits() const { return cache_hits_; }
   int64_t cache_misses() const { return cache_misses_; }
   int64_t cache_evictions() const { return cache_evictions_; }
@@ -143,6 +146,7 @@ class BlockManager {
   int64_t live_seqs_ = 0;
   int64_t cow_copies_ = 0;
   int64_t alloc_failures_ = 0;
+  int64_t table_entries_ = 0;
   bool touched_ = false;  // any allocation happened
 };
 

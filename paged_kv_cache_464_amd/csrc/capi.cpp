@@ -81,6 +81,7 @@ struct pa_pool {
   bool bound = false;
   int device = -1;
   int num_cus = 256;
+  int32_t load_policy = PA_LOADS_AUTO;  // K/V loads of the decode kernel
   void* scratch = nullptr;           // device address of `scratch` on `device`
   hipError_t scratch_err = hipSuccess;
   pa::PoolGeom geom{};
@@ -242,6 +243,17 @@ int bm_status(pa::BmStatus s, int32_t seq) {
   }
 }
 
+// Whether decode launches use ordinary (cached) K/V loads: forced by the
+// pool's policy, or, by default, when the pool's used blocks have on average
+// at least 1.5 holders (sequences whose tables name them), i.e. when a
+// launch's sequences are likely to read many blocks more than once.
+bool use_cached_loads(const pa_pool* p) {
+  if (p->load_policy == PA_LOADS_STREAMING) return false;
+  if (p->load_policy == PA_LOADS_CACHED) return true;
+  const int64_t used = p->num_blocks - p->bm.free_count();
+  return used > 0 && 2 * p->bm.table_entries() >= 3 * used;
+}
+
 pa::DecodeLaunch make_launch(int32_t layer, const void* q, int32_t num_q_heads,
                              const int32_t* tables, int32_t max_blocks, const int32_t* lens,
                              int32_t num_seqs, const int32_t* order, float scale, const Plan& pl,
@@ -333,6 +345,21 @@ int pa_pool_info_get(const pa_pool* p, pa_pool_info* out) {
   // 1/sqrt(d): the square root and the division each rounded to fp32.
   out->softmax_scale = 1.0f / std::sqrt(static_cast<float>(p->head_dim));
   out->reserved = 0;
+  return PA_OK;
+}
+
+int pa_pool_set_load_policy(pa_pool* p, int32_t policy) {
+  if (!p) return fail(PA_ERR_INVALID, "pool is NULL");
+  if (policy != PA_LOADS_AUTO && policy != PA_LOADS_STREAMING && policy != PA_LOADS_CACHED)
+    return fail(PA_ERR_INVALID, "unknown load policy %d", policy);
+  p->load_policy = policy;
+  return PA_OK;
+}
+
+int pa_pool_load_policy(const pa_pool* p, int32_t* policy_out, int32_t* cached_now_out) {
+  if (!p || !policy_out) return fail(PA_ERR_INVALID, "NULL argument");
+  *policy_out = p->load_policy;
+  if (cached_now_out) *cached_now_out = use_cached_loads(p) ? 1 : 0;
   return PA_OK;
 }
 
@@ -648,6 +675,7 @@ static int run_decode(pa_pool* p, int32_t layer, const void* q, int32_t num_q_he
   d.k_new = nt.k;
   d.v_new = nt.v;
   d.new_slots = nt.slots;
+  d.cached_loads = use_cached_loads(p) ? 1 : 0;
   auto s = static_cast<hipStream_t>(stream);
   const bool rec = p->profiling && p->launches++ % p->every == 0 && p->n_records < p->max_records;
   hipEvent_t* ev = rec ? &p->ev[4 * static_cast<size_t>(p->n_records)] : nullptr;

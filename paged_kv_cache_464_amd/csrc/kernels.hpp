@@ -69,6 +69,7 @@ struct DecodeLaunch {
   int chunks_per_wave;   // k: chunks in one run (split modes)
   int waves_per_unit;    // runs per (sequence, KV head) = ceil(C / k) (split modes)
   float scale;
+  int cached_loads;  // 1: ordinary K/V loads (blocks shared by many sequences); 0: nontemporal
 };
 
 // t0/t1: optional events stamped at the kernel's start and end (null: untimed).

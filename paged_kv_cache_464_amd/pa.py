@@ -16,7 +16,7 @@ import torch
 from . import _lib
 from ._lib import (PA_DTYPE_FP16, PA_DTYPE_FP8_E4M3, PA_DTYPE_INT8, PA_ERR_BAD_SEQ, PA_ERR_NO_BLOCKS,  # noqa: F401
                    PA_DEV_BAD_BLOCK, PA_DEV_BAD_LEN, PA_DEV_BAD_ORDER, PA_DEV_BAD_SLOT,
-                   PA_NOALLOC_SCRATCH_BYTES)
+                   PA_LOADS_AUTO, PA_LOADS_CACHED, PA_LOADS_STREAMING, PA_NOALLOC_SCRATCH_BYTES)
 
 
 class PAError(RuntimeError):
@@ -115,6 +115,18 @@ def _info(h) -> dict:
 def pa_pool_set_free_order(h, perm):
     arr, ptr = _i32_host(perm)
     _check(_L().pa_pool_set_free_order(C.c_void_p(h), ptr, len(arr)))
+
+
+def pa_pool_set_load_policy(h, policy):
+    """PA_LOADS_AUTO, PA_LOADS_STREAMING or PA_LOADS_CACHED (K/V loads of decode)."""
+    _check(_L().pa_pool_set_load_policy(C.c_void_p(h), int(policy)))
+
+
+def pa_pool_load_policy(h):
+    """(policy, whether a decode launched now would use ordinary loads)."""
+    pol, now = C.c_int32(), C.c_int32()
+    _check(_L().pa_pool_load_policy(C.c_void_p(h), C.byref(pol), C.byref(now)))
+    return pol.value, bool(now.value)
 
 
 def pa_pool_bind(h, dev_ptr: int, k_scales=None, v_scales=None):

@@ -245,6 +245,31 @@ TestDifferential = DifferentialMachine.TestCase
 TestDifferential.settings = settings(max_examples=80, stateful_step_count=50, deadline=None)
 
 
+def test_load_policy_follows_block_sharing():
+    """Auto takes ordinary (cached) K/V loads once used blocks average 1.5 or
+    more block-table entries, and the policy can be forced either way."""
+    h = _pool(64, 8)
+    assert pa.pa_pool_load_policy(h) == (pa.PA_LOADS_AUTO, False)  # nothing used
+    s = pa.pa_seq_create(h)
+    pa.pa_alloc(h, s, 80)                            # 10 blocks, one holder each
+    assert pa.pa_pool_load_policy(h)[1] is False
+    c = pa.pa_fork(h, s)                             # 20 entries over 10 blocks
+    assert pa.pa_pool_load_policy(h)[1] is True
+    pa.pa_alloc(h, c, 80)                            # 30 entries over 20 blocks: exactly 1.5
+    assert pa.pa_pool_load_policy(h)[1] is True
+    pa.pa_alloc(h, c, 8)                             # 31 over 21: below
+    assert pa.pa_pool_load_policy(h)[1] is False
+    pa.pa_pool_set_load_policy(h, pa.PA_LOADS_CACHED)
+    assert pa.pa_pool_load_policy(h) == (pa.PA_LOADS_CACHED, True)
+    pa.pa_pool_set_load_policy(h, pa.PA_LOADS_STREAMING)
+    pa.pa_free(h, s)
+    pa.pa_fork(h, c)
+    assert pa.pa_pool_load_policy(h) == (pa.PA_LOADS_STREAMING, False)
+    with pytest.raises(pa.PAError):
+        pa.pa_pool_set_load_policy(h, 3)
+    pa.pa_pool_destroy(h)
+
+
 def test_order_longest_first_is_a_stable_descending_sort():
     """pa_order_longest_first against numpy's stable argsort of -lens, with ties."""
     rng = np.random.default_rng(464)

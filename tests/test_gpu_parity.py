@@ -472,6 +472,35 @@ def test_write_kv_decode_equals_write_then_decode(dtype, bs, hq, hkv):
     assert c.pool.device_status() == 0
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_cached_and_streaming_loads_give_identical_results(dtype, bs):
+    """The two K/V load flavours of the decode kernel compute the same thing
+    bit for bit: every schedule, both column-tile counts, plain and fused."""
+    lens = [1, 16, 17, 700, 33, 1000, 64, 5]
+    nb = int(sum(-(-t // bs) for t in lens)) + 4
+    say("load flavours", dtype, bs)
+    for hq, hkv in ((32, 8), (32, 1)):
+        c = build_case(lens, hq, hkv, bs, nb, 3300 + bs + hq + hkv, dtype)
+        last_slots = torch.tensor([int(c.slots[i][-1]) for i in range(len(lens))], dtype=torch.int32,
+                                  device="cuda")
+        last = [int(c.offsets[i + 1] - 1) for i in range(len(lens))]
+        k_new, v_new = c.k[last].contiguous(), c.v[last].contiguous()
+        for mode in (-1, 0, 64, 512):
+            if mode > 0 and mode % bs:
+                continue
+            outs = []
+            for pol in (pa.PA_LOADS_STREAMING, pa.PA_LOADS_CACHED):
+                pa.pa_pool_set_load_policy(c.pool.handle, pol)
+                assert pa.pa_pool_load_policy(c.pool.handle)[1] == (pol == pa.PA_LOADS_CACHED)
+                outs.append(c.pool.decode(0, c.q, c.tables, c.lens_dev, partition_tokens=mode))
+                outs.append(c.pool.write_kv_decode(0, k_new, v_new, last_slots, c.q, c.tables, c.lens_dev,
+                                                   partition_tokens=mode))
+            assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3]), (hq, hkv, mode)
+            assert torch.equal(outs[0], outs[1])
+        assert c.pool.device_status() == 0
+
+
 def test_write_kv_decode_slot_rules():
     """A negative slot skips the store (the pool's copy is used); a slot that is
     not the table's slot of token T-1 is flagged and skipped."""
