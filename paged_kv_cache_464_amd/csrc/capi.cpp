@@ -755,7 +755,7 @@ namespace {
 
 // Work items of a multi-token launch: for every sequence with query tokens,
 // tiles of multi_token_tile(G) tokens, the later tiles (which see more keys)
-// first.  Returns the number of items, or -1 after fail() for a bad
+// first within a sequence; wide and narrow tiles alternate.  Returns the number of items, or -1 after fail() for a bad
 // query_start.
 int64_t multi_token_items(const pa_pool* p, const int32_t* query_start, int32_t num_seqs, int32_t group,
                           std::vector<int32_t>* items) {
@@ -772,13 +772,33 @@ int64_t multi_token_items(const pa_pool* p, const int32_t* query_start, int32_t 
   if (items) {
     items->clear();
     items->reserve(static_cast<size_t>(4 * n_items));
+    // Narrow items (decode tokens: HBM-bound) and wide ones (prefill tiles:
+    // more query tokens than one wave takes, MFMA-bound) alternate, so that
+    // both kinds run on every CU at once and the matrix cores and the memory
+    // system work together (with the prefill tiles first the two kinds ran
+    // one after the other).
+    std::vector<int32_t> wide_items, short_items;
+    const int tw = pa::multi_token_wave_tile(group);
     for (int32_t i = 0; i < num_seqs; ++i) {
       const int32_t n_i = query_start[i + 1] - query_start[i];
       for (int32_t t = (n_i + tq - 1) / tq - 1; t >= 0; --t) {
-        items->push_back(i);
-        items->push_back(t * tq);
-        items->push_back(query_start[i] + t * tq);
-        items->push_back(n_i);
+        const int32_t nq = std::min<int32_t>(n_i - t * tq, tq);
+        std::vector<int32_t>& dst = nq > tw ? wide_items : short_items;
+        dst.push_back(i);
+        dst.push_back(t * tq);
+        dst.push_back(query_start[i] + t * tq);
+        dst.push_back(n_i);
+      }
+    }
+    size_t a = 0, b = 0;
+    while (a < wide_items.size() || b < short_items.size()) {
+      if (b < short_items.size()) {
+        items->insert(items->end(), short_items.begin() + b, short_items.begin() + b + 4);
+        b += 4;
+      }
+      if (a < wide_items.size()) {
+        items->insert(items->end(), wide_items.begin() + a, wide_items.begin() + a + 4);
+        a += 4;
       }
     }
   }

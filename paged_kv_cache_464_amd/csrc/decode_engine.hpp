@@ -465,15 +465,16 @@ struct WaveDecoder {
     return b;
   }
 
-  // Nontemporal in decode where every tile is read once; ordinary loads in
-  // multi-token attention, whose waves re-read each other's key tiles, and in
-  // decode over blocks that many sequences share (CACHED): a block's sharers
+  // Nontemporal where every tile is read once (decode; multi-token items of
+  // at most one wave's tokens, e.g. decode tokens); ordinary loads (CACHED)
+  // for the wide multi-token items, whose waves re-read each other's key
+  // tiles, and for decode over blocks that many sequences share: a block's sharers
   // run close together on one XCD (same KV head, nearby sequences), and with
   // nontemporal loads its lines leave L2 before the other sharers read them
   // (measured on MI355X, 160 beams sharing prefixes: 2.34x the unique bytes
   // fetched with nontemporal loads, 1.12x with ordinary ones).
   static __device__ u32x4 ld16(const uint8_t* a) {
-    if constexpr (MULTI || CACHED) return *reinterpret_cast<const u32x4*>(a);
+    if constexpr (CACHED) return *reinterpret_cast<const u32x4*>(a);
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
   }
 
@@ -1239,7 +1240,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
   constexpr int NT = 2;
   constexpr int kD = D;
-  using Dec = WaveDecoder<D, KIND, BS, NT, false, true>;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = p.num_q_heads / g.kv_heads;
@@ -1262,10 +1262,10 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
     }
     return;
   }
-  Dec dec;
-  dec.bind(g, p, seq, kvh, lane);
   int kmax;
   if (wide) {
+    WaveDecoder<D, KIND, BS, NT, false, true, true> dec;  // key tiles shared by the four waves
+    dec.bind(g, p, seq, kvh, lane);
     const int jw = w * tq;  // this wave's first token within the item
     if (jw >= nq_item) return;  // no tokens for this wave (no barrier on this path)
     const int nq = (nq_item - jw) < tq ? (nq_item - jw) : tq;
@@ -1287,6 +1287,8 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
       if (col < nq * group) multi_token_store(p, dec, dec.oacc[nt], dec.out_mul / l, row0 + jw, col, kvh, group);
     }
   } else {
+    WaveDecoder<D, KIND, BS, NT, false, true, false> dec;  // each key tile read once
+    dec.bind(g, p, seq, kvh, lane);
     auto raw_tok = [&](int j) -> int64_t { return 16ll * (w + kWaves * j); };
     multi_token_setup(dec, T - n_i + j0, nq_item, group, row0, kmax);
     const int n = (kmax + 16 * kWaves - 1) / (16 * kWaves);

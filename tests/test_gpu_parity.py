@@ -372,6 +372,89 @@ def test_copy_blocks_all_layers(dtype):
             assert torch.equal(kd, k[ly]) and torch.equal(vd, v[ly])
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
+def test_copy_blocks_more_than_one_launch_of_pairs(dtype):
+    """130 distinct pairs (three launches of at most 64 pairs) across 3 layers,
+    checked byte for byte against the oracle's copy_block; then a batch of
+    more than 64 copy-on-write appends (pa_alloc_batch) against the oracle."""
+    say("copy_blocks 130", dtype)
+    layers, bs, n = 3, 16, 300
+    kw = {}
+    ks = vs = kz = vz = None
+    if dtype != "fp16":
+        ks, vs = np.full((layers, 2), 0.03, np.float32), np.full((layers, 2), 0.05, np.float32)
+        kw = {"k_scales": ks, "v_scales": vs}
+        if dtype == "int8":
+            kz, vz = np.full((layers, 2), 3, np.int32), np.full((layers, 2), -2, np.int32)
+            kw.update(k_zeros=kz, v_zeros=vz)
+    order = free_order(909, n)
+    pool = pa.PagedKVPool(layers, 2, 128, bs, n, dtype, free_order=order, **kw)
+    st = OracleKVStore(layers, n, 2, bs, 128, dtype, ks, vs, kz, vz)
+    rng = np.random.default_rng(909)
+    blocks = rng.permutation(n)
+    src, dst = [int(b) for b in blocks[:130]], [int(b) for b in blocks[130:260]]
+    slots = np.concatenate([np.arange(b * bs, (b + 1) * bs) for b in src]).astype(np.int32)
+    sl_d = torch.from_numpy(slots).cuda()
+    for ly in range(layers):
+        k = normal_fp16((len(slots), 2, 128), 910 + ly, 1, "cuda")
+        v = normal_fp16((len(slots), 2, 128), 910 + ly, 2, "cuda")
+        pool.write_kv(ly, k, v, sl_d)
+        st.write(ly, k.cpu().numpy(), v.cpu().numpy(), slots)
+    pool.copy_blocks(src, dst)
+    for a, b in zip(src, dst):
+        st.copy_block(a, b)
+    dslots = np.concatenate([np.arange(b * bs, (b + 1) * bs) for b in dst]).astype(np.int32)
+    for ly in range(layers):
+        kg, vg = pool.gather_kv(ly, torch.from_numpy(dslots).cuda())
+        ok, ov = st.read_slots(ly, dslots)
+        if dtype == "fp16":
+            kg, vg, ok, ov = (x.view(np.uint16) for x in (kg.cpu().numpy(), vg.cpu().numpy(), ok, ov))
+        else:
+            kg, vg = kg.cpu().numpy(), vg.cpu().numpy()
+        np.testing.assert_array_equal(kg, ok)
+        np.testing.assert_array_equal(vg, ov)
+    # More than 64 copy-on-write appends in one batch: 70 forks of sequences
+    # with a partial last block, each appending one token.
+    pool2 = pa.PagedKVPool(1, 2, 128, bs, 400, dtype, free_order=free_order(911, 400),
+                           **{k_: v_[:1] for k_, v_ in kw.items()})
+    orc = OracleAllocator(400, bs, free_order(911, 400))
+    st2 = OracleKVStore(1, 400, 2, bs, 128, dtype, *(None if x is None else x[:1] for x in (ks, vs, kz, vz)))
+    parents = []
+    for i in range(70):
+        s_ = pool2.seq_create()
+        assert s_ == orc.seq_create()
+        sl, _ = pool2.alloc(s_, 21)
+        orc.alloc(s_, 21)
+        k = normal_fp16((21, 2, 128), 920 + i, 1, "cuda")
+        v = normal_fp16((21, 2, 128), 920 + i, 2, "cuda")
+        pool2.write_kv(0, k, v, torch.from_numpy(sl).cuda())
+        st2.write(0, k.cpu().numpy(), v.cpu().numpy(), sl)
+        parents.append(s_)
+    kids = []
+    for s_ in parents:
+        c = pool2.fork(s_)
+        assert c == orc.fork(s_)
+        kids.append(c)
+    slots2, cow = pool2.alloc_batch(kids, [1] * len(kids))
+    assert (cow[:, 0] >= 0).sum() == 70
+    for c, pr in zip(kids, cow):
+        _, ocow = orc.alloc(c, 1)
+        assert tuple(pr) == ocow
+        st2.copy_block(*ocow)
+    torch.cuda.synchronize()
+    t = np.arange(21)
+    for c in kids:  # the copied tokens of each fork read back like the oracle's
+        sl = np.asarray(orc.tables[c])[t // bs] * bs + t % bs
+        kg, vg = pool2.gather_kv(0, torch.from_numpy(sl.astype(np.int32)).cuda())
+        ok, ov = st2.read_slots(0, sl)
+        if dtype == "fp16":
+            assert (kg.cpu().numpy().view(np.uint16) == ok.view(np.uint16)).all()
+            assert (vg.cpu().numpy().view(np.uint16) == ov.view(np.uint16)).all()
+        else:
+            assert (kg.cpu().numpy() == ok).all() and (vg.cpu().numpy() == ov).all()
+    assert pool.device_status() == 0 and pool2.device_status() == 0
+
+
 def test_kernel_timing_samples_every_nth_launch():
     """pa_profile_begin(max, every) stamps launches 0, every, 2*every, ... only,
     for the decode kernel and, in split mode, the reduce kernel."""
