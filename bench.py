@@ -16,7 +16,10 @@ in HBM.
 The other workloads (``tiny``, ``cb_prefix``, ``long_ctx``,
 ``fp8_{gqa,mqa}_bs{8,16,32}``, ``int8_{gqa,mqa}_bs16``, ``prefix_cache``,
 ``beam_k5``) time one pool layer R times per step ("1 layer
-timed xR").  When one layer's KV would fit in the 256 MB last-level cache, the
+timed xR").  ``beam_k5`` decodes with the shared-prefix pair of launches
+(``pa_decode_shared_prefix``: the beams' common prompt read once per beam
+group, then each beam's own tokens, groups planned once per step);
+``--shared-prefix-min 0`` times the plain fused decode instead.  When one layer's KV would fit in the 256 MB last-level cache, the
 pool holds several copies of it and launch r reads copy r mod copies, so that
 the bandwidth figure is HBM's and not the cache's.
 
@@ -68,6 +71,14 @@ MULTI_TOKEN_WORKLOADS = ("prefill_chunks", "mixed_batch")
 # Workloads whose sequences share physical blocks: their roofline is priced on
 # the bytes that must come from HBM, each shared block once.
 SHARING_WORKLOADS = ("cb_prefix", "prefix_cache", "beam_k5")
+# Shared-prefix decode by default where it was measured faster than the plain
+# fused decode: the beams share 2040 of about 2060 tokens.  prefix_cache and
+# cb_prefix ran slower with it on MI355X: prefix_cache's shared pass (1024
+# shared tokens of 1088-2048) costs more than the re-reads it saves, which
+# the L2 serves; cb_prefix shares 192 tokens, under the 256-token minimum, so
+# only the private pass runs, a single pass per sequence, slower than the
+# plain decode's split schedule on its 129-2560-token mix.
+SHARED_PREFIX_DEFAULT = {"beam_k5": 256}
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 
 
@@ -149,6 +160,11 @@ class DecodeBench:
             self.copies = max(1, -(-(4 * LLC_BYTES) // layer_bytes))
         self.partition = w.partition_tokens if args.partition is None else args.partition
         self.separate_write = bool(args.separate_write)
+        # Shared-prefix decode for the workloads whose sequences share blocks:
+        # groups found on the host each step, planned (one upload) and run on
+        # every launch.  0 turns it off.
+        sp = SHARED_PREFIX_DEFAULT.get(name, 0) if args.shared_prefix_min is None else args.shared_prefix_min
+        self.sp_min = sp if name in SHARING_WORKLOADS and not self.separate_write else 0
         # Room for the appended tokens: one more block per sequence per 16 steps.
         self.num_blocks = w.num_blocks + self.S * (-(-total_steps // self.bs) + 1)
         self.order = free_order(w.seed, self.num_blocks)
@@ -215,6 +231,15 @@ class DecodeBench:
         self.mb_cap = int(-(-(self.setup_lens.max() + total_steps) // self.bs))
         ws = pa.pa_decode_workspace_bytes(self.pool.handle, self.S, self.hq, self.mb_cap, self.partition)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.dev)
+        self.sp_groups_log = []
+        if self.sp_min:
+            # Largest shared-prefix workspace of this batch: one work item per
+            # sequence (every group a singleton with a shared run).
+            one = max(1, 16 // self.bs)
+            worst = (np.arange(self.S, dtype=np.int32), np.arange(self.S + 1, dtype=np.int32),
+                     np.full(self.S, one, dtype=np.int32))
+            n = pa.pa_decode_shared_prefix_workspace_bytes(self.pool.handle, self.S, self.hq, worst, self.mb_cap)
+            self.sp_workspace = torch.empty(n, dtype=torch.uint8, device=self.dev)
         # Step metadata (slot mapping, lengths, longest-first sequence order,
         # block tables) is packed into one int32 buffer so that each step makes
         # a single upload: two pinned host copies used alternately (each guarded
@@ -353,18 +378,28 @@ class DecodeBench:
         self.meta_d.copy_(self.pinned[k], non_blocking=True)
         self.uploaded[k].record()
         h, st = self.pool.handle, self.stream
-        for r in range(self.R):
-            layer = r % self.copies
-            if self.separate_write:
-                pa.pa_write_kv(h, layer, self.k_new[r], self.v_new[r], self.slots_d, stream=st)
-                pa.pa_decode(h, layer, self.q[r], self.tables_d, self.lens_d, out=self.out[r],
-                             partition_tokens=self.partition, workspace=self.workspace, stream=st,
-                             seq_order=self.order_d)
-            else:
-                pa.pa_write_kv_decode(h, layer, self.k_new[r], self.v_new[r], self.slots_d, self.q[r],
-                                      self.tables_d, self.lens_d, out=self.out[r],
-                                      partition_tokens=self.partition, workspace=self.workspace,
-                                      stream=st, seq_order=self.order_d)
+        if self.sp_min:
+            groups = self.pool.shared_prefix_groups(tables, lens, self.sp_min)
+            plan = pa.pa_shared_prefix_plan(h, self.S, self.hq, self.mb_cap, groups, workspace=self.sp_workspace,
+                                            stream=st)
+            self.sp_groups_log.append(groups)
+            for r in range(self.R):
+                pa.pa_decode_shared_prefix(h, r % self.copies, self.q[r], self.tables_d, self.lens_d, plan,
+                                           out=self.out[r], stream=st, k_new=self.k_new[r], v_new=self.v_new[r],
+                                           slot_mapping=self.slots_d)
+        else:
+            for r in range(self.R):
+                layer = r % self.copies
+                if self.separate_write:
+                    pa.pa_write_kv(h, layer, self.k_new[r], self.v_new[r], self.slots_d, stream=st)
+                    pa.pa_decode(h, layer, self.q[r], self.tables_d, self.lens_d, out=self.out[r],
+                                 partition_tokens=self.partition, workspace=self.workspace, stream=st,
+                                 seq_order=self.order_d)
+                else:
+                    pa.pa_write_kv_decode(h, layer, self.k_new[r], self.v_new[r], self.slots_d, self.q[r],
+                                          self.tables_d, self.lens_d, out=self.out[r],
+                                          partition_tokens=self.partition, workspace=self.workspace,
+                                          stream=st, seq_order=self.order_d)
         per_tok = 2 * self.hkv * 128 * self.elem
         scales = 2 * self.hkv * 4 if self.fp8 else (4 * self.hkv * 4 if self.int8 else 0)
         self.kv_bytes_log.append(int(lens.astype(np.int64).sum()) * per_tok + scales)
@@ -402,6 +437,16 @@ class DecodeBench:
                     pool.free(old[b])
             self.beams[g] = new
         self.seqs = [s for b in self.beams for s in b]
+
+    def shared_prefix_info(self):
+        """Groups of the last timed step's shared-prefix plan."""
+        members, gstart, shared = self.sp_groups_log[-1]
+        sizes = np.diff(gstart)
+        on = shared > 0
+        return {"min_shared_tokens": self.sp_min, "groups_with_shared_pass": int(on.sum()),
+                "sequences_in_them": int(sizes[on].sum()),
+                "shared_tokens_per_member": int((shared[on] * sizes[on]).sum() * self.bs) // max(int(sizes[on].sum()), 1),
+                "host": "pa_shared_prefix_groups + pa_shared_prefix_plan once per step, inside the timed step"}
 
     def _unique_tokens(self, tables, lens):
         """Tokens held in distinct physical blocks (a shared block counted once)."""
@@ -717,6 +762,10 @@ def main(argv=None):
     ap.add_argument("--separate-write", action="store_true",
                     help="scatter the new tokens with pa_write_kv and attend with pa_decode "
                          "(two launches per layer) instead of the fused pa_write_kv_decode")
+    ap.add_argument("--shared-prefix-min", type=int, default=None,
+                    help="for the workloads whose sequences share blocks: decode with pa_decode_shared_prefix, "
+                         "grouping sequences that share at least this many leading tokens (0 = plain fused "
+                         "decode; default 256 for beam_k5, 0 for the others)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)
@@ -748,6 +797,8 @@ def main(argv=None):
     bench.kv_bytes_log.clear()
     bench.tables_log.clear()
     bench.lens_log.clear()
+    if hasattr(bench, "sp_groups_log"):
+        bench.sp_groups_log.clear()
     stamp = min(max(args.stamp_steps, 1), args.steps)
     gc.collect()
     gc.disable()  # no collector pauses inside the timed steps
@@ -835,7 +886,9 @@ def main(argv=None):
             "num_blocks": bench.num_blocks, "partition_tokens": bench.partition,
             "step": (f"alloc 1 token/seq + {bench.R} x "
                      + ("(write_kv, then paged decode)" if bench.separate_write
-                        else "fused (write_kv + paged decode) launch") + "; attention only"),
+                        else "fused shared-prefix decode (shared pass + fused write and private pass)"
+                        if bench.sp_min else "fused (write_kv + paged decode) launch") + "; attention only"),
+            **({"shared_prefix": bench.shared_prefix_info()} if bench.sp_min else {}),
             "kv_loads": "ordinary (cached)" if pa.pa_pool_load_policy(bench.pool.handle)[1] else "nontemporal",
             **({"prefix_cache": bench.cache_info} if hasattr(bench, "cache_info") else {}),
             **({"beam": {**bench.w.extra, "search_steps": bench.beam_step,

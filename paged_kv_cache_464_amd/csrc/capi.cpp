@@ -139,7 +139,7 @@ struct Plan {
   uint64_t ws_bytes, off_l, off_o;
 };
 
-constexpr int kModeSingle = 0, kModeSplit4 = 1, kModeSplit1 = 2;
+constexpr int kModeSingle = 0, kModeSplit4 = 1, kModeSplit1 = 2, kModePrivate = 3;
 
 int make_plan(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
               int32_t partition_tokens, Plan* out) {
@@ -753,6 +753,37 @@ int pa_write_kv_decode(pa_pool* p, int32_t layer, const void* k_new, const void*
 
 namespace {
 
+// Copies n int32 from host memory to device memory `dst` on stream s through
+// the pool's ring of pinned staging buffers (each reused once the event of
+// the upload that last read it has completed, so the host can run several
+// launches ahead of the device).
+int upload_ints(pa_pool* p, void* dst, const int32_t* src, size_t n, hipStream_t s) {
+  hipError_t e;
+  pa_pool::Staging& st = p->mt_ring[p->mt_next];
+  p->mt_next = (p->mt_next + 1) % pa_pool::kStagingRing;
+  if (st.done) {
+    e = hipEventSynchronize(st.done);  // this buffer's last upload has been read
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  } else {
+    e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+  }
+  if (st.cap < n) {
+    if (st.host) (void)hipHostFree(st.host);
+    st.host = nullptr;
+    st.cap = 0;
+    e = hipHostMalloc(reinterpret_cast<void**>(&st.host), n * sizeof(int32_t), hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
+    st.cap = n;
+  }
+  std::memcpy(st.host, src, n * sizeof(int32_t));
+  e = hipMemcpyAsync(dst, st.host, n * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(staging)");
+  e = hipEventRecord(st.done, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return PA_OK;
+}
+
 // Work items of a multi-token launch: for every sequence with query tokens,
 // tiles of multi_token_tile(G) tokens, the later tiles (which see more keys)
 // first within a sequence; wide and narrow tiles alternate.  Returns the number of items, or -1 after fail() for a bad
@@ -850,28 +881,7 @@ int pa_multi_token_attention(pa_pool* p, int32_t layer, const void* q, int32_t n
   if (n_items * p->kv_heads > 0x7FFFFFFF) return fail(PA_ERR_INVALID, "too many query tiles");
   auto s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  pa_pool::Staging& st = p->mt_ring[p->mt_next];
-  p->mt_next = (p->mt_next + 1) % pa_pool::kStagingRing;
-  if (st.done) {
-    e = hipEventSynchronize(st.done);  // this buffer's last upload has been read
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-  } else {
-    e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-  }
-  if (st.cap < items.size()) {
-    if (st.host) (void)hipHostFree(st.host);
-    st.host = nullptr;
-    st.cap = 0;
-    e = hipHostMalloc(reinterpret_cast<void**>(&st.host), items.size() * sizeof(int32_t), hipHostMallocDefault);
-    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(work items)");
-    st.cap = items.size();
-  }
-  std::memcpy(st.host, items.data(), items.size() * sizeof(int32_t));
-  e = hipMemcpyAsync(workspace, st.host, need, hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work items)");
-  e = hipEventRecord(st.done, s);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((rc = upload_ints(p, workspace, items.data(), items.size(), s))) return rc;
   pa::DecodeLaunch d{};
   d.layer = layer;
   d.q = q;
@@ -1005,6 +1015,248 @@ int pa_profile_end(pa_pool* p, pa_profile* out) {
   p->profiling = false;
   p->n_records = 0;
   *out = r;
+  return PA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of a shared-prefix decode: the shared pass's partials and the
+// uploaded int32 tail (starts[S], members[S], items[4 * n_items]).
+struct SharedLayout {
+  uint64_t off_l, off_o, off_i, bytes;
+};
+
+SharedLayout shared_layout(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int64_t n_items) {
+  const uint64_t rows = static_cast<uint64_t>(num_seqs) * num_q_heads;
+  SharedLayout L;
+  L.off_l = align_up(rows * 4, 256);
+  L.off_o = L.off_l + align_up(rows * 4, 256);
+  L.off_i = L.off_o + align_up(rows * p->head_dim * 4, 256);
+  L.bytes = L.off_i + align_up((2ull * num_seqs + 4ull * n_items) * 4, 256);
+  return L;
+}
+
+// Checks the groups of a shared-prefix decode and builds the int32 tail
+// (starts by sequence, members, shared-pass items).  Returns the number of
+// items, or -1 after fail().
+int64_t shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
+                           const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
+                           int32_t num_groups, std::vector<int32_t>* tail) {
+  if (num_groups < 0 || (num_seqs > 0 && (!members || !group_start || !shared_blocks)))
+    return fail(PA_ERR_INVALID, "members, group_start and shared_blocks are required"), -1;
+  if (num_seqs > 0 && (group_start[0] != 0 || group_start[num_groups] != num_seqs))
+    return fail(PA_ERR_INVALID, "group_start must run from 0 to num_seqs"), -1;
+  const int group = num_q_heads / p->kv_heads;
+  const int per_item = group >= 32 ? 1 : 32 / group;  // members whose heads fit 32 columns
+  std::vector<char> seen(static_cast<size_t>(num_seqs), 0);
+  tail->assign(2 * static_cast<size_t>(num_seqs), 0);
+  int32_t* starts = tail->data();
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t m = members[i];
+    if (m < 0 || m >= num_seqs || seen[m]) return fail(PA_ERR_INVALID, "members must be a permutation"), -1;
+    seen[m] = 1;
+    (*tail)[num_seqs + i] = m;
+  }
+  int64_t n_items = 0;
+  std::vector<int32_t> items;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int32_t a = group_start[g], b = group_start[g + 1];
+    if (b < a) return fail(PA_ERR_INVALID, "group_start decreases at group %d", g), -1;
+    const int64_t ts = static_cast<int64_t>(shared_blocks[g]) * p->block_size;
+    if (shared_blocks[g] < 0 || shared_blocks[g] > max_blocks || ts % 16 != 0)
+      return fail(PA_ERR_INVALID, "shared_blocks[%d] = %d: not a multiple of 16 tokens inside the table", g,
+                  shared_blocks[g]), -1;
+    if (ts == 0) continue;
+    for (int32_t i = a; i < b; ++i) starts[members[i]] = static_cast<int32_t>(ts);
+    for (int32_t i = a; i < b; i += per_item) {
+      items.push_back(i);
+      items.push_back(std::min<int32_t>(per_item, b - i));
+      items.push_back(static_cast<int32_t>(ts));
+      items.push_back(0);
+      ++n_items;
+    }
+  }
+  tail->insert(tail->end(), items.begin(), items.end());
+  return n_items;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_shared_prefix_groups(const pa_pool* p, const int32_t* tables, const int32_t* lens, int32_t n,
+                            int32_t max_blocks, int32_t min_shared_tokens, int32_t* members_out,
+                            int32_t* group_start_out, int32_t* shared_blocks_out, int32_t* num_groups_out) {
+  if (!p || n < 0 || max_blocks < 1 || !num_groups_out ||
+      (n > 0 && (!tables || !lens || !members_out || !group_start_out || !shared_blocks_out)))
+    return fail(PA_ERR_INVALID, "bad arguments to pa_shared_prefix_groups");
+  const int32_t bs = p->block_size;
+  const int32_t quantum = bs >= 16 ? 1 : 16 / bs;  // blocks per 16 tokens
+  // Candidates: sequences with at least one 16-token run of full blocks
+  // before the block of their last token, keyed by their first block.
+  std::vector<int32_t> order;
+  std::vector<int32_t> singles;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t full = lens[i] >= 1 ? (static_cast<int64_t>(lens[i]) - 1) / bs : 0;
+    if (full >= quantum && tables[static_cast<int64_t>(i) * max_blocks] >= 0) order.push_back(i);
+    else singles.push_back(i);
+  }
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return tables[static_cast<int64_t>(x) * max_blocks] < tables[static_cast<int64_t>(y) * max_blocks];
+  });
+  int32_t ng = 0, pos = 0;
+  group_start_out[0] = 0;
+  auto emit = [&](const int32_t* seqs, int32_t cnt, int32_t shared) {
+    for (int32_t k = 0; k < cnt; ++k) members_out[pos++] = seqs[k];
+    shared_blocks_out[ng] = shared;
+    group_start_out[++ng] = pos;
+  };
+  for (size_t a = 0; a < order.size();) {
+    size_t b = a + 1;
+    const int32_t* row0 = tables + static_cast<int64_t>(order[a]) * max_blocks;
+    while (b < order.size() && tables[static_cast<int64_t>(order[b]) * max_blocks] == row0[0]) ++b;
+    // Longest common run of block ids, inside every member's full blocks
+    // that precede its last token, rounded down to 16 tokens.
+    int64_t k = max_blocks;
+    for (size_t i = a; i < b; ++i) k = std::min<int64_t>(k, (static_cast<int64_t>(lens[order[i]]) - 1) / bs);
+    for (size_t i = a + 1; i < b && k > 0; ++i) {
+      const int32_t* row = tables + static_cast<int64_t>(order[i]) * max_blocks;
+      int64_t c = 0;
+      while (c < k && row[c] == row0[c]) ++c;
+      k = c;
+    }
+    k -= k % quantum;
+    if (b - a >= 2 && k * bs >= min_shared_tokens && k > 0) {
+      emit(order.data() + a, static_cast<int32_t>(b - a), static_cast<int32_t>(k));
+    } else {
+      for (size_t i = a; i < b; ++i) emit(&order[i], 1, 0);
+    }
+    a = b;
+  }
+  for (int32_t i : singles) emit(&i, 1, 0);
+  *num_groups_out = ng;
+  return PA_OK;
+}
+
+int pa_decode_shared_prefix_workspace_bytes(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads,
+                                            const int32_t* members, const int32_t* group_start,
+                                            const int32_t* shared_blocks, int32_t num_groups,
+                                            int32_t max_blocks, uint64_t* bytes_out) {
+  if (!p || !bytes_out || num_seqs < 0) return fail(PA_ERR_INVALID, "bad arguments");
+  if (num_q_heads < 1 || num_q_heads % p->kv_heads != 0 || num_q_heads / p->kv_heads > 32)
+    return fail(PA_ERR_INVALID, "num_q_heads %d must be a multiple of kv_heads %d with a group of at most 32",
+                num_q_heads, p->kv_heads);
+  std::vector<int32_t> tail;
+  const int64_t n_items = shared_groups_tail(p, num_seqs, num_q_heads, max_blocks, members, group_start,
+                                             shared_blocks, num_groups, &tail);
+  if (n_items < 0) return PA_ERR_INVALID;
+  *bytes_out = num_seqs == 0 ? 0 : shared_layout(p, num_seqs, num_q_heads, n_items).bytes;
+  return PA_OK;
+}
+
+int pa_shared_prefix_plan(pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
+                          const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
+                          int32_t num_groups, void* workspace, uint64_t workspace_bytes, void* stream,
+                          pa_shared_plan* plan) {
+  int rc = check_bound(p);
+  if (rc) return rc;
+  if (!plan || num_seqs < 0) return fail(PA_ERR_INVALID, "bad arguments to pa_shared_prefix_plan");
+  *plan = pa_shared_plan{};
+  if (num_q_heads < 1 || num_q_heads % p->kv_heads != 0 || num_q_heads / p->kv_heads > 32)
+    return fail(PA_ERR_INVALID, "num_q_heads %d must be a multiple of kv_heads %d with a group of at most 32",
+                num_q_heads, p->kv_heads);
+  if (max_blocks < 1 || static_cast<int64_t>(max_blocks) * p->block_size > 0x7FFFFFFF)
+    return fail(PA_ERR_INVALID, "max_blocks %d out of range", max_blocks);
+  std::vector<int32_t> tail;
+  const int64_t n_items = shared_groups_tail(p, num_seqs, num_q_heads, max_blocks, members, group_start,
+                                             shared_blocks, num_groups, &tail);
+  if (n_items < 0) return PA_ERR_INVALID;
+  if (n_items * p->kv_heads > 0x7FFFFFFF) return fail(PA_ERR_INVALID, "too many shared-pass items");
+  if (num_seqs > 0) {
+    const SharedLayout L = shared_layout(p, num_seqs, num_q_heads, n_items);
+    if (!workspace || workspace_bytes < L.bytes || misaligned(workspace, 16))
+      return fail(PA_ERR_INVALID, "a 16-byte aligned workspace of %llu bytes is needed",
+                  static_cast<unsigned long long>(L.bytes));
+    auto* ints = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + L.off_i);
+    if ((rc = upload_ints(p, ints, tail.data(), tail.size(), static_cast<hipStream_t>(stream)))) return rc;
+  }
+  plan->pool = p;
+  plan->num_seqs = num_seqs;
+  plan->num_q_heads = num_q_heads;
+  plan->max_blocks = max_blocks;
+  plan->num_items = static_cast<int32_t>(n_items);
+  plan->workspace = workspace;
+  plan->workspace_bytes = workspace_bytes;
+  return PA_OK;
+}
+
+int pa_decode_shared_prefix(pa_pool* p, int32_t layer, const pa_shared_plan* plan, const void* q,
+                            const int32_t* block_tables, const int32_t* context_lens, const void* k_new,
+                            const void* v_new, const int32_t* slot_mapping, float scale, void* out,
+                            void* stream) {
+  if (!plan || plan->pool != p) return fail(PA_ERR_INVALID, "the plan was not made for this pool");
+  const int32_t num_seqs = plan->num_seqs, num_q_heads = plan->num_q_heads, max_blocks = plan->max_blocks;
+  int rc = check_decode_args(p, layer, q, block_tables, context_lens, num_seqs, scale);
+  if (rc) return rc;
+  if (scale == 0.0f) return fail(PA_ERR_INVALID, "scale must be nonzero");
+  const bool fused = k_new || v_new || slot_mapping;
+  if (fused && (!k_new || !v_new || !slot_mapping))
+    return fail(PA_ERR_INVALID, "k_new, v_new and slot_mapping go together");
+  if (misaligned(k_new, 16) || misaligned(v_new, 16))
+    return fail(PA_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || misaligned(out, 8)) return fail(PA_ERR_INVALID, "out must be non-NULL and 8-byte aligned");
+  const SharedLayout L = shared_layout(p, num_seqs, num_q_heads, plan->num_items);
+  if (!plan->workspace || plan->workspace_bytes < L.bytes || plan->num_items < 0)
+    return fail(PA_ERR_INVALID, "the plan's workspace is too small");
+  auto s = static_cast<hipStream_t>(stream);
+  auto* ws = static_cast<uint8_t*>(plan->workspace);
+  auto* ints = reinterpret_cast<int32_t*>(ws + L.off_i);
+  pa::DecodeLaunch d{};
+  d.layer = layer;
+  d.q = q;
+  d.tables = block_tables;
+  d.lens = context_lens;
+  d.out = out;
+  d.num_seqs = num_seqs;
+  d.num_q_heads = num_q_heads;
+  d.max_blocks = max_blocks;
+  d.mode = kModePrivate;
+  d.partition_tokens = static_cast<int>(align_up(static_cast<uint64_t>(max_blocks) * p->block_size, 16));
+  d.num_partitions = 1;
+  d.chunks_per_wave = 1;
+  d.waves_per_unit = 1;
+  d.scale = scale;
+  d.cached_loads = use_cached_loads(p) ? 1 : 0;
+  d.starts = ints;
+  d.members = ints + num_seqs;
+  d.work = ints + 2 * num_seqs;
+  d.num_items = plan->num_items;
+  d.shared_m = reinterpret_cast<float*>(ws);
+  d.shared_l = reinterpret_cast<float*>(ws + L.off_l);
+  d.shared_o = reinterpret_cast<float*>(ws + L.off_o);
+  if (fused) {
+    d.k_new = k_new;
+    d.v_new = v_new;
+    d.new_slots = slot_mapping;
+  }
+  // Timing covers both launches: from the shared pass's start to the private
+  // pass's end.
+  const bool rec = p->profiling && p->launches++ % p->every == 0 && p->n_records < p->max_records;
+  hipEvent_t* ev = rec ? &p->ev[4 * static_cast<size_t>(p->n_records)] : nullptr;
+  hipError_t e = hipSuccess;
+  if (plan->num_items > 0) {
+    e = pa::launch_shared_prefix(p->geom, d, s, rec ? ev[0] : nullptr, nullptr);
+    if (e != hipSuccess) return hip_fail(e, "shared-prefix launch");
+  }
+  e = pa::launch_decode(p->geom, d, s, (rec && plan->num_items == 0) ? ev[0] : nullptr, rec ? ev[1] : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "private-pass launch");
+  if (rec) {
+    p->has_reduce[p->n_records] = 0;
+    ++p->n_records;
+  }
   return PA_OK;
 }
 

@@ -159,9 +159,11 @@ struct WaveDecoder {
   int gq, n, T, max_blocks, num_blocks;
   // MULTI: keys visible to this lane's column of each tile (its position + 1)
   // and the smallest limit of the wave's columns; the query rows of the
-  // columns start at mt_row0 (column c: token c / group, head c % group) and
-  // columns at or past mt_ncols are padding.
+  // columns start at mt_row0 (column c: token c / group, head c % group), or
+  // are mt_rowmap[c / group] when that is set (columns of several
+  // sequences), and columns at or past mt_ncols are padding.
   int lim[NT], lim_min, mt_row0, mt_ncols;
+  const int32_t* mt_rowmap;
   uint64_t block_stride;
   const ConstI32* trow;
   const uint8_t* kbase;
@@ -216,6 +218,7 @@ struct WaveDecoder {
     kbase = g.k_layer(p.layer) + static_cast<uint64_t>(kvh) * g.tile_bytes;
     vbase = g.v_layer(p.layer) + static_cast<uint64_t>(kvh) * g.tile_bytes;
     bad = 0;
+    mt_rowmap = nullptr;
     knew = vnew = nullptr;
     new_kinv = new_vinv = 1.0f;
     new_kz = new_vz = 0.0f;
@@ -261,8 +264,8 @@ struct WaveDecoder {
       if constexpr (MULTI) {
         valid = col < mt_ncols;
         const int c = valid ? col : 0;
-        qh = static_cast<const _Float16*>(p.q) +
-             ((static_cast<int64_t>(mt_row0) + c / group) * p.num_q_heads + kvh * group + c % group) * kD;
+        const int64_t row = mt_rowmap ? mt_rowmap[c / group] : static_cast<int64_t>(mt_row0) + c / group;
+        qh = static_cast<const _Float16*>(p.q) + (row * p.num_q_heads + kvh * group + c % group) * kD;
       }
 #pragma unroll
       for (int u = 0; u < NKU; ++u) {
@@ -950,6 +953,8 @@ enum DecodeMode : int {
   kSingle = 0,   // one workgroup per (sequence, KV head), fp16 output
   kSplit4 = 1,   // a workgroup's four waves share each chunk of a chunk run
   kSplit1 = 2,   // each wave streams its own chunk run
+  kPrivate = 3,  // kSingle from each sequence's start on, merged with the
+                 // shared pass's partials (shared-prefix decode)
 };
 
 // Context length of a sequence, clamped to the table width; bad lengths set
@@ -985,13 +990,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 void decode_kernel(PoolGeom g, DecodeLaunch p) {
   constexpr int kD = D;
   constexpr int ELEM = kind_bytes(KIND);
+  constexpr bool kOne = MODE == kSingle || MODE == kPrivate;  // one pass per (sequence, KV head)
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int group = p.num_q_heads / g.kv_heads;
   const int64_t num_units = static_cast<int64_t>(p.num_seqs) * g.kv_heads;
   int64_t unit;
   int r = 0;
-  if constexpr (MODE == kSingle) {
+  if constexpr (kOne) {
     unit = blockIdx.x;
   } else if constexpr (MODE == kSplit4) {
     unit = blockIdx.x / p.waves_per_unit;
@@ -1021,9 +1027,19 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
                         : c_begin + p.chunks_per_wave;
   const int qs = P >> 6;   // kSplit4: steps of each wave per chunk
   const int spc = P >> 4;  // kSplit1: steps per chunk
+  // Shared-prefix decode, private pass: the tokens before s0 were attended by
+  // the shared pass; s0 is a multiple of 16 inside the table (else 0).  The
+  // plain single pass keeps s0 = 0 at compile time.
+  int s0 = 0;
+  if constexpr (MODE == kPrivate) {
+    if (p.starts) {
+      s0 = ((const ConstI32*)p.starts)[seq];
+      s0 = (s0 < 0 || static_cast<int64_t>(s0) >= static_cast<int64_t>(p.max_blocks) * BS) ? 0 : (s0 & ~15);
+    }
+  }
   // First token of scheduled step j, before any clamping to the context.
   auto raw_tok = [&](int j) -> int64_t {
-    if constexpr (MODE == kSingle) return 16ll * (w + kWaves * j);
+    if constexpr (kOne) return s0 + 16ll * (w + kWaves * j);
     else if constexpr (MODE == kSplit4) return static_cast<int64_t>(c_begin + j / qs) * P + 16 * (w + kWaves * (j % qs));
     else return static_cast<int64_t>(c_begin) * P + 16ll * j;
   };
@@ -1046,8 +1062,8 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
   if constexpr (FUSE) {
     if (T > 0) {
       const int t_last = T - 1;
-      if constexpr (MODE == kSingle) {
-        owner = ((t_last >> 4) % kWaves) == w;
+      if constexpr (kOne) {
+        owner = t_last >= s0 && (((t_last - s0) >> 4) % kWaves) == w;
       } else {
         const int c_t = t_last / P;
         const bool in_run = c_t >= c_begin && c_t < c_end;
@@ -1087,19 +1103,21 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
     }
   };
 
-  if constexpr (MODE == kSingle) {
-    if (T == 0) {
-      // Nothing to attend to: defined output of zeros.
+  if constexpr (kOne) {
+    if (T <= s0) {
+      // Nothing to attend to (or a start at or past the context, a contract
+      // violation): defined output of zeros.
+      if (s0 > 0 && threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
       for (int i = threadIdx.x; i < group * kD; i += kWaves * 64)
         static_cast<_Float16*>(p.out)[(static_cast<int64_t>(seq) * p.num_q_heads + kvh * group) * kD + i] = 0;
       return;
     }
   }
   // Chunks of the run that hold tokens, and the scheduled steps of each wave.
-  const int c_last = (MODE == kSingle) ? 0 : ((T + P - 1) / P < c_end ? (T + P - 1) / P : c_end);
+  const int c_last = (kOne) ? 0 : ((T + P - 1) / P < c_end ? (T + P - 1) / P : c_end);
   int n;
-  if constexpr (MODE == kSingle) {
-    n = (T + 16 * kWaves - 1) / (16 * kWaves);  // same count for every wave
+  if constexpr (kOne) {
+    n = (T - s0 + 16 * kWaves - 1) / (16 * kWaves);  // same count for every wave
   } else if constexpr (MODE == kSplit4) {
     if (c_begin >= c_last) return;  // whole workgroup
     const int rest = static_cast<int>(T - static_cast<int64_t>(c_last - 1) * P);  // tokens of the run's last chunk
@@ -1122,14 +1140,32 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
   const int gq = dec.gq;
   const int64_t row0 = static_cast<int64_t>(seq) * p.num_q_heads + kvh * group;
 
-  if constexpr (MODE == kSingle) {
+  if constexpr (kOne) {
     __shared__ MergeLds<NT, D> sm;
     stream_steps(dec, n, tok_of, real, first, [](int) {});
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
-    merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float, float L, float) {
+    merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float M, float L, float) {
       (void)nt;
-      const float inv_l = dec.out_mul / L;
       _Float16* po = static_cast<_Float16*>(p.out) + (row0 + col) * kD + 4 * gq;
+      if (MODE == kPrivate && s0 > 0) {
+        // Log-sum-exp merge with the shared pass's partials of this row:
+        // out = (acc * 2^(M - X) + o_s * l_s * 2^(m_s - X)) / (L * 2^(M - X) + l_s * 2^(m_s - X)).
+        const int64_t row = row0 + col;
+        const float m_s = p.shared_m[row], l_s = p.shared_l[row];
+        const float X = fmaxf(M, m_s);
+        const float a = exp2f(M - X) * dec.out_mul;
+        const float b = exp2f(m_s - X) * l_s;
+        const float inv = 1.0f / (L * exp2f(M - X) + b);
+        const float* ps = p.shared_o + row * kD + 4 * gq;
+#pragma unroll
+        for (int rr = 0; rr < D / 16; ++rr) {
+          const f32x4 os = *reinterpret_cast<const f32x4*>(ps + rr * 16);
+          const f32x4 v = (acc[rr] * a + os * b) * inv;
+          *reinterpret_cast<f16x4*>(po + rr * 16) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        }
+        return;
+      }
+      const float inv_l = dec.out_mul / L;
 #pragma unroll
       for (int rr = 0; rr < D / 16; ++rr) {
         const f32x4 a = acc[rr] * inv_l;
@@ -1307,6 +1343,83 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
   }
 }
 
+// Shared pass of the shared-prefix decode.  Sequences whose block tables
+// begin with the same blocks (beams of one search, requests on one cached
+// system prompt: youngju.dev "KV cache and paged attention", section "prefix
+// 공유와 copy-on-write") read those blocks once here for all of them: the
+// query heads of up to 32 / G members are the MFMA columns of one item
+// (column c: member c / G, head c % G), the four waves take key steps w,
+// w + 4, ... of the shared tokens and merge in LDS, and every (member, head)
+// row gets its partials over the shared tokens: m (the largest score, base
+// 2), l = sum 2^(s - m), o = sum 2^(s - m) v / l (times the V scale).  The
+// private pass (decode_kernel in mode kPrivate) attends to each
+// sequence's remaining tokens and merges these partials by log-sum-exp.
+// Workgroup = (item, KV head); items hold (first member, members, shared
+// tokens); the blocks are read through the first member's table.
+template <int D, int KIND, int BS>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void shared_prefix_kernel(PoolGeom g, DecodeLaunch p) {
+  constexpr int NT = 2;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = p.num_q_heads / g.kv_heads;
+  const int item = static_cast<int>(blockIdx.x / g.kv_heads);
+  const int kvh = static_cast<int>(blockIdx.x % g.kv_heads);
+  const ConstI32* wk = (const ConstI32*)(p.work + 4 * static_cast<int64_t>(item));
+  const int m0 = wk[0], nm = wk[1], ts = wk[2];
+  // The host checks the items when it uploads them; an item that does not
+  // fit this launch (a member run outside the batch, more than 32 columns, a
+  // member outside the batch, a shared length outside the table or not a
+  // multiple of 16) is flagged and its rows left alone.  Every wave reaches
+  // the same verdict, so the workgroup leaves together.
+  if (m0 < 0 || nm < 1 || nm * group > 32 || m0 > p.num_seqs - nm || ts < 16 || (ts & 15) != 0 ||
+      static_cast<int64_t>(ts) > static_cast<int64_t>(p.max_blocks) * BS) {
+    if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
+    return;
+  }
+  const int32_t* mem = p.members + m0;
+  const int mine = lane < nm ? ((const ConstI32*)mem)[lane] : 0;
+  if (__ballot(static_cast<uint32_t>(mine) >= static_cast<uint32_t>(p.num_seqs)) != 0) {
+    if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
+    return;
+  }
+  const int seq0 = __builtin_amdgcn_readfirstlane(mine);
+  WaveDecoder<D, KIND, BS, NT, false, true, true> dec;  // items of one group re-read the tiles
+  dec.bind(g, p, seq0, kvh, lane);
+  const int ncols = nm * group;
+  dec.T = ts;
+  dec.lim_min = ts;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) dec.lim[nt] = ts;
+  dec.mt_row0 = 0;
+  dec.mt_ncols = ncols;
+  dec.mt_rowmap = mem;
+  auto raw_tok = [&](int j) -> int64_t { return 16ll * (w + kWaves * j); };
+  const int n = (ts + 16 * kWaves - 1) / (16 * kWaves);
+  const int last_tok = ((ts - 1) >> 4) << 4;
+  auto real = [&](int j) { return raw_tok(j) < ts; };
+  auto tok_of = [&](int j) -> int { return real(j) ? static_cast<int>(raw_tok(j)) : last_tok; };
+  dec.load_q(g, p, seq0, kvh, group);
+  dec.reset();
+  __shared__ MergeLds<NT, D> sm;
+  stream_pairs(dec, n, tok_of, real);
+  dec.finish_l();
+  if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
+  const int gq = dec.gq;
+  merge_waves(dec, sm, w, ncols, [&](int, int col, f32x4* acc, float M, float L, float Mt) {
+    const int seq = mem[col / group];
+    const int64_t row = static_cast<int64_t>(seq) * p.num_q_heads + kvh * group + col % group;
+    const float inv_l = dec.out_mul / L;
+    float* po = p.shared_o + row * D + 4 * gq;
+#pragma unroll
+    for (int rr = 0; rr < D / 16; ++rr) *reinterpret_cast<f32x4*>(po + rr * 16) = acc[rr] * inv_l;
+    if (gq == 0) {
+      p.shared_m[row] = Mt;
+      p.shared_l[row] = (M == Mt) ? L : L * exp2f(M - Mt);
+    }
+  });
+}
+
 // Log-sum-exp merge of the chunk partials of one (sequence, query head):
 // out = sum_c w_c o_c / sum_c w_c with w_c = l_c * 2^(m_c - max_c m_c).
 // One 256-thread workgroup per row.  The chunks go in blocks of 256: thread
@@ -1469,6 +1582,9 @@ hipError_t launch_decode_nt(const PoolGeom& g, const DecodeLaunch& d, hipStream_
     case kSingle:
       return launch_kernel(decode_kernel<D, KIND, BS, NT, kSingle, FUSE, CACHED>, dim3(static_cast<unsigned>(units)),
                            block, s, t0, t1, g, d);
+    case kPrivate:
+      return launch_kernel(decode_kernel<D, KIND, BS, NT, kPrivate, FUSE, CACHED>, dim3(static_cast<unsigned>(units)),
+                           block, s, t0, t1, g, d);
     case kSplit4:
       return launch_kernel(decode_kernel<D, KIND, BS, NT, kSplit4, FUSE, CACHED>,
                            dim3(static_cast<unsigned>(units * d.waves_per_unit)), block, s, t0, t1, g, d);
@@ -1520,6 +1636,19 @@ hipError_t launch_multi_token_kd(const PoolGeom& g, const DecodeLaunch& d, const
     case 8: return launch_kernel(multi_token_kernel<D, KIND, 8>, grid, block, s, t0, t1, g, d);
     case 16: return launch_kernel(multi_token_kernel<D, KIND, 16>, grid, block, s, t0, t1, g, d);
     case 32: return launch_kernel(multi_token_kernel<D, KIND, 32>, grid, block, s, t0, t1, g, d);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Shared pass of one (head_dim, element kind).
+template <int D, int KIND>
+hipError_t launch_shared_prefix_kd(const PoolGeom& g, const DecodeLaunch& d, const dim3& grid, hipStream_t s,
+                                   hipEvent_t t0, hipEvent_t t1) {
+  const dim3 block(kWaves * 64);
+  switch (g.block_size) {
+    case 8: return launch_kernel(shared_prefix_kernel<D, KIND, 8>, grid, block, s, t0, t1, g, d);
+    case 16: return launch_kernel(shared_prefix_kernel<D, KIND, 16>, grid, block, s, t0, t1, g, d);
+    case 32: return launch_kernel(shared_prefix_kernel<D, KIND, 32>, grid, block, s, t0, t1, g, d);
     default: return hipErrorInvalidValue;
   }
 }

@@ -11,7 +11,9 @@ namespace dk {
   extern template hipError_t launch_decode_kd<D, KIND>(const PoolGeom&, const DecodeLaunch&, int, hipStream_t, \
                                                        hipEvent_t, hipEvent_t);                                \
   extern template hipError_t launch_multi_token_kd<D, KIND>(const PoolGeom&, const DecodeLaunch&, const dim3&, \
-                                                            hipStream_t, hipEvent_t, hipEvent_t);
+                                                            hipStream_t, hipEvent_t, hipEvent_t);              \
+  extern template hipError_t launch_shared_prefix_kd<D, KIND>(const PoolGeom&, const DecodeLaunch&, const dim3&, \
+                                                              hipStream_t, hipEvent_t, hipEvent_t);
 PA_DECLARE_INST(64, kF16)
 PA_DECLARE_INST(64, kF8)
 PA_DECLARE_INST(64, kI8)
@@ -42,14 +44,38 @@ hipError_t multi_token_for_dim(const PoolGeom& g, const DecodeLaunch& d, const d
   }
 }
 
+template <int D>
+hipError_t shared_prefix_for_dim(const PoolGeom& g, const DecodeLaunch& d, const dim3& grid, hipStream_t s,
+                                 hipEvent_t t0, hipEvent_t t1) {
+  switch (g.kind) {
+    case kF16: return launch_shared_prefix_kd<D, kF16>(g, d, grid, s, t0, t1);
+    case kF8: return launch_shared_prefix_kd<D, kF8>(g, d, grid, s, t0, t1);
+    case kI8: return launch_shared_prefix_kd<D, kI8>(g, d, grid, s, t0, t1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace dk
+
+hipError_t launch_shared_prefix(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
+                                hipEvent_t t1) {
+  const int64_t wgs = static_cast<int64_t>(d.num_items) * g.kv_heads;
+  if (wgs <= 0) return hipSuccess;
+  if (!d.work || !d.members || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(wgs));
+  switch (g.head_dim) {
+    case 64: return dk::shared_prefix_for_dim<64>(g, d, grid, s, t0, t1);
+    case 128: return dk::shared_prefix_for_dim<128>(g, d, grid, s, t0, t1);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
                          hipEvent_t t1) {
   const int group = d.num_q_heads / g.kv_heads;
   const int nt = group > 16 ? 2 : 1;
   if (static_cast<int64_t>(d.num_seqs) * g.kv_heads <= 0) return hipSuccess;
-  if (d.mode != dk::kSingle) {
+  if (d.mode != dk::kSingle && d.mode != dk::kPrivate) {
     // The split schedules need whole steps per chunk (and per wave quarter).
     const int quantum = d.mode == dk::kSplit4 ? 64 : 16;
     if (d.waves_per_unit < 1 || d.chunks_per_wave < 1 || d.partition_tokens < quantum ||

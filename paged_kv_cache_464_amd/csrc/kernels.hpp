@@ -70,6 +70,18 @@ struct DecodeLaunch {
   int waves_per_unit;    // runs per (sequence, KV head) = ceil(C / k) (split modes)
   float scale;
   int cached_loads;  // 1: ordinary K/V loads (blocks shared by many sequences); 0: nontemporal
+  // Shared-prefix decode.  Shared pass: `work` holds items of four int32
+  // (first member, members, shared tokens, 0) indexing `members` (sequence
+  // ids, group by group); it writes each member's (max, sum, normalised O)
+  // over the shared tokens into shared_m / shared_l / shared_o
+  // [S][Hq] / [S][Hq] / [S][Hq][D].  Private pass (single pass only):
+  // sequence i attends to tokens starts[i] .. T_i - 1 and, when starts[i] > 0,
+  // merges the shared pass's partials into its output.
+  const int32_t* members;
+  const int32_t* starts;
+  float* shared_m;
+  float* shared_l;
+  float* shared_o;
 };
 
 // t0/t1: optional events stamped at the kernel's start and end (null: untimed).
@@ -77,6 +89,10 @@ hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s
                          hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
                              hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// Shared pass of the shared-prefix decode (d.work, d.num_items, d.members,
+// d.shared_*).
+hipError_t launch_shared_prefix(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
+                                hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Causal attention of several query tokens per sequence (d.work, d.num_items;
 // d.q and d.out are [query rows][Hq][D]).
 hipError_t launch_multi_token(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,

@@ -409,6 +409,94 @@ def pa_write_kv_decode(h, layer, k_new, v_new, slot_mapping, q, block_tables, co
     return out
 
 
+def pa_shared_prefix_groups(h, tables, lens, min_shared_tokens=256):
+    """Groups of sequences sharing leading blocks, from host block tables
+    [n][max_blocks] and lengths: (members, group_start, shared_blocks) host
+    int32 arrays (see pa_decode_shared_prefix)."""
+    t = np.ascontiguousarray(np.asarray(tables, dtype=np.int32))
+    ln, lp = _i32_host(lens)
+    n, mb = t.shape
+    if len(ln) != n:
+        raise ValueError("lens and tables differ in length")
+    members = np.empty(max(n, 1), dtype=np.int32)
+    gstart = np.empty(n + 1, dtype=np.int32)
+    shared = np.empty(max(n, 1), dtype=np.int32)
+    ng = C.c_int32()
+    ip = lambda a: a.ctypes.data_as(C.POINTER(C.c_int32))
+    _check(_L().pa_shared_prefix_groups(C.c_void_p(h), ip(t), lp, n, mb, int(min_shared_tokens), ip(members),
+                                        ip(gstart), ip(shared), C.byref(ng)))
+    g = ng.value
+    return members[:n].copy(), gstart[:g + 1].copy(), shared[:g].copy()
+
+
+def _groups_args(groups):
+    members, gstart, shared = (np.ascontiguousarray(np.asarray(a, dtype=np.int32)) for a in groups)
+    ip = lambda a: a.ctypes.data_as(C.POINTER(C.c_int32))
+    return (members, gstart, shared), ip(members), ip(gstart), ip(shared), len(shared)
+
+
+def pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, groups, max_blocks):
+    keep, mp, gp, sp, ng = _groups_args(groups)
+    b = C.c_uint64()
+    _check(_L().pa_decode_shared_prefix_workspace_bytes(C.c_void_p(h), int(num_seqs), int(num_q_heads), mp, gp,
+                                                        sp, ng, int(max_blocks), C.byref(b)))
+    return b.value
+
+
+class SharedPlan:
+    """A checked, uploaded group list (pa_shared_prefix_plan) and the
+    workspace it lives in; one plan serves every layer of a step."""
+
+    def __init__(self, plan, workspace, groups):
+        self.plan, self.workspace, self.groups = plan, workspace, groups
+
+
+def pa_shared_prefix_plan(h, num_seqs, num_q_heads, max_blocks, groups, workspace=None, stream=None,
+                          device="cuda"):
+    keep, mp, gp, sp, ng = _groups_args(groups)
+    need = pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, keep, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    plan = _lib.pa_shared_plan()
+    _check(_L().pa_shared_prefix_plan(C.c_void_p(h), int(num_seqs), int(num_q_heads), int(max_blocks), mp, gp,
+                                      sp, ng, C.c_void_p(workspace.data_ptr()), nbytes, _stream(stream),
+                                      C.byref(plan)))
+    return SharedPlan(plan, workspace, keep)
+
+
+def pa_decode_shared_prefix(h, layer, q, block_tables, context_lens, groups, out=None, scale=None,
+                            workspace=None, stream=None, k_new=None, v_new=None, slot_mapping=None):
+    """Decode where groups of sequences share leading blocks.  ``groups`` is a
+    SharedPlan (pa_shared_prefix_plan) or the (members, group_start,
+    shared_blocks) arrays of pa_shared_prefix_groups, planned here on the
+    call's stream.  With k_new, v_new and slot_mapping, the new tokens are
+    scattered as in pa_write_kv_decode."""
+    info, s, hq, mb, qp, tp, lp = _decode_args(h, q, block_tables, context_lens)
+    if not isinstance(groups, SharedPlan):
+        groups = pa_shared_prefix_plan(h, s, hq, mb, groups, workspace, stream, q.device)
+    p = groups.plan
+    if (p.num_seqs, p.num_q_heads, p.max_blocks) != (s, hq, mb):
+        raise ValueError(f"the plan is for {p.num_seqs} sequences, {p.num_q_heads} query heads and tables "
+                         f"{p.max_blocks} wide; got {s}, {hq}, {mb}")
+    if out is None:
+        out = torch.empty_like(q)
+    op = _dev(out, torch.float16, tuple(q.shape), "out")
+    kp = vp = slp = C.c_void_p(0)
+    if k_new is not None or v_new is not None or slot_mapping is not None:
+        shape = (s, info["kv_heads"], info["head_dim"])
+        kp = _dev(k_new, torch.float16, shape, "k_new")
+        vp = _dev(v_new, torch.float16, shape, "v_new")
+        slp = _dev(slot_mapping, torch.int32, (s,), "slot_mapping")
+    if scale is None:
+        scale = info["softmax_scale"]
+    _check(_L().pa_decode_shared_prefix(C.c_void_p(h), int(layer), C.byref(p), qp, tp, lp, kp, vp, slp,
+                                        float(scale), op, _stream(stream)))
+    return out
+
+
 def pa_multi_token_workspace_bytes(h, query_start, num_q_heads):
     qs, qsp = _i32_host(query_start)
     b = C.c_uint64()
@@ -614,6 +702,15 @@ class PagedKVPool:
     def write_kv_decode(self, layer, k_new, v_new, slot_mapping, q, block_tables, context_lens, **kw):
         return pa_write_kv_decode(self.handle, layer, k_new, v_new, slot_mapping, q, block_tables,
                                   context_lens, **kw)
+
+    def shared_prefix_groups(self, tables, lens, min_shared_tokens=256):
+        return pa_shared_prefix_groups(self.handle, tables, lens, min_shared_tokens)
+
+    def shared_prefix_plan(self, num_seqs, num_q_heads, max_blocks, groups, **kw):
+        return pa_shared_prefix_plan(self.handle, num_seqs, num_q_heads, max_blocks, groups, **kw)
+
+    def decode_shared_prefix(self, layer, q, block_tables, context_lens, groups, **kw):
+        return pa_decode_shared_prefix(self.handle, layer, q, block_tables, context_lens, groups, **kw)
 
     def device_status(self, clear=False):
         return pa_device_status(self.handle, clear)
