@@ -232,14 +232,9 @@ class DecodeBench:
         ws = pa.pa_decode_workspace_bytes(self.pool.handle, self.S, self.hq, self.mb_cap, self.partition)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.dev)
         self.sp_groups_log = []
-        if self.sp_min:
-            # Largest shared-prefix workspace of this batch: one work item per
-            # sequence (every group a singleton with a shared run).
-            one = max(1, 16 // self.bs)
-            worst = (np.arange(self.S, dtype=np.int32), np.arange(self.S + 1, dtype=np.int32),
-                     np.full(self.S, one, dtype=np.int32))
-            n = pa.pa_decode_shared_prefix_workspace_bytes(self.pool.handle, self.S, self.hq, worst, self.mb_cap)
-            self.sp_workspace = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        self.sp_chunk = args.shared_prefix_chunk
+        # Grown to the groups' need in the first step (a warmup step).
+        self.sp_workspace = torch.empty(256, dtype=torch.uint8, device=self.dev)
         # Step metadata (slot mapping, lengths, longest-first sequence order,
         # block tables) is packed into one int32 buffer so that each step makes
         # a single upload: two pinned host copies used alternately (each guarded
@@ -380,8 +375,12 @@ class DecodeBench:
         h, st = self.pool.handle, self.stream
         if self.sp_min:
             groups = self.pool.shared_prefix_groups(tables, lens, self.sp_min)
+            need = pa.pa_decode_shared_prefix_workspace_bytes(h, self.S, self.hq, groups, self.mb_cap, self.sp_chunk)
+            if need > self.sp_workspace.numel():
+                self.sp_workspace = self.torch.empty(2 * need, dtype=self.torch.uint8, device=self.dev)
             plan = pa.pa_shared_prefix_plan(h, self.S, self.hq, self.mb_cap, groups, workspace=self.sp_workspace,
-                                            stream=st)
+                                            stream=st, chunk_tokens=self.sp_chunk)
+            self.sp_plan_log = plan.plan
             self.sp_groups_log.append(groups)
             for r in range(self.R):
                 pa.pa_decode_shared_prefix(h, r % self.copies, self.q[r], self.tables_d, self.lens_d, plan,
@@ -443,7 +442,9 @@ class DecodeBench:
         members, gstart, shared = self.sp_groups_log[-1]
         sizes = np.diff(gstart)
         on = shared > 0
+        pl = self.sp_plan_log
         return {"min_shared_tokens": self.sp_min, "groups_with_shared_pass": int(on.sum()),
+                "chunk_tokens": pl.chunk_tokens, "shared_items": pl.num_items, "partial_slots": pl.num_slots,
                 "sequences_in_them": int(sizes[on].sum()),
                 "shared_tokens_per_member": int((shared[on] * sizes[on]).sum() * self.bs) // max(int(sizes[on].sum()), 1),
                 "host": "pa_shared_prefix_groups + pa_shared_prefix_plan once per step, inside the timed step"}
@@ -766,6 +767,8 @@ def main(argv=None):
                     help="for the workloads whose sequences share blocks: decode with pa_decode_shared_prefix, "
                          "grouping sequences that share at least this many leading tokens (0 = plain fused "
                          "decode; default 256 for beam_k5, 0 for the others)")
+    ap.add_argument("--shared-prefix-chunk", type=int, default=0,
+                    help="shared tokens per shared-prefix work item (a multiple of 64; 0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--cpu-sample-seqs", type=int, default=32)

@@ -406,10 +406,11 @@ int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const vo
  * blocks (beams of one search, requests on one cached system prompt) read
  * identical K/V there (youngju.dev page, section "prefix 공유와 copy-on-write";
  * iq-blog ch.4, section "Prefix Caching"): the attention of each sequence is
- * split at the end of the shared blocks, a first launch reads the shared
- * blocks once per group for all its members' query heads, a second attends
- * to each sequence's own remaining tokens and merges the two by log-sum-exp.
- * The result is that of pa_decode (pa_write_kv_decode when k_new, v_new and
+ * split at the end of the shared blocks.  In one launch, some workgroups read
+ * chunks of a group's shared blocks once for all its members' query heads
+ * while others attend to each sequence's own remaining tokens; a second,
+ * short launch merges each grouped sequence's pieces by log-sum-exp.  The
+ * result is that of pa_decode (pa_write_kv_decode when k_new, v_new and
  * slot_mapping are given) up to rounding.
  *
  * pa_shared_prefix_groups (host only) finds groups from host block tables
@@ -425,43 +426,51 @@ int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const vo
  * permutation of 0..num_seqs-1, group_start[0] = 0 and group_start[num_groups]
  * = num_seqs, shared_blocks[g] * block_size a multiple of 16 and at most
  * max_blocks) for a batch of num_seqs sequences with num_q_heads query heads
- * and block tables max_blocks wide, and uploads the group list on `stream`
+ * and block tables max_blocks wide, and uploads on `stream` the group list
  * into `workspace` (device memory of
- * pa_decode_shared_prefix_workspace_bytes() bytes, 16-byte aligned, owned by
- * the caller, which keeps it alive while the plan is used).  It fills *plan;
- * bad group arrays give PA_ERR_INVALID and upload nothing.  One plan serves
- * every layer of a step: the group list is uploaded once.
+ * pa_decode_shared_prefix_workspace_bytes() bytes for the same groups and
+ * chunk_tokens, 16-byte aligned, owned by the caller, which keeps it alive
+ * while the plan is used).  chunk_tokens: shared tokens per workgroup, a
+ * multiple of 64, or 0 for the library's choice (about one shared
+ * workgroup per CU, at least 256 tokens).  It fills *plan; bad group arrays
+ * give PA_ERR_INVALID and upload nothing.  One plan serves every layer of a
+ * step: the group list is uploaded once.
  *
  * pa_decode_shared_prefix runs one layer on a plan: q, block_tables,
  * context_lens, scale and out as in pa_decode with the plan's num_seqs,
  * num_q_heads and max_blocks.  The caller guarantees what the plan cannot
  * see on the host: every member's table holds its group's shared blocks
  * first, and its context has more tokens than them (a context at or below
- * them sets PA_DEV_BAD_LEN and gives zeros).  k_new, v_new, slot_mapping:
- * all NULL, or the fused scatter of pa_write_kv_decode (the new token lies
- * past the shared blocks, so it is written in the second launch).  The shared
- * partials live in the plan's workspace: calls on one plan must be on one
- * stream, in order, and a later plan on the same workspace replaces it (the
- * kernels check every index they take from the workspace: a stale plan can
- * give wrong rows, never an access outside the batch or the workspace). */
+ * them sets PA_DEV_BAD_LEN and gives the shared tokens' attention alone).
+ * k_new, v_new, slot_mapping: all NULL, or the fused scatter of
+ * pa_write_kv_decode (the new token lies past the shared blocks, in the
+ * sequence's own piece).  The partials live in the plan's workspace: calls
+ * on one plan must be on one stream, in order, and a later
+ * plan on the same workspace replaces it (the kernels check every index they
+ * take from the workspace: a stale plan can give wrong rows, never an access
+ * outside the batch or the workspace). */
 int pa_shared_prefix_groups(const pa_pool* pool, const int32_t* tables, const int32_t* lens, int32_t n,
                             int32_t max_blocks, int32_t min_shared_tokens, int32_t* members_out,
                             int32_t* group_start_out, int32_t* shared_blocks_out, int32_t* num_groups_out);
 int pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                             const int32_t* members, const int32_t* group_start,
                                             const int32_t* shared_blocks, int32_t num_groups,
-                                            int32_t max_blocks, uint64_t* bytes_out);
+                                            int32_t max_blocks, int32_t chunk_tokens, uint64_t* bytes_out);
+#define PA_SHARED_REREAD 1 /* pa_shared_plan.flags: several items read one shared chunk */
 typedef struct pa_shared_plan {
   const pa_pool* pool;       /* the pool the plan was made for */
   int32_t num_seqs, num_q_heads, max_blocks;
-  int32_t num_items;         /* workgroups of the shared launch per KV head */
+  int32_t num_items;         /* shared work items (each a workgroup per KV head) */
+  int32_t num_slots;         /* partial slots: shared chunks + 1 for every grouped sequence */
+  int32_t chunk_tokens;      /* shared tokens per work item */
+  int32_t flags;             /* PA_SHARED_REREAD: several items read one chunk (ordinary loads) */
   void* workspace;           /* the caller's workspace, as passed to the plan */
   uint64_t workspace_bytes;
 } pa_shared_plan;
 int pa_shared_prefix_plan(pa_pool* pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                           const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
-                          int32_t num_groups, void* workspace, uint64_t workspace_bytes, void* stream,
-                          pa_shared_plan* plan);
+                          int32_t num_groups, int32_t chunk_tokens, void* workspace, uint64_t workspace_bytes,
+                          void* stream, pa_shared_plan* plan);
 int pa_decode_shared_prefix(pa_pool* pool, int32_t layer, const pa_shared_plan* plan, const void* q,
                             const int32_t* block_tables, const int32_t* context_lens, const void* k_new,
                             const void* v_new, const int32_t* slot_mapping, float scale, void* out,

@@ -1022,64 +1022,119 @@ int pa_profile_end(pa_pool* p, pa_profile* out) {
 
 namespace {
 
-// Workspace of a shared-prefix decode: the shared pass's partials and the
-// uploaded int32 tail (starts[S], members[S], items[4 * n_items]).
+// Workspace of a shared-prefix decode: the pieces' partials (m, l, o of
+// every slot and query head), then the uploaded int32 tail: starts[S],
+// slot0[S], members[S] and the shared items (4 ints each).
 struct SharedLayout {
-  uint64_t off_l, off_o, off_i, bytes;
+  uint64_t off_l, off_o, off_c, bytes;
 };
 
-SharedLayout shared_layout(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int64_t n_items) {
-  const uint64_t rows = static_cast<uint64_t>(num_seqs) * num_q_heads;
+SharedLayout shared_layout(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int64_t n_items,
+                           int64_t n_slots) {
+  const uint64_t rows = static_cast<uint64_t>(n_slots) * num_q_heads;
   SharedLayout L;
-  L.off_l = align_up(rows * 4, 256);
-  L.off_o = L.off_l + align_up(rows * 4, 256);
-  L.off_i = L.off_o + align_up(rows * p->head_dim * 4, 256);
-  L.bytes = L.off_i + align_up((2ull * num_seqs + 4ull * n_items) * 4, 256);
+  L.off_l = align_up(std::max<uint64_t>(rows, 1) * 4, 256);
+  L.off_o = L.off_l + align_up(std::max<uint64_t>(rows, 1) * 4, 256);
+  L.off_c = L.off_o + align_up(std::max<uint64_t>(rows, 1) * p->head_dim * 4, 256);
+  L.bytes = L.off_c + align_up((3ull * num_seqs + 4ull * n_items) * 4, 256);
   return L;
 }
 
-// Checks the groups of a shared-prefix decode and builds the int32 tail
-// (starts by sequence, members, shared-pass items).  Returns the number of
-// items, or -1 after fail().
-int64_t shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
-                           const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
-                           int32_t num_groups, std::vector<int32_t>* tail) {
+struct SharedTail {
+  std::vector<int32_t> ints;  // starts, slot0, members, items
+  int64_t n_items = 0, n_slots = 0;
+  int32_t chunk = 0;
+  bool reread = false;  // some chunk is read by several items (a group of more than 32 / G members)
+};
+
+// Checks the groups of a shared-prefix decode, picks the shared chunk length
+// and builds the int32 tail.  Returns PA_OK or the status of fail().
+int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
+                       const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
+                       int32_t num_groups, int32_t chunk_tokens, SharedTail* out) {
   if (num_groups < 0 || (num_seqs > 0 && (!members || !group_start || !shared_blocks)))
-    return fail(PA_ERR_INVALID, "members, group_start and shared_blocks are required"), -1;
+    return fail(PA_ERR_INVALID, "members, group_start and shared_blocks are required");
   if (num_seqs > 0 && (group_start[0] != 0 || group_start[num_groups] != num_seqs))
-    return fail(PA_ERR_INVALID, "group_start must run from 0 to num_seqs"), -1;
+    return fail(PA_ERR_INVALID, "group_start must run from 0 to num_seqs");
+  if (chunk_tokens < 0 || chunk_tokens % 64 != 0)
+    return fail(PA_ERR_INVALID, "chunk_tokens %d must be 0 (library choice) or a positive multiple of 64",
+                chunk_tokens);
   const int group = num_q_heads / p->kv_heads;
   const int per_item = group >= 32 ? 1 : 32 / group;  // members whose heads fit 32 columns
-  std::vector<char> seen(static_cast<size_t>(num_seqs), 0);
-  tail->assign(2 * static_cast<size_t>(num_seqs), 0);
-  int32_t* starts = tail->data();
+  const size_t S = static_cast<size_t>(num_seqs);
+  std::vector<char> seen(S, 0);
   for (int32_t i = 0; i < num_seqs; ++i) {
     const int32_t m = members[i];
-    if (m < 0 || m >= num_seqs || seen[m]) return fail(PA_ERR_INVALID, "members must be a permutation"), -1;
+    if (m < 0 || m >= num_seqs || seen[m]) return fail(PA_ERR_INVALID, "members must be a permutation");
     seen[m] = 1;
-    (*tail)[num_seqs + i] = m;
   }
-  int64_t n_items = 0;
-  std::vector<int32_t> items;
+  // Shared runs, and the work items of one chunk per group.
+  int64_t base_items = 0, max_ts = 0;
   for (int32_t g = 0; g < num_groups; ++g) {
     const int32_t a = group_start[g], b = group_start[g + 1];
-    if (b < a) return fail(PA_ERR_INVALID, "group_start decreases at group %d", g), -1;
+    if (b < a) return fail(PA_ERR_INVALID, "group_start decreases at group %d", g);
     const int64_t ts = static_cast<int64_t>(shared_blocks[g]) * p->block_size;
     if (shared_blocks[g] < 0 || shared_blocks[g] > max_blocks || ts % 16 != 0)
       return fail(PA_ERR_INVALID, "shared_blocks[%d] = %d: not a multiple of 16 tokens inside the table", g,
-                  shared_blocks[g]), -1;
+                  shared_blocks[g]);
     if (ts == 0) continue;
-    for (int32_t i = a; i < b; ++i) starts[members[i]] = static_cast<int32_t>(ts);
-    for (int32_t i = a; i < b; i += per_item) {
-      items.push_back(i);
-      items.push_back(std::min<int32_t>(per_item, b - i));
-      items.push_back(static_cast<int32_t>(ts));
-      items.push_back(0);
-      ++n_items;
+    base_items += (b - a + per_item - 1) / per_item;
+    max_ts = std::max(max_ts, ts);
+  }
+  // Chunk length: enough shared workgroups for one per CU (the second slot
+  // of each CU runs the private pieces beside them), in whole 64-token runs
+  // of the four waves, at least 256 tokens.  Measured on MI355X (beam
+  // search, 32 groups of 5 beams over 2040 shared tokens, 8 KV heads): 69.0
+  // us per launch with one 2048-token chunk per group, 72.1 with 1024, 79.0
+  // with 512.
+  int64_t chunk = chunk_tokens;
+  if (chunk == 0) {
+    chunk = std::max<int64_t>(max_ts, 64);
+    if (base_items > 0) {
+      const int64_t target = p->num_cus;
+      const int64_t parts = (target + base_items * p->kv_heads - 1) / (base_items * p->kv_heads);
+      chunk = align_up(static_cast<uint64_t>((max_ts + parts - 1) / parts), 64);
+      chunk = std::max<int64_t>(std::min<int64_t>(chunk, align_up(static_cast<uint64_t>(max_ts), 64)), 256);
     }
   }
-  tail->insert(tail->end(), items.begin(), items.end());
-  return n_items;
+  if (chunk > 0x7FFFFFFF) return fail(PA_ERR_INVALID, "chunk_tokens out of range");
+  out->chunk = static_cast<int32_t>(chunk);
+  std::vector<int32_t>& t = out->ints;
+  t.assign(3 * S, 0);
+  int32_t* starts = t.data();
+  int32_t* slot0 = starts + S;
+  int32_t* mem_out = slot0 + S;
+  for (size_t i = 0; i < S; ++i) slot0[i] = -1;
+  for (int32_t i = 0; i < num_seqs; ++i) mem_out[i] = members[i];
+  int64_t slots = 0, n_items = 0;
+  std::vector<int32_t> items;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int32_t a = group_start[g], b = group_start[g + 1];
+    const int64_t ts = static_cast<int64_t>(shared_blocks[g]) * p->block_size;
+    if (ts == 0) continue;
+    const int64_t chunks = (ts + chunk - 1) / chunk;
+    for (int32_t i = a; i < b; ++i) {
+      starts[members[i]] = static_cast<int32_t>(ts);
+      slot0[members[i]] = static_cast<int32_t>(slots);
+      slots += chunks + 1;
+      if (slots > 0x7FFFFFFF / std::max(num_q_heads, 1)) return fail(PA_ERR_INVALID, "too many partial slots");
+    }
+    if (b - a > per_item) out->reread = true;
+    for (int64_t c = 0; c < chunks; ++c) {
+      for (int32_t i = a; i < b; i += per_item) {
+        items.push_back(i);
+        items.push_back(std::min<int32_t>(per_item, b - i));
+        items.push_back(static_cast<int32_t>(ts));
+        items.push_back(static_cast<int32_t>(c));
+        ++n_items;
+      }
+    }
+  }
+  if ((n_items + num_seqs) * p->kv_heads > 0x7FFFFFFF) return fail(PA_ERR_INVALID, "too many workgroups");
+  t.insert(t.end(), items.begin(), items.end());
+  out->n_items = n_items;
+  out->n_slots = slots;
+  return PA_OK;
 }
 
 }  // namespace
@@ -1143,23 +1198,23 @@ int pa_shared_prefix_groups(const pa_pool* p, const int32_t* tables, const int32
 int pa_decode_shared_prefix_workspace_bytes(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads,
                                             const int32_t* members, const int32_t* group_start,
                                             const int32_t* shared_blocks, int32_t num_groups,
-                                            int32_t max_blocks, uint64_t* bytes_out) {
+                                            int32_t max_blocks, int32_t chunk_tokens, uint64_t* bytes_out) {
   if (!p || !bytes_out || num_seqs < 0) return fail(PA_ERR_INVALID, "bad arguments");
   if (num_q_heads < 1 || num_q_heads % p->kv_heads != 0 || num_q_heads / p->kv_heads > 32)
     return fail(PA_ERR_INVALID, "num_q_heads %d must be a multiple of kv_heads %d with a group of at most 32",
                 num_q_heads, p->kv_heads);
-  std::vector<int32_t> tail;
-  const int64_t n_items = shared_groups_tail(p, num_seqs, num_q_heads, max_blocks, members, group_start,
-                                             shared_blocks, num_groups, &tail);
-  if (n_items < 0) return PA_ERR_INVALID;
-  *bytes_out = num_seqs == 0 ? 0 : shared_layout(p, num_seqs, num_q_heads, n_items).bytes;
+  SharedTail t;
+  int rc = shared_groups_tail(p, num_seqs, num_q_heads, max_blocks, members, group_start, shared_blocks,
+                              num_groups, chunk_tokens, &t);
+  if (rc) return rc;
+  *bytes_out = num_seqs == 0 ? 0 : shared_layout(p, num_seqs, num_q_heads, t.n_items, t.n_slots).bytes;
   return PA_OK;
 }
 
 int pa_shared_prefix_plan(pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                           const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
-                          int32_t num_groups, void* workspace, uint64_t workspace_bytes, void* stream,
-                          pa_shared_plan* plan) {
+                          int32_t num_groups, int32_t chunk_tokens, void* workspace, uint64_t workspace_bytes,
+                          void* stream, pa_shared_plan* plan) {
   int rc = check_bound(p);
   if (rc) return rc;
   if (!plan || num_seqs < 0) return fail(PA_ERR_INVALID, "bad arguments to pa_shared_prefix_plan");
@@ -1169,24 +1224,26 @@ int pa_shared_prefix_plan(pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int
                 num_q_heads, p->kv_heads);
   if (max_blocks < 1 || static_cast<int64_t>(max_blocks) * p->block_size > 0x7FFFFFFF)
     return fail(PA_ERR_INVALID, "max_blocks %d out of range", max_blocks);
-  std::vector<int32_t> tail;
-  const int64_t n_items = shared_groups_tail(p, num_seqs, num_q_heads, max_blocks, members, group_start,
-                                             shared_blocks, num_groups, &tail);
-  if (n_items < 0) return PA_ERR_INVALID;
-  if (n_items * p->kv_heads > 0x7FFFFFFF) return fail(PA_ERR_INVALID, "too many shared-pass items");
+  SharedTail t;
+  if ((rc = shared_groups_tail(p, num_seqs, num_q_heads, max_blocks, members, group_start, shared_blocks,
+                               num_groups, chunk_tokens, &t)))
+    return rc;
   if (num_seqs > 0) {
-    const SharedLayout L = shared_layout(p, num_seqs, num_q_heads, n_items);
+    const SharedLayout L = shared_layout(p, num_seqs, num_q_heads, t.n_items, t.n_slots);
     if (!workspace || workspace_bytes < L.bytes || misaligned(workspace, 16))
       return fail(PA_ERR_INVALID, "a 16-byte aligned workspace of %llu bytes is needed",
                   static_cast<unsigned long long>(L.bytes));
-    auto* ints = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + L.off_i);
-    if ((rc = upload_ints(p, ints, tail.data(), tail.size(), static_cast<hipStream_t>(stream)))) return rc;
+    auto* ints = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + L.off_c);
+    if ((rc = upload_ints(p, ints, t.ints.data(), t.ints.size(), static_cast<hipStream_t>(stream)))) return rc;
   }
   plan->pool = p;
   plan->num_seqs = num_seqs;
   plan->num_q_heads = num_q_heads;
   plan->max_blocks = max_blocks;
-  plan->num_items = static_cast<int32_t>(n_items);
+  plan->num_items = static_cast<int32_t>(t.n_items);
+  plan->num_slots = static_cast<int32_t>(t.n_slots);
+  plan->chunk_tokens = t.chunk;
+  plan->flags = t.reread ? PA_SHARED_REREAD : 0;
   plan->workspace = workspace;
   plan->workspace_bytes = workspace_bytes;
   return PA_OK;
@@ -1208,12 +1265,15 @@ int pa_decode_shared_prefix(pa_pool* p, int32_t layer, const pa_shared_plan* pla
     return fail(PA_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
   if (num_seqs == 0) return PA_OK;
   if (!out || misaligned(out, 8)) return fail(PA_ERR_INVALID, "out must be non-NULL and 8-byte aligned");
-  const SharedLayout L = shared_layout(p, num_seqs, num_q_heads, plan->num_items);
-  if (!plan->workspace || plan->workspace_bytes < L.bytes || plan->num_items < 0)
+  if (plan->num_items < 0 || plan->num_slots < 0 || plan->chunk_tokens < 64 || plan->chunk_tokens % 64 != 0)
+    return fail(PA_ERR_INVALID, "the plan is not one pa_shared_prefix_plan made");
+  const SharedLayout L = shared_layout(p, num_seqs, num_q_heads, plan->num_items, plan->num_slots);
+  if (!plan->workspace || plan->workspace_bytes < L.bytes)
     return fail(PA_ERR_INVALID, "the plan's workspace is too small");
   auto s = static_cast<hipStream_t>(stream);
   auto* ws = static_cast<uint8_t*>(plan->workspace);
-  auto* ints = reinterpret_cast<int32_t*>(ws + L.off_i);
+  auto* ints = reinterpret_cast<int32_t*>(ws + L.off_c);
+  const size_t S = static_cast<size_t>(num_seqs);
   pa::DecodeLaunch d{};
   d.layer = layer;
   d.q = q;
@@ -1229,30 +1289,29 @@ int pa_decode_shared_prefix(pa_pool* p, int32_t layer, const pa_shared_plan* pla
   d.chunks_per_wave = 1;
   d.waves_per_unit = 1;
   d.scale = scale;
-  d.cached_loads = use_cached_loads(p) ? 1 : 0;
+  // The shared pieces read each shared block once; ordinary (cached) loads
+  // only where several items of a group read the same chunk, nontemporal
+  // ones otherwise (beams: 46.0 against 52.2 us for their shared pieces).
+  d.cached_loads = (plan->flags & PA_SHARED_REREAD) ? 1 : 0;
+  d.part_m = reinterpret_cast<float*>(ws);
+  d.part_l = reinterpret_cast<float*>(ws + L.off_l);
+  d.part_o = reinterpret_cast<float*>(ws + L.off_o);
   d.starts = ints;
-  d.members = ints + num_seqs;
-  d.work = ints + 2 * num_seqs;
+  d.slot0 = d.starts + S;
+  d.members = d.slot0 + S;
+  d.work = d.members + S;
   d.num_items = plan->num_items;
-  d.shared_m = reinterpret_cast<float*>(ws);
-  d.shared_l = reinterpret_cast<float*>(ws + L.off_l);
-  d.shared_o = reinterpret_cast<float*>(ws + L.off_o);
+  d.sp_chunk = plan->chunk_tokens;
+  d.sp_slots = plan->num_slots;
   if (fused) {
     d.k_new = k_new;
     d.v_new = v_new;
     d.new_slots = slot_mapping;
   }
-  // Timing covers both launches: from the shared pass's start to the private
-  // pass's end.
   const bool rec = p->profiling && p->launches++ % p->every == 0 && p->n_records < p->max_records;
   hipEvent_t* ev = rec ? &p->ev[4 * static_cast<size_t>(p->n_records)] : nullptr;
-  hipError_t e = hipSuccess;
-  if (plan->num_items > 0) {
-    e = pa::launch_shared_prefix(p->geom, d, s, rec ? ev[0] : nullptr, nullptr);
-    if (e != hipSuccess) return hip_fail(e, "shared-prefix launch");
-  }
-  e = pa::launch_decode(p->geom, d, s, (rec && plan->num_items == 0) ? ev[0] : nullptr, rec ? ev[1] : nullptr);
-  if (e != hipSuccess) return hip_fail(e, "private-pass launch");
+  const hipError_t e = pa::launch_shared_prefix(p->geom, d, s, rec ? ev[0] : nullptr, rec ? ev[1] : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "shared-prefix launch");
   if (rec) {
     p->has_reduce[p->n_records] = 0;
     ++p->n_records;

@@ -949,6 +949,35 @@ __device__ inline void merge_waves(Dec& dec, MergeLds<Dec::kNT, Dec::kD>& sm, in
   }
 }
 
+// Merge of a shared-prefix decode: the pieces of one grouped sequence (its
+// group's shared chunks and its own tokens) wrote partials m, l, o into slots
+// slot0 .. slot0 + parts - 1; out = sum_c w_c o_c / sum_c w_c with
+// w_c = l_c * 2^(m_c - max_c m_c), for every query head of the KV head.  One
+// workgroup per (sequence, KV head); lanes take four dims of one head.
+template <int D>
+__device__ inline void sp_merge_rows(const DecodeLaunch& p, int seq, int kvh, int group, int64_t slot0,
+                                     int parts) {
+  const int hq = p.num_q_heads;
+  const int64_t r0 = static_cast<int64_t>(kvh) * group;
+  for (int e = threadIdx.x; e < group * (D / 4); e += kWaves * 64) {
+    const int h = e / (D / 4), d4 = e % (D / 4);
+    float M = -__builtin_inff();
+    for (int c = 0; c < parts; ++c) M = fmaxf(M, p.part_m[(slot0 + c) * hq + r0 + h]);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float den = 0.0f;
+    for (int c = 0; c < parts; ++c) {
+      const int64_t idx = (slot0 + c) * hq + r0 + h;
+      const float mc = p.part_m[idx];
+      const float wc = (mc == -__builtin_inff()) ? 0.0f : p.part_l[idx] * exp2f(mc - M);
+      den += wc;
+      acc += *reinterpret_cast<const f32x4*>(p.part_o + idx * D + 4 * d4) * wc;
+    }
+    const f32x4 v = acc * (1.0f / den);
+    *reinterpret_cast<f16x4*>(static_cast<_Float16*>(p.out) + (static_cast<int64_t>(seq) * hq + r0 + h) * D +
+                              4 * d4) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+  }
+}
+
 enum DecodeMode : int {
   kSingle = 0,   // one workgroup per (sequence, KV head), fp16 output
   kSplit4 = 1,   // a workgroup's four waves share each chunk of a chunk run
@@ -986,8 +1015,8 @@ __device__ inline int context_len(const PoolGeom& g, const DecodeLaunch& p, int 
 // though they fit in 256 without spills; with two, MQA decode ran 10-13%
 // faster on MI355X (one-tile variants measured the same either way).
 template <int D, int KIND, int BS, int NT, int MODE, bool FUSE, bool CACHED>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_kernel(PoolGeom g, DecodeLaunch p) {
+__device__ __forceinline__ void decode_body(const PoolGeom& g, const DecodeLaunch& p, uint32_t bid,
+                                            MergeLds<NT, D>& sm) {
   constexpr int kD = D;
   constexpr int ELEM = kind_bytes(KIND);
   constexpr bool kOne = MODE == kSingle || MODE == kPrivate;  // one pass per (sequence, KV head)
@@ -998,12 +1027,12 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
   int64_t unit;
   int r = 0;
   if constexpr (kOne) {
-    unit = blockIdx.x;
+    unit = bid;
   } else if constexpr (MODE == kSplit4) {
-    unit = blockIdx.x / p.waves_per_unit;
-    r = static_cast<int>(blockIdx.x % p.waves_per_unit);
+    unit = bid / p.waves_per_unit;
+    r = static_cast<int>(bid % p.waves_per_unit);
   } else {
-    const int64_t v = static_cast<int64_t>(blockIdx.x) * kWaves + w;
+    const int64_t v = static_cast<int64_t>(bid) * kWaves + w;
     unit = v / p.waves_per_unit;
     r = static_cast<int>(v % p.waves_per_unit);
     if (unit >= num_units) return;  // whole waves only: no barrier in this mode
@@ -1031,10 +1060,19 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
   // the shared pass; s0 is a multiple of 16 inside the table (else 0).  The
   // plain single pass keeps s0 = 0 at compile time.
   int s0 = 0;
+  int64_t sp_slot = 0;  // this piece's partial slot
   if constexpr (MODE == kPrivate) {
-    if (p.starts) {
-      s0 = ((const ConstI32*)p.starts)[seq];
-      s0 = (s0 < 0 || static_cast<int64_t>(s0) >= static_cast<int64_t>(p.max_blocks) * BS) ? 0 : (s0 & ~15);
+    s0 = ((const ConstI32*)p.starts)[seq];
+    s0 = (s0 < 0 || static_cast<int64_t>(s0) >= static_cast<int64_t>(p.max_blocks) * BS) ? 0 : (s0 & ~15);
+    if (s0 > 0) {
+      const int sp_parts = (s0 + p.sp_chunk - 1) / p.sp_chunk + 1;  // shared chunks + this piece
+      const int slot0 = ((const ConstI32*)p.slot0)[seq];
+      if (slot0 < 0 || slot0 > p.sp_slots - sp_parts) {
+        // Inconsistent with the plan: flagged, attended as a plain single pass.
+        if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
+        s0 = 0;
+      }
+      sp_slot = static_cast<int64_t>(slot0) + sp_parts - 1;
     }
   }
   // First token of scheduled step j, before any clamping to the context.
@@ -1105,9 +1143,21 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
 
   if constexpr (kOne) {
     if (T <= s0) {
-      // Nothing to attend to (or a start at or past the context, a contract
-      // violation): defined output of zeros.
-      if (s0 > 0 && threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
+      // Nothing to attend to: defined output of zeros.  A context at or
+      // below its shared tokens (a contract violation) is flagged and
+      // contributes an empty part, so the output is the shared tokens' alone.
+      if constexpr (MODE == kPrivate) {
+        if (s0 > 0) {
+          if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
+          const int64_t idx0 = sp_slot * p.num_q_heads + kvh * group;
+          for (int i = threadIdx.x; i < group * kD; i += kWaves * 64) p.part_o[idx0 * kD + i] = 0.0f;
+          for (int i = threadIdx.x; i < group; i += kWaves * 64) {
+            p.part_m[idx0 + i] = -__builtin_inff();
+            p.part_l[idx0 + i] = 0.0f;
+          }
+          return;
+        }
+      }
       for (int i = threadIdx.x; i < group * kD; i += kWaves * 64)
         static_cast<_Float16*>(p.out)[(static_cast<int64_t>(seq) * p.num_q_heads + kvh * group) * kD + i] = 0;
       return;
@@ -1141,30 +1191,24 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
   const int64_t row0 = static_cast<int64_t>(seq) * p.num_q_heads + kvh * group;
 
   if constexpr (kOne) {
-    __shared__ MergeLds<NT, D> sm;
     stream_steps(dec, n, tok_of, real, first, [](int) {});
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
-    merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float M, float L, float) {
+    merge_waves(dec, sm, w, group, [&](int nt, int col, f32x4* acc, float M, float L, float Mt) {
       (void)nt;
-      _Float16* po = static_cast<_Float16*>(p.out) + (row0 + col) * kD + 4 * gq;
       if (MODE == kPrivate && s0 > 0) {
-        // Log-sum-exp merge with the shared pass's partials of this row:
-        // out = (acc * 2^(M - X) + o_s * l_s * 2^(m_s - X)) / (L * 2^(M - X) + l_s * 2^(m_s - X)).
-        const int64_t row = row0 + col;
-        const float m_s = p.shared_m[row], l_s = p.shared_l[row];
-        const float X = fmaxf(M, m_s);
-        const float a = exp2f(M - X) * dec.out_mul;
-        const float b = exp2f(m_s - X) * l_s;
-        const float inv = 1.0f / (L * exp2f(M - X) + b);
-        const float* ps = p.shared_o + row * kD + 4 * gq;
+        // The private tokens' partials, in the sequence's last slot.
+        const int64_t idx = sp_slot * p.num_q_heads + kvh * group + col;
+        const float inv_l = dec.out_mul / L;
+        float* po = p.part_o + idx * kD + 4 * gq;
 #pragma unroll
-        for (int rr = 0; rr < D / 16; ++rr) {
-          const f32x4 os = *reinterpret_cast<const f32x4*>(ps + rr * 16);
-          const f32x4 v = (acc[rr] * a + os * b) * inv;
-          *reinterpret_cast<f16x4*>(po + rr * 16) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+        for (int rr = 0; rr < D / 16; ++rr) *reinterpret_cast<f32x4*>(po + rr * 16) = acc[rr] * inv_l;
+        if (gq == 0) {
+          p.part_m[idx] = Mt;
+          p.part_l[idx] = (!Dec::kLazy || M == Mt) ? L : L * exp2f(M - Mt);
         }
         return;
       }
+      _Float16* po = static_cast<_Float16*>(p.out) + (row0 + col) * kD + 4 * gq;
       const float inv_l = dec.out_mul / L;
 #pragma unroll
       for (int rr = 0; rr < D / 16; ++rr) {
@@ -1174,7 +1218,6 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
     });
     store_new();  // after the merge: its barriers would wait for these stores
   } else if constexpr (MODE == kSplit4) {
-    __shared__ MergeLds<NT, D> sm;
     auto after = [&](int j) {
       if ((j + 1) % qs != 0 && j + 1 != n) return;
       const int64_t c = c_begin + j / qs;
@@ -1223,6 +1266,13 @@ void decode_kernel(PoolGeom g, DecodeLaunch p) {
     if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
     store_new();
   }
+}
+
+template <int D, int KIND, int BS, int NT, int MODE, bool FUSE, bool CACHED>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(PoolGeom g, DecodeLaunch p) {
+  __shared__ MergeLds<NT, D> sm;
+  decode_body<D, KIND, BS, NT, MODE, FUSE, CACHED>(g, p, blockIdx.x, sm);
 }
 
 // Causal attention of a tile of new query tokens of one sequence over its
@@ -1343,81 +1393,127 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
   }
 }
 
-// Shared pass of the shared-prefix decode.  Sequences whose block tables
-// begin with the same blocks (beams of one search, requests on one cached
+// Shared-prefix decode: one launch whose first workgroups read the blocks
+// that groups of sequences share (beams of one search, requests on one cached
 // system prompt: youngju.dev "KV cache and paged attention", section "prefix
-// 공유와 copy-on-write") read those blocks once here for all of them: the
-// query heads of up to 32 / G members are the MFMA columns of one item
-// (column c: member c / G, head c % G), the four waves take key steps w,
-// w + 4, ... of the shared tokens and merge in LDS, and every (member, head)
-// row gets its partials over the shared tokens: m (the largest score, base
-// 2), l = sum 2^(s - m), o = sum 2^(s - m) v / l (times the V scale).  The
-// private pass (decode_kernel in mode kPrivate) attends to each
-// sequence's remaining tokens and merges these partials by log-sum-exp.
-// Workgroup = (item, KV head); items hold (first member, members, shared
-// tokens); the blocks are read through the first member's table.
-template <int D, int KIND, int BS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void shared_prefix_kernel(PoolGeom g, DecodeLaunch p) {
+// 공유와 copy-on-write") once for all the group's members, and whose other
+// workgroups attend to each sequence's own tokens, every piece of a grouped
+// sequence writing partials; a second launch (shared_merge_kernel) merges
+// them.
+//
+// Shared piece (shared_body): an item is (first member, members, shared
+// tokens ts, chunk c) and takes the group's tokens [c * chunk, min((c + 1) *
+// chunk, ts)) for up to 32 / G members, whose query heads are the MFMA
+// columns of one tile pair (column k: member k / G, head k % G); the four
+// waves take key steps w, w + 4, ... and merge in LDS, and every (member,
+// head) row gets its partials m (the largest score, base 2), l = sum 2^(s -
+// m), o = sum 2^(s - m) v / l (times the V scale) in slot slot0[member] + c.
+// The blocks are read through the first member's table, with ordinary loads
+// where several items of a group re-read them, nontemporal ones otherwise.
+template <int D, int KIND, int BS, bool CACHED>
+__device__ __forceinline__ void shared_body(const PoolGeom& g, const DecodeLaunch& p, uint32_t bid,
+                                            MergeLds<2, D>& sm) {
   constexpr int NT = 2;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = p.num_q_heads / g.kv_heads;
-  const int item = static_cast<int>(blockIdx.x / g.kv_heads);
-  const int kvh = static_cast<int>(blockIdx.x % g.kv_heads);
+  const int item = static_cast<int>(bid / g.kv_heads);
+  const int kvh = static_cast<int>(bid % g.kv_heads);
   const ConstI32* wk = (const ConstI32*)(p.work + 4 * static_cast<int64_t>(item));
-  const int m0 = wk[0], nm = wk[1], ts = wk[2];
+  const int m0 = wk[0], nm = wk[1], ts = wk[2], c = wk[3];
+  const int chunk = p.sp_chunk;
+  const int parts = (ts + chunk - 1) / chunk + 1;
   // The host checks the items when it uploads them; an item that does not
   // fit this launch (a member run outside the batch, more than 32 columns, a
-  // member outside the batch, a shared length outside the table or not a
-  // multiple of 16) is flagged and its rows left alone.  Every wave reaches
-  // the same verdict, so the workgroup leaves together.
+  // member outside the batch or without room for its slots, a shared length
+  // outside the table or not a multiple of 16, a chunk past it) is flagged
+  // and its rows left alone.  Every wave reaches the same verdict, so the
+  // workgroup leaves together.
   if (m0 < 0 || nm < 1 || nm * group > 32 || m0 > p.num_seqs - nm || ts < 16 || (ts & 15) != 0 ||
-      static_cast<int64_t>(ts) > static_cast<int64_t>(p.max_blocks) * BS) {
+      static_cast<int64_t>(ts) > static_cast<int64_t>(p.max_blocks) * BS || c < 0 ||
+      static_cast<int64_t>(c) * chunk >= ts) {
     if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
     return;
   }
   const int32_t* mem = p.members + m0;
   const int mine = lane < nm ? ((const ConstI32*)mem)[lane] : 0;
-  if (__ballot(static_cast<uint32_t>(mine) >= static_cast<uint32_t>(p.num_seqs)) != 0) {
+  const int my_slot0 = lane < nm ? ((const ConstI32*)p.slot0)[mine] : 0;
+  if (__ballot(static_cast<uint32_t>(mine) >= static_cast<uint32_t>(p.num_seqs) || my_slot0 < 0 ||
+               my_slot0 > p.sp_slots - parts) != 0) {
     if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
     return;
   }
   const int seq0 = __builtin_amdgcn_readfirstlane(mine);
-  WaveDecoder<D, KIND, BS, NT, false, true, true> dec;  // items of one group re-read the tiles
+  const int t0 = c * chunk;
+  const int t1 = (ts - t0 < chunk) ? ts : t0 + chunk;
+  WaveDecoder<D, KIND, BS, NT, false, true, CACHED> dec;
   dec.bind(g, p, seq0, kvh, lane);
   const int ncols = nm * group;
-  dec.T = ts;
-  dec.lim_min = ts;
+  dec.T = t1;
+  dec.lim_min = t1;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) dec.lim[nt] = ts;
+  for (int nt = 0; nt < NT; ++nt) dec.lim[nt] = t1;
   dec.mt_row0 = 0;
   dec.mt_ncols = ncols;
   dec.mt_rowmap = mem;
-  auto raw_tok = [&](int j) -> int64_t { return 16ll * (w + kWaves * j); };
-  const int n = (ts + 16 * kWaves - 1) / (16 * kWaves);
-  const int last_tok = ((ts - 1) >> 4) << 4;
-  auto real = [&](int j) { return raw_tok(j) < ts; };
+  auto raw_tok = [&](int j) -> int64_t { return t0 + 16ll * (w + kWaves * j); };
+  const int n = (t1 - t0 + 16 * kWaves - 1) / (16 * kWaves);
+  const int last_tok = ((t1 - 1) >> 4) << 4;
+  auto real = [&](int j) { return raw_tok(j) < t1; };
   auto tok_of = [&](int j) -> int { return real(j) ? static_cast<int>(raw_tok(j)) : last_tok; };
   dec.load_q(g, p, seq0, kvh, group);
   dec.reset();
-  __shared__ MergeLds<NT, D> sm;
   stream_pairs(dec, n, tok_of, real);
   dec.finish_l();
   if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
   const int gq = dec.gq;
   merge_waves(dec, sm, w, ncols, [&](int, int col, f32x4* acc, float M, float L, float Mt) {
     const int seq = mem[col / group];
-    const int64_t row = static_cast<int64_t>(seq) * p.num_q_heads + kvh * group + col % group;
+    const int64_t idx = (static_cast<int64_t>(((const ConstI32*)p.slot0)[seq]) + c) * p.num_q_heads +
+                        kvh * group + col % group;
     const float inv_l = dec.out_mul / L;
-    float* po = p.shared_o + row * D + 4 * gq;
+    float* po = p.part_o + idx * D + 4 * gq;
 #pragma unroll
     for (int rr = 0; rr < D / 16; ++rr) *reinterpret_cast<f32x4*>(po + rr * 16) = acc[rr] * inv_l;
     if (gq == 0) {
-      p.shared_m[row] = Mt;
-      p.shared_l[row] = (M == Mt) ? L : L * exp2f(M - Mt);
+      p.part_m[idx] = Mt;
+      p.part_l[idx] = (M == Mt) ? L : L * exp2f(M - Mt);
     }
   });
+}
+
+// The shared-prefix pieces: workgroups 0 .. items * Hkv - 1 are shared
+// pieces, the rest (sequence, KV head) private pieces (decode_body in mode
+// kPrivate: tokens starts[i] .. T_i - 1 into the sequence's last slot, or the
+// whole context straight into `out` for a sequence in no group).  One LDS
+// buffer serves either body.  The pieces are independent, so the private
+// ones run beside the long shared ones.
+// Merge launch: one workgroup per (sequence, KV head); sequences in no
+// group leave at once.
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void shared_merge_kernel(PoolGeom g, DecodeLaunch p) {
+  const int kvh = static_cast<int>(blockIdx.x % g.kv_heads);
+  const int seq = static_cast<int>(blockIdx.x / g.kv_heads);
+  const int s0 = ((const ConstI32*)p.starts)[seq];
+  const int slot0 = ((const ConstI32*)p.slot0)[seq];
+  if (s0 <= 0 || slot0 < 0 || static_cast<int64_t>(s0) >= static_cast<int64_t>(p.max_blocks) * g.block_size)
+    return;
+  const int parts = ((s0 & ~15) + p.sp_chunk - 1) / p.sp_chunk + 1;
+  if (slot0 > p.sp_slots - parts) return;  // flagged by the pieces
+  sp_merge_rows<D>(p, seq, kvh, p.num_q_heads / g.kv_heads, slot0, parts);
+}
+
+template <int D, int KIND, int BS, int NT, bool FUSE, bool CACHED>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void shared_prefix_kernel(PoolGeom g, DecodeLaunch p) {
+  __shared__ MergeLds<2, D> sm;
+  const uint32_t n_shared = static_cast<uint32_t>(p.num_items) * g.kv_heads;
+  if (blockIdx.x < n_shared) {
+    shared_body<D, KIND, BS, CACHED>(g, p, blockIdx.x, sm);
+  } else {
+    decode_body<D, KIND, BS, NT, kPrivate, FUSE, CACHED>(g, p, blockIdx.x - n_shared,
+                                                          *reinterpret_cast<MergeLds<NT, D>*>(&sm));
+  }
 }
 
 // Log-sum-exp merge of the chunk partials of one (sequence, query head):
@@ -1582,9 +1678,6 @@ hipError_t launch_decode_nt(const PoolGeom& g, const DecodeLaunch& d, hipStream_
     case kSingle:
       return launch_kernel(decode_kernel<D, KIND, BS, NT, kSingle, FUSE, CACHED>, dim3(static_cast<unsigned>(units)),
                            block, s, t0, t1, g, d);
-    case kPrivate:
-      return launch_kernel(decode_kernel<D, KIND, BS, NT, kPrivate, FUSE, CACHED>, dim3(static_cast<unsigned>(units)),
-                           block, s, t0, t1, g, d);
     case kSplit4:
       return launch_kernel(decode_kernel<D, KIND, BS, NT, kSplit4, FUSE, CACHED>,
                            dim3(static_cast<unsigned>(units * d.waves_per_unit)), block, s, t0, t1, g, d);
@@ -1640,15 +1733,41 @@ hipError_t launch_multi_token_kd(const PoolGeom& g, const DecodeLaunch& d, const
   }
 }
 
-// Shared pass of one (head_dim, element kind).
-template <int D, int KIND>
-hipError_t launch_shared_prefix_kd(const PoolGeom& g, const DecodeLaunch& d, const dim3& grid, hipStream_t s,
-                                   hipEvent_t t0, hipEvent_t t1) {
+// Shared-prefix launch of one (head_dim, element kind): grid = the shared
+// items' workgroups, then one per (sequence, KV head).
+template <int D, int KIND, int BS, bool FUSE, bool CACHED>
+hipError_t launch_shared_prefix_f(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s, hipEvent_t t0,
+                                  hipEvent_t t1) {
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(d.num_items) + d.num_seqs) * g.kv_heads));
   const dim3 block(kWaves * 64);
+  const bool merge = d.num_items > 0;
+  hipError_t e =
+      nt == 1 ? launch_kernel(shared_prefix_kernel<D, KIND, BS, 1, FUSE, CACHED>, grid, block, s, t0,
+                              merge ? nullptr : t1, g, d)
+              : launch_kernel(shared_prefix_kernel<D, KIND, BS, 2, FUSE, CACHED>, grid, block, s, t0,
+                              merge ? nullptr : t1, g, d);
+  if (e != hipSuccess || !merge) return e;
+  const dim3 mgrid(static_cast<unsigned>(static_cast<int64_t>(d.num_seqs) * g.kv_heads));
+  return launch_kernel(shared_merge_kernel<D>, mgrid, block, s, nullptr, t1, g, d);
+}
+
+template <int D, int KIND, int BS>
+hipError_t launch_shared_prefix_bs(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s, hipEvent_t t0,
+                                   hipEvent_t t1) {
+  if (d.new_slots)
+    return d.cached_loads ? launch_shared_prefix_f<D, KIND, BS, true, true>(g, d, nt, s, t0, t1)
+                          : launch_shared_prefix_f<D, KIND, BS, true, false>(g, d, nt, s, t0, t1);
+  return d.cached_loads ? launch_shared_prefix_f<D, KIND, BS, false, true>(g, d, nt, s, t0, t1)
+                        : launch_shared_prefix_f<D, KIND, BS, false, false>(g, d, nt, s, t0, t1);
+}
+
+template <int D, int KIND>
+hipError_t launch_shared_prefix_kd(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s, hipEvent_t t0,
+                                   hipEvent_t t1) {
   switch (g.block_size) {
-    case 8: return launch_kernel(shared_prefix_kernel<D, KIND, 8>, grid, block, s, t0, t1, g, d);
-    case 16: return launch_kernel(shared_prefix_kernel<D, KIND, 16>, grid, block, s, t0, t1, g, d);
-    case 32: return launch_kernel(shared_prefix_kernel<D, KIND, 32>, grid, block, s, t0, t1, g, d);
+    case 8: return launch_shared_prefix_bs<D, KIND, 8>(g, d, nt, s, t0, t1);
+    case 16: return launch_shared_prefix_bs<D, KIND, 16>(g, d, nt, s, t0, t1);
+    case 32: return launch_shared_prefix_bs<D, KIND, 32>(g, d, nt, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -15,9 +15,8 @@ template hipError_t launch_decode_kd<PA_INST_D, PA_INST_KIND>(const PoolGeom&, c
 template hipError_t launch_multi_token_kd<PA_INST_D, PA_INST_KIND>(const PoolGeom&, const DecodeLaunch&,
                                                                    const dim3&, hipStream_t, hipEvent_t,
                                                                    hipEvent_t);
-template hipError_t launch_shared_prefix_kd<PA_INST_D, PA_INST_KIND>(const PoolGeom&, const DecodeLaunch&,
-                                                                     const dim3&, hipStream_t, hipEvent_t,
-                                                                     hipEvent_t);
+template hipError_t launch_shared_prefix_kd<PA_INST_D, PA_INST_KIND>(const PoolGeom&, const DecodeLaunch&, int,
+                                                                     hipStream_t, hipEvent_t, hipEvent_t);
 
 }  // namespace dk
 }  // namespace pa

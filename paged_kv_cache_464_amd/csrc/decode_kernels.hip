@@ -12,7 +12,7 @@ namespace dk {
                                                        hipEvent_t, hipEvent_t);                                \
   extern template hipError_t launch_multi_token_kd<D, KIND>(const PoolGeom&, const DecodeLaunch&, const dim3&, \
                                                             hipStream_t, hipEvent_t, hipEvent_t);              \
-  extern template hipError_t launch_shared_prefix_kd<D, KIND>(const PoolGeom&, const DecodeLaunch&, const dim3&, \
+  extern template hipError_t launch_shared_prefix_kd<D, KIND>(const PoolGeom&, const DecodeLaunch&, int,         \
                                                               hipStream_t, hipEvent_t, hipEvent_t);
 PA_DECLARE_INST(64, kF16)
 PA_DECLARE_INST(64, kF8)
@@ -45,12 +45,12 @@ hipError_t multi_token_for_dim(const PoolGeom& g, const DecodeLaunch& d, const d
 }
 
 template <int D>
-hipError_t shared_prefix_for_dim(const PoolGeom& g, const DecodeLaunch& d, const dim3& grid, hipStream_t s,
-                                 hipEvent_t t0, hipEvent_t t1) {
+hipError_t shared_prefix_for_dim(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s, hipEvent_t t0,
+                                 hipEvent_t t1) {
   switch (g.kind) {
-    case kF16: return launch_shared_prefix_kd<D, kF16>(g, d, grid, s, t0, t1);
-    case kF8: return launch_shared_prefix_kd<D, kF8>(g, d, grid, s, t0, t1);
-    case kI8: return launch_shared_prefix_kd<D, kI8>(g, d, grid, s, t0, t1);
+    case kF16: return launch_shared_prefix_kd<D, kF16>(g, d, nt, s, t0, t1);
+    case kF8: return launch_shared_prefix_kd<D, kF8>(g, d, nt, s, t0, t1);
+    case kI8: return launch_shared_prefix_kd<D, kI8>(g, d, nt, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }
@@ -59,13 +59,15 @@ hipError_t shared_prefix_for_dim(const PoolGeom& g, const DecodeLaunch& d, const
 
 hipError_t launch_shared_prefix(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
                                 hipEvent_t t1) {
-  const int64_t wgs = static_cast<int64_t>(d.num_items) * g.kv_heads;
+  const int64_t wgs = (static_cast<int64_t>(d.num_items) + d.num_seqs) * g.kv_heads;
   if (wgs <= 0) return hipSuccess;
-  if (!d.work || !d.members || wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(wgs));
+  if (!d.starts || !d.slot0 || (d.num_items > 0 && (!d.work || !d.members)) ||
+      d.num_items < 0 || wgs > 0x7FFFFFFF || d.sp_chunk < 64 || d.sp_chunk % 64 != 0)
+    return hipErrorInvalidValue;
+  const int nt = d.num_q_heads / g.kv_heads > 16 ? 2 : 1;
   switch (g.head_dim) {
-    case 64: return dk::shared_prefix_for_dim<64>(g, d, grid, s, t0, t1);
-    case 128: return dk::shared_prefix_for_dim<128>(g, d, grid, s, t0, t1);
+    case 64: return dk::shared_prefix_for_dim<64>(g, d, nt, s, t0, t1);
+    case 128: return dk::shared_prefix_for_dim<128>(g, d, nt, s, t0, t1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -70,18 +70,19 @@ struct DecodeLaunch {
   int waves_per_unit;    // runs per (sequence, KV head) = ceil(C / k) (split modes)
   float scale;
   int cached_loads;  // 1: ordinary K/V loads (blocks shared by many sequences); 0: nontemporal
-  // Shared-prefix decode.  Shared pass: `work` holds items of four int32
-  // (first member, members, shared tokens, 0) indexing `members` (sequence
-  // ids, group by group); it writes each member's (max, sum, normalised O)
-  // over the shared tokens into shared_m / shared_l / shared_o
-  // [S][Hq] / [S][Hq] / [S][Hq][D].  Private pass (single pass only):
-  // sequence i attends to tokens starts[i] .. T_i - 1 and, when starts[i] > 0,
-  // merges the shared pass's partials into its output.
+  // Shared-prefix decode.  `work` holds items of four int32 (first member,
+  // members, shared tokens, chunk) indexing `members` (sequence ids, group by
+  // group); sequence i attends privately to tokens starts[i] .. T_i - 1.  A
+  // grouped sequence's pieces (its group's shared chunks of sp_chunk tokens,
+  // then its private tokens) write partials into slots slot0[i],
+  // slot0[i] + 1, ... of part_m / part_l / part_o ([slot][Hq] / [slot][Hq] /
+  // [slot][Hq][D], sp_slots slots), which a second launch merges into `out`.
+  // A sequence in no group (starts[i] = 0) writes `out` directly.
   const int32_t* members;
   const int32_t* starts;
-  float* shared_m;
-  float* shared_l;
-  float* shared_o;
+  const int32_t* slot0;
+  int sp_chunk;
+  int sp_slots;
 };
 
 // t0/t1: optional events stamped at the kernel's start and end (null: untimed).
@@ -89,8 +90,10 @@ hipError_t launch_decode(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s
                          hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_lse_reduce(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
                              hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
-// Shared pass of the shared-prefix decode (d.work, d.num_items, d.members,
-// d.shared_*).
+// Shared-prefix decode: the shared chunks and every sequence's private
+// tokens in one launch, then the merge of the grouped sequences' partials
+// (d.work, d.num_items, d.members, d.starts, d.slot0, d.part_*, d.sp_chunk,
+// d.sp_slots).
 hipError_t launch_shared_prefix(const PoolGeom& g, const DecodeLaunch& d, hipStream_t stream,
                                 hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Causal attention of several query tokens per sequence (d.work, d.num_items;

@@ -435,11 +435,11 @@ def _groups_args(groups):
     return (members, gstart, shared), ip(members), ip(gstart), ip(shared), len(shared)
 
 
-def pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, groups, max_blocks):
+def pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, groups, max_blocks, chunk_tokens=0):
     keep, mp, gp, sp, ng = _groups_args(groups)
     b = C.c_uint64()
     _check(_L().pa_decode_shared_prefix_workspace_bytes(C.c_void_p(h), int(num_seqs), int(num_q_heads), mp, gp,
-                                                        sp, ng, int(max_blocks), C.byref(b)))
+                                                        sp, ng, int(max_blocks), int(chunk_tokens), C.byref(b)))
     return b.value
 
 
@@ -452,9 +452,9 @@ class SharedPlan:
 
 
 def pa_shared_prefix_plan(h, num_seqs, num_q_heads, max_blocks, groups, workspace=None, stream=None,
-                          device="cuda"):
+                          device="cuda", chunk_tokens=0):
     keep, mp, gp, sp, ng = _groups_args(groups)
-    need = pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, keep, max_blocks)
+    need = pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, keep, max_blocks, chunk_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     nbytes = workspace.numel() * workspace.element_size()
@@ -462,13 +462,14 @@ def pa_shared_prefix_plan(h, num_seqs, num_q_heads, max_blocks, groups, workspac
         raise ValueError(f"workspace needs {need} bytes")
     plan = _lib.pa_shared_plan()
     _check(_L().pa_shared_prefix_plan(C.c_void_p(h), int(num_seqs), int(num_q_heads), int(max_blocks), mp, gp,
-                                      sp, ng, C.c_void_p(workspace.data_ptr()), nbytes, _stream(stream),
-                                      C.byref(plan)))
+                                      sp, ng, int(chunk_tokens), C.c_void_p(workspace.data_ptr()), nbytes,
+                                      _stream(stream), C.byref(plan)))
     return SharedPlan(plan, workspace, keep)
 
 
 def pa_decode_shared_prefix(h, layer, q, block_tables, context_lens, groups, out=None, scale=None,
-                            workspace=None, stream=None, k_new=None, v_new=None, slot_mapping=None):
+                            workspace=None, stream=None, k_new=None, v_new=None, slot_mapping=None,
+                            chunk_tokens=0):
     """Decode where groups of sequences share leading blocks.  ``groups`` is a
     SharedPlan (pa_shared_prefix_plan) or the (members, group_start,
     shared_blocks) arrays of pa_shared_prefix_groups, planned here on the
@@ -476,7 +477,7 @@ def pa_decode_shared_prefix(h, layer, q, block_tables, context_lens, groups, out
     scattered as in pa_write_kv_decode."""
     info, s, hq, mb, qp, tp, lp = _decode_args(h, q, block_tables, context_lens)
     if not isinstance(groups, SharedPlan):
-        groups = pa_shared_prefix_plan(h, s, hq, mb, groups, workspace, stream, q.device)
+        groups = pa_shared_prefix_plan(h, s, hq, mb, groups, workspace, stream, q.device, chunk_tokens)
     p = groups.plan
     if (p.num_seqs, p.num_q_heads, p.max_blocks) != (s, hq, mb):
         raise ValueError(f"the plan is for {p.num_seqs} sequences, {p.num_q_heads} query heads and tables "

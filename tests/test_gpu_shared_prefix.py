@@ -1,5 +1,8 @@
 """GPU parity of the shared-prefix decode (pa_decode_shared_prefix) against
-the oracle's decode.
+the oracle's decode.  One launch: chunks of each group's shared tokens and
+every sequence's own tokens run as separate pieces, and the last piece of a
+sequence merges their partials; small chunk lengths make many pieces per
+sequence at these sizes.
 
 Sequences are built the way the pages share blocks: a prompt written once
 and forked into several members (beams, parallel samples), each member then
@@ -148,11 +151,12 @@ def test_shared_prefix_decode_matches_the_oracle(case):
     st = oracle_store(t)
     q = normal_fp16((len(t.batch), hq, D), 464_200, 3, "cuda")
     ref = attention.decode(st, 0, q.cpu().numpy(), t.tables_np, t.lens_np)
-    for min_tokens in (256, 16):
+    for min_tokens, chunk in ((256, 0), (16, 0), (256, 64), (16, 192)):
         g = t.pool.shared_prefix_groups(t.tables_np, t.lens_np, min_tokens)
         _check_groups_cover(t, g, 3 if min_tokens == 256 else 3 + (bs <= 16))
-        out = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, g)
-        assert_close(out, ref, dtype, f"shared prefix min={min_tokens}")
+        out = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, g, chunk_tokens=chunk)
+        assert_close(out, ref, dtype, f"shared prefix min={min_tokens} chunk={chunk}")
+        assert t.pool.device_status() == 0
     # Every group a singleton: the private pass alone over every token.
     n = len(t.batch)
     none = (np.arange(n, dtype=np.int32), np.arange(n + 1, dtype=np.int32), np.zeros(n, dtype=np.int32))
@@ -187,7 +191,8 @@ def test_fused_shared_prefix_step_writes_like_write_kv_decode(dtype, bs):
     g = t.pool.shared_prefix_groups(t.tables_np, t.lens_np, 256)
     assert sum(1 for k in g[2] if k > 0) == 2
     before = t.pool.pool_bytes().clone()
-    out_sp = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, g, k_new=kn, v_new=vn, slot_mapping=sl)
+    out_sp = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, g, k_new=kn, v_new=vn, slot_mapping=sl,
+                                         chunk_tokens=128)
     after_sp = t.pool.pool_bytes().clone()
     t.pool.pool_bytes().copy_(before)
     out_wd = t.pool.write_kv_decode(0, kn, vn, sl, q, t.tables, t.lens)
@@ -249,8 +254,8 @@ def test_shared_prefix_workspace_reuse_plans_and_empty_batch():
     st = oracle_store(t)
     q = normal_fp16((len(t.batch), 32, 128), 464_203, 3, "cuda")
     g = t.pool.shared_prefix_groups(t.tables_np, t.lens_np, 16)
-    ws = torch.empty(pa.pa_decode_shared_prefix_workspace_bytes(t.pool.handle, len(t.batch), 32, g, t.mb),
-                     dtype=torch.uint8, device="cuda")
+    need = [pa.pa_decode_shared_prefix_workspace_bytes(t.pool.handle, len(t.batch), 32, g, t.mb, c) for c in (0, 64)]
+    ws = torch.empty(max(need), dtype=torch.uint8, device="cuda")
     out = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, g, workspace=ws)
     assert_close(out, attention.decode(st, 0, q.cpu().numpy(), t.tables_np, t.lens_np), "fp16", "first call")
     keep = [i for i, s in enumerate(t.batch) if i % 2 == 0]
@@ -260,9 +265,11 @@ def test_shared_prefix_workspace_reuse_plans_and_empty_batch():
     out2 = t.pool.decode_shared_prefix(0, q2, torch.from_numpy(tb).cuda(), torch.from_numpy(ln).cuda(), g2,
                                        workspace=ws)
     assert_close(out2, attention.decode(st, 0, q2.cpu().numpy(), tb, ln), "fp16", "second call")
-    # One plan, several launches (the layers of a step): the group list is
-    # uploaded once; each launch matches the oracle.
-    plan = t.pool.shared_prefix_plan(len(t.batch), 32, t.mb, g, workspace=ws)
+    # One plan, several launches (the layers of a step): the group list and
+    # the zeroed counters are uploaded once, and each launch leaves the
+    # counters at zero for the next; each launch matches the oracle.
+    plan = t.pool.shared_prefix_plan(len(t.batch), 32, t.mb, g, workspace=ws, chunk_tokens=64)
+    assert plan.plan.num_items > len(t.batch) // 4 and plan.plan.chunk_tokens == 64
     for rep in range(3):
         qr = normal_fp16((len(t.batch), 32, 128), 464_203, 10 + rep, "cuda")
         o = t.pool.decode_shared_prefix(0, qr, t.tables, t.lens, plan)

@@ -83,6 +83,13 @@ def test_beam_and_prompt_groups(bs):
     for b in bad:
         with pytest.raises(pa.PAError):
             pa.pa_decode_shared_prefix_workspace_bytes(h, n, 8, b, mb)
+    # chunk lengths: multiples of 64 (0: the library's choice); shorter
+    # chunks need more partial slots
+    sizes = [pa.pa_decode_shared_prefix_workspace_bytes(h, n, 8, groups, mb, c) for c in (0, 64, 128, 1024)]
+    assert sizes[1] >= sizes[2] >= sizes[3] > 0
+    for c in (-64, 100, 32):
+        with pytest.raises(pa.PAError):
+            pa.pa_decode_shared_prefix_workspace_bytes(h, n, 8, groups, mb, c)
     pa.pa_pool_destroy(h)
 
 
