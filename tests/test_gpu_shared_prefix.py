@@ -282,3 +282,77 @@ def test_shared_prefix_workspace_reuse_plans_and_empty_batch():
     t.pool.decode_shared_prefix(0, e, torch.zeros((0, 1), dtype=torch.int32, device="cuda"),
                                 torch.zeros(0, dtype=torch.int32, device="cuda"), empty)
     assert t.pool.device_status() == 0
+
+
+def test_beam_k5_full_size_in_the_benchmark_configuration():
+    """The benchmark's beam_k5 step at full size: 32 groups of 5 beams over a
+    2040-token prompt, 16-token blocks, 32 query / 8 KV heads; each search
+    step re-selects the survivors (forks, frees), appends one token per beam
+    in one batch (copy-on-write copies enqueued), plans the groups found on
+    the host tables and runs the fused shared-prefix call with the library's
+    own chunk choice.  After the last step, 10 sampled beams (every query
+    head) match the oracle, whose store holds each sampled beam's whole
+    context at the slots its table gives."""
+    from workloads import beam_parents, workload
+    w = workload("beam_k5")
+    e = w.extra
+    groups, k, prompt = e["groups"], e["k"], e["prompt"]
+    hq, hkv, bs, D = w.q_heads, w.kv_heads, w.block_size, w.head_dim
+    say("beam_k5 full size, shared-prefix decode")
+    steps = 6
+    nb = w.num_blocks + groups * k * (steps // bs + 2)
+    pool = pa.PagedKVPool(1, hkv, D, bs, nb, free_order=free_order(w.seed, nb))
+    pool.pool_bytes().fill_(0xFF)
+    rows = {}  # seq -> (k rows, v rows) of its context, fp16 on the device
+    beams = []
+    for g in range(groups):
+        s = pool.seq_create()
+        sl, _ = pool.alloc(s, prompt)
+        kp = normal_fp16((prompt, hkv, D), w.seed, 500 + g, "cuda")
+        vp = normal_fp16((prompt, hkv, D), w.seed, 600 + g, "cuda")
+        pool.write_kv(0, kp, vp, torch.from_numpy(sl).cuda())
+        kids = [s] + [pool.fork(s) for _ in range(k - 1)]
+        for c in kids:
+            rows[c] = (kp, vp)
+        beams.append(kids)
+    q = None
+    for step in range(steps):
+        for g, parents in enumerate(beam_parents(w.seed, step, groups, k)):
+            old, new, used = beams[g], [], set()
+            for par in parents:
+                if par in used:
+                    c = pool.fork(old[par])
+                    rows[c] = rows[old[par]]
+                    new.append(c)
+                else:
+                    used.add(par)
+                    new.append(old[par])
+            for b in range(k):
+                if b not in used:
+                    pool.free(old[b])
+                    del rows[old[b]]
+            beams[g] = new
+        seqs = [s for b in beams for s in b]
+        slots, _ = pool.alloc_batch(seqs, [1] * len(seqs))
+        kn = normal_fp16((len(seqs), hkv, D), w.seed, 1000 + step, "cuda")
+        vn = normal_fp16((len(seqs), hkv, D), w.seed, 2000 + step, "cuda")
+        for i, s in enumerate(seqs):
+            rows[s] = (torch.cat([rows[s][0], kn[i:i + 1]]), torch.cat([rows[s][1], vn[i:i + 1]]))
+        mb = max(pool.seq_len(s)[1] for s in seqs)
+        tables, lens = pool.block_tables(seqs, mb)
+        grp = pool.shared_prefix_groups(tables, lens, 256)
+        assert sum(1 for x in grp[2] if x > 0) == groups
+        q = normal_fp16((len(seqs), hq, D), w.seed, 3000 + step, "cuda")
+        out = pool.decode_shared_prefix(0, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), grp,
+                                        k_new=kn, v_new=vn,
+                                        slot_mapping=torch.from_numpy(np.asarray(slots, np.int32)).cuda())
+    sample = list(range(0, len(seqs), len(seqs) // 10))[:10]
+    st = OracleKVStore(1, nb, hkv, bs, D)
+    for i in sample:
+        s = seqs[i]
+        n = int(lens[i])
+        pos = np.arange(n)
+        st.write(0, rows[s][0][:n].cpu().numpy(), rows[s][1][:n].cpu().numpy(), tables[i][pos // bs] * bs + pos % bs)
+    ref = attention.decode(st, 0, q.cpu().numpy()[sample], tables[sample], lens[sample])
+    assert_close(out[sample], ref, "fp16", "beam_k5 full size, sampled beams")
+    assert pool.device_status() == 0
