@@ -892,7 +892,9 @@ def main(argv=None):
                         else "fused shared-prefix decode (shared pass + fused write and private pass)"
                         if bench.sp_min else "fused (write_kv + paged decode) launch") + "; attention only"),
             **({"shared_prefix": bench.shared_prefix_info()} if bench.sp_min else {}),
-            "kv_loads": "ordinary (cached)" if pa.pa_pool_load_policy(bench.pool.handle)[1] else "nontemporal",
+            "kv_loads": ((("ordinary (cached)" if bench.sp_plan_log.flags & pa.PA_SHARED_REREAD else "nontemporal")
+                          + " (shared-prefix plan)") if bench.sp_min else
+                         "ordinary (cached)" if pa.pa_pool_load_policy(bench.pool.handle)[1] else "nontemporal"),
             **({"prefix_cache": bench.cache_info} if hasattr(bench, "cache_info") else {}),
             **({"beam": {**bench.w.extra, "search_steps": bench.beam_step,
                          "cow_copies": bench.pool.stats()["cow_copies"],

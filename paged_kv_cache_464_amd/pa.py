@@ -16,7 +16,8 @@ import torch
 from . import _lib
 from ._lib import (PA_DTYPE_FP16, PA_DTYPE_FP8_E4M3, PA_DTYPE_INT8, PA_ERR_BAD_SEQ, PA_ERR_NO_BLOCKS,  # noqa: F401
                    PA_DEV_BAD_BLOCK, PA_DEV_BAD_LEN, PA_DEV_BAD_ORDER, PA_DEV_BAD_SLOT,
-                   PA_LOADS_AUTO, PA_LOADS_CACHED, PA_LOADS_STREAMING, PA_NOALLOC_SCRATCH_BYTES)
+                   PA_LOADS_AUTO, PA_LOADS_CACHED, PA_LOADS_STREAMING, PA_NOALLOC_SCRATCH_BYTES,
+                   PA_SHARED_REREAD)
 
 
 class PAError(RuntimeError):
