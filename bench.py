@@ -375,11 +375,12 @@ class DecodeBench:
         h, st = self.pool.handle, self.stream
         if self.sp_min:
             groups = self.pool.shared_prefix_groups(tables, lens, self.sp_min)
-            need = pa.pa_decode_shared_prefix_workspace_bytes(h, self.S, self.hq, groups, self.mb_cap, self.sp_chunk)
+            need = pa.pa_decode_shared_prefix_workspace_bytes(h, self.S, self.hq, groups, self.mb_cap, self.sp_chunk,
+                                                              lens)
             if need > self.sp_workspace.numel():
                 self.sp_workspace = self.torch.empty(2 * need, dtype=self.torch.uint8, device=self.dev)
             plan = pa.pa_shared_prefix_plan(h, self.S, self.hq, self.mb_cap, groups, workspace=self.sp_workspace,
-                                            stream=st, chunk_tokens=self.sp_chunk)
+                                            stream=st, chunk_tokens=self.sp_chunk, lens=lens)
             self.sp_plan_log = plan.plan
             self.sp_groups_log.append(groups)
             for r in range(self.R):
@@ -445,6 +446,7 @@ class DecodeBench:
         pl = self.sp_plan_log
         return {"min_shared_tokens": self.sp_min, "groups_with_shared_pass": int(on.sum()),
                 "chunk_tokens": pl.chunk_tokens, "shared_items": pl.num_items, "partial_slots": pl.num_slots,
+                "private_pieces": pl.num_private,
                 "sequences_in_them": int(sizes[on].sum()),
                 "shared_tokens_per_member": int((shared[on] * sizes[on]).sum() * self.bs) // max(int(sizes[on].sum()), 1),
                 "host": "pa_shared_prefix_groups + pa_shared_prefix_plan once per step, inside the timed step"}

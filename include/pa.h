@@ -432,7 +432,12 @@ int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const vo
  * chunk_tokens, 16-byte aligned, owned by the caller, which keeps it alive
  * while the plan is used).  chunk_tokens: shared tokens per workgroup, a
  * multiple of 64, or 0 for the library's choice (about one shared
- * workgroup per CU, at least 256 tokens).  It fills *plan; bad group arrays
+ * workgroup per CU, at least 256 tokens).  lens: the host context lengths
+ * (int32 [num_seqs]) or NULL; with them, a group whose members all have at
+ * most 128 tokens past the shared run is folded: one workgroup per member
+ * run streams the shared tokens and then each member's own tokens, with no
+ * partials and no merge (beams of one search).  They only steer the plan;
+ * the launch reads the device lengths.  It fills *plan; bad group arrays
  * give PA_ERR_INVALID and upload nothing.  One plan serves every layer of a
  * step: the group list is uploaded once.
  *
@@ -455,7 +460,8 @@ int pa_shared_prefix_groups(const pa_pool* pool, const int32_t* tables, const in
 int pa_decode_shared_prefix_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                             const int32_t* members, const int32_t* group_start,
                                             const int32_t* shared_blocks, int32_t num_groups,
-                                            int32_t max_blocks, int32_t chunk_tokens, uint64_t* bytes_out);
+                                            int32_t max_blocks, int32_t chunk_tokens, const int32_t* lens,
+                                            uint64_t* bytes_out);
 #define PA_SHARED_REREAD 1 /* pa_shared_plan.flags: several items read one shared chunk */
 typedef struct pa_shared_plan {
   const pa_pool* pool;       /* the pool the plan was made for */
@@ -463,14 +469,15 @@ typedef struct pa_shared_plan {
   int32_t num_items;         /* shared work items (each a workgroup per KV head) */
   int32_t num_slots;         /* partial slots: shared chunks + 1 for every grouped sequence */
   int32_t chunk_tokens;      /* shared tokens per work item */
+  int32_t num_private;       /* sequences with a private piece (not in a folded group) */
   int32_t flags;             /* PA_SHARED_REREAD: several items read one chunk (ordinary loads) */
   void* workspace;           /* the caller's workspace, as passed to the plan */
   uint64_t workspace_bytes;
 } pa_shared_plan;
 int pa_shared_prefix_plan(pa_pool* pool, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                           const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
-                          int32_t num_groups, int32_t chunk_tokens, void* workspace, uint64_t workspace_bytes,
-                          void* stream, pa_shared_plan* plan);
+                          int32_t num_groups, int32_t chunk_tokens, const int32_t* lens, void* workspace,
+                          uint64_t workspace_bytes, void* stream, pa_shared_plan* plan);
 int pa_decode_shared_prefix(pa_pool* pool, int32_t layer, const pa_shared_plan* plan, const void* q,
                             const int32_t* block_tables, const int32_t* context_lens, const void* k_new,
                             const void* v_new, const int32_t* slot_mapping, float scale, void* out,

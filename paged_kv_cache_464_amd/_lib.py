@@ -58,7 +58,8 @@ class pa_profile(C.Structure):
 class pa_shared_plan(C.Structure):
     _fields_ = [("pool", C.c_void_p), ("num_seqs", C.c_int32), ("num_q_heads", C.c_int32),
                 ("max_blocks", C.c_int32), ("num_items", C.c_int32), ("num_slots", C.c_int32),
-                ("chunk_tokens", C.c_int32), ("flags", C.c_int32), ("workspace", C.c_void_p),
+                ("chunk_tokens", C.c_int32), ("num_private", C.c_int32), ("flags", C.c_int32),
+                ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_uint64)]
 
 
@@ -101,9 +102,9 @@ SIGNATURES = {
     "pa_order_longest_first": (C.c_int, [_PI32, _I32, _PI32]),
     "pa_shared_prefix_groups": (C.c_int, [_P, _PI32, _PI32, _I32, _I32, _I32, _PI32, _PI32, _PI32, _PI32]),
     "pa_decode_shared_prefix_workspace_bytes": (C.c_int, [_P, _I32, _I32, _PI32, _PI32, _PI32, _I32, _I32, _I32,
-                                                          C.POINTER(C.c_uint64)]),
-    "pa_shared_prefix_plan": (C.c_int, [_P, _I32, _I32, _I32, _PI32, _PI32, _PI32, _I32, _I32, _P, C.c_uint64,
-                                        _P, C.POINTER(pa_shared_plan)]),
+                                                          _PI32, C.POINTER(C.c_uint64)]),
+    "pa_shared_prefix_plan": (C.c_int, [_P, _I32, _I32, _I32, _PI32, _PI32, _PI32, _I32, _I32, _PI32, _P,
+                                        C.c_uint64, _P, C.POINTER(pa_shared_plan)]),
     "pa_decode_shared_prefix": (C.c_int, [_P, _I32, C.POINTER(pa_shared_plan), _P, _P, _P, _P, _P, _P,
                                           C.c_float, _P, _P]),
     "pa_stream_read": (C.c_int, [_P, C.c_uint64, _P, _P]),

@@ -1024,7 +1024,8 @@ namespace {
 
 // Workspace of a shared-prefix decode: the pieces' partials (m, l, o of
 // every slot and query head), then the uploaded int32 tail: starts[S],
-// slot0[S], members[S] and the shared items (4 ints each).
+// slot0[S], members[S], the sequences with private pieces (S entries, the
+// first n_private used) and the shared items (4 ints each).
 struct SharedLayout {
   uint64_t off_l, off_o, off_c, bytes;
 };
@@ -1036,13 +1037,20 @@ SharedLayout shared_layout(const pa_pool* p, int32_t num_seqs, int32_t num_q_hea
   L.off_l = align_up(std::max<uint64_t>(rows, 1) * 4, 256);
   L.off_o = L.off_l + align_up(std::max<uint64_t>(rows, 1) * 4, 256);
   L.off_c = L.off_o + align_up(std::max<uint64_t>(rows, 1) * p->head_dim * 4, 256);
-  L.bytes = L.off_c + align_up((3ull * num_seqs + 4ull * n_items) * 4, 256);
+  L.bytes = L.off_c + align_up((4ull * num_seqs + 4ull * n_items) * 4, 256);
   return L;
 }
 
+// Groups whose members have at most this many tokens of their own past the
+// shared run are folded: one workgroup per member run streams the shared
+// tokens and then each member's own tokens (one wave per member), so those
+// members need neither a private piece nor a merge.  Measured on MI355X with
+// beam search (32 groups of 5 beams, 2040 shared tokens, 4 to 70 own).
+constexpr int64_t kFoldTokens = 128;
+
 struct SharedTail {
-  std::vector<int32_t> ints;  // starts, slot0, members, items
-  int64_t n_items = 0, n_slots = 0;
+  std::vector<int32_t> ints;  // starts, slot0, members, private sequences, items
+  int64_t n_items = 0, n_slots = 0, n_private = 0;
   int32_t chunk = 0;
   bool reread = false;  // some chunk is read by several items (a group of more than 32 / G members)
 };
@@ -1051,7 +1059,7 @@ struct SharedTail {
 // and builds the int32 tail.  Returns PA_OK or the status of fail().
 int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                        const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
-                       int32_t num_groups, int32_t chunk_tokens, SharedTail* out) {
+                       int32_t num_groups, int32_t chunk_tokens, const int32_t* lens, SharedTail* out) {
   if (num_groups < 0 || (num_seqs > 0 && (!members || !group_start || !shared_blocks)))
     return fail(PA_ERR_INVALID, "members, group_start and shared_blocks are required");
   if (num_seqs > 0 && (group_start[0] != 0 || group_start[num_groups] != num_seqs))
@@ -1068,7 +1076,9 @@ int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, 
     if (m < 0 || m >= num_seqs || seen[m]) return fail(PA_ERR_INVALID, "members must be a permutation");
     seen[m] = 1;
   }
-  // Shared runs, and the work items of one chunk per group.
+  // Shared runs, which groups fold (with the host lengths), and the work
+  // items of one chunk per unfolded group.
+  std::vector<char> fold(static_cast<size_t>(num_groups), 0);
   int64_t base_items = 0, max_ts = 0;
   for (int32_t g = 0; g < num_groups; ++g) {
     const int32_t a = group_start[g], b = group_start[g + 1];
@@ -1078,6 +1088,13 @@ int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, 
       return fail(PA_ERR_INVALID, "shared_blocks[%d] = %d: not a multiple of 16 tokens inside the table", g,
                   shared_blocks[g]);
     if (ts == 0) continue;
+    bool f = lens != nullptr;
+    for (int32_t i = a; f && i < b; ++i) {
+      const int64_t own = static_cast<int64_t>(lens[members[i]]) - ts;
+      f = own >= 1 && own <= kFoldTokens;
+    }
+    fold[g] = f;
+    if (f) continue;
     base_items += (b - a + per_item - 1) / per_item;
     max_ts = std::max(max_ts, ts);
   }
@@ -1100,18 +1117,35 @@ int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, 
   if (chunk > 0x7FFFFFFF) return fail(PA_ERR_INVALID, "chunk_tokens out of range");
   out->chunk = static_cast<int32_t>(chunk);
   std::vector<int32_t>& t = out->ints;
-  t.assign(3 * S, 0);
+  t.assign(4 * S, 0);
   int32_t* starts = t.data();
   int32_t* slot0 = starts + S;
   int32_t* mem_out = slot0 + S;
+  int32_t* priv = mem_out + S;
   for (size_t i = 0; i < S; ++i) slot0[i] = -1;
   for (int32_t i = 0; i < num_seqs; ++i) mem_out[i] = members[i];
-  int64_t slots = 0, n_items = 0;
+  int64_t slots = 0, n_items = 0, n_priv = 0;
   std::vector<int32_t> items;
   for (int32_t g = 0; g < num_groups; ++g) {
     const int32_t a = group_start[g], b = group_start[g + 1];
     const int64_t ts = static_cast<int64_t>(shared_blocks[g]) * p->block_size;
-    if (ts == 0) continue;
+    if (ts == 0) {
+      for (int32_t i = a; i < b; ++i) priv[n_priv++] = members[i];
+      continue;
+    }
+    if (b - a > per_item) out->reread = true;
+    if (fold[g]) {
+      for (int32_t i = a; i < b; ++i) starts[members[i]] = static_cast<int32_t>(ts);
+      for (int32_t i = a; i < b; i += per_item) {
+        items.push_back(i);
+        items.push_back(std::min<int32_t>(per_item, b - i));
+        items.push_back(static_cast<int32_t>(ts));
+        items.push_back(-1);
+        ++n_items;
+      }
+      continue;
+    }
+    for (int32_t i = a; i < b; ++i) priv[n_priv++] = members[i];
     const int64_t chunks = (ts + chunk - 1) / chunk;
     for (int32_t i = a; i < b; ++i) {
       starts[members[i]] = static_cast<int32_t>(ts);
@@ -1119,7 +1153,6 @@ int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, 
       slots += chunks + 1;
       if (slots > 0x7FFFFFFF / std::max(num_q_heads, 1)) return fail(PA_ERR_INVALID, "too many partial slots");
     }
-    if (b - a > per_item) out->reread = true;
     for (int64_t c = 0; c < chunks; ++c) {
       for (int32_t i = a; i < b; i += per_item) {
         items.push_back(i);
@@ -1134,6 +1167,7 @@ int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, 
   t.insert(t.end(), items.begin(), items.end());
   out->n_items = n_items;
   out->n_slots = slots;
+  out->n_private = n_priv;
   return PA_OK;
 }
 
@@ -1198,14 +1232,15 @@ int pa_shared_prefix_groups(const pa_pool* p, const int32_t* tables, const int32
 int pa_decode_shared_prefix_workspace_bytes(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads,
                                             const int32_t* members, const int32_t* group_start,
                                             const int32_t* shared_blocks, int32_t num_groups,
-                                            int32_t max_blocks, int32_t chunk_tokens, uint64_t* bytes_out) {
+                                            int32_t max_blocks, int32_t chunk_tokens, const int32_t* lens,
+                                            uint64_t* bytes_out) {
   if (!p || !bytes_out || num_seqs < 0) return fail(PA_ERR_INVALID, "bad arguments");
   if (num_q_heads < 1 || num_q_heads % p->kv_heads != 0 || num_q_heads / p->kv_heads > 32)
     return fail(PA_ERR_INVALID, "num_q_heads %d must be a multiple of kv_heads %d with a group of at most 32",
                 num_q_heads, p->kv_heads);
   SharedTail t;
   int rc = shared_groups_tail(p, num_seqs, num_q_heads, max_blocks, members, group_start, shared_blocks,
-                              num_groups, chunk_tokens, &t);
+                              num_groups, chunk_tokens, lens, &t);
   if (rc) return rc;
   *bytes_out = num_seqs == 0 ? 0 : shared_layout(p, num_seqs, num_q_heads, t.n_items, t.n_slots).bytes;
   return PA_OK;
@@ -1213,8 +1248,8 @@ int pa_decode_shared_prefix_workspace_bytes(const pa_pool* p, int32_t num_seqs, 
 
 int pa_shared_prefix_plan(pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                           const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
-                          int32_t num_groups, int32_t chunk_tokens, void* workspace, uint64_t workspace_bytes,
-                          void* stream, pa_shared_plan* plan) {
+                          int32_t num_groups, int32_t chunk_tokens, const int32_t* lens, void* workspace,
+                          uint64_t workspace_bytes, void* stream, pa_shared_plan* plan) {
   int rc = check_bound(p);
   if (rc) return rc;
   if (!plan || num_seqs < 0) return fail(PA_ERR_INVALID, "bad arguments to pa_shared_prefix_plan");
@@ -1226,7 +1261,7 @@ int pa_shared_prefix_plan(pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int
     return fail(PA_ERR_INVALID, "max_blocks %d out of range", max_blocks);
   SharedTail t;
   if ((rc = shared_groups_tail(p, num_seqs, num_q_heads, max_blocks, members, group_start, shared_blocks,
-                               num_groups, chunk_tokens, &t)))
+                               num_groups, chunk_tokens, lens, &t)))
     return rc;
   if (num_seqs > 0) {
     const SharedLayout L = shared_layout(p, num_seqs, num_q_heads, t.n_items, t.n_slots);
@@ -1242,6 +1277,7 @@ int pa_shared_prefix_plan(pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int
   plan->max_blocks = max_blocks;
   plan->num_items = static_cast<int32_t>(t.n_items);
   plan->num_slots = static_cast<int32_t>(t.n_slots);
+  plan->num_private = static_cast<int32_t>(t.n_private);
   plan->chunk_tokens = t.chunk;
   plan->flags = t.reread ? PA_SHARED_REREAD : 0;
   plan->workspace = workspace;
@@ -1265,7 +1301,8 @@ int pa_decode_shared_prefix(pa_pool* p, int32_t layer, const pa_shared_plan* pla
     return fail(PA_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
   if (num_seqs == 0) return PA_OK;
   if (!out || misaligned(out, 8)) return fail(PA_ERR_INVALID, "out must be non-NULL and 8-byte aligned");
-  if (plan->num_items < 0 || plan->num_slots < 0 || plan->chunk_tokens < 64 || plan->chunk_tokens % 64 != 0)
+  if (plan->num_items < 0 || plan->num_slots < 0 || plan->chunk_tokens < 64 || plan->chunk_tokens % 64 != 0 ||
+      plan->num_private < 0 || plan->num_private > num_seqs)
     return fail(PA_ERR_INVALID, "the plan is not one pa_shared_prefix_plan made");
   const SharedLayout L = shared_layout(p, num_seqs, num_q_heads, plan->num_items, plan->num_slots);
   if (!plan->workspace || plan->workspace_bytes < L.bytes)
@@ -1299,10 +1336,12 @@ int pa_decode_shared_prefix(pa_pool* p, int32_t layer, const pa_shared_plan* pla
   d.starts = ints;
   d.slot0 = d.starts + S;
   d.members = d.slot0 + S;
-  d.work = d.members + S;
+  d.order = d.members + S;  // the sequences with private pieces
+  d.work = d.order + S;
   d.num_items = plan->num_items;
   d.sp_chunk = plan->chunk_tokens;
   d.sp_slots = plan->num_slots;
+  d.sp_private = plan->num_private;
   if (fused) {
     d.k_new = k_new;
     d.v_new = v_new;

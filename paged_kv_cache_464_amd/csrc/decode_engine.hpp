@@ -1393,6 +1393,92 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
   }
 }
 
+// Partials of a folded item's shared tokens, per (member, head) column.
+template <int D>
+struct FoldLds {
+  float m[32];
+  float l[32];
+  float o[32][D + 4];  // rows padded by four floats
+};
+
+// Private tokens of one member of a folded shared-prefix item, by one wave:
+// tokens ts .. T - 1 of sequence `seq` (with the fused write of its new token
+// when p.new_slots is set), then the log-sum-exp merge with the item's shared
+// partials of the member's columns col0 .. col0 + G - 1 (in `fl`) into the
+// fp16 output.  A context at or below ts (a contract violation) is flagged
+// and the output is the shared tokens' alone.
+template <int D, int KIND, int BS, int NTP, bool FUSE, bool CACHED>
+__device__ inline void folded_private(const PoolGeom& g, const DecodeLaunch& p, int seq, int kvh, int group,
+                                      int ts, int col0, const FoldLds<D>& fl, uint8_t* lds_new, int lane) {
+  constexpr int ELEM = kind_bytes(KIND);
+  using Dec = WaveDecoder<D, KIND, BS, NTP, FUSE, false, CACHED>;
+  Dec dec;
+  if constexpr (FUSE && ELEM == 1) dec.lds_new = lds_new;
+  dec.bind(g, p, seq, kvh, lane);
+  const int T = context_len<BS>(g, p, seq, lane == 0);
+  dec.T = T;
+  dec.load_q(g, p, seq, kvh, group);
+  dec.reset();
+  const bool own = T > ts;  // this wave runs every private step, so it holds token T - 1
+  if (!own && lane == 0) atomicOr(g.status, kDevBadLen);
+  if constexpr (FUSE) {
+    if (own && p.new_slots) {
+      dec.new_slot = ((const ConstI32*)p.new_slots)[seq];
+      dec.new_blk = dec.trow[(T - 1) / BS];
+      const int64_t off = (static_cast<int64_t>(seq) * g.kv_heads + kvh) * D;
+      dec.knew = static_cast<const _Float16*>(p.k_new) + off;
+      dec.vnew = static_cast<const _Float16*>(p.v_new) + off;
+      if constexpr (ELEM == 1) {
+        const int lhs = g.layers * g.kv_heads;
+        const int lh = p.layer * g.kv_heads + kvh;
+        dec.new_kinv = g.scales[2 * lhs + lh];
+        dec.new_vinv = g.scales[3 * lhs + lh];
+        if constexpr (KIND == kI8) {
+          dec.new_kz = g.scales[4 * lhs + lh];
+          dec.new_vz = g.scales[5 * lhs + lh];
+        }
+      }
+      dec.load_new();
+    }
+  }
+  if (own) {
+    const int n = (T - ts + 15) >> 4;
+    const int last_tok = ((T - 1) >> 4) << 4;
+    auto real = [&](int j) { return j < n; };
+    auto tok_of = [&](int j) -> int { return j < n ? ts + 16 * j : last_tok; };
+    FirstIds first;
+#pragma unroll
+    for (int j = 0; j < 2 * kDepth - 1; ++j) dec.fetch_ids(tok_of(j), first.lo[j], first.hi[j]);
+    stream_steps(dec, n, tok_of, real, first, [](int) {});
+    if constexpr (FUSE) {
+      if (dec.knew && !dec.owns_new && dec.new_slot >= 0 && lane == 0) atomicOr(g.status, kDevBadSlot);
+    }
+  }
+  if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
+  const int gq = dec.gq;
+#pragma unroll
+  for (int nt = 0; nt < NTP; ++nt) {
+    const float L = sum_across_rows(dec.l_part[nt]);
+    const int c = nt * 16 + dec.n;
+    if (c >= group) continue;
+    const int cs = col0 + c;
+    const float m_s = fl.m[cs], l_s = fl.l[cs];
+    const float r = dec.m_run[nt];  // the reference of the accumulators (-inf: nothing attended)
+    const float X = fmaxf(r, m_s);
+    const float a = (r == -__builtin_inff()) ? 0.0f : exp2f(r - X);
+    const float b = l_s * exp2f(m_s - X);
+    const float inv = 1.0f / (L * a + b);
+    _Float16* po = static_cast<_Float16*>(p.out) +
+                   (static_cast<int64_t>(seq) * p.num_q_heads + kvh * group + c) * D + 4 * gq;
+#pragma unroll
+    for (int rr = 0; rr < D / 16; ++rr) {
+      const f32x4 os = *reinterpret_cast<const f32x4*>(&fl.o[cs][rr * 16 + 4 * gq]);
+      const f32x4 v = (dec.oacc[nt][rr] * (a * dec.out_mul) + os * b) * inv;
+      *reinterpret_cast<f16x4*>(po + rr * 16) = f16x4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    }
+  }
+}
+
 // Shared-prefix decode: one launch whose first workgroups read the blocks
 // that groups of sequences share (beams of one search, requests on one cached
 // system prompt: youngju.dev "KV cache and paged attention", section "prefix
@@ -1410,9 +1496,9 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
 // m), o = sum 2^(s - m) v / l (times the V scale) in slot slot0[member] + c.
 // The blocks are read through the first member's table, with ordinary loads
 // where several items of a group re-read them, nontemporal ones otherwise.
-template <int D, int KIND, int BS, bool CACHED>
+template <int D, int KIND, int BS, int NTP, bool FUSE, bool CACHED>
 __device__ __forceinline__ void shared_body(const PoolGeom& g, const DecodeLaunch& p, uint32_t bid,
-                                            MergeLds<2, D>& sm) {
+                                            MergeLds<2, D>& sm, FoldLds<D>& fl, uint8_t* lds_new) {
   constexpr int NT = 2;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1421,8 +1507,9 @@ __device__ __forceinline__ void shared_body(const PoolGeom& g, const DecodeLaunc
   const int kvh = static_cast<int>(bid % g.kv_heads);
   const ConstI32* wk = (const ConstI32*)(p.work + 4 * static_cast<int64_t>(item));
   const int m0 = wk[0], nm = wk[1], ts = wk[2], c = wk[3];
+  const bool folded = c < 0;  // the whole shared run, then each member's own tokens in this workgroup
   const int chunk = p.sp_chunk;
-  const int parts = (ts + chunk - 1) / chunk + 1;
+  const int parts = folded ? 0 : (ts + chunk - 1) / chunk + 1;
   // The host checks the items when it uploads them; an item that does not
   // fit this launch (a member run outside the batch, more than 32 columns, a
   // member outside the batch or without room for its slots, a shared length
@@ -1430,22 +1517,22 @@ __device__ __forceinline__ void shared_body(const PoolGeom& g, const DecodeLaunc
   // and its rows left alone.  Every wave reaches the same verdict, so the
   // workgroup leaves together.
   if (m0 < 0 || nm < 1 || nm * group > 32 || m0 > p.num_seqs - nm || ts < 16 || (ts & 15) != 0 ||
-      static_cast<int64_t>(ts) > static_cast<int64_t>(p.max_blocks) * BS || c < 0 ||
+      static_cast<int64_t>(ts) > static_cast<int64_t>(p.max_blocks) * BS || c < -1 ||
       static_cast<int64_t>(c) * chunk >= ts) {
     if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
     return;
   }
   const int32_t* mem = p.members + m0;
   const int mine = lane < nm ? ((const ConstI32*)mem)[lane] : 0;
-  const int my_slot0 = lane < nm ? ((const ConstI32*)p.slot0)[mine] : 0;
+  const int my_slot0 = (lane < nm && !folded) ? ((const ConstI32*)p.slot0)[mine] : 0;
   if (__ballot(static_cast<uint32_t>(mine) >= static_cast<uint32_t>(p.num_seqs) || my_slot0 < 0 ||
                my_slot0 > p.sp_slots - parts) != 0) {
     if (threadIdx.x == 0) atomicOr(g.status, kDevBadLen);
     return;
   }
   const int seq0 = __builtin_amdgcn_readfirstlane(mine);
-  const int t0 = c * chunk;
-  const int t1 = (ts - t0 < chunk) ? ts : t0 + chunk;
+  const int t0 = folded ? 0 : c * chunk;
+  const int t1 = (folded || ts - t0 < chunk) ? ts : t0 + chunk;
   WaveDecoder<D, KIND, BS, NT, false, true, CACHED> dec;
   dec.bind(g, p, seq0, kvh, lane);
   const int ncols = nm * group;
@@ -1467,6 +1554,23 @@ __device__ __forceinline__ void shared_body(const PoolGeom& g, const DecodeLaunc
   dec.finish_l();
   if (dec.bad && lane == 0) atomicOr(g.status, dec.bad);
   const int gq = dec.gq;
+  if (folded) {
+    // Shared partials into LDS, then each wave takes members w, w + 4, ...
+    merge_waves(dec, sm, w, ncols, [&](int, int col, f32x4* acc, float M, float L, float Mt) {
+      const float inv_l = dec.out_mul / L;
+#pragma unroll
+      for (int rr = 0; rr < D / 16; ++rr) *reinterpret_cast<f32x4*>(&fl.o[col][rr * 16 + 4 * gq]) = acc[rr] * inv_l;
+      if (gq == 0) {
+        fl.m[col] = Mt;
+        fl.l[col] = (M == Mt) ? L : L * exp2f(M - Mt);
+      }
+    });
+    __syncthreads();
+    for (int mi = w; mi < nm; mi += kWaves)
+      folded_private<D, KIND, BS, NTP, FUSE, CACHED>(g, p, ((const ConstI32*)mem)[mi], kvh, group, ts, mi * group,
+                                                     fl, lds_new, lane);
+    return;
+  }
   merge_waves(dec, sm, w, ncols, [&](int, int col, f32x4* acc, float M, float L, float Mt) {
     const int seq = mem[col / group];
     const int64_t idx = (static_cast<int64_t>(((const ConstI32*)p.slot0)[seq]) + c) * p.num_q_heads +
@@ -1483,9 +1587,10 @@ __device__ __forceinline__ void shared_body(const PoolGeom& g, const DecodeLaunc
 }
 
 // The shared-prefix pieces: workgroups 0 .. items * Hkv - 1 are shared
-// pieces, the rest (sequence, KV head) private pieces (decode_body in mode
-// kPrivate: tokens starts[i] .. T_i - 1 into the sequence's last slot, or the
-// whole context straight into `out` for a sequence in no group).  One LDS
+// pieces, the rest (sequence, KV head) private pieces of the sequences
+// listed in `order` (decode_body in mode kPrivate: tokens starts[i] .. T_i -
+// 1 into the sequence's last slot, or the whole context straight into `out`
+// for a sequence in no group; a folded item's members have none).  One LDS
 // buffer serves either body.  The pieces are independent, so the private
 // ones run beside the long shared ones.
 // Merge launch: one workgroup per (sequence, KV head); sequences in no
@@ -1509,7 +1614,10 @@ void shared_prefix_kernel(PoolGeom g, DecodeLaunch p) {
   __shared__ MergeLds<2, D> sm;
   const uint32_t n_shared = static_cast<uint32_t>(p.num_items) * g.kv_heads;
   if (blockIdx.x < n_shared) {
-    shared_body<D, KIND, BS, CACHED>(g, p, blockIdx.x, sm);
+    __shared__ FoldLds<D> fl;
+    __shared__ __attribute__((aligned(16))) uint8_t new_codes[kWaves][2 * D];
+    shared_body<D, KIND, BS, NT, FUSE, CACHED>(g, p, blockIdx.x, sm, fl,
+                                               new_codes[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)]);
   } else {
     decode_body<D, KIND, BS, NT, kPrivate, FUSE, CACHED>(g, p, blockIdx.x - n_shared,
                                                           *reinterpret_cast<MergeLds<NT, D>*>(&sm));
@@ -1738,9 +1846,9 @@ hipError_t launch_multi_token_kd(const PoolGeom& g, const DecodeLaunch& d, const
 template <int D, int KIND, int BS, bool FUSE, bool CACHED>
 hipError_t launch_shared_prefix_f(const PoolGeom& g, const DecodeLaunch& d, int nt, hipStream_t s, hipEvent_t t0,
                                   hipEvent_t t1) {
-  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(d.num_items) + d.num_seqs) * g.kv_heads));
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(d.num_items) + d.sp_private) * g.kv_heads));
   const dim3 block(kWaves * 64);
-  const bool merge = d.num_items > 0;
+  const bool merge = d.sp_slots > 0;  // some group's pieces wrote partials
   hipError_t e =
       nt == 1 ? launch_kernel(shared_prefix_kernel<D, KIND, BS, 1, FUSE, CACHED>, grid, block, s, t0,
                               merge ? nullptr : t1, g, d)

@@ -59,9 +59,10 @@ hipError_t shared_prefix_for_dim(const PoolGeom& g, const DecodeLaunch& d, int n
 
 hipError_t launch_shared_prefix(const PoolGeom& g, const DecodeLaunch& d, hipStream_t s, hipEvent_t t0,
                                 hipEvent_t t1) {
-  const int64_t wgs = (static_cast<int64_t>(d.num_items) + d.num_seqs) * g.kv_heads;
+  const int64_t wgs = (static_cast<int64_t>(d.num_items) + d.sp_private) * g.kv_heads;
   if (wgs <= 0) return hipSuccess;
-  if (!d.starts || !d.slot0 || (d.num_items > 0 && (!d.work || !d.members)) ||
+  if (!d.starts || !d.slot0 || (d.sp_private > 0 && !d.order) || d.sp_private < 0 ||
+      d.sp_private > d.num_seqs || (d.num_items > 0 && (!d.work || !d.members)) ||
       d.num_items < 0 || wgs > 0x7FFFFFFF || d.sp_chunk < 64 || d.sp_chunk % 64 != 0)
     return hipErrorInvalidValue;
   const int nt = d.num_q_heads / g.kv_heads > 16 ? 2 : 1;

@@ -78,11 +78,15 @@ struct DecodeLaunch {
   // slot0[i] + 1, ... of part_m / part_l / part_o ([slot][Hq] / [slot][Hq] /
   // [slot][Hq][D], sp_slots slots), which a second launch merges into `out`.
   // A sequence in no group (starts[i] = 0) writes `out` directly.
+  // Folded items (chunk -1) take a group's whole shared run and then each
+  // member's own tokens in the same workgroup, writing `out` directly; the
+  // private pieces are the sequences listed in `order` (sp_private of them).
   const int32_t* members;
   const int32_t* starts;
   const int32_t* slot0;
   int sp_chunk;
   int sp_slots;
+  int sp_private;
 };
 
 // t0/t1: optional events stamped at the kernel's start and end (null: untimed).

@@ -436,11 +436,23 @@ def _groups_args(groups):
     return (members, gstart, shared), ip(members), ip(gstart), ip(shared), len(shared)
 
 
-def pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, groups, max_blocks, chunk_tokens=0):
+def _lens_arg(lens, num_seqs):
+    if lens is None:
+        return None, None
+    arr, ptr = _i32_host(lens)
+    if len(arr) != num_seqs:
+        raise ValueError("lens must hold one length per sequence")
+    return arr, ptr
+
+
+def pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, groups, max_blocks, chunk_tokens=0,
+                                            lens=None):
     keep, mp, gp, sp, ng = _groups_args(groups)
+    la, lp = _lens_arg(lens, num_seqs)
     b = C.c_uint64()
     _check(_L().pa_decode_shared_prefix_workspace_bytes(C.c_void_p(h), int(num_seqs), int(num_q_heads), mp, gp,
-                                                        sp, ng, int(max_blocks), int(chunk_tokens), C.byref(b)))
+                                                        sp, ng, int(max_blocks), int(chunk_tokens), lp,
+                                                        C.byref(b)))
     return b.value
 
 
@@ -453,9 +465,13 @@ class SharedPlan:
 
 
 def pa_shared_prefix_plan(h, num_seqs, num_q_heads, max_blocks, groups, workspace=None, stream=None,
-                          device="cuda", chunk_tokens=0):
+                          device="cuda", chunk_tokens=0, lens=None):
+    """Checks and uploads the groups (see pa_decode_shared_prefix).  ``lens``:
+    host context lengths, which let the plan fold groups whose members have
+    few tokens of their own (None: no folding)."""
     keep, mp, gp, sp, ng = _groups_args(groups)
-    need = pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, keep, max_blocks, chunk_tokens)
+    la, lp = _lens_arg(lens, num_seqs)
+    need = pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, keep, max_blocks, chunk_tokens, la)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     nbytes = workspace.numel() * workspace.element_size()
@@ -463,22 +479,23 @@ def pa_shared_prefix_plan(h, num_seqs, num_q_heads, max_blocks, groups, workspac
         raise ValueError(f"workspace needs {need} bytes")
     plan = _lib.pa_shared_plan()
     _check(_L().pa_shared_prefix_plan(C.c_void_p(h), int(num_seqs), int(num_q_heads), int(max_blocks), mp, gp,
-                                      sp, ng, int(chunk_tokens), C.c_void_p(workspace.data_ptr()), nbytes,
+                                      sp, ng, int(chunk_tokens), lp, C.c_void_p(workspace.data_ptr()), nbytes,
                                       _stream(stream), C.byref(plan)))
     return SharedPlan(plan, workspace, keep)
 
 
 def pa_decode_shared_prefix(h, layer, q, block_tables, context_lens, groups, out=None, scale=None,
                             workspace=None, stream=None, k_new=None, v_new=None, slot_mapping=None,
-                            chunk_tokens=0):
+                            chunk_tokens=0, lens=None):
     """Decode where groups of sequences share leading blocks.  ``groups`` is a
     SharedPlan (pa_shared_prefix_plan) or the (members, group_start,
     shared_blocks) arrays of pa_shared_prefix_groups, planned here on the
-    call's stream.  With k_new, v_new and slot_mapping, the new tokens are
-    scattered as in pa_write_kv_decode."""
+    call's stream (``lens``: host context lengths for the plan's folding).
+    With k_new, v_new and slot_mapping, the new tokens are scattered as in
+    pa_write_kv_decode."""
     info, s, hq, mb, qp, tp, lp = _decode_args(h, q, block_tables, context_lens)
     if not isinstance(groups, SharedPlan):
-        groups = pa_shared_prefix_plan(h, s, hq, mb, groups, workspace, stream, q.device, chunk_tokens)
+        groups = pa_shared_prefix_plan(h, s, hq, mb, groups, workspace, stream, q.device, chunk_tokens, lens)
     p = groups.plan
     if (p.num_seqs, p.num_q_heads, p.max_blocks) != (s, hq, mb):
         raise ValueError(f"the plan is for {p.num_seqs} sequences, {p.num_q_heads} query heads and tables "

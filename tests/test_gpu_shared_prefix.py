@@ -151,11 +151,19 @@ def test_shared_prefix_decode_matches_the_oracle(case):
     st = oracle_store(t)
     q = normal_fp16((len(t.batch), hq, D), 464_200, 3, "cuda")
     ref = attention.decode(st, 0, q.cpu().numpy(), t.tables_np, t.lens_np)
-    for min_tokens, chunk in ((256, 0), (16, 0), (256, 64), (16, 192)):
+    # With the host lengths the plan folds the groups whose members have at
+    # most 128 tokens of their own (the 5-member group, the 2-member groups
+    # when their tails are short) and chunks the others, in one launch.
+    for min_tokens, chunk, fold in ((256, 0, False), (16, 0, False), (256, 64, False), (16, 192, False),
+                                    (256, 0, True), (16, 128, True)):
         g = t.pool.shared_prefix_groups(t.tables_np, t.lens_np, min_tokens)
         _check_groups_cover(t, g, 3 if min_tokens == 256 else 3 + (bs <= 16))
-        out = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, g, chunk_tokens=chunk)
-        assert_close(out, ref, dtype, f"shared prefix min={min_tokens} chunk={chunk}")
+        lens = t.lens_np if fold else None
+        plan = t.pool.shared_prefix_plan(len(t.batch), hq, t.mb, g, chunk_tokens=chunk, lens=lens)
+        if fold:
+            assert plan.plan.num_private < len(t.batch)  # the 5-member group at least is folded
+        out = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, plan)
+        assert_close(out, ref, dtype, f"shared prefix min={min_tokens} chunk={chunk} fold={fold}")
         assert t.pool.device_status() == 0
     # Every group a singleton: the private pass alone over every token.
     n = len(t.batch)
@@ -165,13 +173,15 @@ def test_shared_prefix_decode_matches_the_oracle(case):
     assert t.pool.device_status() == 0
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("dtype,bs", [("fp16", 16), ("fp8", 8), ("int8", 32)])
-def test_fused_shared_prefix_step_writes_like_write_kv_decode(dtype, bs):
+def test_fused_shared_prefix_step_writes_like_write_kv_decode(dtype, bs, fold):
     """One generation step of every member: the new token appended (slots
-    from the allocator), written and attended in the fused call; the pool's
-    bytes equal those pa_write_kv_decode leaves, and both outputs match the
-    oracle."""
-    say("fused shared prefix", dtype, bs)
+    from the allocator), written and attended in the fused call (fold: by
+    the folded items, whose waves take each member's own tokens; else by the
+    private pieces); the pool's bytes equal those pa_write_kv_decode leaves,
+    and both outputs match the oracle."""
+    say("fused shared prefix", dtype, bs, "folded" if fold else "pieces")
     hq, hkv, D = 32, 8, 128
     rng = np.random.default_rng(464_201 + bs)
     groups = [(513, [int(x) for x in rng.integers(1, 60, 6)]), (777, [int(x) for x in rng.integers(1, 90, 9)])]
@@ -191,8 +201,10 @@ def test_fused_shared_prefix_step_writes_like_write_kv_decode(dtype, bs):
     g = t.pool.shared_prefix_groups(t.tables_np, t.lens_np, 256)
     assert sum(1 for k in g[2] if k > 0) == 2
     before = t.pool.pool_bytes().clone()
-    out_sp = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, g, k_new=kn, v_new=vn, slot_mapping=sl,
-                                         chunk_tokens=128)
+    plan = t.pool.shared_prefix_plan(len(t.batch), hq, t.mb, g, chunk_tokens=128,
+                                     lens=t.lens_np if fold else None)
+    assert plan.plan.num_private == (2 if fold else len(t.batch))  # the two singletons
+    out_sp = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, plan, k_new=kn, v_new=vn, slot_mapping=sl)
     after_sp = t.pool.pool_bytes().clone()
     t.pool.pool_bytes().copy_(before)
     out_wd = t.pool.write_kv_decode(0, kn, vn, sl, q, t.tables, t.lens)
@@ -289,8 +301,8 @@ def test_beam_k5_full_size_in_the_benchmark_configuration():
     2040-token prompt, 16-token blocks, 32 query / 8 KV heads; each search
     step re-selects the survivors (forks, frees), appends one token per beam
     in one batch (copy-on-write copies enqueued), plans the groups found on
-    the host tables and runs the fused shared-prefix call with the library's
-    own chunk choice.  After the last step, 10 sampled beams (every query
+    the host tables with the host lengths (every group folds: the beams have
+    a few tokens of their own) and runs the fused shared-prefix call.  After the last step, 10 sampled beams (every query
     head) match the oracle, whose store holds each sampled beam's whole
     context at the slots its table gives."""
     from workloads import beam_parents, workload
@@ -343,7 +355,9 @@ def test_beam_k5_full_size_in_the_benchmark_configuration():
         grp = pool.shared_prefix_groups(tables, lens, 256)
         assert sum(1 for x in grp[2] if x > 0) == groups
         q = normal_fp16((len(seqs), hq, D), w.seed, 3000 + step, "cuda")
-        out = pool.decode_shared_prefix(0, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), grp,
+        plan = pool.shared_prefix_plan(len(seqs), hq, mb, grp, lens=lens)  # as the benchmark plans it
+        assert plan.plan.num_private == 0 and plan.plan.num_slots == 0  # every group folded
+        out = pool.decode_shared_prefix(0, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), plan,
                                         k_new=kn, v_new=vn,
                                         slot_mapping=torch.from_numpy(np.asarray(slots, np.int32)).cuda())
     sample = list(range(0, len(seqs), len(seqs) // 10))[:10]

@@ -90,6 +90,12 @@ def test_beam_and_prompt_groups(bs):
     for c in (-64, 100, 32):
         with pytest.raises(pa.PAError):
             pa.pa_decode_shared_prefix_workspace_bytes(h, n, 8, groups, mb, c)
+    # With the host lengths the beam groups (at most 71 tokens of their own
+    # past the shared blocks) fold: no partial slots for their members.
+    folded = pa.pa_decode_shared_prefix_workspace_bytes(h, n, 8, groups, mb, 0, lens)
+    assert 0 < folded < sizes[0]
+    with pytest.raises(ValueError):
+        pa.pa_decode_shared_prefix_workspace_bytes(h, n, 8, groups, mb, 0, lens[:-1])
     pa.pa_pool_destroy(h)
 
 
