@@ -16,9 +16,10 @@ in HBM.
 The other workloads (``tiny``, ``cb_prefix``, ``long_ctx``,
 ``fp8_{gqa,mqa}_bs{8,16,32}``, ``int8_{gqa,mqa}_bs16``, ``prefix_cache``,
 ``beam_k5``) time one pool layer R times per step ("1 layer
-timed xR").  ``beam_k5`` decodes with the shared-prefix pair of launches
-(``pa_decode_shared_prefix``: the beams' common prompt read once per beam
-group, then each beam's own tokens, groups planned once per step);
+timed xR").  ``beam_k5`` decodes with the shared-prefix launch
+(``pa_decode_shared_prefix``: groups found and planned once per step with the
+host lengths, every beam group folded, so one workgroup per group and KV
+head reads the common prompt once and then each beam's own tokens);
 ``--shared-prefix-min 0`` times the plain fused decode instead.  When one layer's KV would fit in the 256 MB last-level cache, the
 pool holds several copies of it and launch r reads copy r mod copies, so that
 the bandwidth figure is HBM's and not the cache's.
