@@ -16,11 +16,14 @@ in HBM.
 The other workloads (``tiny``, ``cb_prefix``, ``long_ctx``,
 ``fp8_{gqa,mqa}_bs{8,16,32}``, ``int8_{gqa,mqa}_bs16``, ``prefix_cache``,
 ``beam_k5``) time one pool layer R times per step ("1 layer
-timed xR").  ``beam_k5`` decodes with the shared-prefix launch
-(``pa_decode_shared_prefix``: groups found and planned once per step with the
-host lengths, every beam group folded, so one workgroup per group and KV
-head reads the common prompt once and then each beam's own tokens);
-``--shared-prefix-min 0`` times the plain fused decode instead.  When one layer's KV would fit in the 256 MB last-level cache, the
+timed xR").  ``beam_k5`` and ``prefix_cache`` decode with the shared-prefix
+launch (``pa_decode_shared_prefix``: groups found and planned once per step
+with the host lengths; every beam group folds, so one workgroup per group
+and KV head reads the common prompt once and then each beam's own tokens;
+the cached system prompts are read once per group of requests, and the
+requests' own tokens run as private pieces, longest first, merged by a
+second launch); ``--shared-prefix-min 0`` times the plain fused decode
+instead.  When one layer's KV would fit in the 256 MB last-level cache, the
 pool holds several copies of it and launch r reads copy r mod copies, so that
 the bandwidth figure is HBM's and not the cache's.
 
@@ -73,13 +76,14 @@ MULTI_TOKEN_WORKLOADS = ("prefill_chunks", "mixed_batch")
 # the bytes that must come from HBM, each shared block once.
 SHARING_WORKLOADS = ("cb_prefix", "prefix_cache", "beam_k5")
 # Shared-prefix decode by default where it was measured faster than the plain
-# fused decode: the beams share 2040 of about 2060 tokens.  prefix_cache and
-# cb_prefix ran slower with it on MI355X: prefix_cache's shared pass (1024
-# shared tokens of 1088-2048) costs more than the re-reads it saves, which
-# the L2 serves; cb_prefix shares 192 tokens, under the 256-token minimum, so
-# only the private pass runs, a single pass per sequence, slower than the
-# plain decode's split schedule on its 129-2560-token mix.
-SHARED_PREFIX_DEFAULT = {"beam_k5": 256}
+# fused decode on MI355X (µs per launch): beam_k5, whose beams share 2040 of
+# about 2060 tokens and fold (51.9 against 88.0), and prefix_cache, whose
+# requests share 1024-token system prompts and whose private pieces run
+# longest first (129.3 against 135.8).  cb_prefix shares only 192 tokens
+# among 100 of its 256 sequences and ran slower with it (163.6 against
+# 147.5): the other sequences' pieces share the launch with the shared
+# items' larger register budget.
+SHARED_PREFIX_DEFAULT = {"beam_k5": 256, "prefix_cache": 256}
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 
 
@@ -769,7 +773,7 @@ def main(argv=None):
     ap.add_argument("--shared-prefix-min", type=int, default=None,
                     help="for the workloads whose sequences share blocks: decode with pa_decode_shared_prefix, "
                          "grouping sequences that share at least this many leading tokens (0 = plain fused "
-                         "decode; default 256 for beam_k5, 0 for the others)")
+                         "decode; default 256 for beam_k5 and prefix_cache, 0 for cb_prefix)")
     ap.add_argument("--shared-prefix-chunk", type=int, default=0,
                     help="shared tokens per shared-prefix work item (a multiple of 64; 0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -1164,6 +1164,13 @@ int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, 
     }
   }
   if ((n_items + num_seqs) * p->kv_heads > 0x7FFFFFFF) return fail(PA_ERR_INVALID, "too many workgroups");
+  if (lens) {
+    // Longest own part first, as pa_order_longest_first does for the plain
+    // decode: the last workgroups to start are then the short ones.
+    std::stable_sort(priv, priv + n_priv, [&](int32_t x, int32_t y) {
+      return static_cast<int64_t>(lens[x]) - starts[x] > static_cast<int64_t>(lens[y]) - starts[y];
+    });
+  }
   t.insert(t.end(), items.begin(), items.end());
   out->n_items = n_items;
   out->n_slots = slots;
