@@ -370,3 +370,62 @@ def test_beam_k5_full_size_in_the_benchmark_configuration():
     ref = attention.decode(st, 0, q.cpu().numpy()[sample], tables[sample], lens[sample])
     assert_close(out[sample], ref, "fp16", "beam_k5 full size, sampled beams")
     assert pool.device_status() == 0
+
+
+def test_prefix_cache_full_size_in_the_benchmark_configuration():
+    """The benchmark's prefix_cache step at full size: 256 requests on four
+    1024-token system prompts with 64-1024-token suffixes, created through the
+    prefix cache (only uncached tokens written), one appended token per
+    request, groups planned with the host lengths (the private pieces longest
+    first) and the fused shared-prefix call; 12 sampled requests (every query
+    head) match the oracle.  K/V of token id x at position t: row
+    (131 x + t) of a seeded table, so equal prefixes carry equal K/V."""
+    from workloads import prefix_cache_prompts, workload
+    w = workload("prefix_cache")
+    e = w.extra
+    hq, hkv, bs, D = w.q_heads, w.kv_heads, w.block_size, w.head_dim
+    say("prefix_cache full size, shared-prefix decode")
+    prompts = prefix_cache_prompts(w.seed, w.num_seqs, e["systems"], e["system_tokens"], e["suffix"])
+    rows_n = 8192
+    table_k = normal_fp16((rows_n, hkv, D), w.seed, 700, "cuda")
+    table_v = normal_fp16((rows_n, hkv, D), w.seed, 701, "cuda")
+    nb = w.num_blocks + 2 * w.num_seqs
+    pool = pa.PagedKVPool(1, hkv, D, bs, nb, free_order=free_order(w.seed, nb))
+    pool.pool_bytes().fill_(0xFF)
+
+    def rows(toks, start):
+        idx = torch.tensor([(int(x) * 131 + start + i) % rows_n for i, x in enumerate(toks)], device="cuda")
+        return table_k[idx].contiguous(), table_v[idx].contiguous()
+
+    seqs = []
+    for toks in prompts:
+        s, cached, slots = pool.seq_create_cached(toks)
+        if len(slots):
+            k, v = rows(toks[cached:], cached)
+            pool.write_kv(0, k, v, torch.from_numpy(slots).cuda())
+        seqs.append(s)
+    assert pool.stats()["cache_hits"] > 0
+    new_ids = [90_000 + i for i in range(len(seqs))]
+    slots, _ = pool.alloc_batch(seqs, [1] * len(seqs))
+    ctx = [list(p) + [t] for p, t in zip(prompts, new_ids)]
+    kn = torch.stack([rows([t], len(c) - 1)[0][0] for t, c in zip(new_ids, ctx)]).contiguous()
+    vn = torch.stack([rows([t], len(c) - 1)[1][0] for t, c in zip(new_ids, ctx)]).contiguous()
+    mb = max(pool.seq_len(s)[1] for s in seqs)
+    tables, lens = pool.block_tables(seqs, mb)
+    grp = pool.shared_prefix_groups(tables, lens, 256)
+    assert sum(1 for x in grp[2] if x > 0) == e["systems"]
+    plan = pool.shared_prefix_plan(len(seqs), hq, mb, grp, lens=lens)
+    assert plan.plan.num_private == len(seqs) and plan.plan.num_items > 0
+    q = normal_fp16((len(seqs), hq, D), w.seed, 702, "cuda")
+    out = pool.decode_shared_prefix(0, q, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(), plan,
+                                    k_new=kn, v_new=vn,
+                                    slot_mapping=torch.from_numpy(np.asarray(slots, np.int32)).cuda())
+    sample = list(range(0, len(seqs), len(seqs) // 12))[:12]
+    st = OracleKVStore(1, nb, hkv, bs, D)
+    for i in sample:
+        pos = np.arange(int(lens[i]))
+        k, v = rows(ctx[i], 0)
+        st.write(0, k.cpu().numpy(), v.cpu().numpy(), tables[i][pos // bs] * bs + pos % bs)
+    ref = attention.decode(st, 0, q.cpu().numpy()[sample], tables[sample], lens[sample])
+    assert_close(out[sample], ref, "fp16", "prefix_cache full size, sampled requests")
+    assert pool.device_status() == 0
