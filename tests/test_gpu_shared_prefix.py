@@ -429,3 +429,37 @@ def test_prefix_cache_full_size_in_the_benchmark_configuration():
     ref = attention.decode(st, 0, q.cpu().numpy()[sample], tables[sample], lens[sample])
     assert_close(out[sample], ref, "fp16", "prefix_cache full size, sampled requests")
     assert pool.device_status() == 0
+
+
+@pytest.mark.parametrize("fold", [False, True])
+def test_shared_run_past_a_context_is_flagged(fold):
+    """Host-forced contract violation: a group claims more shared blocks
+    than one member's context holds (the plan cannot see device lengths;
+    with fold, stale host lengths make the plan fold the group).  The launch
+    flags PA_DEV_BAD_LEN (the shared pieces read the padding entries of the
+    shortest member's table as block 0, flagged too, so that group's rows
+    are undefined), and the other groups and the singletons still match the
+    oracle."""
+    say("shared run past a context", "folded" if fold else "pieces")
+    t = build_tree([(640, [3, 40, 17]), (300, [5, 9])], [100, 900], 32, 8, 16, seed=464_400)
+    g = t.pool.shared_prefix_groups(t.tables_np, t.lens_np, 256)
+    members, gstart, shared = [a.copy() for a in g]
+    gi = int(np.argmax(shared))  # the 640-token group: 40 shared blocks
+    mem = members[gstart[gi]:gstart[gi + 1]]
+    shortest = min(int(t.lens_np[m]) for m in mem)
+    shared[gi] = (shortest + 15) // 16 + 1  # past the shortest member's last token
+    assert shared[gi] <= t.mb
+    lens_host = t.lens_np.copy()
+    if fold:
+        lens_host[mem] = shared[gi] * 16 + 8  # stale lengths: the plan folds the group
+    plan = t.pool.shared_prefix_plan(len(t.batch), 32, t.mb, (members, gstart, shared), lens=lens_host if fold else None)
+    q = normal_fp16((len(t.batch), 32, 128), 464_400, 3, "cuda")
+    t.pool.device_status(clear=True)
+    out = t.pool.decode_shared_prefix(0, q, t.tables, t.lens, plan)
+    torch.cuda.synchronize()
+    status = t.pool.device_status(clear=True)
+    assert status & pa.PA_DEV_BAD_LEN
+    ok = [i for i, s in enumerate(t.batch) if i not in set(int(m) for m in mem)]
+    st = oracle_store(t)
+    ref = attention.decode(st, 0, q.cpu().numpy()[ok], t.tables_np[ok], t.lens_np[ok])
+    assert_close(out[ok], ref, "fp16", "sequences outside the broken group")
