@@ -137,6 +137,17 @@ struct StepRegs {
   u32x4 v[kLoads];
 };
 
+// Device-memory (global address space) bytes.
+using GlobalBytes = const __attribute__((address_space(1))) uint8_t*;
+
+// A wave-uniform device-memory pointer, moved to scalar registers.
+__device__ inline GlobalBytes uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<GlobalBytes>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // The per-wave engine: operands, softmax state and the load / compute of one
 // 16-token step of one (sequence, KV head).  Lane (gq, n): gq = lane / 16 is
 // its row group, n = lane % 16 its head column.  FUSE: the launch also
@@ -451,10 +462,12 @@ struct WaveDecoder {
   }
 
   // Block ids of the step starting at token tb (scalar loads; the table index
-  // is clamped to the table width, so any tb is safe to ask for).
-  __device__ void fetch_ids(int64_t tb, int& lo, int& hi) const {
-    const int64_t b = tb / BS;
-    const int64_t last = max_blocks - 1;
+  // is clamped to the table width, so any tb is safe to ask for).  Token
+  // positions are non-negative and below 2^31: 32-bit arithmetic keeps the
+  // index math and the clamp on the scalar unit.
+  __device__ void fetch_ids(int tb, int& lo, int& hi) const {
+    const int b = static_cast<int>(static_cast<uint32_t>(tb) / BS);
+    const int last = max_blocks - 1;
     lo = trow[b < last ? b : last];
     hi = 0;
     if constexpr (BS == 8) hi = trow[b + 1 < last ? b + 1 : last];
@@ -479,6 +492,11 @@ struct WaveDecoder {
   static __device__ u32x4 ld16(const uint8_t* a) {
     if constexpr (CACHED) return *reinterpret_cast<const u32x4*>(a);
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a));
+  }
+  static __device__ u32x4 ld16(GlobalBytes a) {
+    using GlobalChunk = const __attribute__((address_space(1))) u32x4*;
+    if constexpr (CACHED) return *reinterpret_cast<GlobalChunk>(a);
+    return __builtin_nontemporal_load(reinterpret_cast<GlobalChunk>(a));
   }
 
   // Loads of the step starting at token tb, whose blocks are id_lo (and
@@ -506,8 +524,10 @@ struct WaveDecoder {
         koff_sub = static_cast<uint64_t>(sub) * 16 * kD * ELEM;
         voff_sub = static_cast<uint64_t>(sub) * 4 * 16 * X * ELEM;
       }
-      const uint8_t* kp = kbase + static_cast<uint64_t>(b) * block_stride + koff_sub;
-      const uint8_t* vp = vbase + static_cast<uint64_t>(b) * block_stride + voff_sub;
+      // The tiles' base addresses are wave-uniform: held in scalar registers,
+      // each load takes the lane's 32-bit offset (no 64-bit vector address math).
+      const GlobalBytes kp = uniform_ptr(kbase + static_cast<uint64_t>(b) * block_stride + koff_sub);
+      const GlobalBytes vp = uniform_ptr(vbase + static_cast<uint64_t>(b) * block_stride + voff_sub);
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         if constexpr (DO_K) r.k[j] = ld16(kp + koff[j]);
@@ -1355,7 +1375,7 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
     const int jw = w * tq;  // this wave's first token within the item
     if (jw >= nq_item) return;  // no tokens for this wave (no barrier on this path)
     const int nq = (nq_item - jw) < tq ? (nq_item - jw) : tq;
-    auto raw_tok = [](int j) -> int64_t { return 16ll * j; };
+    auto raw_tok = [](int j) -> int { return 16 * j; };
     multi_token_setup(dec, T - n_i + j0 + jw, nq, group, row0 + jw, kmax);
     const int n = (kmax + 15) >> 4;
     const int last_tok = ((kmax - 1) >> 4) << 4;
@@ -1375,7 +1395,7 @@ void multi_token_kernel(PoolGeom g, DecodeLaunch p) {
   } else {
     WaveDecoder<D, KIND, BS, NT, false, true, false> dec;  // each key tile read once
     dec.bind(g, p, seq, kvh, lane);
-    auto raw_tok = [&](int j) -> int64_t { return 16ll * (w + kWaves * j); };
+    auto raw_tok = [&](int j) -> int { return 16 * (w + kWaves * j); };
     multi_token_setup(dec, T - n_i + j0, nq_item, group, row0, kmax);
     const int n = (kmax + 16 * kWaves - 1) / (16 * kWaves);
     const int last_tok = ((kmax - 1) >> 4) << 4;
@@ -1543,7 +1563,7 @@ __device__ __forceinline__ void shared_body(const PoolGeom& g, const DecodeLaunc
   dec.mt_row0 = 0;
   dec.mt_ncols = ncols;
   dec.mt_rowmap = mem;
-  auto raw_tok = [&](int j) -> int64_t { return t0 + 16ll * (w + kWaves * j); };
+  auto raw_tok = [&](int j) -> int { return t0 + 16 * (w + kWaves * j); };
   const int n = (t1 - t0 + 16 * kWaves - 1) / (16 * kWaves);
   const int last_tok = ((t1 - 1) >> 4) << 4;
   auto real = [&](int j) { return raw_tok(j) < t1; };
