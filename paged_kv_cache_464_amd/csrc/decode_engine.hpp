@@ -285,17 +285,20 @@ struct WaveDecoder {
         qop[nt][u] = valid ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
-    if constexpr (MULTI) {
-      // The pair softmax needs qk_mul > 0: a negative scale's sign moves into
-      // q (exact in fp16).  A zero scale is refused by the host.
-      if (qk_mul < 0.0f) {
-        qk_mul = -qk_mul;
+    // The softmax needs qk_mul > 0, so that the largest raw score times
+    // qk_mul is the largest logit: a negative scale's sign moves into q
+    // (exact in fp16), and a zero scale (decode only; multi-token attention
+    // refuses it) becomes 2^-100, which leaves every logit at most 2^-60 from
+    // 0, i.e. every exponential exactly 1 in fp32, and keeps masked scores at
+    // -inf.
+    if (qk_mul < 0.0f) {
+      qk_mul = -qk_mul;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int u = 0; u < NKU; ++u) qop[nt][u] = -qop[nt][u];
-      }
+        for (int u = 0; u < NKU; ++u) qop[nt][u] = -qop[nt][u];
     }
+    qk_mul = fmaxf(qk_mul, 0x1p-100f);
   }
 
   // Fused scatter (owner wave only).  Before the stream, the lanes that will
@@ -642,17 +645,10 @@ struct WaveDecoder {
     }
   }
 
-  // Attention over the 16 tokens tb .. tb+15 held in r (those >= T masked).
-  // Scales one column's four raw scores to base-2 logits, masks those past
-  // the context, and returns the column's maximum over the step's 16 tokens.
-  __device__ float scale_mask(f32x4& sc, bool tail, int valid_here) const {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float x = sc[e] * qk_mul;
-      if (tail && e >= valid_here) x = -__builtin_inff();
-      sc[e] = x;
-    }
-    return max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+  // The largest base-2 logit of one column over the step's 16 tokens, from
+  // its four raw scores in each lane (qk_mul > 0).
+  __device__ float col_max(const f32x4& sc) const {
+    return max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))) * qk_mul;
   }
 
   // Moves column tile nt's reference to m_new, rescaling what it holds.
@@ -674,13 +670,15 @@ struct WaveDecoder {
     for (int nt = 0; nt < NT; ++nt) l_part[nt] = lacc[nt][0] * 0.25f;
   }
 
-  // INJ: the step may hold the fused new token (only the last scheduled
-  // steps of a stream are compiled with it, so the steady-state loop carries
-  // none of its code).
-  template <bool INJ = false>
+  // LAST: one of the stream's last kDepth scheduled steps, the only ones that
+  // can reach the end of the context (the step holding token T - 1 is the
+  // last real one) and hold the fused new token; the other steps are
+  // compiled without the tail mask and the injection.
+  template <bool LAST = false>
   __device__ void compute(Regs& r, int tb) {
+    static_assert(!MULTI, "multi-token steps go through the pair functions");
     bool new_here = false;  // step holds the fused new token, to be used
-    if constexpr (FUSE && INJ) {
+    if constexpr (FUSE && LAST) {
       if (knew && tb + 16 >= T && new_slot_ok()) {
         new_here = true;
         owns_new = true;
@@ -691,13 +689,23 @@ struct WaveDecoder {
     // S^T = K Q^T
     f32x4 s[NT];
     raw_scores(r.k, s);
-    // Scores of tokens tb + 4*gq + e for head column n; mask the tail (MULTI:
-    // each column's causal limit).  vtail / valid_here: tokens of this lane's
-    // 4 that exist (for the V mask).
-    const bool vtail = tb + 16 > T;
+    // Scores of tokens tb + 4*gq + e for head column n; mask the tail.
+    // vtail / valid_here: tokens of this lane's 4 that exist (also for the
+    // V mask).  The tail is masked on the raw scores
+    // (the slots past the context may hold anything), only in the last steps
+    // (as selects: a branch straight after the score MFMAs has left the
+    // compiler's wait states for their results out of the path that skips
+    // it); each probability is then one exp2(fma(s, qk_mul, -ref)).
+    const bool vtail = LAST && tb + 16 > T;
     const int valid_here = T - (tb + 4 * gq);
-    const bool tail = MULTI ? tb + 16 > lim_min : vtail;
-    auto valid_col = [&](int nt) { return MULTI ? lim[nt] - (tb + 4 * gq) : valid_here; };
+    if constexpr (LAST) {
+      const int vh = vtail ? valid_here : 4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e >= vh) s[nt][e] = -__builtin_inff();
+    }
     if constexpr (kLazy) {
       // The reference moves only when a score exceeds it by kRescaleSlack or
       // more, so exponentials stay below 2^kRescaleSlack (exact in fp16 and
@@ -706,7 +714,7 @@ struct WaveDecoder {
       bool need = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float m = scale_mask(s[nt], tail, valid_col(nt));
+        const float m = col_max(s[nt]);
         m_true[nt] = fmaxf(m_true[nt], m);
         need |= m - m_run[nt] >= kRescaleSlack;
       }
@@ -723,14 +731,7 @@ struct WaveDecoder {
       bool grow = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = s[nt][e] * qk_mul;
-          if (tail && e >= valid_col(nt)) x = -__builtin_inff();
-          s[nt][e] = x;
-        }
-        const float m = max_across_rows(fmaxf(fmaxf(s[nt][0], s[nt][1]), fmaxf(s[nt][2], s[nt][3])));
-        mnew[nt] = fmaxf(m_run[nt], m);
+        mnew[nt] = fmaxf(m_run[nt], col_max(s[nt]));
         grow |= mnew[nt] > m_run[nt];
       }
       if (__any(grow)) {
@@ -742,15 +743,13 @@ struct WaveDecoder {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float pe[4];
-      // MULTI: a column may have seen only masked keys so far (reference
-      // -inf); its scores here are all -inf too and must give 0, not NaN.
-      const float mref = (MULTI && m_run[nt] == -__builtin_inff()) ? 0.0f : m_run[nt];
+      const float mref = m_run[nt];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(s[nt][e] - mref);
+      for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(__builtin_fmaf(s[nt][e], qk_mul, -mref));
       l_part[nt] += (pe[0] + pe[1]) + (pe[2] + pe[3]);
       pop[nt] = f16x4{(_Float16)pe[0], (_Float16)pe[1], (_Float16)pe[2], (_Float16)pe[3]};
     }
-    if constexpr (FUSE && INJ) {
+    if constexpr (FUSE && LAST) {
       if (new_here) {
         inject_v(r);
         store_new_v(r);
@@ -826,7 +825,7 @@ __device__ inline void stream_steps(Dec& dec, int n, TokOf tok_of, Real real, Fi
     cur_hi[d] = f.hi[d + D - 1];
   }
   // One block of D scheduled steps; LAST: the final block, whose steps may
-  // hold the fused new token.
+  // reach the end of the context and hold the fused new token.
   auto block = [&](int j, auto last) {
 #pragma unroll
     for (int d = 0; d < D; ++d) dec.fetch_ids(tok_at(j + d + 2 * D - 1), nxt_lo[d], nxt_hi[d]);
@@ -844,12 +843,8 @@ __device__ inline void stream_steps(Dec& dec, int n, TokOf tok_of, Real real, Fi
       cur_hi[d] = nxt_hi[d];
     }
   };
-  if constexpr (Dec::kFuse) {
-    for (int j = 0; j < n_pad - D; j += D) block(j, std::false_type{});
-    block(n_pad - D, std::true_type{});
-  } else {
-    for (int j = 0; j < n_pad; j += D) block(j, std::false_type{});
-  }
+  for (int j = 0; j < n_pad - D; j += D) block(j, std::false_type{});
+  block(n_pad - D, std::true_type{});
 }
 
 // MULTI: runs steps j = 0 .. n-1 (padded to pairs) two at a time.  tok_of
