@@ -423,9 +423,10 @@ int pa_write_kv_decode(pa_pool* pool, int32_t layer, const void* k_new, const vo
  * group's shared blocks (0: no shared pass), *num_groups_out.
  *
  * pa_shared_prefix_plan checks such groups (host arrays; members a
- * permutation of 0..num_seqs-1, group_start[0] = 0 and group_start[num_groups]
- * = num_seqs, shared_blocks[g] * block_size a multiple of 16 and at most
- * max_blocks) for a batch of num_seqs sequences with num_q_heads query heads
+ * permutation of 0..num_seqs-1, group_start non-decreasing from
+ * group_start[0] = 0 to group_start[num_groups] = num_seqs, each
+ * shared_blocks[g] at most max_blocks and times block_size a multiple of
+ * 16) for a batch of num_seqs sequences with num_q_heads query heads
  * and block tables max_blocks wide, and uploads on `stream` the group list
  * into `workspace` (device memory of
  * pa_decode_shared_prefix_workspace_bytes() bytes for the same groups and

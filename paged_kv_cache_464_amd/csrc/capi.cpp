@@ -1060,10 +1060,17 @@ struct SharedTail {
 int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
                        const int32_t* members, const int32_t* group_start, const int32_t* shared_blocks,
                        int32_t num_groups, int32_t chunk_tokens, const int32_t* lens, SharedTail* out) {
-  if (num_groups < 0 || (num_seqs > 0 && (!members || !group_start || !shared_blocks)))
+  if (num_groups < 0 || num_seqs < 0) return fail(PA_ERR_INVALID, "num_groups and num_seqs must be >= 0");
+  if ((num_seqs > 0 && !members) || ((num_seqs > 0 || num_groups > 0) && (!group_start || !shared_blocks)))
     return fail(PA_ERR_INVALID, "members, group_start and shared_blocks are required");
-  if (num_seqs > 0 && (group_start[0] != 0 || group_start[num_groups] != num_seqs))
-    return fail(PA_ERR_INVALID, "group_start must run from 0 to num_seqs");
+  // group_start must be a non-decreasing run from 0 to num_seqs before any
+  // group's members are read.
+  if (num_seqs > 0 || num_groups > 0) {
+    if (group_start[0] != 0 || group_start[num_groups] != num_seqs)
+      return fail(PA_ERR_INVALID, "group_start must run from 0 to num_seqs");
+    for (int32_t g = 0; g < num_groups; ++g)
+      if (group_start[g + 1] < group_start[g]) return fail(PA_ERR_INVALID, "group_start decreases at group %d", g);
+  }
   if (chunk_tokens < 0 || chunk_tokens % 64 != 0)
     return fail(PA_ERR_INVALID, "chunk_tokens %d must be 0 (library choice) or a positive multiple of 64",
                 chunk_tokens);
@@ -1082,7 +1089,6 @@ int shared_groups_tail(const pa_pool* p, int32_t num_seqs, int32_t num_q_heads, 
   int64_t base_items = 0, max_ts = 0;
   for (int32_t g = 0; g < num_groups; ++g) {
     const int32_t a = group_start[g], b = group_start[g + 1];
-    if (b < a) return fail(PA_ERR_INVALID, "group_start decreases at group %d", g);
     const int64_t ts = static_cast<int64_t>(shared_blocks[g]) * p->block_size;
     if (shared_blocks[g] < 0 || shared_blocks[g] > max_blocks || ts % 16 != 0)
       return fail(PA_ERR_INVALID, "shared_blocks[%d] = %d: not a multiple of 16 tokens inside the table", g,

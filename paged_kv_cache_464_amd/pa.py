@@ -430,8 +430,10 @@ def pa_shared_prefix_groups(h, tables, lens, min_shared_tokens=256):
     return members[:n].copy(), gstart[:g + 1].copy(), shared[:g].copy()
 
 
-def _groups_args(groups):
-    members, gstart, shared = (np.ascontiguousarray(np.asarray(a, dtype=np.int32)) for a in groups)
+def _groups_args(groups, num_seqs):
+    members, gstart, shared = (np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1)) for a in groups)
+    if len(members) != num_seqs or len(gstart) != len(shared) + 1:
+        raise ValueError("groups must be (members[num_seqs], group_start[num_groups + 1], shared_blocks[num_groups])")
     ip = lambda a: a.ctypes.data_as(C.POINTER(C.c_int32))
     return (members, gstart, shared), ip(members), ip(gstart), ip(shared), len(shared)
 
@@ -447,7 +449,7 @@ def _lens_arg(lens, num_seqs):
 
 def pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, groups, max_blocks, chunk_tokens=0,
                                             lens=None):
-    keep, mp, gp, sp, ng = _groups_args(groups)
+    keep, mp, gp, sp, ng = _groups_args(groups, num_seqs)
     la, lp = _lens_arg(lens, num_seqs)
     b = C.c_uint64()
     _check(_L().pa_decode_shared_prefix_workspace_bytes(C.c_void_p(h), int(num_seqs), int(num_q_heads), mp, gp,
@@ -469,7 +471,7 @@ def pa_shared_prefix_plan(h, num_seqs, num_q_heads, max_blocks, groups, workspac
     """Checks and uploads the groups (see pa_decode_shared_prefix).  ``lens``:
     host context lengths, which let the plan fold groups whose members have
     few tokens of their own (None: no folding)."""
-    keep, mp, gp, sp, ng = _groups_args(groups)
+    keep, mp, gp, sp, ng = _groups_args(groups, num_seqs)
     la, lp = _lens_arg(lens, num_seqs)
     need = pa_decode_shared_prefix_workspace_bytes(h, num_seqs, num_q_heads, keep, max_blocks, chunk_tokens, la)
     if workspace is None:
