@@ -531,7 +531,9 @@ int pa_order_longest_first(const int32_t* lens, int32_t n, int32_t* order_out);
  *    o[num_seqs][num_q_heads][C][head_dim]  sum_t 2^(s_t - m) v_t / l
  * Chunks at or past ceil(T_i / P) are not written.
  * pa_lse_reduce merges chunks 0 .. ceil(T_i/P)-1 into out:
- *    out = sum_c w_c o_c / sum_c w_c,  w_c = l_c * 2^(m_c - max_c m_c). */
+ *    out = sum_c w_c o_c / sum_c w_c,  w_c = l_c * 2^(m_c - max_c m_c).
+ * Both take the workspace 16-byte aligned and out 8-byte aligned, as
+ * pa_decode does (PA_ERR_INVALID otherwise). */
 int pa_decode_partials(pa_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
                        const int32_t* block_tables, int32_t max_blocks,
                        const int32_t* context_lens, int32_t num_seqs, const int32_t* seq_order,

@@ -944,6 +944,8 @@ int pa_lse_reduce(pa_pool* p, const void* workspace, uint64_t workspace_bytes,
   if (!workspace || workspace_bytes < pl.ws_bytes || !out || !context_lens)
     return fail(PA_ERR_INVALID, "workspace of %llu bytes, out and context_lens needed",
                 static_cast<unsigned long long>(pl.ws_bytes));
+  if (misaligned(workspace, 16) || misaligned(out, 8))
+    return fail(PA_ERR_INVALID, "the workspace must be 16-byte and out 8-byte aligned, as for pa_decode");
   const pa::DecodeLaunch d = make_launch(0, nullptr, num_q_heads, nullptr, max_blocks, context_lens,
                                          num_seqs, nullptr, 1.0f, pl, out, const_cast<void*>(workspace));
   const hipError_t e = pa::launch_lse_reduce(p->geom, d, static_cast<hipStream_t>(stream));

@@ -263,6 +263,10 @@ def test_partials_match_oracle_split(dtype, P):
     pa.pa_decode_partials(c.pool.handle, 0, c.q, c.tables, c.lens_dev, P, workspace=ws)
     pa.pa_lse_reduce(c.pool.handle, ws, c.lens_dev, 16, c.max_blocks, P, out)
     assert_close(out, oracle_decode(c, range(len(lens))), dtype, "reduce")
+    # a misaligned workspace is refused on the host, before any launch
+    big = torch.empty(ws.numel() + 64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pa.PAError):
+        pa.pa_lse_reduce(c.pool.handle, big[8:8 + ws.numel()], c.lens_dev, 16, c.max_blocks, P, out)
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "fp8"])
