@@ -67,7 +67,7 @@ KERNEL_SOURCES.append(os.path.join(ROOT, "paged_kv_cache_464_amd", "build.py")) 
 LLC_BYTES = 256 << 20  # MI355X Infinity Cache
 PREFIX_ROW_TABLE = 1 << 16  # distinct K/V rows of the prefix_cache workload
 CPU_SAMPLE_TOKENS = 1 << 18  # bound on the context tokens the CPU oracle is given
-BENCH_WORKLOADS = ["gqa_32x4096", "tiny", "cb_prefix", "long_ctx",
+BENCH_WORKLOADS = ["gqa_32x4096", "gqa_32x4096_tp8", "tiny", "cb_prefix", "long_ctx",
                    "fp8_gqa_bs8", "fp8_gqa_bs16", "fp8_gqa_bs32",
                    "fp8_mqa_bs8", "fp8_mqa_bs16", "fp8_mqa_bs32", "int8_gqa_bs16", "int8_mqa_bs16",
                    "prefix_cache", "beam_k5", "prefill_chunks", "mixed_batch"]

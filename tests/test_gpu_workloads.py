@@ -44,6 +44,35 @@ def test_gqa_32x4096_full_pool_sampled():
     assert c.pool.device_status() == 0
 
 
+def test_gqa_32x4096_tp8_share_sampled():
+    """One GPU's share of gqa_32x4096 under 8-way tensor parallelism: 32 layers
+    of one KV head and its 4 query heads, 32 x 4096 tokens, in layer 31 of a
+    pool whose other bytes hold NaN.  Every schedule against the oracle, and
+    the fused step the benchmark times equal to write + decode bit for bit."""
+    w = workload("gqa_32x4096_tp8")
+    say("gqa_32x4096_tp8 full pool")
+    c = build_case(w.context, w.q_heads, w.kv_heads, w.block_size, w.num_blocks, w.seed,
+                   layers=w.layers, layer=31, poison=True)
+    sample = [0, 13, 31]
+    ref = oracle_decode(c, sample)
+    wide, _ = c.pool.block_tables(c.seqs, 258)
+    wide = torch.from_numpy(wide).cuda()
+    for tables, mode in ((wide, 0), (c.tables, 0), (c.tables, -1), (c.tables, 512), (c.tables, 64)):
+        out = c.pool.decode(31, c.q, tables, c.lens_dev, partition_tokens=mode)
+        assert_close(out[sample], ref, "fp16", f"tp8 P={mode}")
+    last = [int(c.offsets[i + 1] - 1) for i in range(len(w.context))]
+    last_slots = torch.tensor([int(s[-1]) for s in c.slots], dtype=torch.int32, device="cuda")
+    k_new, v_new = c.k[last].contiguous(), c.v[last].contiguous()
+    plain = c.pool.decode(31, c.q, wide, c.lens_dev, partition_tokens=0)
+    nan = torch.full((len(last), 1, 128), float("nan"), dtype=torch.float16, device="cuda")
+    c.pool.write_kv(31, nan, nan, last_slots)
+    fused = c.pool.write_kv_decode(31, k_new, v_new, last_slots, c.q, wide, c.lens_dev, partition_tokens=0)
+    assert torch.equal(fused, plain)
+    k2, v2 = c.pool.gather_kv(31, last_slots)
+    assert torch.equal(k2, k_new) and torch.equal(v2, v_new)
+    assert c.pool.device_status() == 0
+
+
 def test_cb_prefix_workload_all_sequences():
     """256 sequences: 100 forks of a 200-token prefix (copy-on-write on first append)
     plus 156 prompts, round-robin appends; every sequence checked."""

@@ -56,6 +56,10 @@ WORKLOADS = {
     "tiny": Workload(1, "tiny", 1, 8, 2, 128, 16, "fp16", 8, 2, context=(40, 20)),
     "gqa_32x4096": Workload(2, "gqa_32x4096", 32, 32, 8, 128, 16, "fp16", 8192, 32,
                             context=(4096,) * 32),
+    # One GPU's share of gqa_32x4096 when its KV heads are split over 8 GPUs
+    # (tensor parallelism): every layer's one KV head and its 4 query heads.
+    "gqa_32x4096_tp8": Workload(2, "gqa_32x4096_tp8", 32, 4, 1, 128, 16, "fp16", 8192, 32,
+                                context=(4096,) * 32),
     "cb_prefix": Workload(3, "cb_prefix", 1, 32, 8, 128, 16, "fp16", 16384, 256, repeats=32),
     "long_ctx": Workload(4, "long_ctx", 1, 64, 8, 128, 16, "fp16", 65536, 8,
                          context=(131072,) * 8, partition_tokens=512, repeats=80),
