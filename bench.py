@@ -801,15 +801,23 @@ def main(argv=None):
 
     multi = args.workload in MULTI_TOKEN_WORKLOADS
     bench = MultiTokenBench(args.workload, args) if multi else DecodeBench(args.workload, args)
-    for _ in range(args.warmup):
+    stamp = min(max(args.stamp_steps, 1), args.steps)
+    # The launch timing's events are created and first recorded in the last
+    # warm-up step (its figures are dropped): creating them on the host inside
+    # the timed steps held the launches back.
+    if args.warmup == 0:
+        pa.pa_profile_begin(bench.pool.handle, stamp * bench.R, args.time_every)
+    for i in range(args.warmup):
+        if i == args.warmup - 1:
+            pa.pa_profile_begin(bench.pool.handle, stamp * bench.R, args.time_every)
         bench.step()
     torch.cuda.synchronize()
+    pa.pa_profile_end(bench.pool.handle)
     bench.kv_bytes_log.clear()
     bench.tables_log.clear()
     bench.lens_log.clear()
     if hasattr(bench, "sp_groups_log"):
         bench.sp_groups_log.clear()
-    stamp = min(max(args.stamp_steps, 1), args.steps)
     gc.collect()
     gc.disable()  # no collector pauses inside the timed steps
     # One event per step boundary on the launch stream: per-step GPU-timeline
@@ -828,7 +836,8 @@ def main(argv=None):
     gc.enable()
     step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
     step_stats = {"median": float(np.median(step_ms)), "min": float(step_ms.min()),
-                  "max": float(step_ms.max()), "steps": args.steps,
+                  "max": float(step_ms.max()), "slowest": int(step_ms.argmax()), "steps": args.steps,
+                  "each": [round(float(t), 4) for t in step_ms],
                   "clock": "HIP events at the step boundaries on the launch stream"}
     prof = pa.pa_profile_end(bench.pool.handle)
     status = bench.pool.device_status()
