@@ -57,6 +57,12 @@ def test_pool_bytes_match_page_arithmetic():
     h8 = pa.pa_pool_create(32, 8, 128, 16, pa.PA_DTYPE_FP8_E4M3, 32 * 4096 // 16)
     assert pa.pa_pool_info_get(h8)["kv_bytes"] * 2 == 17179869184  # fp8 halves the KV bytes
     pa.pa_pool_destroy(h8)
+    # One GPU's share under tensor parallelism over 8 GPUs (one KV head each):
+    # an eighth of the bytes, 16384 per token.
+    h1 = pa.pa_pool_create(32, 1, 128, 16, pa.PA_DTYPE_FP16, 32 * 4096 // 16)
+    assert pa.pa_pool_info_get(h1)["kv_bytes"] * 8 == 17179869184
+    assert pa.pa_pool_info_get(h1)["kv_bytes"] // (32 * 4096) == 16384
+    pa.pa_pool_destroy(h1)
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32])
