@@ -203,7 +203,7 @@ def _lens(seed, n, hi):
 
 @pytest.mark.parametrize("dtype", ["fp16", "fp8", "int8"])
 @pytest.mark.parametrize("bs", [8, 16, 32])
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (32, 1), (8, 8), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (32, 1), (8, 8), (16, 2), (4, 1)])
 def test_decode_matrix(dtype, bs, hq, hkv):
     seed = 1000 + bs * 7 + hq * 3 + hkv + {"fp16": 0, "fp8": 500, "int8": 800}[dtype]
     lens = _lens(seed, 6, 700)
