@@ -1044,8 +1044,16 @@ __device__ __forceinline__ void decode_body(const PoolGeom& g, const DecodeLaunc
   if constexpr (kOne) {
     unit = bid;
   } else if constexpr (MODE == kSplit4) {
-    unit = bid / p.waves_per_unit;
-    r = static_cast<int>(bid % p.waves_per_unit);
+    // Workgroup b runs on XCD b mod 8: the runs of each block of eight
+    // consecutive units are numbered so that all runs of a unit share one
+    // XCD (its query and table row are then fetched by one L2), and units
+    // keep their order between blocks.
+    const int64_t wpu = p.waves_per_unit;
+    const int64_t blk = static_cast<int64_t>(bid) / (8 * wpu);
+    const int64_t within = static_cast<int64_t>(bid) % (8 * wpu);
+    const int64_t ub = (num_units - 8 * blk) < 8 ? (num_units - 8 * blk) : 8;
+    unit = 8 * blk + within % ub;
+    r = static_cast<int>(within / ub);
   } else {
     const int64_t v = static_cast<int64_t>(bid) * kWaves + w;
     unit = v / p.waves_per_unit;
